@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of the VDN hybrid attention forward on one MI355X.
+
+One step = one call of vdn_hybrid_attn_fwd (gate GEMM, window/anchor softmax,
+VDA gram / solve / scan / readout, output GEMM) over one batch of seeded
+synthetic bf16 input already resident in HBM.  The default workload is the
+102-latent-frame layer: batch 1, 24 heads, head_dim 128 (D = 3072),
+102 frames x 4032 tokens (411,264 tokens), 5-frame chunks, +-1 chunk, first
+and last frame anchors.
+
+Prints one JSON line: tokens/s and ms per layer call, the dominant kernel's
+roofline fraction (window softmax, MFMA bf16) from HIP events recorded in the
+timed region, per-phase milliseconds, and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hybrid attn fwd tokens/s + ms/layer @102 latent frames; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def frame_key_counts(T, C, W, a0, a1):
+    """Allowed key frames of each query frame under the chunk-window/anchor rule."""
+    counts = []
+    for t in range(T):
+        if (a0 and t == 0) or (a1 and t == T - 1):
+            counts.append(T)
+            continue
+        c = t // C
+        lo, hi = max(0, (c - W) * C), min(T, (c + W + 1) * C)
+        n = hi - lo
+        if a0 and lo > 0:
+            n += 1
+        if a1 and hi < T:
+            n += 1
+        counts.append(n)
+    return counts
+
+
+def window_flops(cfg):
+    """Algorithmic flops of one softmax-branch launch: 2 * d flops for q.k and
+    2 * d for p*v per allowed (query, key) pair; masked pairs are not counted."""
+    pairs_per_head = cfg.tokens_per_frame ** 2 * sum(
+        frame_key_counts(cfg.frames, cfg.chunk_frames, cfg.window_chunks,
+                         cfg.anchor_first, cfg.anchor_last))
+    return 4 * cfg.head_dim * cfg.batch * cfg.heads * pairs_per_head, pairs_per_head
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle, unmodified, timed on a bounded sample of the workload
+    (one head's full forward+backward scans, a sample of readout tokens,
+    softmax rows of an interior and an anchor frame, gate/projection rows),
+    scaled to the whole layer by exact token and head counts."""
+    import numpy as np
+    from oracle import vdn_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    L, D = T * N, cfg.model_dim
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    q, k, v = f64(inp["q"][0, 0]), f64(inp["k"][0, 0]), f64(inp["v"][0, 0])
+    gamma, beta = f64(inp["gamma"][0, 0]), f64(inp["beta"][0, 0])
+    w = np.ones(d)
+
+    t0 = time.perf_counter()
+    sf, sb = O.vda_states(k, v, gamma, beta)
+    t_states = time.perf_counter() - t0
+
+    tmid = min(7, T - 1)
+    R = min(256, N)
+    t0 = time.perf_counter()
+    O.vda_readout(q[tmid, :R], sf[tmid], sb[tmid], w, cfg.rms_eps)
+    t_readout_tok = (time.perf_counter() - t0) / R
+
+    allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+    Rs = min(64, N)
+    t0 = time.perf_counter()
+    O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(tmid * N, tmid * N + Rs))
+    t_win_tok = (time.perf_counter() - t0) / Rs
+    t0 = time.perf_counter()
+    O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(0, Rs))
+    t_anchor_tok = (time.perf_counter() - t0) / Rs
+
+    xr = f64(inp["x"][0, :Rs])
+    wgs, wgl, wos, wol = (f64(inp[n]) for n in ("w_gs", "w_gl", "w_os", "w_ol"))
+    t0 = time.perf_counter()
+    g_s, g_l = O.gates(xr, wgs, wgl)
+    _ = (g_s * xr) @ wos + (g_l * xr) @ wol
+    t_gemm_tok = (time.perf_counter() - t0) / Rs
+
+    n_anchor = (int(cfg.anchor_first) + int(cfg.anchor_last and T > 1)) * N
+    total = B * (H * (t_states + L * t_readout_tok + n_anchor * t_anchor_tok + (L - n_anchor) * t_win_tok)
+                 + L * t_gemm_tok)
+    sample = (f"head 0 of {H}: VDA forward+backward scans over all {T} frames; readout of {R} tokens; "
+              f"softmax of {Rs} tokens of frame {tmid} and {Rs} of anchor frame 0; gates and projections "
+              f"of {Rs} tokens; scaled by exact token/head counts to the B{B} H{H} T{T} N{N} layer "
+              f"(extrapolated layer time {total:.0f} s)")
+    return {"value": B * L / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4, help="workload index (3 or 4 are full layers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from video_diffusion_hybrid_vda_amd import synth, vdn
+
+    cfg = synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    ws = vdn.workspace(shape, vdn.VDN_OP_HYBRID)
+    B, L, D = cfg.batch, cfg.seq_len, cfg.model_dim
+    out = torch.empty(B, L, D, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        vdn.vdn_hybrid_attn_fwd(shape, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"],
+                                inp["beta"], inp["w_gs"], inp["w_gl"], inp["rms_w"], inp["w_os"],
+                                inp["w_ol"], out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    vdn.vdn_timing_start()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = vdn.vdn_timing_stop()
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    flops, pairs = window_flops(cfg)
+    n_attn, attn_ms = phases["window_attn"]
+    attn_avg_ms = attn_ms / max(n_attn, 1)
+    achieved = flops / (attn_avg_ms * 1e-3) / 1e12
+    density = pairs / float(L) ** 2
+    phase_ms = {k: round(v[1] / max(v[0], 1), 3) for k, v in phases.items() if v[0] > 0}
+
+    result = {
+        "metric": METRIC,
+        "value": B * L / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; Q,V,x ~ N(0,1), K rows unit-norm, beta ~ U(0.1,1), gamma ~ U(0.9,1), W ~ N(0,0.02^2))",
+        "config": {"workload": cfg.name, "batch": B, "heads": cfg.heads, "head_dim": cfg.head_dim,
+                   "frames": cfg.frames, "tokens_per_frame": cfg.tokens_per_frame, "tokens": B * L,
+                   "chunk_frames": cfg.chunk_frames, "window_chunks": cfg.window_chunks,
+                   "anchors": "first+last", "softmax_density": round(density, 5)},
+        "roofline": {"bound": "mfma", "kernel": "window_attn", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
+                     "traffic": None},
+        "gpu_ms_per_step": round(gpu_ms_per_step, 3),
+        "phases_ms": phase_ms,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * vdn.h - C ABI of libvdn.so: the Video DeltaNet (VDN) hybrid attention
+ * forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the video-to-video attention of Video DeltaNet as described
+ * in the 10100.com article on the paper (section 方法概述, parts 1-3) and the
+ * hotpaper.ai abstract page "Video DeltaNet: A Video-Native Hybrid Attention
+ * for Livestream Video Generation":
+ *   softmax branch  O_s: one softmax per query token over the keys of its own
+ *                   5-frame VAE chunk and one chunk on each side, plus every
+ *                   token of the first and last latent frame; those two frames
+ *                   attend the whole sequence (part 1);
+ *   linear branch   O_l: Video Delta Attention, a frame-level delta rule
+ *                   S_t = (gamma_t S_{t-1} + B_t)(I + A_t)^-1 with
+ *                   A_t = beta_t K_t^T K_t and B_t = beta_t V_t^T K_t, run as a
+ *                   forward and a backward scan over frames; each direction's
+ *                   readout S_t q goes through RMSNorm and the two are summed
+ *                   (part 2, and the forward-plus-backward scan figure);
+ *   calibration     out = (g_s * O_s) W_os + (g_l * O_l) W_ol with content-
+ *                   dependent sigmoid gates g_s = sigmoid(x W_gs),
+ *                   g_l = sigmoid(x W_gl) (part 3).
+ *
+ * Notation: B batch, H heads, d head_dim, T latent frames, N tokens per frame,
+ * L = T*N tokens, D = H*d model width.  Token l = t*N + n.
+ *
+ * Layouts (all row-major, contiguous, element type = shape->dtype unless
+ * stated otherwise):
+ *   q, k, v           [B, H, T, N, d]   rows of k must be L2-normalised by the
+ *                                       caller (the operator does not do it)
+ *   gamma, beta       [B, H, T]         float32, per-frame decay / write strength
+ *   x                 [B, L, D]         layer input the gates read
+ *   w_gs, w_gl,
+ *   w_os, w_ol        [D, D]            y = x @ W (input dimension first)
+ *   rms_w             [D]               float32 RMSNorm weight (head h uses
+ *                                       rms_w[h*d .. h*d+d-1]); NULL = ones
+ *   gate_s, gate_l    [B, L, D]         gate values already in (0,1); NULL = 1
+ *   out               [B, L, D]
+ *   states            [2, B, H, T, d, d] float32; [0] forward-scan state after
+ *                                       frame t, [1] backward-scan state after
+ *                                       frame t; S is d_v x d_k (row = value dim)
+ *   lse               [B, H, L]         float32 natural-log softmax denominator
+ *                                       of the scaled logits
+ *
+ * Ownership: the caller allocates and owns every buffer, including the device
+ * workspace `ws` whose size vdn_workspace_bytes() returns.  All data pointers
+ * are device pointers (hipMalloc'd or equivalent) except `shape`, which is a
+ * host pointer read before the call returns.  The library allocates no device
+ * memory and keeps no pointer after it returns.
+ *
+ * Execution: every compute entry point validates its arguments on the host,
+ * then enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL =
+ * the null stream) and returns without synchronising.  Outputs are valid once
+ * the stream has been synchronised.  Calls on distinct streams with distinct
+ * buffers may run concurrently.  Inputs and outputs must not overlap.
+ *
+ * Errors: functions return VDN_OK (0) or a negative status; on a negative
+ * status nothing has been enqueued (except VDN_ERR_HIP, raised when a launch
+ * fails), and vdn_last_error() returns a message for the calling thread.
+ * Parameter ranges (beta >= 0 so that I + A_t is positive definite,
+ * 0 <= gamma <= 1) are preconditions: they live in device memory and are not
+ * read back.  NaN/Inf inputs propagate to the outputs; they are not trapped.
+ */
+#ifndef VDN_H
+#define VDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDN_OK 0
+#define VDN_ERR_INVALID_ARG (-1) /* NULL pointer, bad op code, misaligned pointer */
+#define VDN_ERR_BAD_SHAPE (-2)   /* dimension < 1, head_dim not 32/64/128, ... */
+#define VDN_ERR_DTYPE (-3)       /* dtype not VDN_F32 / VDN_BF16 */
+#define VDN_ERR_WORKSPACE (-4)   /* ws NULL or ws_bytes < vdn_workspace_bytes() */
+#define VDN_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
+
+enum vdn_dtype { VDN_F32 = 0, VDN_BF16 = 1 };
+
+enum vdn_op {
+  VDN_OP_HYBRID = 0,      /* vdn_hybrid_attn_fwd    */
+  VDN_OP_VDA_SCAN = 1,    /* vda_scan_fwd           */
+  VDN_OP_WINDOW_ATTN = 2  /* window_anchor_attn_fwd */
+};
+
+typedef struct vdn_shape {
+  int32_t batch;            /* B >= 1 */
+  int32_t heads;            /* H >= 1 */
+  int32_t frames;           /* T >= 1 latent frames */
+  int32_t tokens_per_frame; /* N >= 1 */
+  int32_t head_dim;         /* d in {32, 64, 128} */
+  int32_t chunk_frames;     /* latent frames per VAE temporal chunk (5), >= 1 */
+  int32_t window_chunks;    /* chunks seen on each side of the query chunk (1), >= 0 */
+  int32_t anchor_first;     /* 1: frame 0 is a two-way global anchor */
+  int32_t anchor_last;      /* 1: frame T-1 is a two-way global anchor */
+  float softmax_scale;      /* logit scale; <= 0 selects 1/sqrt(d) */
+  float rms_eps;            /* RMSNorm epsilon (1e-6) */
+  int32_t dtype;            /* enum vdn_dtype: storage of q,k,v,x,W,gates,out */
+} vdn_shape;
+
+/* Bytes of device workspace `op` needs for `shape` (0 on an invalid shape,
+ * with vdn_last_error() set).  The workspace holds per-frame statistics,
+ * transitions and states of the linear branch, anchor-row partial results of
+ * the softmax branch, transposed weights, gates and branch outputs. */
+size_t vdn_workspace_bytes(const vdn_shape* shape, int op); /* >= 256 when valid */
+
+/* Full hybrid attention forward (10100.com article, 方法概述 parts 1-3):
+ *   out = (sigmoid(x W_gs) * O_s) W_os + (sigmoid(x W_gl) * O_l) W_ol.
+ * Inputs x, q, k, v, gamma, beta, w_gs, w_gl, rms_w (nullable), w_os, w_ol;
+ * output out [B, L, D]. */
+int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q,
+                        const void* k, const void* v, const float* gamma,
+                        const float* beta, const void* w_gs, const void* w_gl,
+                        const float* rms_w, const void* w_os, const void* w_ol,
+                        void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Linear branch alone (10100.com article, 方法概述 part 2; forward-plus-
+ * backward scan figure):
+ *   out[b, t*N+n, h*d+i] = gate_l * (RMSNorm(S_fwd_t q) + RMSNorm(S_bwd_t q))_i
+ * gate_l may be NULL (no gate); states may be NULL (kept in the workspace). */
+int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
+                 const void* v, const float* gamma, const float* beta,
+                 const float* rms_w, const void* gate_l, void* out,
+                 float* states, void* ws, size_t ws_bytes, void* stream);
+
+/* Softmax branch alone (10100.com article, 方法概述 part 1):
+ *   out[b, l, h*d+i] = gate_s * (softmax over allowed keys of
+ *                      scale * q_l . k) @ v
+ * gate_s and lse may be NULL. */
+int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
+                           const void* k, const void* v, const void* gate_s,
+                           void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Phase timing, a tracing aid for benchmarks.  Between vdn_timing_start()
+ * and vdn_timing_stop() every compute entry point records a pair of HIP
+ * events on its stream around each of its phases (transposes, gate GEMM,
+ * window attention with its anchor merge, VDA gram / solve / scan / readout,
+ * output GEMM).  vdn_timing_stop() waits for those events, then fills up to
+ * max_stats entries with the phase name, the number of launches recorded and
+ * their summed duration in milliseconds, and returns the number of phases
+ * (or a negative status).  Event recording does not synchronise the stream;
+ * timing state is process-wide, so time one stream at a time. */
+typedef struct vdn_phase_stat {
+  const char* name;  /* static string owned by the library */
+  int32_t launches;
+  float total_ms;
+} vdn_phase_stat;
+
+int vdn_timing_start(void);
+int vdn_timing_stop(vdn_phase_stat* stats, int max_stats);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* vdn_last_error(void);
+
+/* Library version string. */
+const char* vdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_H */

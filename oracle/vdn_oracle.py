@@ -300,7 +300,8 @@ def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
     `states` may carry precomputed (s_fwd, s_bwd) of shape [B, H, T, d, d].
     Returns out [B, len(rows), D].
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    # q, k, v are converted to float64 one (batch, head) slice at a time so that
+    # full-size inputs need not be held in float64 whole.
     gamma, beta, rms_w = _f64(gamma), _f64(beta), _f64(rms_w)
     B, H, T, N, d = q.shape
     rows = np.asarray(rows)
@@ -314,16 +315,18 @@ def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
     g_s, g_l = gates(xr, _f64(w_gs), _f64(w_gl))
     for b in range(B):
         for h in range(H):
-            o, _ = window_attention(q[b, h], k[b, h], v[b, h], allowed, scale, rows)
+            qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+            o, _ = window_attention(qh, kh, vh, allowed, scale, rows)
             y_s[b, :, h * d:(h + 1) * d] = o
             if states is None:
-                sf, sb = vda_states(k[b, h], v[b, h], gamma[b, h], beta[b, h])
+                sf, sb = vda_states(kh, vh, gamma[b, h], beta[b, h])
             else:
                 sf, sb = states[0][b, h], states[1][b, h]
             w_h = rms_w[h * d:(h + 1) * d]
             for i, r in enumerate(rows):
                 t, n = divmod(int(r), N)
-                y_l[b, i, h * d:(h + 1) * d] = vda_readout(q[b, h, t, n][None], sf[t], sb[t], w_h, eps)[0]
+                y_l[b, i, h * d:(h + 1) * d] = vda_readout(qh[t, n][None], sf[t], sb[t], w_h, eps)[0]
+            del qh, kh, vh
     return (g_s * y_s) @ _f64(w_os) + (g_l * y_l) @ _f64(w_ol)
 
 

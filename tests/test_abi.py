@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: libvdn.so loads, exports every function that
+include/vdn.h declares, and rejects bad arguments on the host before any HIP
+call (these calls never launch a kernel, so no GPU is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdn.h")
+LIB = os.path.join(ROOT, "video_diffusion_hybrid_vda_amd", "libvdn.so")
+
+
+@pytest.fixture(scope="module")
+def vdn():
+    if not os.path.exists(LIB):
+        from video_diffusion_hybrid_vda_amd import build
+        build.build()
+    from video_diffusion_hybrid_vda_amd import vdn as binding
+    return binding
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_declares_the_entry_points():
+    fns = header_functions()
+    for name in ("vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
+                 "vdn_workspace_bytes", "vdn_last_error", "vdn_version", "vdn_timing_start",
+                 "vdn_timing_stop"):
+        assert name in fns, fns
+
+
+def test_library_exports_every_declared_function(vdn):
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    lib = ctypes.CDLL(LIB)
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(vdn.EXPORTS) == set(header_functions())
+
+
+def test_library_is_gfx950_only():
+    data = open(LIB, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx[0-9a-z]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_version_and_clean_error_state(vdn):
+    assert "gfx950" in vdn.vdn_version()
+
+
+def test_shape_struct_layout(vdn):
+    assert ctypes.sizeof(vdn.vdn_shape) == 12 * 4
+
+
+def _shape(vdn, **kw):
+    base = dict(batch=1, heads=2, frames=12, tokens_per_frame=6, head_dim=32, dtype="bf16")
+    base.update(kw)
+    return vdn.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), -2), (dict(head_dim=256), -2), (dict(frames=0), -2),
+    (dict(tokens_per_frame=0), -2), (dict(batch=0), -2), (dict(heads=-1), -2),
+    (dict(chunk_frames=0), -2), (dict(window_chunks=-1), -2), (dict(dtype=7), -3),
+    (dict(rms_eps=-1.0), -2), (dict(anchor_first=2), -2),
+])
+def test_bad_shapes_rejected_before_launch(vdn, kw, status):
+    s = _shape(vdn, **kw)
+    fake = 1 << 20     # never dereferenced: validation fails first
+    for call in (
+        lambda: vdn._lib.vdn_hybrid_attn_fwd(ctypes.byref(s), *([fake] * 12), fake, 1 << 40, None),
+        lambda: vdn._lib.vda_scan_fwd(ctypes.byref(s), *([fake] * 9), fake, 1 << 40, None),
+        lambda: vdn._lib.window_anchor_attn_fwd(ctypes.byref(s), *([fake] * 6), fake, 1 << 40, None),
+    ):
+        assert call() == status
+        assert vdn.vdn_last_error() != ""
+    assert vdn._lib.vdn_workspace_bytes(ctypes.byref(s), 0) == 0
+
+
+def test_null_and_misaligned_pointers_rejected(vdn):
+    s = _shape(vdn)
+    fake = 1 << 20
+    args = [fake] * 12
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11):     # rms_w (index 8) is nullable
+        a = list(args)
+        a[i] = None
+        assert vdn._lib.vdn_hybrid_attn_fwd(ctypes.byref(s), *a, fake, 1 << 40, None) == -1
+    a = list(args)
+    a[1] = fake + 2
+    assert vdn._lib.vdn_hybrid_attn_fwd(ctypes.byref(s), *a, fake, 1 << 40, None) == -1
+    assert "aligned" in vdn.vdn_last_error()
+    assert vdn._lib.vda_scan_fwd(None, *([fake] * 9), fake, 1 << 40, None) == -1
+    with pytest.raises(vdn.VdnError) as ei:
+        vdn.window_anchor_attn_fwd(s, None, fake, fake, None, fake, None, None)
+    assert ei.value.status == -1
+
+
+def test_workspace_too_small_rejected(vdn):
+    s = _shape(vdn)
+    fake = 1 << 20
+    vda_args = [fake] * 8 + [None]          # states NULL: kept in the workspace
+    for op, call in (
+        (0, lambda n, w: vdn._lib.vdn_hybrid_attn_fwd(ctypes.byref(s), *([fake] * 12), w, n, None)),
+        (1, lambda n, w: vdn._lib.vda_scan_fwd(ctypes.byref(s), *vda_args, w, n, None)),
+    ):
+        need = vdn.vdn_workspace_bytes(s, op)
+        assert need >= 256
+        assert call(need - 1, fake) == -4
+        assert "workspace" in vdn.vdn_last_error()
+        assert call(need, None) == -4
+
+
+def test_workspace_sizes_cover_the_layout(vdn):
+    """Hybrid workspace at the 102-frame headline shape holds the gates and
+    branch outputs (2 x [B*L, 2D] bf16), the VDA matrices and the anchor
+    partials; all sizes are 256-byte multiples."""
+    s = vdn.make_shape(1, 24, 102, 4032, 128, "bf16")
+    L, D = 102 * 4032, 24 * 128
+    hyb = vdn.vdn_workspace_bytes(s, 0)
+    vda = vdn.vdn_workspace_bytes(s, 1)
+    att = vdn.vdn_workspace_bytes(s, 2)
+    assert hyb >= 2 * L * 2 * D * 2 + vda + att
+    assert vda >= 4 * 24 * 102 * 128 * 128 * 4
+    assert att >= 2 * 24 * 2 * 4032 * 128 * 4       # two anchor frames, >= 2 key splits
+    assert hyb % 256 == 0 and vda % 256 == 0 and att % 256 == 0
+    with pytest.raises(vdn.VdnError):
+        vdn.vdn_workspace_bytes(s, 9)
+
+
+def test_timing_session_without_launches(vdn):
+    """Starting and stopping a timing session with no recorded launch touches
+    no GPU and reports every phase with zero launches."""
+    vdn.vdn_timing_start()
+    stats = vdn.vdn_timing_stop()
+    assert "window_attn" in stats and "vda_scan" in stats
+    assert all(n == 0 for n, _ in stats.values())

@@ -1,0 +1,287 @@
+"""GPU parity: every C-ABI entry point against the fp64 oracle on the same
+seeded inputs.
+
+Error measure: max |gpu - oracle| / RMS(oracle), bounded by 2e-2 for bf16
+I/O with fp32 accumulation and by 1e-4 for the fp32 path.  Small shapes are
+compared element by element; they span several query/key tiles, ragged
+tails, every mask regime (dense, banded, anchors on/off, split anchor rows)
+and head_dim 32/64/128.  Full-size shapes are compared on sampled tokens and
+heads, plus invariants that hold at any size.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import vdn_oracle as O
+from video_diffusion_hybrid_vda_amd import synth
+from video_diffusion_hybrid_vda_amd.synth import VdnConfig
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# states are fp32 in both paths (bf16 inputs are exact in fp32)
+STATE_TOL = {"f32": 1e-4, "bf16": 1e-3}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vdn():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch: the HIP path cannot run")
+    from video_diffusion_hybrid_vda_amd import vdn as binding
+    return binding
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
+
+
+def gpu_inputs(cfg, with_layer=True, sharp=False):
+    inp = synth.make_inputs(cfg, device="cpu", with_layer=with_layer)
+    if sharp:  # sharper softmax: scale q up and drop the key normalisation
+        dt = synth.DTYPES[cfg.dtype]
+        g = torch.Generator().manual_seed(cfg.seed + 999)
+        inp["q"] = (inp["q"].float() * 4).to(dt)
+        inp["k"] = torch.randn(inp["k"].shape, generator=g).to(dt)
+    return {k: v.cuda() for k, v in inp.items()}
+
+
+def oracle_kwargs(cfg):
+    return dict(chunk_frames=cfg.chunk_frames, window_chunks=cfg.window_chunks,
+                anchor_first=cfg.anchor_first, anchor_last=cfg.anchor_last, eps=cfg.rms_eps)
+
+
+TINY = [
+    ("config1_f32", synth.CONFIGS[1]),
+    ("config1_bf16", synth.CONFIGS[1].replace(dtype="bf16")),
+    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=11)),
+    ("H2_T12_N1_d64_bf16", VdnConfig(1, 2, 64, 12, 1, dtype="bf16", seed=12)),
+    ("T13_N5_d128_f32", VdnConfig(1, 1, 128, 13, 5, dtype="f32", seed=13)),
+    ("T23_N3_d64_noanchor_W0_f32", VdnConfig(1, 2, 64, 23, 3, dtype="f32", window_chunks=0,
+                                             anchor_first=False, anchor_last=False, seed=14)),
+    ("T40_N20_d32_splitanchor_f32", VdnConfig(1, 1, 32, 40, 20, dtype="f32", seed=15)),
+    ("H2_T17_N130_d128_bf16", VdnConfig(1, 2, 128, 17, 130, dtype="bf16", seed=16)),
+    ("T1_N7_d32_f32", VdnConfig(1, 1, 32, 1, 7, dtype="f32", seed=17)),
+    ("T9_N4_lastanchor_d32_f32", VdnConfig(1, 1, 32, 9, 4, dtype="f32", anchor_first=False, seed=18)),
+    ("T31_N4_C3_W2_d64_bf16", VdnConfig(1, 2, 64, 31, 4, dtype="bf16", chunk_frames=3,
+                                        window_chunks=2, seed=19)),
+    ("T42_N33_d64_bf16", VdnConfig(1, 1, 64, 42, 33, dtype="bf16", seed=20)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", TINY, ids=[t[0] for t in TINY])
+def test_hybrid_tiny(vdn, name, cfg):
+    log(f"[hybrid] {name}")
+    inp = gpu_inputs(cfg)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
+    ref = O.hybrid_layer(*(np32(inp[k]) for k in ("x", "q", "k", "v", "gamma", "beta", "w_gs",
+                                                  "w_gl", "rms_w", "w_os", "w_ol")),
+                         **oracle_kwargs(cfg))
+    err = rel_err(np32(out), ref)
+    log(f"  rel err {err:.3e} (tol {TOL[cfg.dtype]})")
+    assert err <= TOL[cfg.dtype]
+
+
+WINDOW = [
+    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=31), False),
+    ("T17_N6_d32_sharp_f32", VdnConfig(1, 2, 32, 17, 6, dtype="f32", seed=32), True),
+    ("T23_N70_d128_sharp_bf16", VdnConfig(1, 1, 128, 23, 70, dtype="bf16", seed=33), True),
+    ("T40_N20_d64_split_bf16", VdnConfig(1, 2, 64, 40, 20, dtype="bf16", seed=34), False),
+    ("T12_N200_d128_f32", VdnConfig(1, 1, 128, 12, 200, dtype="f32", seed=35), False),
+    ("T60_N3_d32_W3_split_f32", VdnConfig(1, 1, 32, 60, 3, dtype="f32", window_chunks=3, seed=36), True),
+]
+
+
+@pytest.mark.parametrize("name,cfg,sharp", WINDOW, ids=[t[0] for t in WINDOW])
+def test_window_attn(vdn, name, cfg, sharp):
+    log(f"[window] {name}")
+    inp = gpu_inputs(cfg, with_layer=False, sharp=sharp)
+    shape = vdn.shape_from_config(cfg)
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    gen = torch.Generator().manual_seed(cfg.seed + 5)
+    gate = torch.rand(B, T * N, H * d, generator=gen).to(synth.DTYPES[cfg.dtype]).cuda()
+    out, lse = vdn.window_attn(shape, inp, gate_s=gate, with_lse=True)
+    out_ng = vdn.window_attn(shape, inp)
+    torch.cuda.synchronize()
+    allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+    q, k, v = np32(inp["q"]), np32(inp["k"]), np32(inp["v"])
+    ref = np.zeros((B, H, T * N, d))
+    ref_lse = np.zeros((B, H, T * N))
+    for b in range(B):
+        for h in range(H):
+            o, l = O.window_attention(q[b, h].astype(np.float64), k[b, h].astype(np.float64),
+                                      v[b, h].astype(np.float64), allowed, 1 / np.sqrt(d))
+            ref[b, h], ref_lse[b, h] = o, l
+    ref_tok = np.transpose(ref, (0, 2, 1, 3)).reshape(B, T * N, H * d)
+    g = np32(gate).astype(np.float64)
+    e1 = rel_err(np32(out), g * ref_tok)
+    e2 = rel_err(np32(out_ng), ref_tok)
+    e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
+    log(f"  gated {e1:.3e} ungated {e2:.3e} lse abs {e3:.3e}")
+    assert e1 <= TOL[cfg.dtype] and e2 <= TOL[cfg.dtype]
+    assert e3 <= (1e-4 if cfg.dtype == "f32" else 1e-2)
+
+
+VDA = [
+    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=41)),
+    ("T13_N300_d128_f32", VdnConfig(1, 1, 128, 13, 300, dtype="f32", seed=42)),
+    ("H3_T9_N40_d64_bf16", VdnConfig(1, 3, 64, 9, 40, dtype="bf16", seed=43)),
+    ("T5_N1000_d128_bf16", VdnConfig(1, 1, 128, 5, 1000, dtype="bf16", seed=44)),
+    ("T6_N2_d128_f32_rankdef", VdnConfig(1, 1, 128, 6, 2, dtype="f32", beta_lo=0.0, seed=45)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", VDA, ids=[t[0] for t in VDA])
+def test_vda_scan(vdn, name, cfg):
+    log(f"[vda] {name}")
+    inp = gpu_inputs(cfg, with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    gen = torch.Generator().manual_seed(cfg.seed + 6)
+    inp["rms_w"] = (0.5 + torch.rand(H * d, generator=gen)).cuda()
+    gate = torch.rand(B, T * N, H * d, generator=gen).to(synth.DTYPES[cfg.dtype]).cuda()
+    out, states = vdn.vda_scan(shape, inp, gate_l=gate, with_states=True)
+    torch.cuda.synchronize()
+    o_l, sf, sb = O.vda_branch(*(np32(inp[k]).astype(np.float64) for k in ("q", "k", "v", "gamma", "beta", "rms_w")),
+                               cfg.rms_eps)
+    ref = np32(gate).astype(np.float64) * O.merge_heads(o_l)
+    st = np32(states)
+    es = max(rel_err(st[0], sf), rel_err(st[1], sb))
+    eo = rel_err(np32(out), ref)
+    log(f"  states {es:.3e} out {eo:.3e}")
+    assert es <= STATE_TOL[cfg.dtype]
+    assert eo <= TOL[cfg.dtype]
+
+
+def test_vda_config2_full(vdn):
+    """VDA scan only at its full shape: B1 H8 d64 T42 N1560, bf16, no gate."""
+    cfg = synth.CONFIGS[2]
+    log(f"[vda] {cfg.name}")
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg)
+    out, states = vdn.vda_scan(shape, inp, with_states=True)
+    torch.cuda.synchronize()
+    rms_w = np.ones(cfg.model_dim)
+    o_l, sf, sb = O.vda_branch(*(np32(inp[k]).astype(np.float64) for k in ("q", "k", "v", "gamma", "beta")),
+                               rms_w, cfg.rms_eps)
+    st = np32(states)
+    es = max(rel_err(st[0], sf), rel_err(st[1], sb))
+    eo = rel_err(np32(out), O.merge_heads(o_l))
+    log(f"  states {es:.3e} out {eo:.3e}")
+    assert es <= STATE_TOL["bf16"] and eo <= TOL["bf16"]
+
+
+def test_vda_invariants(vdn):
+    """Backward scan equals the forward scan of time-reversed inputs (bit for
+    bit: same kernels, same order of operations); beta = 0 gives zero states."""
+    cfg = VdnConfig(1, 2, 128, 11, 257, dtype="bf16", seed=51)
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg)
+    out, st = vdn.vda_scan(shape, inp, with_states=True)
+    flip = {k: torch.flip(inp[k], dims=[2]).contiguous() for k in ("q", "k", "v", "gamma", "beta")}
+    out_r, st_r = vdn.vda_scan(shape, flip, with_states=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st[1], torch.flip(st_r[0], dims=[3]))
+    assert torch.equal(st[0], torch.flip(st_r[1], dims=[3]))
+    zero = dict(inp, beta=torch.zeros_like(inp["beta"]))
+    out0, st0 = vdn.vda_scan(shape, zero, with_states=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st0).item() == 0
+    assert torch.count_nonzero(out0).item() == 0
+
+
+# ---------------------------------------------------------------- full size
+
+def test_window_attn_config4_sampled(vdn):
+    """Softmax branch at the 102-frame headline shape (B1 H24 d128 N4032),
+    the launch the benchmark times, checked on sampled query tokens of three
+    heads (anchor frames, chunk edges, the ragged last chunk, random)."""
+    cfg = synth.CONFIGS[4]
+    log(f"[window] {cfg.name}")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg)
+    out, lse = vdn.window_attn(shape, inp, with_lse=True)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    T, N, d = cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    rows = np.array(synth.sample_tokens(cfg, 40))
+    allowed = O.allowed_frames(T)
+    worst = 0.0
+    for h in (0, 11, 23):
+        q = np32(inp["q"][0, h]).astype(np.float64)
+        k = np32(inp["k"][0, h]).astype(np.float64)
+        v = np32(inp["v"][0, h]).astype(np.float64)
+        o, l = O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), rows)
+        got = np32(out[0, rows, h * d:(h + 1) * d])
+        worst = max(worst, rel_err(got, o))
+        assert np.max(np.abs(np32(lse[0, h, rows]) - l)) <= 1e-2
+    log(f"  rel err {worst:.3e} ({time.time() - t0:.1f}s)")
+    assert worst <= TOL["bf16"]
+
+
+def test_vda_config4_two_heads(vdn):
+    """Linear branch at the headline shape: all states of two heads and the
+    output at sampled tokens."""
+    cfg = synth.CONFIGS[4]
+    log(f"[vda] {cfg.name}")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg)
+    out, states = vdn.vda_scan(shape, inp, with_states=True)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    T, N, d = cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    rows = synth.sample_tokens(cfg, 24)
+    w = np.ones(d)
+    for h in (0, 23):
+        k = np32(inp["k"][0, h]).astype(np.float64)
+        v = np32(inp["v"][0, h]).astype(np.float64)
+        sf, sb = O.vda_states(k, v, np32(inp["gamma"][0, h]), np32(inp["beta"][0, h]))
+        es = max(rel_err(np32(states[0, 0, h]), sf), rel_err(np32(states[1, 0, h]), sb))
+        q = np32(inp["q"][0, h]).astype(np.float64)
+        ref = np.stack([O.vda_readout(q[r // N, r % N][None], sf[r // N], sb[r // N], w, cfg.rms_eps)[0]
+                        for r in rows])
+        eo = rel_err(np32(out[0, rows, h * d:(h + 1) * d]), ref)
+        log(f"  head {h}: states {es:.3e} out {eo:.3e} ({time.time() - t0:.1f}s)")
+        assert es <= STATE_TOL["bf16"] and eo <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg_id", [3, 4])
+def test_hybrid_full_sampled(vdn, cfg_id):
+    """Whole layer at full size (every head, D = 3072), output checked at
+    sampled tokens; the oracle runs both scans of all heads."""
+    cfg = synth.CONFIGS[cfg_id]
+    log(f"[hybrid] {cfg.name}")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    rows = synth.sample_tokens(cfg, 12 if cfg_id == 4 else 16)
+    host = {k: (np32(v) if k not in ("q", "k", "v") else v) for k, v in inp.items()}
+    for k in ("q", "k", "v"):
+        host[k] = inp[k].float().cpu().numpy()
+    ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                              host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                              rows, **oracle_kwargs(cfg))
+    err = rel_err(np32(out[:, rows]), ref)
+    log(f"  rel err {err:.3e} ({time.time() - t0:.1f}s)")
+    assert err <= TOL["bf16"]

@@ -1,0 +1,407 @@
+// C ABI of libvdn.so (declared in include/vdn.h): argument validation,
+// workspace layout and the launch sequence of each entry point.  No device
+// memory is allocated here; every buffer comes from the caller.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "vdn.h"
+#include "vdn_internal.h"
+
+using namespace vdn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+size_t elem_size(int dtype) { return dtype == VDN_BF16 ? 2 : 4; }
+
+int check_shape(const vdn_shape* s) {
+  if (!s) return fail(VDN_ERR_INVALID_ARG, "shape is NULL");
+  if (s->dtype != VDN_F32 && s->dtype != VDN_BF16)
+    return fail(VDN_ERR_DTYPE, "dtype %d is not VDN_F32 (0) or VDN_BF16 (1)", s->dtype);
+  if (s->batch < 1 || s->heads < 1 || s->frames < 1 || s->tokens_per_frame < 1)
+    return fail(VDN_ERR_BAD_SHAPE, "batch, heads, frames and tokens_per_frame must be >= 1");
+  if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
+    return fail(VDN_ERR_BAD_SHAPE, "head_dim %d not in {32, 64, 128}", s->head_dim);
+  if (s->chunk_frames < 1) return fail(VDN_ERR_BAD_SHAPE, "chunk_frames must be >= 1");
+  if (s->window_chunks < 0) return fail(VDN_ERR_BAD_SHAPE, "window_chunks must be >= 0");
+  if ((s->anchor_first != 0 && s->anchor_first != 1) || (s->anchor_last != 0 && s->anchor_last != 1))
+    return fail(VDN_ERR_BAD_SHAPE, "anchor_first / anchor_last must be 0 or 1");
+  if (!(s->rms_eps >= 0.f) || !isfinite(s->rms_eps))
+    return fail(VDN_ERR_BAD_SHAPE, "rms_eps must be finite and >= 0");
+  if (!isfinite(s->softmax_scale)) return fail(VDN_ERR_BAD_SHAPE, "softmax_scale must be finite");
+  const int64_t L = (int64_t)s->frames * s->tokens_per_frame;
+  if (L > (1LL << 30)) return fail(VDN_ERR_BAD_SHAPE, "frames * tokens_per_frame exceeds 2^30");
+  const int64_t D = (int64_t)s->heads * s->head_dim;
+  if (D > (1 << 20)) return fail(VDN_ERR_BAD_SHAPE, "heads * head_dim exceeds 2^20");
+  if ((int64_t)s->batch * L > (1LL << 31) - 1)
+    return fail(VDN_ERR_BAD_SHAPE, "batch * frames * tokens_per_frame exceeds 2^31 - 1");
+  return VDN_OK;
+}
+
+// ---- softmax-branch work decomposition
+AttnParams make_attn_params(const vdn_shape* s) {
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  const int T = s->frames, N = s->tokens_per_frame, C = s->chunk_frames, W = s->window_chunks;
+  const int BM = kAttnBM, BN = kAttnBN;
+  p.B = s->batch;
+  p.H = s->heads;
+  p.T = T;
+  p.N = N;
+  p.C = C;
+  p.W = W;
+  p.a0 = s->anchor_first;
+  p.a1 = s->anchor_last;
+  p.nC = (T + C - 1) / C;
+  auto tiles = [&](int frames) { return frames > 0 ? (int)(((int64_t)frames * N + BM - 1) / BM) : 0; };
+  if (p.nC == 1) {
+    p.tiles0 = tiles(T - p.a0 - p.a1);
+    p.n_window_tiles = p.tiles0;
+  } else {
+    p.tiles0 = tiles(C - p.a0);
+    p.tilesM = tiles(C);
+    p.tilesL = tiles(T - p.a1 - (p.nC - 1) * C);
+    p.n_window_tiles = p.tiles0 + (p.nC - 2) * p.tilesM + p.tilesL;
+  }
+  p.nA = 0;
+  if (p.a0) p.anchor_frame[p.nA++] = 0;
+  if (p.a1 && !(p.a0 && T == 1)) p.anchor_frame[p.nA++] = T - 1;
+  p.tiles_per_anchor = (N + BM - 1) / BM;
+  const int64_t L = (int64_t)T * N;
+  const int64_t key_tiles = (L + BN - 1) / BN;
+  // Split anchor rows so each piece sees about as many keys as a window tile.
+  const int64_t win_frames = (int64_t)(2 * W + 1) * C + 2;
+  const int64_t win_keys = (win_frames < T ? win_frames : T) * N;
+  int64_t ns = p.nA ? (L + win_keys - 1) / win_keys : 1;
+  if (ns < 1) ns = 1;
+  if (ns > key_tiles) ns = key_tiles;
+  const int64_t tiles_per_split = (key_tiles + ns - 1) / ns;
+  p.keys_per_split = (int)(tiles_per_split * BN);
+  p.nsplit = (int)((L + p.keys_per_split - 1) / p.keys_per_split);
+  p.tiles_per_bh = p.n_window_tiles + p.nA * p.nsplit * p.tiles_per_anchor;
+  p.total = p.B * p.H * p.tiles_per_bh;
+  const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf((float)s->head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return p;
+}
+
+// ---- workspace layouts
+struct VdaLayout {
+  size_t am, bc, states, total;
+};
+VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
+  const size_t dd = (size_t)s->head_dim * s->head_dim;
+  const size_t frames = (size_t)s->batch * s->heads * s->frames;
+  VdaLayout l;
+  size_t off = 0;
+  l.am = off; off = align_up(off + frames * dd * 4);
+  l.bc = off; off = align_up(off + frames * dd * 4);
+  l.states = off; off = align_up(off + (need_states ? 2 * frames * dd * 4 : 0));
+  l.total = off;
+  return l;
+}
+
+struct AttnLayout {
+  size_t part_o, part_ml, total;
+};
+AttnLayout attn_layout(const vdn_shape* s, const AttnParams& p) {
+  AttnLayout l;
+  size_t off = 0;
+  const size_t rows = p.nsplit > 1 ? (size_t)p.nA * p.B * p.H * p.nsplit * p.N : 0;
+  l.part_o = off; off = align_up(off + rows * s->head_dim * 4);
+  l.part_ml = off; off = align_up(off + rows * 2 * 4);
+  l.total = off;
+  return l;
+}
+
+struct HybridLayout {
+  size_t wg, wo, gates, ybuf, vda, attn, total;
+};
+HybridLayout hybrid_layout(const vdn_shape* s, const AttnParams& p) {
+  const size_t es = elem_size(s->dtype);
+  const size_t D = (size_t)s->heads * s->head_dim;
+  const size_t rows = (size_t)s->batch * s->frames * s->tokens_per_frame;
+  HybridLayout l;
+  size_t off = 0;
+  l.wg = off; off = align_up(off + 2 * D * D * es);       // [W_gs^T ; W_gl^T]   [2D, D]
+  l.wo = off; off = align_up(off + 2 * D * D * es);       // [W_os^T | W_ol^T]   [D, 2D]
+  l.gates = off; off = align_up(off + rows * 2 * D * es); // [g_s | g_l]         [B*L, 2D]
+  l.ybuf = off; off = align_up(off + rows * 2 * D * es);  // [y_s | y_l]         [B*L, 2D]
+  l.vda = off; off = align_up(off + vda_layout(s, true).total);
+  l.attn = off; off = align_up(off + attn_layout(s, p).total);
+  l.total = off;
+  return l;
+}
+
+bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+// ---- opt-in phase timing: HIP event pairs recorded around each phase
+enum Phase {
+  kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhGram, kPhSolve, kPhScan, kPhReadout, kPhOutGemm,
+  kNumPhases
+};
+const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm",  "window_attn",
+                                             "vda_gram",          "vda_solve",  "vda_scan",
+                                             "vda_readout",       "out_gemm"};
+
+struct Timer {
+  std::mutex mu;
+  bool on = false;
+  bool failed = false;
+  struct Rec { int phase; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;   // events are reused across timing sessions
+  size_t used = 0;
+  hipEvent_t take() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) { failed = true; return nullptr; }
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+Timer g_timer;
+
+// Returns a record index, or -1 when timing is off.
+int phase_begin(int phase, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.on || g_timer.failed) return -1;
+  hipEvent_t a = g_timer.take(), b = g_timer.take();
+  if (!a || !b) return -1;
+  hipEventRecord(a, st);
+  g_timer.recs.push_back({phase, a, b});
+  return (int)g_timer.recs.size() - 1;
+}
+
+void phase_end(int idx, hipStream_t st) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (idx < (int)g_timer.recs.size()) hipEventRecord(g_timer.recs[idx].b, st);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(VDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Linear branch on already validated arguments.
+int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
+            const float* gamma, const float* beta, const float* rms_w, const void* gate,
+            int64_t ldg, void* out, int64_t ldo, float* states, char* ws, hipStream_t st) {
+  const VdaLayout l = vda_layout(s, states == nullptr);
+  float* am = (float*)(ws + l.am);
+  float* bc = (float*)(ws + l.bc);
+  float* st_buf = states ? states : (float*)(ws + l.states);
+  const int d = s->head_dim;
+  const int nframes = s->batch * s->heads * s->frames;
+  hipError_t e;
+  int ph = phase_begin(kPhGram, st);
+  e = launch_vda_gram(s->dtype, d, k, v, beta, am, bc, nframes, s->tokens_per_frame, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "vda gram launch");
+  ph = phase_begin(kPhSolve, st);
+  e = launch_vda_solve(d, am, bc, nframes, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "vda solve launch");
+  ph = phase_begin(kPhScan, st);
+  e = launch_vda_scan(d, am, bc, gamma, st_buf, s->batch * s->heads, s->frames, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "vda scan launch");
+  ph = phase_begin(kPhReadout, st);
+  e = launch_vda_readout(s->dtype, d, q, st_buf, rms_w, gate, ldg, out, ldo, s->batch, s->heads,
+                         s->frames, s->tokens_per_frame, s->rms_eps, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "vda readout launch");
+  return VDN_OK;
+}
+
+int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, const void* gate,
+             int64_t ldg, void* out, int64_t ldo, float* lse, char* ws, hipStream_t st) {
+  AttnParams p = make_attn_params(s);
+  const AttnLayout l = attn_layout(s, p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.gate = gate;
+  p.out = out;
+  p.lse = lse;
+  p.ldg = ldg;
+  p.ldo = ldo;
+  p.part_o = (float*)(ws + l.part_o);
+  p.part_ml = (float*)(ws + l.part_ml);
+  const int ph = phase_begin(kPhWindowAttn, st);
+  const hipError_t e = launch_window_attn(s->dtype, s->head_dim, p, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  return VDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vdn_last_error(void) { return g_err; }
+
+const char* vdn_version(void) { return "vdn-mi355x 0.1 (gfx950)"; }
+
+size_t vdn_workspace_bytes(const vdn_shape* shape, int op) {
+  if (check_shape(shape) != VDN_OK) return 0;
+  const AttnParams p = make_attn_params(shape);
+  size_t n = 0;
+  switch (op) {
+    case VDN_OP_HYBRID: n = hybrid_layout(shape, p).total; break;
+    case VDN_OP_VDA_SCAN: n = vda_layout(shape, true).total; break;
+    case VDN_OP_WINDOW_ATTN: n = attn_layout(shape, p).total; break;
+    default: fail(VDN_ERR_INVALID_ARG, "unknown op %d", op); return 0;
+  }
+  // Never 0 for a valid request, so that 0 always signals an error.
+  return n > kAlign ? n : kAlign;
+}
+
+int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k, const void* v,
+                 const float* gamma, const float* beta, const float* rms_w, const void* gate_l,
+                 void* out, float* states, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!q || !k || !v || !gamma || !beta || !out)
+    return fail(VDN_ERR_INVALID_ARG, "vda_scan_fwd: q, k, v, gamma, beta and out must be non-NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(gate_l) ||
+      misaligned(states) || misaligned(ws) || misaligned(gamma) || misaligned(beta))
+    return fail(VDN_ERR_INVALID_ARG, "vda_scan_fwd: device pointers must be 16-byte aligned");
+  const size_t need = vda_layout(shape, states == nullptr).total;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(VDN_ERR_WORKSPACE, "vda_scan_fwd: workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  const int64_t D = (int64_t)shape->heads * shape->head_dim;
+  return run_vda(shape, q, k, v, gamma, beta, rms_w, gate_l, D, out, D, states, (char*)ws,
+                 (hipStream_t)stream);
+}
+
+int window_anchor_attn_fwd(const vdn_shape* shape, const void* q, const void* k, const void* v,
+                           const void* gate_s, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!q || !k || !v || !out)
+    return fail(VDN_ERR_INVALID_ARG, "window_anchor_attn_fwd: q, k, v and out must be non-NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(gate_s) ||
+      misaligned(ws))
+    return fail(VDN_ERR_INVALID_ARG, "window_anchor_attn_fwd: device pointers must be 16-byte aligned");
+  const AttnParams p = make_attn_params(shape);
+  const size_t need = attn_layout(shape, p).total;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(VDN_ERR_WORKSPACE, "window_anchor_attn_fwd: workspace of %zu bytes needed, %zu given",
+                need, ws ? ws_bytes : (size_t)0);
+  const int64_t D = (int64_t)shape->heads * shape->head_dim;
+  return run_attn(shape, q, k, v, gate_s, D, out, D, lse, (char*)ws, (hipStream_t)stream);
+}
+
+int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q, const void* k,
+                        const void* v, const float* gamma, const float* beta, const void* w_gs,
+                        const void* w_gl, const float* rms_w, const void* w_os, const void* w_ol,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!x || !q || !k || !v || !gamma || !beta || !w_gs || !w_gl || !w_os || !w_ol || !out)
+    return fail(VDN_ERR_INVALID_ARG,
+                "vdn_hybrid_attn_fwd: every input except rms_w, and out, must be non-NULL");
+  const void* ptrs[] = {x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol, out, ws};
+  for (const void* ptr : ptrs)
+    if (misaligned(ptr))
+      return fail(VDN_ERR_INVALID_ARG, "vdn_hybrid_attn_fwd: device pointers must be 16-byte aligned");
+  const AttnParams p = make_attn_params(shape);
+  const HybridLayout l = hybrid_layout(shape, p);
+  if (!ws || ws_bytes < l.total)
+    return fail(VDN_ERR_WORKSPACE, "vdn_hybrid_attn_fwd: workspace of %zu bytes needed, %zu given",
+                l.total, ws ? ws_bytes : (size_t)0);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const size_t es = elem_size(shape->dtype);
+  const int D = shape->heads * shape->head_dim;
+  const int rows = shape->batch * shape->frames * shape->tokens_per_frame;
+  char* wg = w + l.wg;
+  char* wo = w + l.wo;
+  char* gates = w + l.gates;
+  char* ybuf = w + l.ybuf;
+  hipError_t e;
+  // weights -> k-contiguous: wg[n][k] (n < D: W_gs, n >= D: W_gl); wo[n][k] (k < D: W_os, else W_ol)
+  int ph = phase_begin(kPhTranspose, st);
+  e = launch_transpose(shape->dtype, w_gs, wg, D, D, D, st);
+  if (e == hipSuccess) e = launch_transpose(shape->dtype, w_gl, wg + (size_t)D * D * es, D, D, D, st);
+  if (e == hipSuccess) e = launch_transpose(shape->dtype, w_os, wo, D, D, 2 * (int64_t)D, st);
+  if (e == hipSuccess) e = launch_transpose(shape->dtype, w_ol, wo + (size_t)D * es, D, D, 2 * (int64_t)D, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  // gates [g_s | g_l] = sigmoid(x [W_gs | W_gl])
+  ph = phase_begin(kPhGateGemm, st);
+  e = launch_gemm_nt(shape->dtype, kEpiSigmoid, x, wg, gates, rows, 2 * D, D, D, D, 2 * (int64_t)D, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "gate gemm launch");
+  // y_s = g_s * softmax branch ; y_l = g_l * linear branch
+  rc = run_attn(shape, q, k, v, gates, 2 * (int64_t)D, ybuf, 2 * (int64_t)D, nullptr, w + l.attn, st);
+  if (rc != VDN_OK) return rc;
+  rc = run_vda(shape, q, k, v, gamma, beta, rms_w, gates + (size_t)D * es, 2 * (int64_t)D,
+               ybuf + (size_t)D * es, 2 * (int64_t)D, nullptr, w + l.vda, st);
+  if (rc != VDN_OK) return rc;
+  // out = [y_s | y_l] [W_os ; W_ol]
+  ph = phase_begin(kPhOutGemm, st);
+  e = launch_gemm_nt(shape->dtype, kEpiStore, ybuf, wo, out, rows, D, 2 * D, 2 * (int64_t)D,
+                     2 * (int64_t)D, D, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "output gemm launch");
+  return VDN_OK;
+}
+
+int vdn_timing_start(void) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  g_timer.on = true;
+  g_timer.failed = false;
+  g_timer.recs.clear();
+  g_timer.used = 0;
+  return VDN_OK;
+}
+
+int vdn_timing_stop(vdn_phase_stat* stats, int max_stats) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  g_timer.on = false;
+  if (g_timer.failed) return fail(VDN_ERR_HIP, "vdn_timing_stop: could not create HIP events");
+  int launches[kNumPhases] = {0};
+  double total[kNumPhases] = {0.0};
+  for (const Timer::Rec& r : g_timer.recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "vdn_timing_stop");
+    launches[r.phase] += 1;
+    total[r.phase] += ms;
+  }
+  g_timer.recs.clear();
+  if (stats) {
+    for (int i = 0; i < kNumPhases && i < max_stats; ++i) {
+      stats[i].name = kPhaseNames[i];
+      stats[i].launches = launches[i];
+      stats[i].total_ms = (float)total[i];
+    }
+  }
+  return kNumPhases;
+}
+
+}  // extern "C"

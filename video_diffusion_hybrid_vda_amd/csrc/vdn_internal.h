@@ -1,0 +1,64 @@
+// Internal interface between the C ABI (vdn_api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vdn {
+
+// Softmax-branch tiling: queries per workgroup and keys per LDS tile.
+constexpr int kAttnBM = 128;
+constexpr int kAttnBN = 64;
+// Linear-branch readout: tokens per workgroup.
+constexpr int kReadoutBT = 64;
+// Linear-branch scan: state rows per workgroup.
+constexpr int kScanRows = 16;
+
+// Work decomposition of the window/anchor softmax.  Per (batch, head) the
+// work items are: the query tiles of every chunk's non-anchor frames (key set
+// = the chunk window plus anchor frames outside it), then for each anchor
+// frame its query tiles times `nsplit` key splits of the whole sequence.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;   // nullable, row stride ldg
+  void* out;          // row stride ldo
+  float* lse;         // nullable, [B, H, L]
+  float* part_o;      // anchor partials [nA, B, H, nsplit, N, d] (nsplit > 1)
+  float* part_ml;     // anchor partial (max, sum) [nA, B, H, nsplit, N, 2]
+  int64_t ldg, ldo;
+  int B, H, T, N;
+  int C, W, a0, a1;
+  int nC;
+  int tiles0, tilesM, tilesL;
+  int n_window_tiles;
+  int nA;
+  int anchor_frame[2];
+  int tiles_per_anchor;
+  int nsplit;
+  int keys_per_split;
+  int tiles_per_bh;
+  int total;
+  float scale_log2;
+};
+
+enum GemmEpilogue { kEpiStore = 0, kEpiSigmoid = 1 };
+
+// dtype: 0 = fp32, 1 = bf16 (the vdn_dtype values).
+hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
+                            int64_t ld_dst, hipStream_t st);
+hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, void* C, int M,
+                          int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st);
+hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st);
+hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
+                           float* A, float* Bm, int nframes, int N, hipStream_t st);
+hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_t st);
+hipError_t launch_vda_scan(int d, const float* M, const float* Cm, const float* gamma,
+                           float* states, int BH, int T, hipStream_t st);
+hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
+                              const float* rms_w, const void* gate, int64_t ldg, void* out,
+                              int64_t ldo, int B, int H, int T, int N, float eps,
+                              hipStream_t st);
+
+}  // namespace vdn
