@@ -137,7 +137,7 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
 /* Phase timing, a tracing aid for benchmarks.  Between vdn_timing_start()
  * and vdn_timing_stop() every compute entry point records a pair of HIP
  * events on its stream around each of its phases (transposes, gate GEMM,
- * window attention with its anchor merge, VDA gram / solve / scan / readout,
+ * window attention, anchor-row merge, VDA gram / solve / scan / readout,
  * output GEMM).  vdn_timing_stop() waits for those events, then fills up to
  * max_stats entries with the phase name, the number of launches recorded and
  * their summed duration in milliseconds, and returns the number of phases

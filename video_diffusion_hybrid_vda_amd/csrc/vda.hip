@@ -202,12 +202,15 @@ __global__ __launch_bounds__(256) void vda_solve_kernel(float* __restrict__ AM,
 // ---------------------------------------------------------------------------
 // scan: S_t = gamma_t S_prev M_t + C_t.  Rows of S are independent given M_t,
 // so each workgroup owns kScanRows rows of one (batch, head, direction) and
-// walks the T frames, staging M_t in LDS.  Writes every S_t (fp32).
+// walks the T frames, staging M_t in LDS.  Writes every S_t in fp32 and, when
+// `split` is non-null, also as an unevaluated bf16 pair hi + lo (hi = bf16(S),
+// lo = bf16(S - hi)) for the bf16 readout, laid out [dir][frame][hi|lo][d][d].
 template <int D, int R>
 __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__ M,
                                                        const float* __restrict__ Cm,
                                                        const float* __restrict__ gamma,
-                                                       float* __restrict__ states, int T,
+                                                       float* __restrict__ states,
+                                                       bf16* __restrict__ split, int T,
                                                        int64_t bhtdd) {
   constexpr int TPR = 256 / R;     // threads per state row
   constexpr int CPT = D / TPR;     // columns per thread
@@ -240,35 +243,54 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
 #pragma unroll
       for (int c = 0; c < CPT; ++c) acc[c] += sv * Ms[q * LDM + col0 + c];
     }
-    const float* crow = Cm + fi * D * D + (int64_t)(r0 + row) * D + col0;
-    float* srow = states + dir * bhtdd + fi * D * D + (int64_t)(r0 + row) * D + col0;
+    const int64_t off = fi * D * D + (int64_t)(r0 + row) * D + col0;
+    const float* crow = Cm + off;
+    float* srow = states + dir * bhtdd + off;
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const float nv = g * acc[c] + crow[c];
       Ss[row * LDM + col0 + c] = nv;
       srow[c] = nv;
+      if (split) {
+        const bf16 hi = (bf16)nv;
+        const bf16 lo = (bf16)(nv - (float)hi);
+        bf16* sp = split + (dir * bhtdd + fi * D * D) * 2 + (int64_t)(r0 + row) * D + col0 + c;
+        sp[0] = hi;
+        sp[D * D] = lo;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // readout: for a tile of tokens of one frame, u = S_t q for both directions
-// (U = Q S^T on MFMA with S staged in LDS in the I/O precision), RMSNorm of
-// each over head_dim, summed, times rms weight and gate.
+// (U = Q S^T on MFMA, S staged in LDS one direction at a time), RMSNorm of
+// each over head_dim, summed, times rms weight; the gate multiply and the
+// store go through LDS so that every lane writes whole 16-byte chunks.
+// In bf16 I/O S enters as the pair hi + lo, so U = Q S_hi^T + Q S_lo^T keeps
+// ~16 mantissa bits of S: u = S q can cancel strongly when q is nearly
+// orthogonal to the state's rows, and RMSNorm would amplify a bf16 rounding
+// of S back to full scale.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vda_readout_kernel(
-    const T* __restrict__ q, const float* __restrict__ states, const float* __restrict__ rms_w,
-    const T* __restrict__ gate, int64_t ldg, T* __restrict__ out, int64_t ldo, int H, int T_,
-    int N, float eps, int tiles_per_frame, int64_t bhtdd) {
+    const T* __restrict__ q, const float* __restrict__ states, const bf16* __restrict__ split,
+    const float* __restrict__ rms_w, const T* __restrict__ gate, int64_t ldg, T* __restrict__ out,
+    int64_t ldo, int H, int T_, int N, float eps, int tiles_per_frame, int64_t bhtdd) {
   using MM = Mma<T>;
+  constexpr bool kSplit = sizeof(T) == 2;
   constexpr int KP = MM::kPack, KS = MM::kStep;
   constexpr int EPC = 16 / sizeof(T);
-  constexpr int LDSS = D + EPC;
+  constexpr int LDSS = D + EPC;            // staged S row stride (elements of T)
   constexpr int CT = D / 16;
   constexpr int KSTEPS = D / KS;
-  __shared__ __attribute__((aligned(16))) T Sf[D * LDSS];
-  __shared__ __attribute__((aligned(16))) T Sb[D * LDSS];
+  constexpr int RT = kReadoutBT / 64;      // 16-token row tiles per wave
+  constexpr int NPART = kSplit ? 2 : 1;    // hi (+ lo)
+  constexpr int LDO = D + 4;               // fp32 output staging row stride
+  constexpr int SBYTES = NPART * D * LDSS * (int)sizeof(T);
+  constexpr int OBYTES = kReadoutBT * LDO * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SBYTES > OBYTES ? SBYTES : OBYTES];
+  T* Sl = reinterpret_cast<T*>(smem);
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane % 16, lg = lane / 16;
@@ -278,69 +300,109 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
   const int64_t bh = fi / T_;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const float* sf = states + fi * D * D;
-  const float* sb = states + bhtdd + fi * D * D;
-  for (int e = tid * 4; e < D * D; e += 1024) {
-    const float4 x = *reinterpret_cast<const float4*>(sf + e);
-    const float4 y = *reinterpret_cast<const float4*>(sb + e);
-    T* pf = Sf + (e / D) * LDSS + (e % D);
-    T* pb = Sb + (e / D) * LDSS + (e % D);
-    pf[0] = from_f32<T>(x.x); pf[1] = from_f32<T>(x.y); pf[2] = from_f32<T>(x.z); pf[3] = from_f32<T>(x.w);
-    pb[0] = from_f32<T>(y.x); pb[1] = from_f32<T>(y.y); pb[2] = from_f32<T>(y.z); pb[3] = from_f32<T>(y.w);
+  const int n0 = tile * kReadoutBT + wave * (16 * RT);
+
+  typename MM::Frag qa[RT][KSTEPS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = n0 + rt * 16 + li;
+    const T* qrow = q + (fi * N + n) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qa[rt][ks] = (n < N) ? MM::load(qrow + ks * KS + lg * KP) : MM::zero();
   }
-  __syncthreads();
 
-  const int n0 = tile * kReadoutBT + wave * 16;
-  const int n = n0 + li;
-  const T* qrow = q + (fi * N + n) * D;
-  typename MM::Frag qa[KSTEPS];
+  f32x4 u[2][RT][CT];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
-    qa[ks] = (n < N) ? MM::load(qrow + ks * KS + lg * KP) : MM::zero();
-
-  f32x4 uf[CT], ub[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    uf[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ub[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uf[ct] = MM::run(qa[ks], MM::load(Sf + (ct * 16 + li) * LDSS + ks * KS + lg * KP), uf[ct]);
-      ub[ct] = MM::run(qa[ks], MM::load(Sb + (ct * 16 + li) * LDSS + ks * KS + lg * KP), ub[ct]);
+  for (int dir = 0; dir < 2; ++dir) {
+    __syncthreads();
+    if constexpr (kSplit) {
+      const bf16* src = split + (dir * bhtdd + fi * D * D) * 2;   // [hi | lo][d][d]
+      for (int c = tid; c < 2 * D * D / 8; c += 256) {
+        const int part = c / (D * D / 8), rem = c % (D * D / 8);
+        const int i = rem / (D / 8), j = (rem % (D / 8)) * 8;
+        *reinterpret_cast<Chunk16*>(Sl + (part * D + i) * LDSS + j) =
+            *reinterpret_cast<const Chunk16*>(src + (int64_t)c * 8);
+      }
+    } else {
+      const float* src = states + dir * bhtdd + fi * D * D;
+      for (int c = tid; c < D * D / 4; c += 256) {
+        const int i = c / (D / 4), j = (c % (D / 4)) * 4;
+        *reinterpret_cast<Chunk16*>(Sl + i * LDSS + j) = *reinterpret_cast<const Chunk16*>(src + (int64_t)c * 4);
+      }
     }
-  }
-  // uf[ct][r] = u_fwd(token n0 + lg*4 + r)[ct*16 + li]
-  float rf[4], rb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float sf2 = 0.f, sb2 = 0.f;
+    __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      sf2 += uf[ct][r] * uf[ct][r];
-      sb2 += ub[ct][r] * ub[ct][r];
-    }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      sf2 += __shfl_xor(sf2, m);
-      sb2 += __shfl_xor(sb2, m);
+      for (int rt = 0; rt < RT; ++rt) u[dir][rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          const typename MM::Frag sfr = MM::load(Sl + (part * D + ct * 16 + li) * LDSS + ks * KS + lg * KP);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) u[dir][rt][ct] = MM::run(qa[rt][ks], sfr, u[dir][rt][ct]);
+        }
+      }
     }
-    rf[r] = 1.f / sqrtf(sf2 / D + eps);
-    rb[r] = 1.f / sqrtf(sb2 / D + eps);
   }
-  const int64_t NL = (int64_t)T_ * N;
+
+  // u[dir][rt][ct][r] = u_dir(token n0 + rt*16 + lg*4 + r)[ct*16 + li]
+  float rn[2][RT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int nn = n0 + lg * 4 + r;
+  for (int dir = 0; dir < 2; ++dir)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) ss += u[dir][rt][ct][r] * u[dir][rt][ct][r];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) ss += __shfl_xor(ss, m);
+        rn[dir][rt][r] = 1.f / sqrtf(ss / D + eps);
+      }
+
+  __syncthreads();   // S no longer needed: reuse LDS for the fp32 output tile
+  float* Ol = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wave * 16 * RT + rt * 16 + lg * 4 + r;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int i = ct * 16 + li;
+        const float w = rms_w ? rms_w[h * D + i] : 1.f;
+        Ol[row * LDO + i] = (u[0][rt][ct][r] * rn[0][rt][r] + u[1][rt][ct][r] * rn[1][rt][r]) * w;
+      }
+    }
+  __syncthreads();
+  const int64_t NL = (int64_t)T_ * N;
+  constexpr int CPRO = D / EPC;          // 16-byte chunks per output row
+  for (int c = tid; c < kReadoutBT * CPRO; c += 256) {
+    const int row = c / CPRO, cc = c % CPRO;
+    const int nn = tile * kReadoutBT + row;
     if (nn >= N) continue;
     const int64_t orow = b * NL + (int64_t)t * N + nn;
+    float o[EPC];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int i = ct * 16 + li;
-      const float w = rms_w ? rms_w[h * D + i] : 1.f;
-      float val = (uf[ct][r] * rf[r] + ub[ct][r] * rb[r]) * w;
-      if (gate) val *= to_f32(gate[orow * ldg + h * D + i]);
-      out[orow * ldo + h * D + i] = from_f32<T>(val);
+    for (int x = 0; x < EPC; x += 4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(Ol + row * LDO + cc * EPC + x);
+      o[x] = v4.x; o[x + 1] = v4.y; o[x + 2] = v4.z; o[x + 3] = v4.w;
     }
+    if (gate) {
+      const Chunk16 gv = *reinterpret_cast<const Chunk16*>(gate + orow * ldg + h * D + cc * EPC);
+      const T* ge = reinterpret_cast<const T*>(&gv);
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) o[x] *= to_f32(ge[x]);
+    }
+    Chunk16 val;
+    T* ve = reinterpret_cast<T*>(&val);
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) ve[x] = from_f32<T>(o[x]);   // the only rounding of the output
+    *reinterpret_cast<Chunk16*>(out + orow * ldo + h * D + cc * EPC) = val;
   }
 }
 
@@ -373,27 +435,27 @@ hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_
 }
 
 hipError_t launch_vda_scan(int d, const float* M, const float* Cm, const float* gamma,
-                           float* states, int BH, int T, hipStream_t st) {
+                           float* states, bf16* split, int BH, int T, hipStream_t st) {
   if (BH == 0) return hipSuccess;
   const int64_t bhtdd = (int64_t)BH * T * d * d;
   dim3 grid(d / kScanRows, BH, 2);
-  if (d == 32) vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, T, bhtdd);
-  else if (d == 64) vda_scan_kernel<64, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, T, bhtdd);
-  else vda_scan_kernel<128, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, T, bhtdd);
+  if (d == 32) vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
+  else if (d == 64) vda_scan_kernel<64, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
+  else vda_scan_kernel<128, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t readout_t(int d, const void* q, const float* states, const float* rms_w,
-                            const void* gate, int64_t ldg, void* out, int64_t ldo, int B, int H,
-                            int T_, int N, float eps, hipStream_t st) {
+static hipError_t readout_t(int d, const void* q, const float* states, const bf16* split,
+                            const float* rms_w, const void* gate, int64_t ldg, void* out, int64_t ldo,
+                            int B, int H, int T_, int N, float eps, hipStream_t st) {
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
   const int64_t blocks = (int64_t)B * H * T_ * tpf;
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
   if (blocks == 0) return hipSuccess;
-#define VDN_READOUT(DD)                                                                   \
-  vda_readout_kernel<T, DD><<<(unsigned)blocks, 256, 0, st>>>(                            \
-      (const T*)q, states, rms_w, (const T*)gate, ldg, (T*)out, ldo, H, T_, N, eps, tpf, \
+#define VDN_READOUT(DD)                                                                         \
+  vda_readout_kernel<T, DD><<<(unsigned)blocks, 256, 0, st>>>(                                  \
+      (const T*)q, states, split, rms_w, (const T*)gate, ldg, (T*)out, ldo, H, T_, N, eps, tpf, \
       bhtdd)
   if (d == 32) VDN_READOUT(32);
   else if (d == 64) VDN_READOUT(64);
@@ -403,11 +465,11 @@ static hipError_t readout_t(int d, const void* q, const float* states, const flo
 }
 
 hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
-                              const float* rms_w, const void* gate, int64_t ldg, void* out,
-                              int64_t ldo, int B, int H, int T, int N, float eps,
+                              const bf16* split, const float* rms_w, const void* gate, int64_t ldg,
+                              void* out, int64_t ldo, int B, int H, int T, int N, float eps,
                               hipStream_t st) {
-  return dtype == 1 ? readout_t<bf16>(d, q, states, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st)
-                    : readout_t<float>(d, q, states, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st);
+  return dtype == 1 ? readout_t<bf16>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st)
+                    : readout_t<float>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st);
 }
 
 }  // namespace vdn

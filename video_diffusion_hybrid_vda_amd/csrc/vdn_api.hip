@@ -60,7 +60,8 @@ AttnParams make_attn_params(const vdn_shape* s) {
   AttnParams p;
   memset(&p, 0, sizeof(p));
   const int T = s->frames, N = s->tokens_per_frame, C = s->chunk_frames, W = s->window_chunks;
-  const int BM = kAttnBM, BN = kAttnBN;
+  const int BM = attn_query_tile(s->dtype, s->head_dim), BN = kAttnBN;
+  p.bm = BM;
   p.B = s->batch;
   p.H = s->heads;
   p.T = T;
@@ -104,7 +105,7 @@ AttnParams make_attn_params(const vdn_shape* s) {
 
 // ---- workspace layouts
 struct VdaLayout {
-  size_t am, bc, states, total;
+  size_t am, bc, states, split, total;
 };
 VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   const size_t dd = (size_t)s->head_dim * s->head_dim;
@@ -114,6 +115,8 @@ VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   l.am = off; off = align_up(off + frames * dd * 4);
   l.bc = off; off = align_up(off + frames * dd * 4);
   l.states = off; off = align_up(off + (need_states ? 2 * frames * dd * 4 : 0));
+  // bf16 I/O: states also as hi/lo bf16 pairs for the readout
+  l.split = off; off = align_up(off + (s->dtype == VDN_BF16 ? 2 * frames * dd * 2 * 2 : 0));
   l.total = off;
   return l;
 }
@@ -154,12 +157,12 @@ bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
 
 // ---- opt-in phase timing: HIP event pairs recorded around each phase
 enum Phase {
-  kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhGram, kPhSolve, kPhScan, kPhReadout, kPhOutGemm,
-  kNumPhases
+  kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhAnchorMerge, kPhGram, kPhSolve, kPhScan,
+  kPhReadout, kPhOutGemm, kNumPhases
 };
-const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm",  "window_attn",
-                                             "vda_gram",          "vda_solve",  "vda_scan",
-                                             "vda_readout",       "out_gemm"};
+const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "window_attn",
+                                             "anchor_merge",      "vda_gram",  "vda_solve",
+                                             "vda_scan",          "vda_readout", "out_gemm"};
 
 struct Timer {
   std::mutex mu;
@@ -209,6 +212,7 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   float* am = (float*)(ws + l.am);
   float* bc = (float*)(ws + l.bc);
   float* st_buf = states ? states : (float*)(ws + l.states);
+  __bf16* split = s->dtype == VDN_BF16 ? (__bf16*)(ws + l.split) : nullptr;
   const int d = s->head_dim;
   const int nframes = s->batch * s->heads * s->frames;
   hipError_t e;
@@ -221,12 +225,12 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda solve launch");
   ph = phase_begin(kPhScan, st);
-  e = launch_vda_scan(d, am, bc, gamma, st_buf, s->batch * s->heads, s->frames, st);
+  e = launch_vda_scan(d, am, bc, gamma, st_buf, split, s->batch * s->heads, s->frames, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda scan launch");
   ph = phase_begin(kPhReadout, st);
-  e = launch_vda_readout(s->dtype, d, q, st_buf, rms_w, gate, ldg, out, ldo, s->batch, s->heads,
-                         s->frames, s->tokens_per_frame, s->rms_eps, st);
+  e = launch_vda_readout(s->dtype, d, q, st_buf, split, rms_w, gate, ldg, out, ldo, s->batch,
+                         s->heads, s->frames, s->tokens_per_frame, s->rms_eps, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda readout launch");
   return VDN_OK;
@@ -246,10 +250,14 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
   p.ldo = ldo;
   p.part_o = (float*)(ws + l.part_o);
   p.part_ml = (float*)(ws + l.part_ml);
-  const int ph = phase_begin(kPhWindowAttn, st);
-  const hipError_t e = launch_window_attn(s->dtype, s->head_dim, p, st);
+  int ph = phase_begin(kPhWindowAttn, st);
+  hipError_t e = launch_window_attn(s->dtype, s->head_dim, p, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
+  ph = phase_begin(kPhAnchorMerge, st);
+  e = launch_attn_merge(s->dtype, s->head_dim, p, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "anchor merge launch");
   return VDN_OK;
 }
 

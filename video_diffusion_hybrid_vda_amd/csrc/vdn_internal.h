@@ -6,11 +6,18 @@
 
 namespace vdn {
 
-// Softmax-branch tiling: queries per workgroup and keys per LDS tile.
+// Softmax-branch tiling of the generic kernel: queries per workgroup and keys
+// per LDS tile.  bf16 with head_dim 128 runs the gfx950-specific kernel with
+// 256 queries per workgroup.
 constexpr int kAttnBM = 128;
 constexpr int kAttnBN = 64;
-// Linear-branch readout: tokens per workgroup.
-constexpr int kReadoutBT = 64;
+constexpr int kAttnBMv2 = 256;
+inline __host__ __device__ bool attn_uses_v2(int dtype, int d) { return dtype == 1 && d == 128; }
+inline __host__ __device__ int attn_query_tile(int dtype, int d) {
+  return attn_uses_v2(dtype, d) ? kAttnBMv2 : kAttnBM;
+}
+// Linear-branch readout: tokens per workgroup (4 waves x 32).
+constexpr int kReadoutBT = 128;
 // Linear-branch scan: state rows per workgroup.
 constexpr int kScanRows = 16;
 
@@ -40,6 +47,7 @@ struct AttnParams {
   int keys_per_split;
   int tiles_per_bh;
   int total;
+  int bm;             // queries per work item (attn_query_tile)
   float scale_log2;
 };
 
@@ -51,14 +59,15 @@ hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int
 hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, void* C, int M,
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st);
 hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st);
+hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st);
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
                            float* A, float* Bm, int nframes, int N, hipStream_t st);
 hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_t st);
 hipError_t launch_vda_scan(int d, const float* M, const float* Cm, const float* gamma,
-                           float* states, int BH, int T, hipStream_t st);
+                           float* states, __bf16* split, int BH, int T, hipStream_t st);
 hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
-                              const float* rms_w, const void* gate, int64_t ldg, void* out,
-                              int64_t ldo, int B, int H, int T, int N, float eps,
-                              hipStream_t st);
+                              const __bf16* split, const float* rms_w, const void* gate,
+                              int64_t ldg, void* out, int64_t ldo, int B, int H, int T, int N,
+                              float eps, hipStream_t st);
 
 }  // namespace vdn

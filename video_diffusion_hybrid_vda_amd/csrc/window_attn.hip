@@ -19,34 +19,25 @@
 
 namespace vdn {
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
-  using MM = Mma<T>;
-  constexpr int KP = MM::kPack, KS = MM::kStep;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int BM = kAttnBM, BN = kAttnBN;
-  constexpr int QW = BM / 4;           // queries per wave
-  constexpr int QT = QW / 16;          // query column tiles per wave
-  constexpr int KT = BN / 16;          // key row tiles per key tile
-  constexpr int DT = D / 16;           // head-dim tiles
-  constexpr int KSTEPS = D / KS;
-  constexpr int LDK = D + EPC;         // K tile row stride (elements)
-  constexpr int LDV = BN + EPC;        // V^T tile row stride (elements)
-  constexpr int CPR = D / EPC;         // 16-byte chunks per token row
-  __shared__ __attribute__((aligned(16))) T Ks[BN * LDK];
-  __shared__ __attribute__((aligned(16))) T Vt[D * LDV];
-
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int li = lane % 16, lg = lane / 16;
-
-  // ---- decode the work item
-  const int lid = xcd_remap(blockIdx.x, p.total);
-  const int bh = lid / p.tiles_per_bh;
-  const int w = lid - bh * p.tiles_per_bh;
-  const int b = bh / p.H, h = bh - b * p.H;
-  const int NL = p.T * p.N;
-  int qbeg, qend, nint = 0, pidx = -1, afr = 0;
+// One softmax work item: a tile of query tokens [qbeg, qend) of one (batch,
+// head) with up to three key-token intervals [kb, ke); pidx >= 0 marks one
+// key split of an anchor frame's rows (partials go to the merge kernel).
+struct WorkItem {
+  int bh, b, h, qbeg, qend, nint, pidx, afr;
   int kb[3], ke[3];
+};
+
+__device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
+  WorkItem wi;
+  const int lid = xcd_remap(blockIdx.x, p.total);
+  wi.bh = lid / p.tiles_per_bh;
+  const int w = lid - wi.bh * p.tiles_per_bh;
+  wi.b = wi.bh / p.H;
+  wi.h = wi.bh - wi.b * p.H;
+  const int NL = p.T * p.N;
+  wi.nint = 0;
+  wi.pidx = -1;
+  wi.afr = 0;
   if (w < p.n_window_tiles) {
     int c, j;
     if (p.nC == 1 || w < p.tiles0) {
@@ -62,13 +53,13 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
     }
     const int qf0 = max(c * p.C, p.a0);
     const int qf1 = min((c + 1) * p.C, p.T - p.a1);
-    qbeg = qf0 * p.N + j * BM;
-    qend = min(qbeg + BM, qf1 * p.N);
+    wi.qbeg = qf0 * p.N + j * BM;
+    wi.qend = min(wi.qbeg + BM, qf1 * p.N);
     const int kf0 = max(0, (c - p.W) * p.C);
     const int kf1 = min(p.T, (c + p.W + 1) * p.C);
-    if (p.a0 && kf0 > 0) { kb[nint] = 0; ke[nint] = p.N; ++nint; }
-    kb[nint] = kf0 * p.N; ke[nint] = kf1 * p.N; ++nint;
-    if (p.a1 && kf1 < p.T) { kb[nint] = (p.T - 1) * p.N; ke[nint] = NL; ++nint; }
+    if (p.a0 && kf0 > 0) { wi.kb[wi.nint] = 0; wi.ke[wi.nint] = p.N; ++wi.nint; }
+    wi.kb[wi.nint] = kf0 * p.N; wi.ke[wi.nint] = kf1 * p.N; ++wi.nint;
+    if (p.a1 && kf1 < p.T) { wi.kb[wi.nint] = (p.T - 1) * p.N; wi.ke[wi.nint] = NL; ++wi.nint; }
   } else {
     int u = w - p.n_window_tiles;
     const int per_anchor = p.nsplit * p.tiles_per_anchor;
@@ -76,14 +67,61 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
     u -= a * per_anchor;
     const int s = u / p.tiles_per_anchor;
     const int j = u - s * p.tiles_per_anchor;
-    afr = p.anchor_frame[a];
-    qbeg = afr * p.N + j * BM;
-    qend = min(qbeg + BM, (afr + 1) * p.N);
-    kb[0] = s * p.keys_per_split;
-    ke[0] = min(kb[0] + p.keys_per_split, NL);
-    nint = 1;
-    if (p.nsplit > 1) pidx = ((a * p.B + b) * p.H + h) * p.nsplit + s;
+    wi.afr = p.anchor_frame[a];
+    wi.qbeg = wi.afr * p.N + j * BM;
+    wi.qend = min(wi.qbeg + BM, (wi.afr + 1) * p.N);
+    wi.kb[0] = s * p.keys_per_split;
+    wi.ke[0] = min(wi.kb[0] + p.keys_per_split, NL);
+    wi.nint = 1;
+    if (p.nsplit > 1) wi.pidx = ((a * p.B + wi.b) * p.H + wi.h) * p.nsplit + s;
   }
+  for (int i = wi.nint; i < 3; ++i) { wi.kb[i] = 0; wi.ke[i] = 0; }
+  // Every field is uniform across the workgroup; the runtime integer divisions
+  // above run on the vector unit, so pin the results to scalar registers.
+  wi.bh = __builtin_amdgcn_readfirstlane(wi.bh);
+  wi.b = __builtin_amdgcn_readfirstlane(wi.b);
+  wi.h = __builtin_amdgcn_readfirstlane(wi.h);
+  wi.qbeg = __builtin_amdgcn_readfirstlane(wi.qbeg);
+  wi.qend = __builtin_amdgcn_readfirstlane(wi.qend);
+  wi.nint = __builtin_amdgcn_readfirstlane(wi.nint);
+  wi.pidx = __builtin_amdgcn_readfirstlane(wi.pidx);
+  wi.afr = __builtin_amdgcn_readfirstlane(wi.afr);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    wi.kb[i] = __builtin_amdgcn_readfirstlane(wi.kb[i]);
+    wi.ke[i] = __builtin_amdgcn_readfirstlane(wi.ke[i]);
+  }
+  return wi;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
+  using MM = Mma<T>;
+  constexpr int KP = MM::kPack, KS = MM::kStep;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int BM = kAttnBM, BN = kAttnBN;   // the generic kernel's query tile
+  constexpr int QW = BM / 4;           // queries per wave
+  constexpr int QT = QW / 16;          // query column tiles per wave
+  constexpr int KT = BN / 16;          // key row tiles per key tile
+  constexpr int DT = D / 16;           // head-dim tiles
+  constexpr int KSTEPS = D / KS;
+  constexpr int LDK = D + EPC;         // K tile row stride (elements)
+  constexpr int LDV = BN + EPC;        // V^T tile row stride (elements)
+  constexpr int CPR = D / EPC;         // 16-byte chunks per token row
+  __shared__ __attribute__((aligned(16))) T Ks[BN * LDK];
+  __shared__ __attribute__((aligned(16))) T Vt[D * LDV];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int li = lane % 16, lg = lane / 16;
+
+  // ---- decode the work item
+  const WorkItem wi = decode_work(p, BM);
+  const int bh = wi.bh, b = wi.b, h = wi.h, qbeg = wi.qbeg, qend = wi.qend, nint = wi.nint;
+  const int pidx = wi.pidx, afr = wi.afr;
+  const int NL = p.T * p.N;
+  int kb[3], ke[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) { kb[i] = wi.kb[i]; ke[i] = wi.ke[i]; }
 
   const T* Qb = (const T*)p.q + (int64_t)bh * NL * D;
   const T* Kb = (const T*)p.k + (int64_t)bh * NL * D;
@@ -251,6 +289,300 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, head_dim 128: the production kernel for the workload shapes.
+//
+// 4 waves x 64 queries = 256 queries per workgroup; 64-key tiles; 32x32x16
+// MFMA.  K and V tiles are copied global -> LDS by the direct-to-LDS DMA path
+// (global_load_lds_dwordx4: lane l writes bytes [16 l, 16 l + 16) of a 1 KB
+// block), in a three-stage ring so tile t+2 streams in while tile t is
+// computed; one barrier per tile.  Both tiles stay row-major in LDS with the
+// 16-byte chunks of each row XOR-swizzled; K fragments are plain 16-byte LDS
+// reads, V fragments are ds_read_b64_tr_b16 transpose reads.  Within a group
+// of 16 lanes that instruction hands lane i the element i%4 of the 8-byte
+// loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4, so a group that loads a
+// 4-key x 16-dim block of row-major V receives, per lane, four consecutive
+// keys of one dimension: the MFMA A operand of O^T = V^T P^T.
+//
+// The running max is refreshed lazily: the output accumulators are rescaled
+// only when some row max of the wave grows by more than 1 in log2 units, so
+// probabilities stay <= 2.  On the near-uniform softmax of unit-norm keys this
+// never triggers after the first tile; on peaked softmax it keeps the
+// dominant probability at (or next to) 1, as exact as a strict running max.
+namespace v2 {
+constexpr int BM = 256, BN = 64, D = 128, STAGES = 3;
+constexpr int ROWB = D * 2;          // bytes per K/V row
+constexpr int TILEB = BN * ROWB;     // 16 KB
+constexpr int STAGEB = 2 * TILEB;    // K tile then V tile
+constexpr float kRescaleSlack = 1.f;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Physical 16-byte chunk of logical chunk c in row r.  For 16 consecutive
+// rows at a fixed chunk (K reads) the 16 results are distinct; for 8 aligned
+// rows x 4 aligned chunks (V transpose reads) each value appears twice, i.e.
+// two passes over the 64 banks, the minimum for 512 bytes.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+}  // namespace v2
+
+__global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p) {
+  using namespace v2;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
+
+  // wave index as a scalar: the DMA's LDS destination (M0) must be wave-uniform
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
+
+  const WorkItem wi = decode_work(p, BM);
+  const int NL = p.T * p.N;
+  const bf16* Qb = (const bf16*)p.q + (int64_t)wi.bh * NL * D;
+  const bf16* Kb = (const bf16*)p.k + (int64_t)wi.bh * NL * D;
+  const bf16* Vb = (const bf16*)p.v + (int64_t)wi.bh * NL * D;
+
+  int ntiles = 0;
+#pragma unroll
+  for (int iv = 0; iv < 3; ++iv)
+    if (iv < wi.nint) ntiles += (wi.ke[iv] - wi.kb[iv] + BN - 1) / BN;
+
+  // Loader.  One buffer descriptor per tensor and key interval (base = this
+  // (batch, head), record count = end of the interval), so rows past the
+  // interval read as zero and are masked out of the softmax.  Each lane's
+  // byte offset inside a 64-row tile is fixed: row blk*4 + lane/16, logical
+  // chunk swz(row, lane%16) lands at physical chunk lane%16.
+  int lane_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 4 + lane / 16;
+    lane_off[i] = row * ROWB + swz(row, lane % 16) * 16;
+  }
+  // interval bounds picked without dynamic indexing, as wave-uniform scalars
+  const int kb0 = wi.kb[0], kb1 = wi.kb[1], kb2 = wi.kb[2];
+  const int ke0 = wi.ke[0], ke1 = wi.ke[1], ke2 = wi.ke[2];
+  auto kb_of = [&](int i) { return i == 0 ? kb0 : (i == 1 ? kb1 : kb2); };
+  auto ke_of = [&](int i) { return i == 0 ? ke0 : (i == 1 ? ke1 : ke2); };
+  int liv = 0, lk0 = kb_of(0), lke = ke_of(0);
+  __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, lke * ROWB, 0x00020000);
+  __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, lke * ROWB, 0x00020000);
+  auto issue = [&](unsigned char* sb) {
+    const int base = lk0 * ROWB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sb + blk * 1024),
+                                               16, base + lane_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sb + TILEB + blk * 1024),
+                                               16, base + lane_off[i], 0, 0, 0);
+    }
+    lk0 += BN;
+    if (lk0 >= lke) {
+      ++liv;
+      if (liv < wi.nint) {
+        lk0 = kb_of(liv);
+        lke = ke_of(liv);
+        rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, lke * ROWB, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, lke * ROWB, 0x00020000);
+      }
+    }
+  };
+
+  if (ntiles > 0) issue(ring);
+  if (ntiles > 1) issue(ring + STAGEB);
+
+  // Q fragments: B operand of S^T = K Q^T; lane holds Q[query l32][16 ks + 8 h .. +7]
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qrow = wi.qbeg + wave * 64 + qt * 32 + l32;
+    const bool ok = qrow < wi.qend;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qf[qt][ks] = ok ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)qrow * D + ks * 16 + h * 8)
+                      : bf16x8{};
+  }
+
+  f32x16 o[4][2];
+  float mrun[2], lsum[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    mrun[qt] = -INFINITY;
+    lsum[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt][qt] = f32x16{};
+  }
+  const float c2 = p.scale_log2;
+  int civ = 0, ck0 = kb_of(0), cke = ke_of(0);
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 s[2][2];
+  float mtile[2];
+
+  // S^T = K Q^T for the tile in stage sb, masking keys >= kn, and the tile's
+  // per-query max (scaled, base 2) in mtile.
+  auto scores = [&](const unsigned char* sb, int kn) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kt * 32 + l32;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + row * ROWB + swz(row, 2 * ks + h) * 16);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mma(kf, qf[qt][ks], s[kt][qt]);
+      }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      if (kn < BN) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kt * 32 + 8 * (r / 4) + 4 * h + (r % 4) >= kn) s[kt][qt][r] = -INFINITY;
+      }
+      float mx = s[0][qt][0];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
+      mtile[qt] = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    }
+  };
+
+  // p = 2^(s c2 - mrun), row sums, then O^T += V^T P^T over four 16-key steps.
+  auto accumulate = [&](const unsigned char* sb) {
+    // pk[qt][s4] = bf16 P^T operand of the 16-key step s4 (accumulator
+    // registers 8(s4%2) .. +7 of key tile s4/2)
+    bf16x8 pk[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mneg = -mrun[qt];
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(s[kt][qt][r], c2, mneg));
+          ps += e;
+          pk[qt][2 * kt + r / 8][r % 8] = (bf16)e;
+        }
+      lsum[qt] += ps;
+    }
+    const unsigned char* vb = sb + TILEB;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int rowA = 16 * s4 + 4 * (g >> 1) + (j16 >> 2);
+      const int rowB = rowA + 8;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+        const int cch = dcol >> 3, off = (dcol & 7) * 2;
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + rowA * ROWB + swz(rowA, cch) * 16 + off));
+        const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vb + rowB * ROWB + swz(rowB, cch) * 16 + off));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mma(vf, pk[qt][s4], o[dt][qt]);
+      }
+    }
+  };
+
+  // Close tile t: advance the compute cursor, wait for tile t+2, barrier.
+  auto finish = [&]() {
+    ck0 += BN;
+    if (ck0 >= cke) {
+      ++civ;
+      if (civ < wi.nint) {
+        ck0 = kb_of(civ);
+        cke = ke_of(civ);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  // The hot loop never touches O on the vector unit (O lives in the matrix
+  // accumulators); a tile whose max outruns the running max by more than the
+  // slack leaves the loop, O is rescaled once, and the loop resumes.
+  int t = 0;
+  while (t < ntiles) {
+    for (; t < ntiles; ++t) {
+      const unsigned char* sb = ring + (t % STAGES) * STAGEB;
+      if (t + 2 < ntiles) issue(ring + ((t + 2) % STAGES) * STAGEB);
+      scores(sb, min(BN, cke - ck0));
+      if (__any(mtile[0] > mrun[0] + kRescaleSlack || mtile[1] > mrun[1] + kRescaleSlack)) break;
+      accumulate(sb);
+      finish();
+    }
+    if (t >= ntiles) break;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float mnew = fmaxf(mrun[qt], mtile[qt]);
+      const float alpha = fast_exp2(mrun[qt] - mnew);
+      mrun[qt] = mnew;
+      lsum[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+    }
+    accumulate(ring + (t % STAGES) * STAGEB);
+    finish();
+    ++t;
+  }
+
+  // ---- epilogue: o[dt][qt][r] = O(query 32 qt + l32, dim 32 dt + 8(r/4) + 4h + r%4)
+  const bf16* gate = (const bf16*)p.gate;
+  bf16* out = (bf16*)p.out;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = lsum[qt] + __shfl_xor(lsum[qt], 32);
+    const int qrow = wi.qbeg + wave * 64 + qt * 32 + l32;
+    if (qrow >= wi.qend) continue;
+    if (wi.pidx < 0) {
+      const float inv = 1.f / lt;
+      const int64_t orow = (int64_t)wi.b * NL + qrow;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * h;
+          float v0 = o[dt][qt][4 * r4] * inv, v1 = o[dt][qt][4 * r4 + 1] * inv;
+          float v2 = o[dt][qt][4 * r4 + 2] * inv, v3 = o[dt][qt][4 * r4 + 3] * inv;
+          if (gate) {
+            const bf16x4 gv = *reinterpret_cast<const bf16x4*>(gate + orow * p.ldg + wi.h * D + d0);
+            v0 *= (float)gv[0]; v1 *= (float)gv[1]; v2 *= (float)gv[2]; v3 *= (float)gv[3];
+          }
+          bf16x4 ov;
+          ov[0] = (bf16)v0; ov[1] = (bf16)v1; ov[2] = (bf16)v2; ov[3] = (bf16)v3;
+          *reinterpret_cast<bf16x4*>(out + orow * p.ldo + wi.h * D + d0) = ov;
+        }
+      if (p.lse && h == 0) p.lse[(int64_t)wi.bh * NL + qrow] = (mrun[qt] + log2f(lt)) * kLn2;
+    } else {
+      const int64_t prow = (int64_t)wi.pidx * p.N + (qrow - wi.afr * p.N);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * h;
+          *reinterpret_cast<float4*>(p.part_o + prow * D + d0) =
+              make_float4(o[dt][qt][4 * r4], o[dt][qt][4 * r4 + 1], o[dt][qt][4 * r4 + 2], o[dt][qt][4 * r4 + 3]);
+        }
+      if (h == 0) {
+        p.part_ml[prow * 2] = mrun[qt];
+        p.part_ml[prow * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
 // Combine the key splits of the anchor query rows: out = sum_s 2^(m_s - M) O_s
 // / sum_s 2^(m_s - M) l_s, then gate.  One thread per (query, quarter of d).
 template <typename T, int D>
@@ -297,18 +629,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 
 template <typename T, int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
-  if (p.total > 0) window_attn_kernel<T, D><<<p.total, 256, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (p.total > 0) {
+    if (attn_uses_v2(sizeof(T) == 2 ? 1 : 0, D))
+      window_attn_bf16_d128_kernel<<<p.total, 256, 0, st>>>(p);
+    else
+      window_attn_kernel<T, D><<<p.total, 256, 0, st>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_merge_t(const AttnParams& p, hipStream_t st) {
   if (p.nsplit > 1 && p.nA > 0) {
     const int blocks = p.nA * p.B * p.H * ((p.N + 63) / 64);
     attn_merge_kernel<T, D><<<blocks, 256, 0, st>>>(p);
-    e = hipGetLastError();
   }
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st) {
+  if (p.bm != attn_query_tile(dtype, d)) return hipErrorInvalidValue;
   if (dtype == 1) {
     if (d == 32) return launch_attn_t<bf16, 32>(p, st);
     if (d == 64) return launch_attn_t<bf16, 64>(p, st);
@@ -317,6 +657,17 @@ hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t
   if (d == 32) return launch_attn_t<float, 32>(p, st);
   if (d == 64) return launch_attn_t<float, 64>(p, st);
   return launch_attn_t<float, 128>(p, st);
+}
+
+hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st) {
+  if (dtype == 1) {
+    if (d == 32) return launch_merge_t<bf16, 32>(p, st);
+    if (d == 64) return launch_merge_t<bf16, 64>(p, st);
+    return launch_merge_t<bf16, 128>(p, st);
+  }
+  if (d == 32) return launch_merge_t<float, 32>(p, st);
+  if (d == 64) return launch_merge_t<float, 64>(p, st);
+  return launch_merge_t<float, 128>(p, st);
 }
 
 }  // namespace vdn
