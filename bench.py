@@ -30,6 +30,14 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the window/anchor softmax kernel on the 102-frame layer, from two
+# rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy calibration
+# (profiles/window_attn_T102_hbm_counters.md).  Valid only for the kernel sources they were
+# taken on: reported as null once those sources change.
+WINDOW_TRAFFIC_BYTES = 240463359256
+WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
+WINDOW_TRAFFIC_SHA = "9b4eb063485a32fb"
+
 
 def frame_key_counts(T, C, W, a0, a1):
     """Allowed key frames of each query frame under the chunk-window/anchor rule."""
@@ -56,6 +64,19 @@ def window_flops(cfg):
         frame_key_counts(cfg.frames, cfg.chunk_frames, cfg.window_chunks,
                          cfg.anchor_first, cfg.anchor_last))
     return 4 * cfg.head_dim * cfg.batch * cfg.heads * pairs_per_head, pairs_per_head
+
+
+def window_traffic(cfg_name):
+    """Measured HBM bytes per window-kernel launch, or None if the workload or the kernel sources
+    differ from the ones the counters were taken on."""
+    import hashlib
+    if "T102" not in cfg_name:
+        return None
+    h = hashlib.sha256()
+    for f in WINDOW_TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "video_diffusion_hybrid_vda_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return WINDOW_TRAFFIC_BYTES if h.hexdigest()[:16] == WINDOW_TRAFFIC_SHA else None
 
 
 def cpu_baseline(cfg, inp):
@@ -122,6 +143,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=4, help="workload index (3 or 4 are full layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="before the timed region, run one plain device-to-device copy of this many MiB "
+                         "(a known-traffic kernel for scaling HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -144,6 +168,14 @@ def main():
         vdn.vdn_hybrid_attn_fwd(shape, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"],
                                 inp["beta"], inp["w_gs"], inp["w_gl"], inp["rms_w"], inp["w_os"],
                                 inp["w_ol"], out, ws)
+
+    if args.calibrate_copy_mb > 0:
+        src = torch.ones(args.calibrate_copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -191,7 +223,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "window_attn", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
-                     "traffic": None},
+                     "traffic": window_traffic(cfg.name)},
         "gpu_ms_per_step": round(gpu_ms_per_step, 3),
         "phases_ms": phase_ms,
     }

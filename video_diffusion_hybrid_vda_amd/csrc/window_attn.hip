@@ -292,17 +292,28 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 // bf16, head_dim 128: the production kernel for the workload shapes.
 //
-// 4 waves x 64 queries = 256 queries per workgroup; 64-key tiles; 32x32x16
-// MFMA.  K and V tiles are copied global -> LDS by the direct-to-LDS DMA path
-// (global_load_lds_dwordx4: lane l writes bytes [16 l, 16 l + 16) of a 1 KB
-// block), in a three-stage ring so tile t+2 streams in while tile t is
-// computed; one barrier per tile.  Both tiles stay row-major in LDS with the
-// 16-byte chunks of each row XOR-swizzled; K fragments are plain 16-byte LDS
-// reads, V fragments are ds_read_b64_tr_b16 transpose reads.  Within a group
-// of 16 lanes that instruction hands lane i the element i%4 of the 8-byte
-// loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4, so a group that loads a
-// 4-key x 16-dim block of row-major V receives, per lane, four consecutive
-// keys of one dimension: the MFMA A operand of O^T = V^T P^T.
+// 4 waves x 64 queries = 256 queries per workgroup, one wave per SIMD;
+// 64-key tiles; 32x32x16 MFMA.  K and V tiles are copied global -> LDS by the
+// direct-to-LDS DMA path (a buffer load with the lds modifier: lane l writes
+// bytes [16 l, 16 l + 16) of a 1 KB block) through a four-stage ring, so
+// tiles t+1 .. t+3 stream in while tile t is consumed; one barrier per tile.
+// Both tiles stay row-major in LDS with the 16-byte chunks of each row
+// XOR-swizzled; K fragments are plain 16-byte LDS reads, V fragments are
+// ds_read_b64_tr_b16 transpose reads.  Within a group of 16 lanes that
+// instruction hands lane i the element i%4 of the 8-byte loads of lanes i/4,
+// 4+i/4, 8+i/4, 12+i/4, so a group that loads a 4-key x 16-dim block of
+// row-major V receives, per lane, four consecutive keys of one dimension:
+// the MFMA A operand of O^T = V^T P^T.
+//
+// With one wave per SIMD the vector work of the softmax only overlaps the
+// matrix work if the wave's own instruction stream interleaves them, so the
+// loop is software-pipelined over half tiles of 32 keys: while the matrix
+// unit computes the scores of half tile j+1 and then P V of half tile j, the
+// vector unit computes the exponentials of half tile j and then the max of
+// half tile j+1.  Scores are produced in vector registers (the softmax reads
+// them there), O, Q and the row sums live in the accumulator registers; the
+// row sums are ones^T P^T on the matrix unit, because the vector unit is the
+// busier one.
 //
 // The running max is refreshed lazily: the output accumulators are rescaled
 // only when some row max of the wave grows by more than 1 in log2 units, so
@@ -310,11 +321,13 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
 // never triggers after the first tile; on peaked softmax it keeps the
 // dominant probability at (or next to) 1, as exact as a strict running max.
 namespace v2 {
-constexpr int BM = 256, BN = 64, D = 128, STAGES = 3;
+constexpr int BM = 256, BN = 64, D = 128, STAGES = 4;
 constexpr int ROWB = D * 2;          // bytes per K/V row
 constexpr int TILEB = BN * ROWB;     // 16 KB
 constexpr int STAGEB = 2 * TILEB;    // K tile then V tile
 constexpr float kRescaleSlack = 1.f;
+constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt not waited for)
+constexpr int kWaitVm8 = 0x0F78;   // s_waitcnt vmcnt(8): all but the last tile's eight loads done
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -327,6 +340,39 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | 
 
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scheduling fences.  pin(x) makes x look redefined at this point, so code
+// that produces x stays above it and code that consumes x stays below it;
+// chunk_fence() keeps memory operations on their side and ends a machine
+// scheduling region.  Both emit no instructions.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
+template <typename T>
+__device__ __forceinline__ void pin_acc(T& x) { asm volatile("" : "+a"(x)); }   // same, in the accumulator file
+__device__ __forceinline__ void chunk_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Score products written out so that their results land in vector registers
+// (where the softmax reads them) while O stays in the accumulator file.  The
+// first step of a chain starts from zero, later steps accumulate in place
+// (back-to-back accumulation into the same registers needs no wait states);
+// the vector unit reads a score buffer only eight or more MFMAs after its last
+// write.
+__device__ __forceinline__ void mma_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
+// max of x over lanes i and i ^ 32 (the swap exchanges the upper half of the
+// first operand with the lower half of the second)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 }  // namespace v2
 
@@ -349,11 +395,11 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   for (int iv = 0; iv < 3; ++iv)
     if (iv < wi.nint) ntiles += (wi.ke[iv] - wi.kb[iv] + BN - 1) / BN;
 
-  // Loader.  One buffer descriptor per tensor and key interval (base = this
-  // (batch, head), record count = end of the interval), so rows past the
-  // interval read as zero and are masked out of the softmax.  Each lane's
-  // byte offset inside a 64-row tile is fixed: row blk*4 + lane/16, logical
-  // chunk swz(row, lane%16) lands at physical chunk lane%16.
+  // Loader.  One buffer descriptor per tensor covering this (batch, head):
+  // rows past its end read as zero; rows past the end of a key interval are
+  // real keys of other frames and are masked out of the softmax.  Each
+  // lane's byte offset inside a 64-row tile is fixed: row blk*4 + lane/16,
+  // logical chunk swz(row, lane%16) lands at physical chunk lane%16.
   int lane_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -366,17 +412,23 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   auto kb_of = [&](int i) { return i == 0 ? kb0 : (i == 1 ? kb1 : kb2); };
   auto ke_of = [&](int i) { return i == 0 ? ke0 : (i == 1 ? ke1 : ke2); };
   int liv = 0, lk0 = kb_of(0), lke = ke_of(0);
-  __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, lke * ROWB, 0x00020000);
-  __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, lke * ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, NL * ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, NL * ROWB, 0x00020000);
+  // The DMA is written as an opaque instruction: the compiler would otherwise
+  // make every later LDS read wait for it (it cannot tell the stages apart);
+  // the loop below waits for each tile's loads explicitly (vmcnt) before the
+  // barrier that publishes the tile.
   auto issue = [&](unsigned char* sb) {
     const int base = lk0 * ROWB;
+    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)sb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int blk = wave * 4 + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sb + blk * 1024),
-                                               16, base + lane_off[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sb + TILEB + blk * 1024),
-                                               16, base + lane_off[i], 0, 0, 0);
+      const int voff = base + lane_off[i];
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk), "{m0}"(lds + blk * 1024)
+                   : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv), "{m0}"(lds + TILEB + blk * 1024)
+                   : "memory");
     }
     lk0 += BN;
     if (lk0 >= lke) {
@@ -384,14 +436,15 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       if (liv < wi.nint) {
         lk0 = kb_of(liv);
         lke = ke_of(liv);
-        rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, lke * ROWB, 0x00020000);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, lke * ROWB, 0x00020000);
       }
     }
   };
 
+  // ring of four 64-key stages: tiles t+1 .. t+3 resident or in flight while
+  // tile t is consumed
   if (ntiles > 0) issue(ring);
   if (ntiles > 1) issue(ring + STAGEB);
+  if (ntiles > 2) issue(ring + 2 * STAGEB);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds Q[query l32][16 ks + 8 h .. +7]
   bf16x8 qf[2][8];
@@ -404,100 +457,32 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       qf[qt][ks] = ok ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)qrow * D + ks * 16 + h * 8)
                       : bf16x8{};
   }
+  // Q lives in the accumulator file (the score products read it from there)
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) pin_acc(qf[qt][ks]);
 
-  f32x16 o[4][2];
-  float mrun[2], lsum[2];
+  // O^T accumulators and the row sums of p: lsum[qt] = ones^T P^T on the
+  // matrix unit, so every register of a lane holds the full row sum of its
+  // query (of the bf16 p, the weights the P V product uses)
+  f32x16 o[4][2], lsum[2];
+  float mrun[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     mrun[qt] = -INFINITY;
-    lsum[qt] = 0.f;
+    lsum[qt] = f32x16{};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt][qt] = f32x16{};
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.f;
   const float c2 = p.scale_log2;
+  // compute cursor: first key and interval end of the tile whose scores are
+  // the most recent ones
   int civ = 0, ck0 = kb_of(0), cke = ke_of(0);
-
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  f32x16 s[2][2];
-  float mtile[2];
-
-  // S^T = K Q^T for the tile in stage sb, masking keys >= kn, and the tile's
-  // per-query max (scaled, base 2) in mtile.
-  auto scores = [&](const unsigned char* sb, int kn) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int row = kt * 32 + l32;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sb + row * ROWB + swz(row, 2 * ks + h) * 16);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mma(kf, qf[qt][ks], s[kt][qt]);
-      }
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (kn < BN) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kt * 32 + 8 * (r / 4) + 4 * h + (r % 4) >= kn) s[kt][qt][r] = -INFINITY;
-      }
-      float mx = s[0][qt][0];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
-      mtile[qt] = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    }
-  };
-
-  // p = 2^(s c2 - mrun), row sums, then O^T += V^T P^T over four 16-key steps.
-  auto accumulate = [&](const unsigned char* sb) {
-    // pk[qt][s4] = bf16 P^T operand of the 16-key step s4 (accumulator
-    // registers 8(s4%2) .. +7 of key tile s4/2)
-    bf16x8 pk[2][4];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float mneg = -mrun[qt];
-      float ps = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kt][qt][r], c2, mneg));
-          ps += e;
-          pk[qt][2 * kt + r / 8][r % 8] = (bf16)e;
-        }
-      lsum[qt] += ps;
-    }
-    const unsigned char* vb = sb + TILEB;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int rowA = 16 * s4 + 4 * (g >> 1) + (j16 >> 2);
-      const int rowB = rowA + 8;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
-        const int cch = dcol >> 3, off = (dcol & 7) * 2;
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vb + rowA * ROWB + swz(rowA, cch) * 16 + off));
-        const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vb + rowB * ROWB + swz(rowB, cch) * 16 + off));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mma(vf, pk[qt][s4], o[dt][qt]);
-      }
-    }
-  };
-
-  // Close tile t: advance the compute cursor, wait for tile t+2, barrier.
-  auto finish = [&]() {
+  auto advance = [&]() {
     ck0 += BN;
     if (ck0 >= cke) {
       ++civ;
@@ -506,36 +491,208 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
         cke = ke_of(civ);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   };
 
-  // The hot loop never touches O on the vector unit (O lives in the matrix
-  // accumulators); a tile whose max outruns the running max by more than the
-  // slack leaves the loop, O is rescaled once, and the loop resumes.
-  int t = 0;
-  while (t < ntiles) {
-    for (; t < ntiles; ++t) {
-      const unsigned char* sb = ring + (t % STAGES) * STAGEB;
-      if (t + 2 < ntiles) issue(ring + ((t + 2) % STAGES) * STAGEB);
-      scores(sb, min(BN, cke - ck0));
-      if (__any(mtile[0] > mrun[0] + kRescaleSlack || mtile[1] > mrun[1] + kRescaleSlack)) break;
-      accumulate(sb);
-      finish();
+  // Q and the first three tiles resident; no vector-memory load is pending
+  // anywhere in the loop except the DMA the loop itself waits for
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  // The softmax runs on half tiles of 32 keys.  Scores of two half tiles are
+  // live at once: the current one (read by the softmax) and the next one
+  // (written by the matrix unit meanwhile).  sc[qt] register r holds the
+  // score of key 8(r/4) + 4h + r%4 of the half tile for query 32 qt + l32.
+  f32x16 sa[2], sb[2];
+  float mtile[2];
+
+  // K fragment of 16-column step ks, rows 32 kt + l32
+  auto load_k = [&](const unsigned char* stage, int kt, int ks) {
+    const int row = kt * 32 + l32;
+    return *reinterpret_cast<const bf16x8*>(stage + row * ROWB + swz(row, 2 * ks + h) * 16);
+  };
+  // V^T fragments of 16-key step s4 of the tile for the four 32-wide column blocks
+  auto load_v = [&](bf16x8 (&vf)[4], const unsigned char* stage, int s4) {
+    const unsigned char* vb = stage + TILEB;
+    const int rowA = 16 * s4 + 4 * (g >> 1) + (j16 >> 2);
+    const int rowB = rowA + 8;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+      const int cch = dcol >> 3, off = (dcol & 7) * 2;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vb + rowA * ROWB + swz(rowA, cch) * 16 + off));
+      const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vb + rowB * ROWB + swz(rowB, cch) * 16 + off));
+      vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    if (t >= ntiles) break;
+  };
+  // keys >= lim of a half tile get score -inf
+  auto mask = [&](f32x16 (&sc)[2], int lim) {
+    const int l = lim - 4 * h;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) >= l) sc[qt][r] = -INFINITY;
+  };
+  // raise the running max to the tile max if it outruns it by more than the
+  // slack, rescaling O and the row sums
+  auto refresh = [&]() {
+    if (__any(mtile[0] > mrun[0] + kRescaleSlack || mtile[1] > mrun[1] + kRescaleSlack)) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float mnew = fmaxf(mrun[qt], mtile[qt]);
+        const float alpha = fast_exp2(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        pin_acc(lsum[qt]);
+        lsum[qt] *= alpha;
+        pin_acc(lsum[qt]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          pin_acc(o[dt][qt]);   // O is copied out here, not on the common path
+          o[dt][qt] *= alpha;
+          pin_acc(o[dt][qt]);
+        }
+      }
+    }
+  };
+
+  // per-query max of a half tile's scores (scaled, base 2) in mtile; the two
+  // half-waves hold the two key halves of each query
+  auto half_max = [&](const f32x16 (&sc)[2]) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const float mnew = fmaxf(mrun[qt], mtile[qt]);
-      const float alpha = fast_exp2(mrun[qt] - mnew);
-      mrun[qt] = mnew;
-      lsum[qt] *= alpha;
+      float mx = sc[qt][0];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qt][r]);
+      mtile[qt] = halves_max(mx) * c2;
+      pin(mtile[qt]);
     }
-    accumulate(ring + (t % STAGES) * STAGEB);
-    finish();
-    ++t;
+  };
+  // between half steps: mask a partial half tile (keys >= lim), then raise
+  // the running max if needed; neither happens on most half tiles
+  auto boundary = [&](f32x16 (&sc)[2], int lim) {
+    if (lim < 32) {
+      asm volatile("");   // a real branch: the masking stays off the common path
+      mask(sc, lim);
+      half_max(sc);
+    }
+    refresh();
+  };
+
+  // One half step: the softmax and P V of the current half tile (scores in
+  // cur, half pkt of the tile in stage pst) run beside the scores of the next
+  // half tile (half skt of the tile in stage sst), which are then reduced to
+  // their max; the matrix unit works while the vector unit does the
+  // exponentials.  It is laid out as chunks (one 16-column step of the scores
+  // or one 16-key step of P V, each with its share of vector work and the
+  // operand reads of a later chunk) that are fenced against each other: the
+  // score chunks carry p of the first 16 keys, the first P V chunk p of the
+  // other 16, the second P V chunk the max of the next scores.  p is rounded
+  // to bf16 for the products.
+  auto half_step = [&](const f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* sst, int skt,
+                       const unsigned char* pst, int pkt) {
+    bf16x8 kf[3], vf[2][4], pk[2][2];
+    // p of registers r0, r0+1 of query tile qt (16-key step r0 / 8)
+    auto soft2 = [&](int qt, int r0) {
+      const float mneg = -mrun[qt];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pk[qt][r0 >> 3][(r0 & 7) + i] = (bf16)fast_exp2(fmaf(cur[qt][r0 + i], c2, mneg));
+    };
+    kf[0] = load_k(sst, skt, 0);
+    kf[1] = load_k(sst, skt, 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      chunk_fence();
+      if (ks < 6) kf[(ks + 2) % 3] = load_k(sst, skt, ks + 2);
+      if (ks == 6) load_v(vf[0], pst, 2 * pkt);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        if (ks == 0) mma_first(nxt[qt], kf[ks % 3], qf[qt][ks]);
+        else mma_acc(nxt[qt], kf[ks % 3], qf[qt][ks]);
+      }
+      soft2(ks >> 2, 2 * (ks & 3));
+      pin(pk[ks >> 2][0]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    chunk_fence();
+    load_v(vf[1], pst, 2 * pkt + 1);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[0][dt], pk[qt][0], o[dt][qt]);
+      lsum[qt] = mma(ones, pk[qt][0], lsum[qt]);
+    }
+#pragma unroll
+    for (int r0 = 8; r0 < 16; r0 += 2) {
+      soft2(0, r0);
+      soft2(1, r0);
+    }
+    pin(pk[0][1]);
+    pin(pk[1][1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    chunk_fence();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[1][dt], pk[qt][1], o[dt][qt]);
+      lsum[qt] = mma(ones, pk[qt][1], lsum[qt]);
+    }
+    half_max(nxt);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    chunk_fence();
+  };
+
+  // stage offsets of tiles t .. t+3
+  int st0 = 0, st1 = STAGEB, st2 = 2 * STAGEB, st3 = 3 * STAGEB;
+  int kn = min(BN, cke - ck0);   // keys of tile t
+  if (ntiles > 0) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 kf = load_k(ring, 0, ks);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        if (ks == 0) mma_first(sa[qt], kf, qf[qt][ks]);
+        else mma_acc(sa[qt], kf, qf[qt][ks]);
+      }
+    }
+    // the vector unit reads the scores next: wait for the last products
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    half_max(sa);
+    boundary(sa, kn);
+  }
+  // Each iteration runs the two halves of tile t; the second one computes
+  // the scores of the first half of tile t+1 (for the last tile they come
+  // from a stale stage and are never used).
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 3 < ntiles) issue(ring + st3);
+    half_step(sa, sb, ring + st0, 1, ring + st0, 0);
+    boundary(sb, kn - 32);
+    half_step(sb, sa, ring + st1, 0, ring + st0, 1);
+    advance();
+    kn = min(BN, cke - ck0);
+    if (t + 3 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (t + 1 < ntiles) boundary(sa, kn);
+    const int sf = st0;
+    st0 = st1;
+    st1 = st2;
+    st2 = st3;
+    st3 = sf;
   }
 
   // ---- epilogue: o[dt][qt][r] = O(query 32 qt + l32, dim 32 dt + 8(r/4) + 4h + r%4)
@@ -543,7 +700,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   bf16* out = (bf16*)p.out;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float lt = lsum[qt] + __shfl_xor(lsum[qt], 32);
+    const float lt = lsum[qt][0];
     const int qrow = wi.qbeg + wave * 64 + qt * 32 + l32;
     if (qrow >= wi.qend) continue;
     if (wi.pidx < 0) {
