@@ -105,6 +105,193 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T* __restrict__ A,
       }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 GEMM for the layer's large shapes (M = tokens, N and K = D or 2D, K a
+// multiple of 32): 256 x 256 output tile per workgroup, eight waves (two
+// per SIMD, so one wave's products cover the other's LDS waits and
+// barriers) of 128 x 64, 32x32x16 MFMA, 128 accumulator registers per wave.
+//
+// Each workgroup computes C^T for its tile (the MFMA A operand is a row
+// block of Bt, the B operand a row block of A), so a lane holds four
+// consecutive n of one m and stores 8 contiguous bytes.  K advances in
+// 32-wide slabs (64 bytes per row) through a four-stage LDS ring filled by
+// the direct-to-LDS DMA (a buffer load with the lds modifier: lane l writes
+// bytes [16 l, 16 l + 16) of a 1 KB block, i.e. 16 rows of one slab); the
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 2) & 3), so the sixteen
+// rows a 16-lane group reads for one fragment cover all 64 banks.  Buffer
+// descriptors start at the tile's first row and end at the matrix's last, so
+// rows past M or N read as zero.  Tiles are visited in groups of eight M
+// panels (every N tile of a group before the next group) on top of the XCD
+// remap, so the workgroups that run together on one XCD share A panels and
+// Bt slices in its L2.
+namespace gemm_big {
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+constexpr int ROWB = BK * 2;                 // bytes per row of a slab
+constexpr int TILEB = BM * ROWB;             // 16 KB per operand and stage
+constexpr int STAGEB = 2 * TILEB;            // A slab, then Bt slab
+constexpr int GROUP_M = 8;
+constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0) (gfx9 encoding)
+constexpr int kWaitVm8 = 0x0F78;             // s_waitcnt vmcnt(8): all but the last two slabs' loads (4 per slab)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+}  // namespace gemm_big
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_nt_big_kernel(const bf16* __restrict__ A,
+                                                               const bf16* __restrict__ Bt,
+                                                               bf16* __restrict__ C, int M, int N, int K,
+                                                               int64_t lda, int64_t ldb, int64_t ldc,
+                                                               int tiles_m, int tiles_n) {
+  using namespace gemm_big;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l32 = lane % 32, h = lane / 32;
+  const int wm = wave >> 2, wn = wave & 3;   // 128-row block of A, 64-row block of Bt
+
+  // tile of this workgroup: XCD-contiguous logical id, then grouped order
+  const int total = tiles_m * tiles_n;
+  const int pid = xcd_remap(blockIdx.x, total);
+  const int group = pid / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in_group = pid - group * GROUP_M * tiles_n;
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // buffer descriptors in scalar registers
+  const int tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsize);
+  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  // DMA: wave w fills rows 32 w .. 32 w + 31 of each slab, two 16-row blocks;
+  // lane l of block i loads row 32 w + 16 i + l/4, global chunk swz^-1
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + m0 * lda), (short)0, (int)(min((int64_t)BM, M - m0) * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Bt + n0 * ldb), (short)0, (int)(min((int64_t)BN, N - n0) * ldb * 2), 0x00020000);
+  int offa[2], offb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * wave + 16 * i + lane / 4;
+    const int c = swz(row, lane % 4);
+    offa[i] = (int)(row * lda * 2) + 16 * c;
+    offb[i] = (int)(row * ldb * 2) + 16 * c;
+  }
+  const int nk = K / BK;
+  // The DMA is an opaque instruction for the compiler (its wait insertion
+  // cannot tell ring stages apart); the loop waits for each slab explicitly.
+  auto issue = [&](int kt, int stage) {
+    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)(ring + stage * STAGEB);
+    const int kb = kt * ROWB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = 2 * wave + i;
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offa[i]), "s"(ra), "s"(kb),
+                   "{m0}"(lds + blk * 1024)
+                   : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offb[i]), "s"(rb), "s"(kb),
+                   "{m0}"(lds + TILEB + blk * 1024)
+                   : "memory");
+    }
+  };
+
+  f32x16 acc[2][4];   // acc[jn][im]: C^T block (n: 32 jn.., m: 32 im..) of this wave's 128 x 64
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x16{};
+
+  // fragments of one 16-column step ks of a slab: fb[j] rows 64 wn + 32 j + l32
+  // of Bt, fa[i] rows 128 wm + 32 i + l32 of A, chunk 2 ks + h
+  auto read_frags = [&](int stage, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+    const unsigned char* sa = ring + stage * STAGEB;
+    const unsigned char* sb = sa + TILEB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rb_row = 64 * wn + 32 * j + l32;
+      fb[j] = *reinterpret_cast<const bf16x8*>(sb + rb_row * ROWB + 16 * swz(rb_row, 2 * ks + h));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra_row = 128 * wm + 32 * i + l32;
+      fa[i] = *reinterpret_cast<const bf16x8*>(sa + ra_row * ROWB + 16 * swz(ra_row, 2 * ks + h));
+    }
+  };
+  auto products = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[j][i], 0, 0, 0);
+  };
+  auto fence = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  for (int s = 0; s < 3; ++s)
+    if (s < nk) issue(s, s);
+  if (nk > 2) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  // Fragment reads run half a slab ahead of their products: the second
+  // step's fragments of slab kt are read at the top of step kt (covered by
+  // the first step's products); then each wave waits for its share of slab
+  // kt+1, the barrier publishes it (and, being a full barrier, waits for
+  // every wave's outstanding LDS reads), and the first step's fragments of
+  // slab kt+1 are read beside the second step's products.  A ring slot is
+  // refilled (slab kt+3 at the top of step kt) after the barrier of step
+  // kt-1, past every read of its previous slab.
+  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+  read_frags(0, 0, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 3 < nk) issue(kt + 3, (kt + 3) % STAGES);
+    read_frags(kt % STAGES, 1, fa1, fb1);
+    fence();
+    products(fa0, fb0);
+    fence();
+    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (kt + 1 < nk) read_frags((kt + 1) % STAGES, 0, fa0, fb0);
+    fence();
+    products(fa1, fb1);
+  }
+
+  // epilogue: acc[jn][im][4 r4 + e] = C[m0 + 128 wm + 32 im + l32][n0 + 64 wn + 32 jn + 8 r4 + 4 h + e]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + 128 * wm + 32 * i + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int64_t n = n0 + 64 * wn + 32 * j + 8 * r4 + 4 * h;
+        if (n >= N) continue;
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = acc[j][i][4 * r4 + e];
+          if (EPI == kEpiSigmoid) x = sigmoidf(x);
+          v[e] = (bf16)x;
+        }
+        *reinterpret_cast<bf16x4*>(C + m * ldc + n) = v;
+      }
+  }
+}
+
+// the big-tile kernel's shape contract: bf16, K a multiple of 32, N of 8, 16-byte
+// aligned rows, and every operand tile's byte range below 2^31
+static bool gemm_big_ok(int dtype, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc, const void* A,
+                        const void* Bt, const void* C) {
+  if (dtype != 1 || M <= 0 || N <= 0 || K <= 0) return false;
+  if (K % 32 || N % 8 || lda % 8 || ldb % 8 || ldc % 8) return false;
+  if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15) return false;
+  if (256 * lda * 2 >= (int64_t(1) << 31) || 256 * ldb * 2 >= (int64_t(1) << 31)) return false;
+  return true;
+}
+
 hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
                             int64_t ld_dst, hipStream_t st) {
   dim3 grid((cols + 63) / 64, (rows + 63) / 64);
@@ -117,6 +304,16 @@ hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int
 
 hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, void* C, int M,
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st) {
+  if (gemm_big_ok(dtype, M, N, K, lda, ldb, ldc, A, Bt, C)) {
+    const int tm = (M + 255) / 256, tn = (N + 255) / 256;
+    if (epi == kEpiSigmoid)
+      gemm_bf16_nt_big_kernel<kEpiSigmoid><<<tm * tn, 512, 0, st>>>(
+          (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
+    else
+      gemm_bf16_nt_big_kernel<kEpiStore><<<tm * tn, 512, 0, st>>>(
+          (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
+    return hipGetLastError();
+  }
   const int tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
   const int total = tiles_m * tiles_n;
   if (total == 0) return hipSuccess;
