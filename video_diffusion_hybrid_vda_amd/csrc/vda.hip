@@ -8,8 +8,8 @@
 //
 // Four kernels, one HBM pass each over the large tensors:
 //   gram    : per (frame, head) A_t and B_t from K_t, V_t     (MFMA, HBM-bound)
-//   solve   : per (frame, head) M_t = (I + A_t)^-1 by a Cholesky factorisation
-//             held in LDS, and C_t = B_t M_t                    (LDS, latency)
+//   solve   : per (frame, head) M_t = (I + A_t)^-1 by Gauss-Jordan elimination
+//             with the columns in registers, and C_t = B_t M_t  (latency)
 //   scan    : S_t = gamma_t S_prev M_t + C_t, both directions    (T-step chain)
 //   readout : u = S_t q both directions, RMSNorm, sum, gate     (MFMA, HBM-bound)
 #include <math.h>
@@ -118,83 +118,72 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// solve: one workgroup per (frame, head).  I + A_t is symmetric positive
-// definite (beta >= 0), so it is factored as L L^T in LDS by a right-looking
-// Cholesky; W = L^-1 by column-parallel forward substitution; M = W^T W;
-// C = B M.  AM holds A_t on entry and M_t on exit; BC holds B_t then C_t.
+// solve: one workgroup of 2d threads per (frame, head).  M_t = (I + A_t)^-1 by
+// Gauss-Jordan elimination of the augmented [I + A_t | I]: thread c keeps
+// column c in registers; at step k the pivot row and the pivot column go
+// through LDS (double-buffered, one barrier per step) and every column is
+// updated with a rank-1 step.  I + A_t is symmetric positive definite (beta
+// >= 0, eigenvalues >= 1), for which elimination without pivoting is stable.
+// Then C_t = B_t M_t through LDS.  AM holds A_t on entry and M_t on exit; BC
+// holds B_t then C_t.
 template <int D>
-__global__ __launch_bounds__(256) void vda_solve_kernel(float* __restrict__ AM,
-                                                        float* __restrict__ BC) {
-  constexpr int LD = D + 1;
-  __shared__ float Ls[D * LD];
-  __shared__ float Ws[D * LD];
-  __shared__ float dg[D];
+__global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM,
+                                                          float* __restrict__ BC) {
+  constexpr int NT = 2 * D, LD = D + 1;
+  __shared__ __attribute__((aligned(16))) float colb[2][D];
+  __shared__ float rowb[2][NT];
+  __shared__ float Ms[D * LD];
+  __shared__ float Bs[D * LD];
   const int64_t f = blockIdx.x;
-  float* a = AM + f * D * D;
+  float* am = AM + f * D * D;
   float* bm = BC + f * D * D;
-  const int tid = threadIdx.x;
+  const int c = threadIdx.x;
 
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    Ls[i * LD + j] = a[e] + (i == j ? 1.f : 0.f);
-  }
-  __syncthreads();
+  float a[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+    a[i] = c < D ? am[i * D + c] + (i == c ? 1.f : 0.f) : (i == c - D ? 1.f : 0.f);
 
-  // Step k updates the trailing block with the still-unscaled column k
-  // (a_ik a_jk / a_kk) and scales column k-1, which step k no longer reads,
-  // so one barrier per step suffices.
-  for (int kk = 0; kk < D; ++kk) {
-    const float akk = Ls[kk * LD + kk];
-    const float inv_akk = 1.f / akk;
-    if (tid == 0) dg[kk] = akk;
-    const int m = D - 1 - kk;
-    for (int e = tid; e < m * m; e += 256) {
-      const int ii = kk + 1 + e / m, jj = kk + 1 + e % m;
-      if (jj <= ii) Ls[ii * LD + jj] -= Ls[ii * LD + kk] * Ls[jj * LD + kk] * inv_akk;
-    }
-    if (kk > 0) {
-      const int c = kk - 1;
-      const float sq = sqrtf(dg[c]);
-      for (int i = c + tid; i < D; i += 256)
-        Ls[i * LD + c] = (i == c) ? sq : Ls[i * LD + c] / sq;
+  // The rows rotate by one per step, so that the pivot row is always a[0]
+  // (all register indices stay compile-time constants): the update writes
+  // row i+1 into slot i and the normalised pivot row goes to slot D-1.  After
+  // D steps every row is back in its place.
+  for (int k = 0; k < D; ++k) {
+    const int buf = k & 1;
+    rowb[buf][c] = a[0];
+    if (c == k) {
+#pragma unroll
+      for (int i = 0; i < D; i += 4)
+        *reinterpret_cast<float4*>(&colb[buf][i]) = make_float4(a[i], a[i + 1], a[i + 2], a[i + 3]);
     }
     __syncthreads();
+    const float x = rowb[buf][c] / rowb[buf][k];
+#pragma unroll
+    for (int i = 0; i < D; i += 4) {
+      const float4 cv = *reinterpret_cast<const float4*>(&colb[buf][i]);
+      if (i > 0) a[i - 1] = a[i] - cv.x * x;
+      a[i] = a[i + 1] - cv.y * x;
+      a[i + 1] = a[i + 2] - cv.z * x;
+      a[i + 2] = a[i + 3] - cv.w * x;
+    }
+    a[D - 1] = x;
   }
-  if (tid == 0) Ls[(D - 1) * LD + (D - 1)] = sqrtf(dg[D - 1]);
-  __syncthreads();
 
-  // W = L^-1: thread j solves L w = e_j; W[i][j] = 0 for i < j falls out.
-  if (tid < D) {
-    const int j = tid;
+  // columns D .. 2D-1 now hold M = (I + A)^-1
+  if (c >= D) {
+#pragma unroll
     for (int i = 0; i < D; ++i) {
-      float s = (i == j) ? 1.f : 0.f;
-      for (int q = 0; q < i; ++q) s -= Ls[i * LD + q] * Ws[q * LD + j];
-      Ws[i * LD + j] = s / Ls[i * LD + i];
+      Ms[i * LD + c - D] = a[i];
+      am[i * D + c - D] = a[i];
     }
   }
-  __syncthreads();
-
-  // M = W^T W (symmetric) into Ls.
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    if (j < i) continue;
-    float s = 0.f;
-    for (int q = i; q < D; ++q) s += Ws[q * LD + i] * Ws[q * LD + j];
-    Ls[i * LD + j] = s;
-    Ls[j * LD + i] = s;
-  }
-  __syncthreads();
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    a[e] = Ls[i * LD + j];
-    Ws[i * LD + j] = bm[e];
-  }
+  for (int e = c; e < D * D; e += NT) Bs[(e / D) * LD + e % D] = bm[e];
   __syncthreads();
   // C = B M
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = c; e < D * D; e += NT) {
     const int i = e / D, j = e % D;
     float s = 0.f;
-    for (int q = 0; q < D; ++q) s += Ws[i * LD + q] * Ls[q * LD + j];
+    for (int q = 0; q < D; ++q) s += Bs[i * LD + q] * Ms[q * LD + j];
     bm[e] = s;
   }
 }
@@ -428,8 +417,8 @@ hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const
 
 hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_t st) {
   if (nframes == 0) return hipSuccess;
-  if (d == 32) vda_solve_kernel<32><<<nframes, 256, 0, st>>>(AM, BC);
-  else if (d == 64) vda_solve_kernel<64><<<nframes, 256, 0, st>>>(AM, BC);
+  if (d == 32) vda_solve_kernel<32><<<nframes, 64, 0, st>>>(AM, BC);
+  else if (d == 64) vda_solve_kernel<64><<<nframes, 128, 0, st>>>(AM, BC);
   else vda_solve_kernel<128><<<nframes, 256, 0, st>>>(AM, BC);
   return hipGetLastError();
 }
