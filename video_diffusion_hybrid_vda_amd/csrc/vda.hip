@@ -396,6 +396,124 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// readout, bf16 and head_dim 128 (the workload shapes).  One workgroup per
+// (frame, head) and 1024 tokens: both directions' S_hi and S_lo are staged in
+// LDS once (4 x 32 KB, the 16-byte chunk c of row i at c ^ (i & 15) so that
+// the sixteen rows a 16-lane group reads cover all banks), then each wave
+// walks 64 tokens at a time computing U^T = S Q^T on 32x32x16 MFMA: the
+// state fragments are the A operand (one LDS read serves both 32-token
+// tiles), the Q fragments come straight from HBM as the B operand.  A lane
+// then holds 64 of the 128 outputs of one token (its partner lane i ^ 32 the
+// other 64), so the RMSNorm needs one cross-lane swap, and gate loads and
+// output stores move four consecutive bf16.
+namespace ro {
+constexpr int D = 128, TOK = 1024, SUB = 64;
+constexpr int MATB = D * D * 2;   // one bf16 d x d matrix
+__device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & 15); }
+}  // namespace ro
+
+__global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ split, const float* __restrict__ rms_w,
+    const bf16* __restrict__ gate, int64_t ldg, bf16* __restrict__ out, int64_t ldo, int H, int T_, int N,
+    float eps, int chunks_per_frame, int64_t bhtdd) {
+  using namespace ro;
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  __shared__ __attribute__((aligned(16))) unsigned char Sl[4 * MATB];   // [2 dir + part][row][chunk]
+  __shared__ float wl[D];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l32 = lane % 32, h = lane / 32;
+  const int chunk = blockIdx.x % chunks_per_frame;
+  const int64_t fi = blockIdx.x / chunks_per_frame;     // (b*H + hh)*T + t
+  const int t = (int)(fi % T_);
+  const int64_t bh = fi / T_;
+  const int hh = (int)(bh % H);
+  const int64_t b = bh / H;
+
+  for (int c = tid; c < 4 * D * D / 8; c += 256) {
+    const int m = c / (D * D / 8), rem = c % (D * D / 8);
+    const int row = rem / 16, ch = rem % 16;
+    const bf16* src = split + ((m >> 1) * bhtdd + fi * D * D) * 2 + (m & 1) * D * D + row * D + ch * 8;
+    *reinterpret_cast<Chunk16*>(Sl + m * MATB + row * 256 + sw(row, ch) * 16) = *reinterpret_cast<const Chunk16*>(src);
+  }
+  if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
+  __syncthreads();
+
+  const int64_t NL = (int64_t)T_ * N;
+  for (int sub = 0; sub < TOK / (4 * SUB); ++sub) {
+    const int n0 = chunk * TOK + (sub * 4 + wave) * SUB;
+    if (n0 >= N) break;
+    // Q^T fragments: lane holds q[token n0 + 32 tt + l32][16 ks + 8 h .. +7]
+    bf16x8 qf[2][8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int n = n0 + 32 * tt + l32;
+      const bf16* qrow = q + (fi * N + n) * D + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qf[tt][ks] = n < N ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks) : bf16x8{};
+    }
+    // acc[dir][tt][dt][r] = u_dir(token n0 + 32 tt + l32)[32 dt + 8(r/4) + 4h + r%4]
+    f32x16 acc[2][2][4];
+#pragma unroll
+    for (int dir = 0; dir < 2; ++dir)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) acc[dir][tt][dt] = f32x16{};
+        const int row = 32 * dt + l32;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int part = 0; part < 2; ++part) {
+            const bf16x8 sf = *reinterpret_cast<const bf16x8*>(Sl + (2 * dir + part) * MATB + row * 256 +
+                                                               sw(row, 2 * ks + h) * 16);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+              acc[dir][tt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[tt][ks], acc[dir][tt][dt], 0, 0, 0);
+          }
+      }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int n = n0 + 32 * tt + l32;
+      float rn[2];
+#pragma unroll
+      for (int dir = 0; dir < 2; ++dir) {
+        float ss = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ss += acc[dir][tt][dt][r] * acc[dir][tt][dt][r];
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+        ss = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+        rn[dir] = 1.f / sqrtf(ss / D + eps);
+      }
+      if (n >= N) continue;
+      const int64_t orow = b * NL + (int64_t)t * N + n;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * dt + 8 * r4 + 4 * h;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[e] = (acc[0][tt][dt][4 * r4 + e] * rn[0] + acc[1][tt][dt][4 * r4 + e] * rn[1]) * wl[d0 + e];
+          if (gate) {
+            const bf16x4 gv = *reinterpret_cast<const bf16x4*>(gate + orow * ldg + hh * D + d0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] *= (float)gv[e];
+          }
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)y[e];   // the only rounding of the output
+          *reinterpret_cast<bf16x4*>(out + orow * ldo + hh * D + d0) = ov;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename T>
 static hipError_t gram_t(int d, const void* k, const void* v, const float* beta, float* A,
                          float* Bm, int nframes, int N, hipStream_t st) {
@@ -438,9 +556,17 @@ template <typename T>
 static hipError_t readout_t(int d, const void* q, const float* states, const bf16* split,
                             const float* rms_w, const void* gate, int64_t ldg, void* out, int64_t ldo,
                             int B, int H, int T_, int N, float eps, hipStream_t st) {
+  const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
+  if (sizeof(T) == 2 && d == 128 && split) {
+    const int cpf = (N + ro::TOK - 1) / ro::TOK;
+    const int64_t nb = (int64_t)B * H * T_ * cpf;
+    if (nb == 0) return hipSuccess;
+    vda_readout_bf16_d128_kernel<<<(unsigned)nb, 256, 0, st>>>((const bf16*)q, split, rms_w, (const bf16*)gate,
+                                                               ldg, (bf16*)out, ldo, H, T_, N, eps, cpf, bhtdd);
+    return hipGetLastError();
+  }
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
   const int64_t blocks = (int64_t)B * H * T_ * tpf;
-  const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
   if (blocks == 0) return hipSuccess;
 #define VDN_READOUT(DD)                                                                         \
   vda_readout_kernel<T, DD><<<(unsigned)blocks, 256, 0, st>>>(                                  \
