@@ -8,12 +8,19 @@ synthetic bf16 input already resident in HBM.  The default workload is the
 102 frames x 4032 tokens (411,264 tokens), 5-frame chunks, +-1 chunk, first
 and last frame anchors.
 
-Prints one JSON line: tokens/s and ms per layer call, the dominant kernel's
-roofline fraction (window softmax, MFMA bf16) from HIP events recorded in the
-timed region, per-phase milliseconds, and the fp64 CPU oracle timed on a
-bounded sample of the same workload on this host.
+Prints one JSON line: tokens/s and ms per layer call (wall clock over the K
+timed calls, plus the median and minimum of the per-call HIP-event times), the
+dominant kernel's roofline fraction (window softmax, MFMA bf16) from HIP
+events recorded in the timed region, per-phase milliseconds, and the fp64 CPU
+oracle timed on a bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+
+With --sweep it instead runs the batch-2 length sweep (B2 H24 d128 N4032,
+T = 42, 62, 82, 102 latent frames): the hybrid layer and the dense
+full-softmax baseline (every key allowed, one output projection, no gates) on
+identical inputs, one JSON line per length with both layer times, the
+softmax-kernel times, the speedup and the softmax density.
 """
 import argparse
 import json
@@ -79,6 +86,87 @@ def window_traffic(cfg_name):
     return WINDOW_TRAFFIC_BYTES if h.hexdigest()[:16] == WINDOW_TRAFFIC_SHA else None
 
 
+def timed_calls(fn, steps, warmup):
+    """Run fn warmup times, then `steps` times with a torch (HIP) event pair
+    around each call on the current stream; returns (wall ms per call,
+    per-call event ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+PAGES_SWEEP = {42: {"density_pct": 42.08, "speedup": 1.8}, 102: {"density_pct": 19.98, "speedup": 3.2}}
+
+
+def length_sweep(args):
+    """Hybrid layer vs dense full-softmax layer on identical inputs, B2 H24 d128 N4032."""
+    import torch
+    from video_diffusion_hybrid_vda_amd import synth, vdn
+    torch.cuda.set_device(0)
+    base = synth.CONFIGS[5]
+    for T in args.sweep_frames:
+        cfg = base.replace(frames=T)
+        inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+        shape = vdn.shape_from_config(cfg)
+        B, L, D = cfg.batch, cfg.seq_len, cfg.model_dim
+        out = torch.empty(B, L, D, dtype=torch.bfloat16, device="cuda")
+        ws_h = vdn.workspace(shape, vdn.VDN_OP_HYBRID)
+
+        def hybrid():
+            vdn.vdn_hybrid_attn_fwd(shape, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"],
+                                    inp["beta"], inp["w_gs"], inp["w_gl"], inp["rms_w"], inp["w_os"],
+                                    inp["w_ol"], out, ws_h)
+
+        vdn.vdn_timing_start()
+        _, h_ms = timed_calls(hybrid, args.sweep_steps, 1)
+        ph_h = vdn.vdn_timing_stop()
+        del ws_h
+        ws_d = vdn.workspace(shape, vdn.VDN_OP_DENSE_ATTN)
+
+        def dense():
+            vdn.vdn_dense_attn_fwd(shape, inp["q"], inp["k"], inp["v"], inp["w_os"], out, ws_d)
+
+        vdn.vdn_timing_start()
+        _, d_ms = timed_calls(dense, args.sweep_steps, 1)
+        ph_d = vdn.vdn_timing_stop()
+        del ws_d
+        _, pairs = window_flops(cfg)
+        win_ms = ph_h["window_attn"][1] / ph_h["window_attn"][0]
+        den_ms = ph_d["window_attn"][1] / ph_d["window_attn"][0]
+        dense_flops = 4 * cfg.head_dim * B * cfg.heads * float(L) ** 2
+        line = {
+            "sweep": "hybrid vs dense layer", "workload": cfg.name.replace("{42,62,82,102}", str(T)),
+            "frames": T, "tokens": B * L, "softmax_density": round(pairs / float(L) ** 2, 5),
+            "hybrid_ms_median": round(median(h_ms), 2), "hybrid_ms_min": round(min(h_ms), 2),
+            "dense_ms_median": round(median(d_ms), 2), "dense_ms_min": round(min(d_ms), 2),
+            "layer_speedup": round(median(d_ms) / median(h_ms), 3),
+            "softmax_kernel_ms": {"window": round(win_ms, 2), "dense": round(den_ms, 2)},
+            "softmax_kernel_speedup": round(den_ms / win_ms, 3),
+            "dense_softmax_tflops": round(dense_flops / (den_ms * 1e-3) / 1e12, 1),
+            "calls": args.sweep_steps, "warmup": 1, "dtype": "bf16", "data": "synthetic",
+            "pages_h200": PAGES_SWEEP.get(T),
+        }
+        print(json.dumps(line), flush=True)
+        del inp, out
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(cfg, inp):
     """The fp64 oracle, unmodified, timed on a bounded sample of the workload
     (one head's full forward+backward scans, a sample of readout tokens,
@@ -139,10 +227,14 @@ def cpu_baseline(cfg, inp):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload index (3 or 4 are full layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="run the batch-2 hybrid-vs-dense length sweep instead of the single workload")
+    ap.add_argument("--sweep-frames", type=int, nargs="+", default=[42, 62, 82, 102])
+    ap.add_argument("--sweep-steps", type=int, default=3)
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling HBM counters)")
@@ -152,6 +244,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        length_sweep(args)
+        return
 
     import torch
     from video_diffusion_hybrid_vda_amd import synth, vdn
@@ -182,19 +278,8 @@ def main():
     torch.cuda.synchronize()
 
     vdn.vdn_timing_start()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_per_step, call_ms = timed_calls(step, args.steps, 0)
     phases = vdn.vdn_timing_stop()
-    ms_per_step = wall * 1e3 / args.steps
-    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
     flops, pairs = window_flops(cfg)
     n_attn, attn_ms = phases["window_attn"]
@@ -224,7 +309,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
                      "traffic": window_traffic(cfg.name)},
-        "gpu_ms_per_step": round(gpu_ms_per_step, 3),
+        "call_ms_median": round(median(call_ms), 3),
+        "call_ms_min": round(min(call_ms), 3),
         "phases_ms": phase_ms,
     }
     if not args.no_cpu_baseline:

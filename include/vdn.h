@@ -58,7 +58,10 @@
  * fails), and vdn_last_error() returns a message for the calling thread.
  * Parameter ranges (beta >= 0 so that I + A_t is positive definite,
  * 0 <= gamma <= 1) are preconditions: they live in device memory and are not
- * read back.  NaN/Inf inputs propagate to the outputs; they are not trapped.
+ * read back, unless vdn_set_param_check(1) has been called (then the entry
+ * points that read gamma and beta check them on the device first and
+ * synchronise the stream to read the verdict).  NaN/Inf inputs propagate to
+ * the outputs; they are not trapped.
  */
 #ifndef VDN_H
 #define VDN_H
@@ -76,13 +79,16 @@ extern "C" {
 #define VDN_ERR_DTYPE (-3)       /* dtype not VDN_F32 / VDN_BF16 */
 #define VDN_ERR_WORKSPACE (-4)   /* ws NULL or ws_bytes < vdn_workspace_bytes() */
 #define VDN_ERR_HIP (-5)         /* a HIP launch or runtime call failed */
+#define VDN_ERR_PARAM_RANGE (-6) /* beta < 0 or gamma outside [0, 1]; reported only while
+                                    vdn_set_param_check(1) is in effect */
 
 enum vdn_dtype { VDN_F32 = 0, VDN_BF16 = 1 };
 
 enum vdn_op {
   VDN_OP_HYBRID = 0,      /* vdn_hybrid_attn_fwd    */
   VDN_OP_VDA_SCAN = 1,    /* vda_scan_fwd           */
-  VDN_OP_WINDOW_ATTN = 2  /* window_anchor_attn_fwd */
+  VDN_OP_WINDOW_ATTN = 2, /* window_anchor_attn_fwd */
+  VDN_OP_DENSE_ATTN = 3   /* vdn_dense_attn_fwd     */
 };
 
 typedef struct vdn_shape {
@@ -133,6 +139,28 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
                            const void* k, const void* v, const void* gate_s,
                            void* out, float* lse, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Dense full-softmax baseline layer, the cost reference of the length sweep
+ * (10100.com article, 实验结果 / 效率阶梯: softmax density and backbone
+ * speedup against dense attention as the number of latent frames grows):
+ *   out = concat_h(softmax over all L keys of scale * q_l . k) @ v) @ w_o
+ * No gates and one output projection w_o [D, D].  The window and anchor fields
+ * of `shape` are ignored (every key frame is allowed); batch, heads, frames,
+ * tokens_per_frame, head_dim, softmax_scale and dtype are read.  The
+ * workspace (op VDN_OP_DENSE_ATTN) holds w_o transposed and the attention
+ * output [B, L, D]. */
+int vdn_dense_attn_fwd(const vdn_shape* shape, const void* q, const void* k,
+                       const void* v, const void* w_o, void* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Opt-in range check of gamma and beta (a debugging aid).  While on, every
+ * call of vdn_hybrid_attn_fwd and vda_scan_fwd first runs one small kernel
+ * over the B*H*T entries of gamma and beta, then waits for the stream and
+ * returns VDN_ERR_PARAM_RANGE (nothing else enqueued) if some beta < 0 or
+ * some gamma lies outside [0, 1].  The verdict travels through a 256-byte
+ * slot of those calls' workspace (always reserved).  Process-wide; off by default.  Returns
+ * the previous setting. */
+int vdn_set_param_check(int on);
 
 /* Phase timing, a tracing aid for benchmarks.  Between vdn_timing_start()
  * and vdn_timing_stop() every compute entry point records a pair of HIP

@@ -32,8 +32,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
-                 "vdn_workspace_bytes", "vdn_last_error", "vdn_version", "vdn_timing_start",
-                 "vdn_timing_stop"):
+                 "vdn_dense_attn_fwd", "vdn_set_param_check", "vdn_workspace_bytes",
+                 "vdn_last_error", "vdn_version", "vdn_timing_start", "vdn_timing_stop"):
         assert name in fns, fns
 
 
@@ -134,6 +134,51 @@ def test_workspace_sizes_cover_the_layout(vdn):
     assert hyb % 256 == 0 and vda % 256 == 0 and att % 256 == 0
     with pytest.raises(vdn.VdnError):
         vdn.vdn_workspace_bytes(s, 9)
+
+
+def test_dense_entry_point_rejects_bad_arguments(vdn):
+    s = _shape(vdn)
+    fake = 1 << 20
+    need = vdn.vdn_workspace_bytes(s, vdn.VDN_OP_DENSE_ATTN)
+    call = lambda args, w, n: vdn._lib.vdn_dense_attn_fwd(ctypes.byref(s), *args, w, n, None)  # noqa: E731
+    for i in range(5):
+        a = [fake] * 5
+        a[i] = None
+        assert call(a, fake, need) == -1
+    a = [fake] * 5
+    a[3] = fake + 8
+    assert call(a, fake, need) == -1
+    assert call([fake] * 5, fake, need - 1) == -4
+    assert call([fake] * 5, None, need) == -4
+
+
+def test_dense_workspace_holds_projection_and_output(vdn):
+    """The dense baseline's workspace holds W_o^T [D, D] and the softmax
+    output [B*L, D]; its window and anchor fields do not change the size."""
+    s = vdn.make_shape(2, 24, 42, 4032, 128, "bf16")
+    L, D = 42 * 4032, 24 * 128
+    n = vdn.vdn_workspace_bytes(s, vdn.VDN_OP_DENSE_ATTN)
+    assert n >= D * D * 2 + 2 * L * D * 2 and n % 256 == 0
+    s2 = vdn.make_shape(2, 24, 42, 4032, 128, "bf16", window_chunks=3, anchor_first=False)
+    assert vdn.vdn_workspace_bytes(s2, vdn.VDN_OP_DENSE_ATTN) == n
+
+
+def test_huge_window_is_the_whole_sequence(vdn):
+    """A window wider than the sequence sizes exactly like one of nC chunks
+    (no integer overflow in the frame-range arithmetic)."""
+    nC = (102 + 4) // 5
+    a = vdn.make_shape(1, 24, 102, 4032, 128, "bf16", window_chunks=nC)
+    b = vdn.make_shape(1, 24, 102, 4032, 128, "bf16", window_chunks=2 ** 31 - 1)
+    for op in (vdn.VDN_OP_HYBRID, vdn.VDN_OP_WINDOW_ATTN):
+        assert vdn.vdn_workspace_bytes(a, op) == vdn.vdn_workspace_bytes(b, op)
+
+
+def test_param_check_switch(vdn):
+    """The range check is off by default; the switch returns the previous
+    setting.  (Its device-side verdict is tested on the GPU.)"""
+    assert vdn.vdn_set_param_check(True) is False
+    assert vdn.vdn_set_param_check(False) is True
+    assert vdn.vdn_set_param_check(False) is False
 
 
 def test_timing_session_without_launches(vdn):

@@ -229,6 +229,67 @@ def test_vda_invariants(vdn):
     assert torch.count_nonzero(out0).item() == 0
 
 
+DENSE = [
+    ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=71)),
+    ("H2_T23_N70_d128_bf16", VdnConfig(1, 2, 128, 23, 70, dtype="bf16", seed=72)),
+    ("T12_N33_d64_bf16", VdnConfig(1, 1, 64, 12, 33, dtype="bf16", window_chunks=0, seed=73)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", DENSE, ids=[t[0] for t in DENSE])
+def test_dense_layer(vdn, name, cfg):
+    """Dense full-softmax baseline (every key allowed, one projection, no
+    gates) against the oracle's dense layer; the shape's window and anchor
+    fields must not matter."""
+    log(f"[dense] {name}")
+    inp = gpu_inputs(cfg)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.dense_attn(shape, inp, inp["w_os"])
+    torch.cuda.synchronize()
+    ref = O.dense_layer(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(inp["w_os"]))
+    err = rel_err(np32(out), ref)
+    exc = excess_err(np32(out), ref, cfg.dtype)
+    log(f"  rel err {err:.3e} excess {exc:.3e}")
+    assert exc <= TOL[cfg.dtype]
+
+
+def test_param_range_check(vdn):
+    """With the range check on, beta < 0 or gamma outside [0, 1] is reported
+    as VDN_ERR_PARAM_RANGE by both entry points that read them; legal values,
+    the closed-interval ends included, run and give the same output as with
+    the check off."""
+    cfg = VdnConfig(1, 2, 64, 9, 40, dtype="bf16", seed=74)
+    inp = gpu_inputs(cfg)
+    shape = vdn.shape_from_config(cfg)
+    edge = dict(inp, beta=inp["beta"].clone(), gamma=inp["gamma"].clone())
+    edge["beta"][0, 0, 0] = 0.0
+    edge["gamma"][0, 0, 1] = 0.0
+    edge["gamma"][0, 1, 2] = 1.0
+    ref_h = vdn.hybrid_attn(shape, edge)
+    ref_l = vdn.vda_scan(shape, edge)
+    torch.cuda.synchronize()
+    prev = vdn.vdn_set_param_check(True)
+    try:
+        assert torch.equal(vdn.hybrid_attn(shape, edge), ref_h)
+        assert torch.equal(vdn.vda_scan(shape, edge), ref_l)
+        for name, idx, val in (("beta", (0, 1, 3), -0.25), ("gamma", (0, 0, 8), 1.5),
+                               ("gamma", (0, 1, 0), -0.1)):
+            log(f"[param check] {name}{idx} = {val}")
+            bad = dict(inp)
+            bad[name] = inp[name].clone()
+            bad[name][idx] = val
+            for call in (vdn.hybrid_attn, vdn.vda_scan):
+                with pytest.raises(vdn.VdnError) as ei:
+                    call(shape, bad)
+                assert ei.value.status == -6
+                assert "beta" in str(ei.value)
+    finally:
+        vdn.vdn_set_param_check(prev)
+    # check off: the ranges are a precondition, nothing is read back
+    vdn.vda_scan(shape, dict(inp, beta=inp["beta"] * 0 - 0.01))
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- full size
 
 def test_window_attn_config4_sampled(vdn):
@@ -308,3 +369,41 @@ def test_hybrid_full_sampled(vdn, cfg_id):
     err = rel_err(np32(out[:, rows]), ref)
     log(f"  rel err {err:.3e} ({time.time() - t0:.1f}s)")
     assert err <= TOL["bf16"]
+
+
+def test_length_sweep_T42_batch2_sampled(vdn):
+    """Batch-2 layer of the length sweep at 42 latent frames (B2 H24 d128
+    N4032): the hybrid layer and the dense baseline on the same inputs, both
+    checked at sampled tokens of both batch entries."""
+    cfg = synth.CONFIGS[5].replace(frames=42)
+    log("[sweep] B2 T42 hybrid + dense")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    dense = vdn.dense_attn(shape, inp, inp["w_os"])
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    rows = synth.sample_tokens(cfg, 10)
+    host = {k: np32(v) for k, v in inp.items() if k not in ("q", "k", "v")}
+    for k in ("q", "k", "v"):
+        host[k] = inp[k].float().cpu().numpy()
+    ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                              host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                              rows, **oracle_kwargs(cfg))
+    err = rel_err(np32(out[:, rows]), ref)
+    log(f"  hybrid rel err {err:.3e} ({time.time() - t0:.1f}s)")
+    assert err <= TOL["bf16"]
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    allowed = np.ones((T, T), dtype=bool)
+    o = np.zeros((B, len(rows), H * d))
+    for b in range(B):
+        for h in range(H):
+            oo, _ = O.window_attention(host["q"][b, h].astype(np.float64), host["k"][b, h].astype(np.float64),
+                                       host["v"][b, h].astype(np.float64), allowed, 1 / np.sqrt(d),
+                                       np.array(rows))
+            o[b, :, h * d:(h + 1) * d] = oo
+    ref_d = o @ host["w_os"].astype(np.float64)
+    err_d = rel_err(np32(dense[:, rows]), ref_d)
+    log(f"  dense rel err {err_d:.3e} ({time.time() - t0:.1f}s)")
+    assert err_d <= TOL["bf16"]

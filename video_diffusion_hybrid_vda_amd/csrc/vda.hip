@@ -526,6 +526,26 @@ static hipError_t gram_t(int d, const void* k, const void* v, const float* beta,
   return hipGetLastError();
 }
 
+// Range check of the per-frame parameters: beta >= 0 keeps I + A_t positive
+// definite, 0 <= gamma <= 1 keeps the decay a contraction.  One workgroup; the
+// result is written unconditionally, so the flag needs no clearing.
+__global__ __launch_bounds__(256) void param_check_kernel(const float* gamma, const float* beta,
+                                                          int n, int* flag) {
+  int bad = 0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float g = gamma[i], b = beta[i];
+    bad |= (b < 0.f) | (g < 0.f) | (g > 1.f);
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) flag[0] = bad ? 1 : 0;
+}
+
+hipError_t launch_param_check(const float* gamma, const float* beta, int n, int* flag,
+                              hipStream_t st) {
+  param_check_kernel<<<1, 256, 0, st>>>(gamma, beta, n, flag);
+  return hipGetLastError();
+}
+
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
                            float* A, float* Bm, int nframes, int N, hipStream_t st) {
   if (nframes == 0) return hipSuccess;

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -59,7 +60,9 @@ int check_shape(const vdn_shape* s) {
 AttnParams make_attn_params(const vdn_shape* s) {
   AttnParams p;
   memset(&p, 0, sizeof(p));
-  const int T = s->frames, N = s->tokens_per_frame, C = s->chunk_frames, W = s->window_chunks;
+  const int T = s->frames, N = s->tokens_per_frame, C = s->chunk_frames;
+  // a window of nC chunks on each side already reaches every frame
+  const int W = s->window_chunks < (T + C - 1) / C ? s->window_chunks : (T + C - 1) / C;
   const int BM = attn_query_tile(s->dtype, s->head_dim), BN = kAttnBN;
   p.bm = BM;
   p.B = s->batch;
@@ -105,7 +108,7 @@ AttnParams make_attn_params(const vdn_shape* s) {
 
 // ---- workspace layouts
 struct VdaLayout {
-  size_t am, bc, states, split, total;
+  size_t am, bc, states, split, flag, total;
 };
 VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   const size_t dd = (size_t)s->head_dim * s->head_dim;
@@ -117,6 +120,7 @@ VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   l.states = off; off = align_up(off + (need_states ? 2 * frames * dd * 4 : 0));
   // bf16 I/O: states also as hi/lo bf16 pairs for the readout
   l.split = off; off = align_up(off + (s->dtype == VDN_BF16 ? 2 * frames * dd * 2 * 2 : 0));
+  l.flag = off; off += kAlign;                                  // parameter-check verdict
   l.total = off;
   return l;
 }
@@ -153,7 +157,52 @@ HybridLayout hybrid_layout(const vdn_shape* s, const AttnParams& p) {
   return l;
 }
 
+// Dense baseline: every key frame allowed, no anchors (they would add nothing).
+vdn_shape dense_shape(const vdn_shape* s) {
+  vdn_shape d = *s;
+  d.window_chunks = (s->frames + s->chunk_frames - 1) / s->chunk_frames;
+  d.anchor_first = 0;
+  d.anchor_last = 0;
+  return d;
+}
+
+struct DenseLayout {
+  size_t wo, ybuf, attn, total;
+};
+DenseLayout dense_layout(const vdn_shape* s) {
+  const vdn_shape ds = dense_shape(s);
+  const size_t es = elem_size(s->dtype);
+  const size_t D = (size_t)s->heads * s->head_dim;
+  const size_t rows = (size_t)s->batch * s->frames * s->tokens_per_frame;
+  DenseLayout l;
+  size_t off = 0;
+  l.wo = off; off = align_up(off + D * D * es);          // W_o^T  [D, D]
+  l.ybuf = off; off = align_up(off + rows * D * es);     // softmax output [B*L, D]
+  l.attn = off; off = align_up(off + attn_layout(&ds, make_attn_params(&ds)).total);
+  l.total = off;
+  return l;
+}
+
 bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
+std::atomic<int> g_param_check{0};
+
+// With the range check on: run it, wait for the stream, report a violation.
+int check_params(const vdn_shape* s, const float* gamma, const float* beta, char* flag_slot,
+                 hipStream_t st) {
+  if (!g_param_check.load(std::memory_order_relaxed)) return VDN_OK;
+  const int n = s->batch * s->heads * s->frames;
+  int* flag = (int*)flag_slot;
+  hipError_t e = launch_param_check(gamma, beta, n, flag, st);
+  int host_flag = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess)
+    return fail(VDN_ERR_HIP, "parameter check: %s", hipGetErrorString(e));
+  if (host_flag)
+    return fail(VDN_ERR_PARAM_RANGE, "parameter check: some beta < 0 or gamma outside [0, 1]");
+  return VDN_OK;
+}
 
 // ---- opt-in phase timing: HIP event pairs recorded around each phase
 enum Phase {
@@ -277,6 +326,7 @@ size_t vdn_workspace_bytes(const vdn_shape* shape, int op) {
     case VDN_OP_HYBRID: n = hybrid_layout(shape, p).total; break;
     case VDN_OP_VDA_SCAN: n = vda_layout(shape, true).total; break;
     case VDN_OP_WINDOW_ATTN: n = attn_layout(shape, p).total; break;
+    case VDN_OP_DENSE_ATTN: n = dense_layout(shape).total; break;
     default: fail(VDN_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
   // Never 0 for a valid request, so that 0 always signals an error.
@@ -297,6 +347,9 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k, const voi
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(VDN_ERR_WORKSPACE, "vda_scan_fwd: workspace of %zu bytes needed, %zu given", need,
                 ws ? ws_bytes : (size_t)0);
+  rc = check_params(shape, gamma, beta, (char*)ws + vda_layout(shape, states == nullptr).flag,
+                    (hipStream_t)stream);
+  if (rc != VDN_OK) return rc;
   const int64_t D = (int64_t)shape->heads * shape->head_dim;
   return run_vda(shape, q, k, v, gamma, beta, rms_w, gate_l, D, out, D, states, (char*)ws,
                  (hipStream_t)stream);
@@ -342,6 +395,8 @@ int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q, co
 
   hipStream_t st = (hipStream_t)stream;
   char* w = (char*)ws;
+  rc = check_params(shape, gamma, beta, w + l.vda + vda_layout(shape, true).flag, st);
+  if (rc != VDN_OK) return rc;
   const size_t es = elem_size(shape->dtype);
   const int D = shape->heads * shape->head_dim;
   const int rows = shape->batch * shape->frames * shape->tokens_per_frame;
@@ -377,6 +432,40 @@ int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q, co
   if (e != hipSuccess) return hip_fail(e, "output gemm launch");
   return VDN_OK;
 }
+
+int vdn_dense_attn_fwd(const vdn_shape* shape, const void* q, const void* k, const void* v,
+                       const void* w_o, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!q || !k || !v || !w_o || !out)
+    return fail(VDN_ERR_INVALID_ARG, "vdn_dense_attn_fwd: q, k, v, w_o and out must be non-NULL");
+  const void* ptrs[] = {q, k, v, w_o, out, ws};
+  for (const void* ptr : ptrs)
+    if (misaligned(ptr))
+      return fail(VDN_ERR_INVALID_ARG, "vdn_dense_attn_fwd: device pointers must be 16-byte aligned");
+  const DenseLayout l = dense_layout(shape);
+  if (!ws || ws_bytes < l.total)
+    return fail(VDN_ERR_WORKSPACE, "vdn_dense_attn_fwd: workspace of %zu bytes needed, %zu given",
+                l.total, ws ? ws_bytes : (size_t)0);
+  const vdn_shape ds = dense_shape(shape);
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const int D = shape->heads * shape->head_dim;
+  const int rows = shape->batch * shape->frames * shape->tokens_per_frame;
+  int ph = phase_begin(kPhTranspose, st);
+  hipError_t e = launch_transpose(shape->dtype, w_o, w + l.wo, D, D, D, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  rc = run_attn(&ds, q, k, v, nullptr, D, w + l.ybuf, D, nullptr, w + l.attn, st);
+  if (rc != VDN_OK) return rc;
+  ph = phase_begin(kPhOutGemm, st);
+  e = launch_gemm_nt(shape->dtype, kEpiStore, w + l.ybuf, w + l.wo, out, rows, D, D, D, D, D, st);
+  phase_end(ph, st);
+  if (e != hipSuccess) return hip_fail(e, "output gemm launch");
+  return VDN_OK;
+}
+
+int vdn_set_param_check(int on) { return g_param_check.exchange(on ? 1 : 0); }
 
 int vdn_timing_start(void) {
   std::lock_guard<std::mutex> lk(g_timer.mu);

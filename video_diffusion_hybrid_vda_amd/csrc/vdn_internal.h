@@ -69,5 +69,8 @@ hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* stat
                               const __bf16* split, const float* rms_w, const void* gate,
                               int64_t ldg, void* out, int64_t ldo, int B, int H, int T, int N,
                               float eps, hipStream_t st);
+// flag[0] = 1 if some beta[i] < 0 or gamma[i] outside [0, 1] (i < n), else 0.
+hipError_t launch_param_check(const float* gamma, const float* beta, int n, int* flag,
+                              hipStream_t st);
 
 }  // namespace vdn

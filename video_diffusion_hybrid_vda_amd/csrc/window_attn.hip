@@ -292,8 +292,9 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 // bf16, head_dim 128: the production kernel for the workload shapes.
 //
-// 4 waves x 64 queries = 256 queries per workgroup, one wave per SIMD;
-// 64-key tiles; 32x32x16 MFMA.  K and V tiles are copied global -> LDS by the
+// 256 queries per workgroup: 4 waves x 64 queries (one wave per SIMD, the
+// default) or 8 waves x 32 queries (two per SIMD); both measure the same on
+// the workload.  64-key tiles; 32x32x16 MFMA.  K and V tiles are copied global -> LDS by the
 // direct-to-LDS DMA path (a buffer load with the lds modifier: lane l writes
 // bytes [16 l, 16 l + 16) of a 1 KB block) through a four-stage ring, so
 // tiles t+1 .. t+3 stream in while tile t is consumed; one barrier per tile.
@@ -322,12 +323,13 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
 // dominant probability at (or next to) 1, as exact as a strict running max.
 namespace v2 {
 constexpr int BM = 256, BN = 64, D = 128, STAGES = 4;
+constexpr int kAttnQT = 2;          // query tiles of 32 per wave: 8 / kAttnQT waves per workgroup
 constexpr int ROWB = D * 2;          // bytes per K/V row
 constexpr int TILEB = BN * ROWB;     // 16 KB
 constexpr int STAGEB = 2 * TILEB;    // K tile then V tile
 constexpr float kRescaleSlack = 1.f;
 constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt not waited for)
-constexpr int kWaitVm8 = 0x0F78;   // s_waitcnt vmcnt(8): all but the last tile's eight loads done
+constexpr int kWaitVm8 = 0x0F78;   // s_waitcnt vmcnt(8): at most the last 8 DMA loads outstanding
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -376,8 +378,12 @@ __device__ __forceinline__ float halves_max(float x) {
 }
 }  // namespace v2
 
-__global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p) {
+template <int QT>
+__global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnParams p) {
   using namespace v2;
+  constexpr int NW = 8 / QT;          // waves per workgroup
+  constexpr int WQ = 32 * QT;         // queries per wave
+  constexpr int BLK = 16 / NW;        // 1 KB DMA blocks per wave and operand of a tile
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
 
   // wave index as a scalar: the DMA's LDS destination (M0) must be wave-uniform
@@ -400,10 +406,10 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // real keys of other frames and are masked out of the softmax.  Each
   // lane's byte offset inside a 64-row tile is fixed: row blk*4 + lane/16,
   // logical chunk swz(row, lane%16) lands at physical chunk lane%16.
-  int lane_off[4];
+  int lane_off[BLK];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 4 + lane / 16;
+  for (int i = 0; i < BLK; ++i) {
+    const int row = (wave * BLK + i) * 4 + lane / 16;
     lane_off[i] = row * ROWB + swz(row, lane % 16) * 16;
   }
   // interval bounds picked without dynamic indexing, as wave-uniform scalars
@@ -422,8 +428,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     const int base = lk0 * ROWB;
     const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)sb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wave * 4 + i;
+    for (int i = 0; i < BLK; ++i) {
+      const int blk = wave * BLK + i;
       const int voff = base + lane_off[i];
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk), "{m0}"(lds + blk * 1024)
                    : "memory");
@@ -447,10 +453,10 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   if (ntiles > 2) issue(ring + 2 * STAGEB);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds Q[query l32][16 ks + 8 h .. +7]
-  bf16x8 qf[2][8];
+  bf16x8 qf[QT][8];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int qrow = wi.qbeg + wave * 64 + qt * 32 + l32;
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
     const bool ok = qrow < wi.qend;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -459,17 +465,17 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   }
   // Q lives in the accumulator file (the score products read it from there)
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) pin_acc(qf[qt][ks]);
 
   // O^T accumulators and the row sums of p: lsum[qt] = ones^T P^T on the
   // matrix unit, so every register of a lane holds the full row sum of its
   // query (of the bf16 p, the weights the P V product uses)
-  f32x16 o[4][2], lsum[2];
-  float mrun[2];
+  f32x16 o[4][QT], lsum[QT];
+  float mrun[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     mrun[qt] = -INFINITY;
     lsum[qt] = f32x16{};
 #pragma unroll
@@ -502,8 +508,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // live at once: the current one (read by the softmax) and the next one
   // (written by the matrix unit meanwhile).  sc[qt] register r holds the
   // score of key 8(r/4) + 4h + r%4 of the half tile for query 32 qt + l32.
-  f32x16 sa[2], sb[2];
-  float mtile[2];
+  f32x16 sa[QT], sb[QT];
+  float mtile[QT];
 
   // K fragment of 16-column step ks, rows 32 kt + l32
   auto load_k = [&](const unsigned char* stage, int kt, int ks) {
@@ -527,10 +533,10 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     }
   };
   // keys >= lim of a half tile get score -inf
-  auto mask = [&](f32x16 (&sc)[2], int lim) {
+  auto mask = [&](f32x16 (&sc)[QT], int lim) {
     const int l = lim - 4 * h;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (8 * (r / 4) + (r % 4) >= l) sc[qt][r] = -INFINITY;
@@ -538,9 +544,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // raise the running max to the tile max if it outruns it by more than the
   // slack, rescaling O and the row sums
   auto refresh = [&]() {
-    if (__any(mtile[0] > mrun[0] + kRescaleSlack || mtile[1] > mrun[1] + kRescaleSlack)) {
+    bool up = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) up |= mtile[qt] > mrun[qt] + kRescaleSlack;
+    if (__any(up)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
         const float mnew = fmaxf(mrun[qt], mtile[qt]);
         const float alpha = fast_exp2(mrun[qt] - mnew);
         mrun[qt] = mnew;
@@ -559,9 +568,9 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
 
   // per-query max of a half tile's scores (scaled, base 2) in mtile; the two
   // half-waves hold the two key halves of each query
-  auto half_max = [&](const f32x16 (&sc)[2]) {
+  auto half_max = [&](const f32x16 (&sc)[QT]) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       float mx = sc[qt][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qt][r]);
@@ -571,7 +580,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   };
   // between half steps: mask a partial half tile (keys >= lim), then raise
   // the running max if needed; neither happens on most half tiles
-  auto boundary = [&](f32x16 (&sc)[2], int lim) {
+  auto boundary = [&](f32x16 (&sc)[QT], int lim) {
     if (lim < 32) {
       asm volatile("");   // a real branch: the masking stays off the common path
       mask(sc, lim);
@@ -590,14 +599,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // score chunks carry p of the first 16 keys, the first P V chunk p of the
   // other 16, the second P V chunk the max of the next scores.  p is rounded
   // to bf16 for the products.
-  auto half_step = [&](const f32x16 (&cur)[2], f32x16 (&nxt)[2], const unsigned char* sst, int skt,
+  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], const unsigned char* sst, int skt,
                        const unsigned char* pst, int pkt) {
-    bf16x8 kf[3], vf[2][4], pk[2][2];
-    // p of registers r0, r0+1 of query tile qt (16-key step r0 / 8)
-    auto soft2 = [&](int qt, int r0) {
-      const float mneg = -mrun[qt];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) pk[qt][r0 >> 3][(r0 & 7) + i] = (bf16)fast_exp2(fmaf(cur[qt][r0 + i], c2, mneg));
+    bf16x8 kf[3], vf[2][4], pk[QT][2];
+    // p of register r of query tile qt (16-key step r / 8)
+    auto soft1 = [&](int qt, int r) {
+      pk[qt][r >> 3][r & 7] = (bf16)fast_exp2(fmaf(cur[qt][r], c2, -mrun[qt]));
     };
     kf[0] = load_k(sst, skt, 0);
     kf[1] = load_k(sst, skt, 1);
@@ -607,49 +614,52 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       if (ks < 6) kf[(ks + 2) % 3] = load_k(sst, skt, ks + 2);
       if (ks == 6) load_v(vf[0], pst, 2 * pkt);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         if (ks == 0) mma_first(nxt[qt], kf[ks % 3], qf[qt][ks]);
         else mma_acc(nxt[qt], kf[ks % 3], qf[qt][ks]);
       }
-      soft2(ks >> 2, 2 * (ks & 3));
-      pin(pk[ks >> 2][0]);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        soft1(qt, ks);
+        pin(pk[qt][0]);
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
     }
     chunk_fence();
     load_v(vf[1], pst, 2 * pkt + 1);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[0][dt], pk[qt][0], o[dt][qt]);
       lsum[qt] = mma(ones, pk[qt][0], lsum[qt]);
     }
 #pragma unroll
-    for (int r0 = 8; r0 < 16; r0 += 2) {
-      soft2(0, r0);
-      soft2(1, r0);
-    }
-    pin(pk[0][1]);
-    pin(pk[1][1]);
+    for (int r = 8; r < 16; ++r)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) soft1(qt, r);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) pin(pk[qt][1]);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 5 * QT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
     chunk_fence();
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[1][dt], pk[qt][1], o[dt][qt]);
       lsum[qt] = mma(ones, pk[qt][1], lsum[qt]);
     }
     half_max(nxt);
 #pragma unroll
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 5 * QT; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
@@ -664,7 +674,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x8 kf = load_k(ring, 0, ks);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         if (ks == 0) mma_first(sa[qt], kf, qf[qt][ks]);
         else mma_acc(sa[qt], kf, qf[qt][ks]);
       }
@@ -699,9 +709,9 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   const bf16* gate = (const bf16*)p.gate;
   bf16* out = (bf16*)p.out;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const float lt = lsum[qt][0];
-    const int qrow = wi.qbeg + wave * 64 + qt * 32 + l32;
+    const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
     if (qrow >= wi.qend) continue;
     if (wi.pidx < 0) {
       const float inv = 1.f / lt;
@@ -788,7 +798,7 @@ template <typename T, int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
   if (p.total > 0) {
     if (attn_uses_v2(sizeof(T) == 2 ? 1 : 0, D))
-      window_attn_bf16_d128_kernel<<<p.total, 256, 0, st>>>(p);
+      window_attn_bf16_d128_kernel<v2::kAttnQT><<<p.total, 512 / v2::kAttnQT, 0, st>>>(p);
     else
       window_attn_kernel<T, D><<<p.total, 256, 0, st>>>(p);
   }

@@ -18,9 +18,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libvdn.so")
 
 VDN_F32, VDN_BF16 = 0, 1
-VDN_OP_HYBRID, VDN_OP_VDA_SCAN, VDN_OP_WINDOW_ATTN = 0, 1, 2
+VDN_OP_HYBRID, VDN_OP_VDA_SCAN, VDN_OP_WINDOW_ATTN, VDN_OP_DENSE_ATTN = 0, 1, 2, 3
 STATUS = {0: "VDN_OK", -1: "VDN_ERR_INVALID_ARG", -2: "VDN_ERR_BAD_SHAPE", -3: "VDN_ERR_DTYPE",
-          -4: "VDN_ERR_WORKSPACE", -5: "VDN_ERR_HIP"}
+          -4: "VDN_ERR_WORKSPACE", -5: "VDN_ERR_HIP", -6: "VDN_ERR_PARAM_RANGE"}
 _TORCH_DTYPE = {VDN_F32: torch.float32, VDN_BF16: torch.bfloat16}
 
 
@@ -77,6 +77,10 @@ def _load():
     lib.vda_scan_fwd.restype = I
     lib.window_anchor_attn_fwd.argtypes = [S] + [P] * 6 + [P, SZ, P]
     lib.window_anchor_attn_fwd.restype = I
+    lib.vdn_dense_attn_fwd.argtypes = [S] + [P] * 6 + [SZ, P]
+    lib.vdn_dense_attn_fwd.restype = I
+    lib.vdn_set_param_check.argtypes = [I]
+    lib.vdn_set_param_check.restype = I
     lib.vdn_last_error.argtypes = []
     lib.vdn_last_error.restype = ctypes.c_char_p
     lib.vdn_version.argtypes = []
@@ -91,7 +95,8 @@ def _load():
 _lib = _load()
 
 EXPORTS = ("vdn_workspace_bytes", "vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
-           "vdn_last_error", "vdn_version", "vdn_timing_start", "vdn_timing_stop")
+           "vdn_dense_attn_fwd", "vdn_set_param_check", "vdn_last_error", "vdn_version",
+           "vdn_timing_start", "vdn_timing_stop")
 
 
 def _ptr(t):
@@ -170,6 +175,17 @@ def window_anchor_attn_fwd(shape, q, k, v, gate_s, out, lse, ws, stream=None) ->
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def vdn_dense_attn_fwd(shape, q, k, v, w_o, out, ws, stream=None) -> int:
+    return _check(_lib.vdn_dense_attn_fwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(w_o), _ptr(out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vdn_set_param_check(on: bool) -> bool:
+    """Turn the device-side gamma/beta range check on or off; returns the previous setting."""
+    return bool(_lib.vdn_set_param_check(int(bool(on))))
+
+
 # ---- convenience wrappers: allocate outputs and workspace through torch, then call
 
 def hybrid_attn(shape, inp: dict, ws=None, stream=None) -> torch.Tensor:
@@ -204,3 +220,13 @@ def window_attn(shape, inp: dict, gate_s=None, with_lse=False, ws=None, stream=N
     ws = workspace(shape, VDN_OP_WINDOW_ATTN, dev) if ws is None else ws
     window_anchor_attn_fwd(shape, inp["q"], inp["k"], inp["v"], gate_s, out, lse, ws, stream)
     return (out, lse) if with_lse else out
+
+
+def dense_attn(shape, inp: dict, w_o, ws=None, stream=None) -> torch.Tensor:
+    B, L = shape.batch, shape.frames * shape.tokens_per_frame
+    D = shape.heads * shape.head_dim
+    dev = inp["q"].device
+    out = torch.empty(B, L, D, dtype=shape.torch_dtype, device=dev)
+    ws = workspace(shape, VDN_OP_DENSE_ATTN, dev) if ws is None else ws
+    vdn_dense_attn_fwd(shape, inp["q"], inp["k"], inp["v"], w_o, out, ws, stream)
+    return out
