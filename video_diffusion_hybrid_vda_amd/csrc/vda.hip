@@ -118,6 +118,175 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// gram, bf16 / head_dim 128 (the workload shape).  One workgroup of four waves
+// per (frame, head); K_t and V_t stream through a four-stage LDS ring of
+// 64-token tiles by the direct-to-LDS DMA path (a buffer load with the lds
+// modifier), row-major with XOR-swizzled 16-byte chunks; token rows past N
+// read as zero.  Wave w consumes token rows 16w .. 16w+15 of every tile.  A
+// ds_read_b64_tr_b16 pair hands each lane eight tokens of one dimension: that
+// register is the A operand (row = dimension) and equally the B operand
+// (column = dimension) of a 32x32x16 MFMA, so K^T K and V^T K need no other
+// data movement.  Each wave accumulates the 10 upper 32x32 tiles of K^T K and
+// the 16 tiles of V^T K over its quarter of the tokens (416 fp32 per lane);
+// the four partial sums are added through LDS at the end, scaled by beta_t,
+// and A's off-diagonal tiles are mirrored.
+namespace gr {
+constexpr int D = 128, BN = 64, ROWB = D * 2, TILEB = BN * ROWB, STAGEB = 2 * TILEB, STAGES = 4;
+constexpr int NA = 10, NTILE = NA + 16;      // output tiles: upper A tiles, then B tiles
+constexpr int TB = 7;                        // tiles per reduction batch (4 x 7 x 16 x 65 floats fit the ring)
+constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0)
+constexpr int kWaitVm8 = 0x0F78;             // vmcnt(8): one tile's loads may be outstanding
+constexpr int kWaitVm16 = 0x4F70;            // vmcnt(16): two tiles' loads may be outstanding
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// Physical chunk of logical 16-byte chunk c of row r: 8 rows x 4 chunks of a
+// transpose read touch every bank exactly twice.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// (tile row block, tile column block) of output tile u
+__device__ __forceinline__ constexpr int tile_i(int u) {
+  return u < 4 ? 0 : u < 7 ? 1 : u < 9 ? 2 : u < 10 ? 3 : (u - NA) / 4;
+}
+__device__ __forceinline__ constexpr int tile_j(int u) {
+  return u < 4 ? u : u < 7 ? u - 3 : u < 9 ? u - 5 : u < 10 ? 3 : (u - NA) % 4;
+}
+// Accumulating products with the accumulator's register file fixed: the 10
+// K^T K tiles in vector registers, the 16 V^T K tiles in accumulator
+// registers (416 fp32 per lane do not fit one file; left to itself the
+// compiler shuttles tiles between the files around every product).
+// The first product of a tile starts from zero, so the accumulators need no
+// initialisation (and no vector-write -> matrix-read wait states).
+__device__ __forceinline__ void mma_v(f32x16& d, bf16x8 a, bf16x8 b, bool first) {
+  if (first) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_a(f32x16& d, bf16x8 a, bf16x8 b, bool first) {
+  if (first) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+}  // namespace gr
+
+__global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __restrict__ k,
+                                                                 const bf16* __restrict__ v,
+                                                                 const float* __restrict__ beta,
+                                                                 float* __restrict__ A,
+                                                                 float* __restrict__ Bm, int N) {
+  using namespace gr;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int g = lane / 16, j16 = lane % 16;
+  const int64_t f = blockIdx.x;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + f * N * D), (short)0, N * ROWB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + f * N * D), (short)0, N * ROWB, 0x00020000);
+
+  // DMA: lane l of block b fills physical chunk l%16 of tile row 4b + l/16
+  int lane_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 4 + lane / 16;
+    lane_off[i] = row * ROWB + swz(row, lane % 16) * 16;
+  }
+  const int ntiles = (N + BN - 1) / BN;
+  auto issue = [&](int t) {
+    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)(ring + (t & 3) * STAGEB);
+    const int base = t * BN * ROWB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      const int voff = base + lane_off[i];
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk), "{m0}"(lds + blk * 1024)
+                   : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv),
+                   "{m0}"(lds + TILEB + blk * 1024)
+                   : "memory");
+    }
+  };
+  // transpose-read offsets inside a tile: tokens 16 wave + 4 (g/2) + {0..3} and
+  // {8..11}, dimension 32 dt + 16 (g%2) + j16
+  int offA[4], offB[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int rowA = 16 * wave + 4 * (g >> 1) + (j16 >> 2), rowB = rowA + 8;
+    const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+    const int cch = dcol >> 3, off = (dcol & 7) * 2;
+    offA[dt] = rowA * ROWB + swz(rowA, cch) * 16 + off;
+    offB[dt] = rowB * ROWB + swz(rowB, cch) * 16 + off;
+  }
+  auto frag = [&](const unsigned char* base, int dt) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + offA[dt]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + offB[dt]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 accA[NA], accB[NTILE - NA];     // set by the first tile's products (N >= 1)
+
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm16);
+    else if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();                       // tile t visible; tile t-1's stage free
+    if (t + 3 < ntiles) issue(t + 3);
+    const unsigned char* sb = ring + (t & 3) * STAGEB;
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      kf[dt] = frag(sb, dt);
+      vf[dt] = frag(sb + TILEB, dt);
+    }
+    const bool first = t == 0;
+#pragma unroll
+    for (int u = 0; u < NA; ++u) mma_v(accA[u], kf[tile_i(u)], kf[tile_j(u)], first);
+#pragma unroll
+    for (int u = NA; u < NTILE; ++u) mma_a(accB[u - NA], vf[tile_i(u)], kf[tile_j(u)], first);
+  }
+  // the last products' results are read by vector instructions below: wait
+  // out the matrix pipeline (fenced so that no read is scheduled above it)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // cross-wave sum through the (drained) ring: P[wave][tile][r][lane], rows padded to 65
+  float* P = reinterpret_cast<float*>(ring);
+  const float bt = beta[f];
+  float* Af = A + f * D * D;
+  float* Bf = Bm + f * D * D;
+#pragma unroll
+  for (int b0 = 0; b0 < NTILE; b0 += TB) {
+    const int nb = NTILE - b0 < TB ? NTILE - b0 : TB;
+    __syncthreads();
+#pragma unroll
+    for (int uu = 0; uu < TB; ++uu)
+      if (uu < nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          P[((wave * TB + uu) * 16 + r) * 65 + lane] = b0 + uu < NA ? accA[b0 + uu][r] : accB[b0 + uu - NA][r];
+    __syncthreads();
+    for (int e = tid; e < nb * 1024; e += 256) {
+      const int uu = e >> 10, u = b0 + uu, w = e & 1023, row = w >> 5, col = w & 31;
+      const int ti = tile_i(u), tj = tile_j(u);
+      auto sum4 = [&](int rr, int cc) {
+        const int r = (rr >> 3) * 4 + (rr & 3), ln = cc + 32 * ((rr >> 2) & 1);
+        float s = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) s += P[((wv * TB + uu) * 16 + r) * 65 + ln];
+        return s;
+      };
+      if (u < NA) {
+        Af[(ti * 32 + row) * D + tj * 32 + col] = bt * sum4(row, col);
+        if (ti != tj) Af[(tj * 32 + row) * D + ti * 32 + col] = bt * sum4(col, row);
+      } else {
+        Bf[(ti * 32 + row) * D + tj * 32 + col] = bt * sum4(row, col);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // solve: one workgroup of 2d threads per (frame, head).  M_t = (I + A_t)^-1 by
 // Gauss-Jordan elimination of the augmented [I + A_t | I]: thread c keeps
 // column c in registers; at step k the pivot row and the pivot column go
@@ -517,7 +686,9 @@ __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
 template <typename T>
 static hipError_t gram_t(int d, const void* k, const void* v, const float* beta, float* A,
                          float* Bm, int nframes, int N, hipStream_t st) {
-  if (d == 32)
+  if (sizeof(T) == 2 && d == 128)
+    vda_gram_bf16_d128_kernel<<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, N);
+  else if (d == 32)
     vda_gram_kernel<T, 32><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, N);
   else if (d == 64)
     vda_gram_kernel<T, 64><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, N);
