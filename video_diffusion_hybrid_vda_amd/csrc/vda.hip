@@ -565,86 +565,143 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// readout, bf16 and head_dim 128 (the workload shapes).  One workgroup per
-// (frame, head) and 1024 tokens: both directions' S_hi and S_lo are staged in
-// LDS once (4 x 32 KB, the 16-byte chunk c of row i at c ^ (i & 15) so that
-// the sixteen rows a 16-lane group reads cover all banks), then each wave
-// walks 64 tokens at a time computing U^T = S Q^T on 32x32x16 MFMA: the
-// state fragments are the A operand (one LDS read serves both 32-token
-// tiles), the Q fragments come straight from HBM as the B operand.  A lane
-// then holds 64 of the 128 outputs of one token (its partner lane i ^ 32 the
-// other 64), so the RMSNorm needs one cross-lane swap, and gate loads and
-// output stores move four consecutive bf16.
+// readout, bf16 and head_dim 128 (the workload shapes).  One workgroup of four
+// waves per (frame, head) walks all N tokens of the frame.  Both directions'
+// S_hi and S_lo are copied into LDS once by the direct-to-LDS DMA (4 x 32 KB;
+// the 16-byte chunk c of row i at c ^ (i & 15), so that the sixteen rows a
+// 16-lane group reads cover all banks).  Each wave then takes 64-token blocks
+// (block = wave + 4k) and computes U^T = S Q^T on 32x32x16 MFMA: the state
+// fragments are the A operand (one LDS read serves both 32-token tiles), the
+// Q fragments come straight from HBM as the B operand.  The loads of the
+// block's gate and of the next block's Q are issued before the block's 256
+// products, so their latency hides behind the matrix work; the accumulators
+// live in the accumulator registers.  A lane holds 64 of the 128 outputs of
+// one token, its partner lane i ^ 32 the other 64: the RMSNorm needs one
+// cross-lane swap, and one swap per four outputs gives each lane eight
+// consecutive dimensions for 16-byte gate loads and output stores.
 namespace ro {
-constexpr int D = 128, TOK = 1024, SUB = 64;
-constexpr int MATB = D * D * 2;   // one bf16 d x d matrix
+constexpr int D = 128, SUB = 64;
+constexpr int MATB = D * D * 2;   // one bf16 d x d matrix, 32 KB
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & 15); }
+// products with the accumulator in the accumulator registers; a chain starts from zero
+__device__ __forceinline__ void mma_first(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
 }  // namespace ro
 
 __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ split, const float* __restrict__ rms_w,
     const bf16* __restrict__ gate, int64_t ldg, bf16* __restrict__ out, int64_t ldo, int H, int T_, int N,
-    float eps, int chunks_per_frame, int64_t bhtdd) {
+    float eps, int64_t bhtdd) {
   using namespace ro;
-  typedef float f32x16 __attribute__((ext_vector_type(16)));
-  __shared__ __attribute__((aligned(16))) unsigned char Sl[4 * MATB];   // [2 dir + part][row][chunk]
+  __shared__ __attribute__((aligned(1024))) unsigned char Sl[4 * MATB];   // [dir][hi, lo][row][chunk]
   __shared__ float wl[D];
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane % 32, h = lane / 32;
-  const int chunk = blockIdx.x % chunks_per_frame;
-  const int64_t fi = blockIdx.x / chunks_per_frame;     // (b*H + hh)*T + t
+  const int64_t fi = blockIdx.x;                       // (b*H + hh)*T + t
   const int t = (int)(fi % T_);
   const int64_t bh = fi / T_;
   const int hh = (int)(bh % H);
   const int64_t b = bh / H;
 
-  for (int c = tid; c < 4 * D * D / 8; c += 256) {
-    const int m = c / (D * D / 8), rem = c % (D * D / 8);
-    const int row = rem / 16, ch = rem % 16;
-    const bf16* src = split + ((m >> 1) * bhtdd + fi * D * D) * 2 + (m & 1) * D * D + row * D + ch * 8;
-    *reinterpret_cast<Chunk16*>(Sl + m * MATB + row * 256 + sw(row, ch) * 16) = *reinterpret_cast<const Chunk16*>(src);
+  // states -> LDS: 1 KB block j of a direction (j < 32: S_hi rows 4j..4j+3,
+  // else S_lo) by wave j / 16; lane l fills physical chunk l % 16 of row l / 16
+  {
+    const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)Sl;
+#pragma unroll
+    for (int dir = 0; dir < 2; ++dir) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(split + (dir * bhtdd + fi * D * D) * 2), (short)0, 2 * MATB, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int blk = wave * 16 + i, part = blk / 32;
+        const int row = (blk % 32) * 4 + lane / 16;
+        const int voff = part * MATB + row * 256 + sw(row, lane % 16) * 16;
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                     "{m0}"(lds0 + dir * 2 * MATB + blk * 1024)
+                     : "memory");
+      }
+    }
   }
   if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
-  __syncthreads();
 
   const int64_t NL = (int64_t)T_ * N;
-  for (int sub = 0; sub < TOK / (4 * SUB); ++sub) {
-    const int n0 = chunk * TOK + (sub * 4 + wave) * SUB;
-    if (n0 >= N) break;
-    // Q^T fragments: lane holds q[token n0 + 32 tt + l32][16 ks + 8 h .. +7]
-    bf16x8 qf[2][8];
+  const bf16* qfr = q + fi * N * D;
+  const int nblk = (N + SUB - 1) / SUB;
+  // Q^T fragments of a block: lane holds q[token 32 tt + l32][16 ks + 8 h .. +7].
+  // Token indices past the frame are clamped to its last token (loads stay
+  // unconditional); those lanes' outputs are never stored.
+  auto load_q = [&](bf16x8 (&dst)[2][8], int blk) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int n = n0 + 32 * tt + l32;
-      const bf16* qrow = q + (fi * N + n) * D + 8 * h;
+      const int n = min(blk * SUB + 32 * tt + l32, N - 1);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        qf[tt][ks] = n < N ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks) : bf16x8{};
+        dst[tt][ks] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 16 * ks + 8 * h);
     }
-    // acc[dir][tt][dt][r] = u_dir(token n0 + 32 tt + l32)[32 dt + 8(r/4) + 4h + r%4]
+  };
+  bf16x8 qf[2][8];
+  load_q(qf, wave);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  for (int blk = wave; blk < nblk; blk += 4) {
+    bf16x8 qn[2][8];
+    load_q(qn, blk + 4);
+    __builtin_amdgcn_sched_barrier(0);   // the loads above go out before the products
+
+    // acc[dir][tt][dt][r] = u_dir(token 32 tt + l32)[32 dt + 8 (r/4) + 4 h + r%4].
+    // 128 steps (dir, dt, ks, part), each one state-fragment read and two
+    // products; fragments are read three steps ahead and the steps are fenced,
+    // so at most four fragments are live.
     f32x16 acc[2][2][4];
+    auto read_sf = [&](int step) {
+      const int dir = step >> 6, dt = (step >> 4) & 3, ks = (step >> 1) & 7, part = step & 1;
+      const int row = 32 * dt + l32;
+      return *reinterpret_cast<const bf16x8*>(Sl + (2 * dir + part) * MATB + row * 256 + sw(row, 2 * ks + h) * 16);
+    };
+    bf16x8 sfb[4];
 #pragma unroll
-    for (int dir = 0; dir < 2; ++dir)
+    for (int i = 0; i < 3; ++i) sfb[i] = read_sf(i);
+    // gate of this block (lane: dims 32 dt + 16 p + 8 h .. +7 of its token), loaded
+    // halfway through the products
+    bf16x8 gv[2][4][2];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+    for (int step = 0; step < 128; ++step) {
+      if (step == 64 && gate) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) acc[dir][tt][dt] = f32x16{};
-        const int row = 32 * dt + l32;
+        for (int tt = 0; tt < 2; ++tt) {
+          const int n = min(blk * SUB + 32 * tt + l32, N - 1);
+          const bf16* grow = gate + (b * NL + (int64_t)t * N + n) * ldg + hh * D + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int part = 0; part < 2; ++part) {
-            const bf16x8 sf = *reinterpret_cast<const bf16x8*>(Sl + (2 * dir + part) * MATB + row * 256 +
-                                                               sw(row, 2 * ks + h) * 16);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-              acc[dir][tt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[tt][ks], acc[dir][tt][dt], 0, 0, 0);
-          }
+            for (int pp = 0; pp < 2; ++pp) gv[tt][dt][pp] = *reinterpret_cast<const bf16x8*>(grow + 32 * dt + 16 * pp);
+        }
       }
+      if (step + 3 < 128) sfb[(step + 3) & 3] = read_sf(step + 3);
+      const int dir = step >> 6, dt = (step >> 4) & 3, ks = (step >> 1) & 7, part = step & 1;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if (ks == 0 && part == 0) mma_first(acc[dir][tt][dt], sfb[step & 3], qf[tt][ks]);
+        else mma_acc(acc[dir][tt][dt], sfb[step & 3], qf[tt][ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the products' results are read by vector instructions below
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int n = n0 + 32 * tt + l32;
+      const int n = blk * SUB + 32 * tt + l32;
       float rn[2];
 #pragma unroll
       for (int dir = 0; dir < 2; ++dir) {
@@ -657,28 +714,39 @@ __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
         ss = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
         rn[dir] = 1.f / sqrtf(ss / D + eps);
       }
-      if (n >= N) continue;
       const int64_t orow = b * NL + (int64_t)t * N + n;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = 32 * dt + 8 * r4 + 4 * h;
-          float y[4];
+        for (int pp = 0; pp < 2; ++pp) {
+          // ya: dims 32dt + 16pp + 4h + e, yb: dims 32dt + 16pp + 8 + 4h + e; after the swap
+          // the lane holds dims 32dt + 16pp + 8h + {0..3} in ya and + {4..7} in yb
+          float ya[4], yb[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            y[e] = (acc[0][tt][dt][4 * r4 + e] * rn[0] + acc[1][tt][dt][4 * r4 + e] * rn[1]) * wl[d0 + e];
-          if (gate) {
-            const bf16x4 gv = *reinterpret_cast<const bf16x4*>(gate + orow * ldg + hh * D + d0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] *= (float)gv[e];
+          for (int e = 0; e < 4; ++e) {
+            const int da = 32 * dt + 16 * pp + 4 * h + e;
+            ya[e] = (acc[0][tt][dt][8 * pp + e] * rn[0] + acc[1][tt][dt][8 * pp + e] * rn[1]) * wl[da];
+            yb[e] = (acc[0][tt][dt][8 * pp + 4 + e] * rn[0] + acc[1][tt][dt][8 * pp + 4 + e] * rn[1]) * wl[da + 8];
+            const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ya[e]), __float_as_uint(yb[e]),
+                                                            false, false);
+            ya[e] = __uint_as_float(x[0]);
+            yb[e] = __uint_as_float(x[1]);
           }
-          bf16x4 ov;
+          bf16x8 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)y[e];   // the only rounding of the output
-          *reinterpret_cast<bf16x4*>(out + orow * ldo + hh * D + d0) = ov;
+          for (int e = 0; e < 4; ++e) {
+            const float ga = gate ? (float)gv[tt][dt][pp][e] : 1.f;
+            const float gb = gate ? (float)gv[tt][dt][pp][4 + e] : 1.f;
+            ov[e] = (bf16)(ya[e] * ga);        // the only rounding of the output
+            ov[4 + e] = (bf16)(yb[e] * gb);
+          }
+          if (n < N) *reinterpret_cast<bf16x8*>(out + orow * ldo + hh * D + 32 * dt + 16 * pp + 8 * h) = ov;
         }
     }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[tt][ks] = qn[tt][ks];
   }
 }
 
@@ -749,11 +817,10 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
                             int B, int H, int T_, int N, float eps, hipStream_t st) {
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
   if (sizeof(T) == 2 && d == 128 && split) {
-    const int cpf = (N + ro::TOK - 1) / ro::TOK;
-    const int64_t nb = (int64_t)B * H * T_ * cpf;
+    const int64_t nb = (int64_t)B * H * T_;
     if (nb == 0) return hipSuccess;
     vda_readout_bf16_d128_kernel<<<(unsigned)nb, 256, 0, st>>>((const bf16*)q, split, rms_w, (const bf16*)gate,
-                                                               ldg, (bf16*)out, ldo, H, T_, N, eps, cpf, bhtdd);
+                                                               ldg, (bf16*)out, ldo, H, T_, N, eps, bhtdd);
     return hipGetLastError();
   }
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
