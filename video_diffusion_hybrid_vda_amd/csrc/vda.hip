@@ -9,8 +9,8 @@
 // Four kernels, one HBM pass each over the large tensors:
 //   gram    : per (frame, head) A_t and B_t from K_t, V_t     (MFMA, HBM-bound)
 //   solve   : per (frame, head) M_t = (I + A_t)^-1 by Gauss-Jordan elimination
-//             with the columns in registers, and C_t = B_t M_t  (latency)
-//   scan    : S_t = gamma_t S_prev M_t + C_t, both directions    (T-step chain)
+//             with the columns in registers                    (latency)
+//   scan    : S_t = (gamma_t S_prev + B_t) M_t, both directions (T-step chain)
 //   readout : u = S_t q both directions, RMSNorm, sum, gate     (MFMA, HBM-bound)
 #include <math.h>
 
@@ -293,25 +293,21 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
 // through LDS (double-buffered, one barrier per step) and every column is
 // updated with a rank-1 step.  I + A_t is symmetric positive definite (beta
 // >= 0, eigenvalues >= 1), for which elimination without pivoting is stable.
-// Then C_t = B_t M_t through LDS.  AM holds A_t on entry and M_t on exit; BC
-// holds B_t then C_t.
+// AM holds A_t on entry and M_t^T on exit (row j = column j of M_t, so the
+// scan reads contiguous runs of a column).
 template <int D>
-__global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM,
-                                                          float* __restrict__ BC) {
-  constexpr int NT = 2 * D, LD = D + 1;
+__global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM) {
   __shared__ __attribute__((aligned(16))) float colb[2][D];
-  __shared__ float rowb[2][NT];
-  __shared__ float Ms[D * LD];
-  __shared__ float Bs[D * LD];
+  __shared__ float rowb[2][2 * D];
   const int64_t f = blockIdx.x;
   float* am = AM + f * D * D;
-  float* bm = BC + f * D * D;
   const int c = threadIdx.x;
 
   float a[D];
 #pragma unroll
   for (int i = 0; i < D; ++i)
     a[i] = c < D ? am[i * D + c] + (i == c ? 1.f : 0.f) : (i == c - D ? 1.f : 0.f);
+  __syncthreads();   // every column is read before any thread overwrites AM below
 
   // The rows rotate by one per step, so that the pivot row is always a[0]
   // (all register indices stay compile-time constants): the update writes
@@ -338,42 +334,36 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
     a[D - 1] = x;
   }
 
-  // columns D .. 2D-1 now hold M = (I + A)^-1
+  // thread D + j now holds column j of M = (I + A)^-1: store it as row j
   if (c >= D) {
+    float* dst = am + (int64_t)(c - D) * D;
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      Ms[i * LD + c - D] = a[i];
-      am[i * D + c - D] = a[i];
-    }
-  }
-  for (int e = c; e < D * D; e += NT) Bs[(e / D) * LD + e % D] = bm[e];
-  __syncthreads();
-  // C = B M
-  for (int e = c; e < D * D; e += NT) {
-    const int i = e / D, j = e % D;
-    float s = 0.f;
-    for (int q = 0; q < D; ++q) s += Bs[i * LD + q] * Ms[q * LD + j];
-    bm[e] = s;
+    for (int i = 0; i < D; i += 4)
+      *reinterpret_cast<float4*>(dst + i) = make_float4(a[i], a[i + 1], a[i + 2], a[i + 3]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// scan: S_t = gamma_t S_prev M_t + C_t.  Rows of S are independent given M_t,
-// so each workgroup owns kScanRows rows of one (batch, head, direction) and
-// walks the T frames, staging M_t in LDS.  Writes every S_t in fp32 and, when
-// `split` is non-null, also as an unevaluated bf16 pair hi + lo (hi = bf16(S),
-// lo = bf16(S - hi)) for the bf16 readout, laid out [dir][frame][hi|lo][d][d].
+// scan: S_t = (gamma_t S_{t-1} + B_t) M_t with S = 0 before the first frame,
+// forward (t ascending) and backward (t descending).  Rows of S are
+// independent given M_t, so each workgroup owns R rows of one (batch, head,
+// direction) and walks the T frames, staging M_t in LDS (transposed back
+// from the solve's M^T).  Writes every S_t in fp32 and, when `split` is
+// non-null, also as an unevaluated bf16 pair hi + lo (hi = bf16(S), lo =
+// bf16(S - hi)) for the bf16 readout, laid out [dir][frame][hi|lo][d][d].
+// This is the path for head_dim 32 and 64; head_dim 128 uses the MFMA kernel
+// below.
 template <int D, int R>
-__global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__ M,
-                                                       const float* __restrict__ Cm,
+__global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__ Mt,
+                                                       const float* __restrict__ Bm,
                                                        const float* __restrict__ gamma,
                                                        float* __restrict__ states,
                                                        bf16* __restrict__ split, int T,
                                                        int64_t bhtdd) {
   constexpr int TPR = 256 / R;     // threads per state row
   constexpr int CPT = D / TPR;     // columns per thread
-  constexpr int LDM = D + 4;
-  __shared__ __attribute__((aligned(16))) float Ms[D * LDM];
+  constexpr int LDM = D + 1;
+  __shared__ float Ms[D * LDM];
   __shared__ float Ss[R * LDM];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * R;
@@ -385,29 +375,29 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
   for (int step = 0; step < T; ++step) {
     const int t = dir ? T - 1 - step : step;
     const int64_t fi = bh * T + t;
-    const float* mt = M + fi * D * D;
-    __syncthreads();
-    for (int e = tid * 4; e < D * D; e += 1024) {
-      const float4 x = *reinterpret_cast<const float4*>(mt + e);
-      *reinterpret_cast<float4*>(Ms + (e / D) * LDM + (e % D)) = x;
-    }
-    __syncthreads();
+    const float* mt = Mt + fi * D * D;
+    const int64_t off = fi * D * D + (int64_t)(r0 + row) * D + col0;
     const float g = gamma[fi];
+    __syncthreads();
+    // Ms[q][c] = M_t[q][c] = Mt[c][q]
+    for (int e = tid; e < D * D; e += 256) Ms[(e % D) * LDM + e / D] = mt[e];
+    // X = gamma S_{t-1} + B_t, in place
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) Ss[row * LDM + col0 + c] = g * Ss[row * LDM + col0 + c] + Bm[off + c];
+    __syncthreads();
     float acc[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
     for (int q = 0; q < D; ++q) {
-      const float sv = Ss[row * LDM + q];
+      const float xv = Ss[row * LDM + q];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] += sv * Ms[q * LDM + col0 + c];
+      for (int c = 0; c < CPT; ++c) acc[c] += xv * Ms[q * LDM + col0 + c];
     }
-    const int64_t off = fi * D * D + (int64_t)(r0 + row) * D + col0;
-    const float* crow = Cm + off;
     float* srow = states + dir * bhtdd + off;
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const float nv = g * acc[c] + crow[c];
+      const float nv = acc[c];
       Ss[row * LDM + col0 + c] = nv;
       srow[c] = nv;
       if (split) {
@@ -417,6 +407,96 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
         sp[0] = hi;
         sp[D * D] = lo;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// scan, head_dim 128, on fp32 MFMA.  One workgroup of four waves per 32 state
+// rows of one (batch, head, direction); wave w produces columns 32w .. 32w+31
+// of those rows with 64 v_mfma_f32_32x32x2_f32 per frame.  The contraction
+// index is permuted so that every operand is a contiguous run: at product s
+// lane half h supplies k = 64h + s, so the A operand is row r0 + l%32 of
+// X = gamma S + B, columns 64h .. 64h+63 (S from LDS, B_t from HBM), and the
+// B operand is row 32w + l%32 of M_t^T, the same columns.  B_{t+1} and
+// M_{t+1}^T are loaded while frame t is multiplied.  The eight workgroups of
+// one (batch, head) share an XCD, so each M_t comes from HBM once per
+// direction.
+namespace sc {
+constexpr int D = 128, R = 32, LD = D + 4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+}  // namespace sc
+
+__global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restrict__ Mt,
+                                                            const float* __restrict__ Bm,
+                                                            const float* __restrict__ gamma,
+                                                            float* __restrict__ states,
+                                                            bf16* __restrict__ split, int T,
+                                                            int64_t bhtdd, int total) {
+  using namespace sc;
+  __shared__ __attribute__((aligned(16))) float Ss[R * LD];   // S_{t-1}, rows r0 .. r0+31
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int l32 = lane % 32, h = lane / 32;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int dir = lid & 1, rb = (lid >> 1) & 3;
+  const int64_t bh = lid >> 3;
+  const int r0 = rb * R, n0 = wave * 32;
+  for (int i = tid; i < R * LD; i += 256) Ss[i] = 0.f;
+
+  auto frame = [&](int step) { return dir ? T - 1 - step : step; };
+  auto load = [&](float4 (&b)[16], float4 (&m)[16], int t) {
+    const int64_t fi = bh * T + t;
+    const float4* bp = reinterpret_cast<const float4*>(Bm + fi * D * D + (int64_t)(r0 + l32) * D + 64 * h);
+    const float4* mp = reinterpret_cast<const float4*>(Mt + fi * D * D + (int64_t)(n0 + l32) * D + 64 * h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      b[i] = bp[i];
+      m[i] = mp[i];
+    }
+  };
+  float4 bx[16], mx[16];
+  load(bx, mx, frame(0));
+  __syncthreads();
+
+  for (int step = 0; step < T; ++step) {
+    const int t = frame(step);
+    const int64_t fi = bh * T + t;
+    const float g = gamma[fi];
+    float4 bn[16], mn[16];
+    load(bn, mn, frame(step + 1 < T ? step + 1 : step));
+    __builtin_amdgcn_sched_barrier(0);   // the next frame's loads go out before this frame's products
+    const float* srow = Ss + l32 * LD + 64 * h;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 sv = *reinterpret_cast<const float4*>(srow + 4 * i);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.x + bx[i].x, mx[i].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.y + bx[i].y, mx[i].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.z + bx[i].z, mx[i].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.w + bx[i].w, mx[i].w, acc, 0, 0, 0);
+    }
+    __syncthreads();   // every wave has read S_{t-1}
+    // acc[r] = S_t[r0 + 8 (r/4) + 4h + r%4][n0 + l32]
+    float* sdst = states + dir * bhtdd + fi * D * D + (int64_t)r0 * D + n0 + l32;
+    bf16* hdst = split ? split + (dir * bhtdd + fi * D * D) * 2 + (int64_t)r0 * D + n0 + l32 : nullptr;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r / 4) + 4 * h + r % 4;
+      Ss[row * LD + n0 + l32] = acc[r];
+      sdst[row * D] = acc[r];
+      if (hdst) {
+        const bf16 hi = (bf16)acc[r];
+        hdst[row * D] = hi;
+        hdst[row * D + D * D] = (bf16)(acc[r] - (float)hi);
+      }
+    }
+    __syncthreads();   // S_t visible
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      bx[i] = bn[i];
+      mx[i] = mn[i];
     }
   }
 }
@@ -792,22 +872,26 @@ hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const
                     : gram_t<float>(d, k, v, beta, A, Bm, nframes, N, st);
 }
 
-hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_t st) {
+hipError_t launch_vda_solve(int d, float* AM, int nframes, hipStream_t st) {
   if (nframes == 0) return hipSuccess;
-  if (d == 32) vda_solve_kernel<32><<<nframes, 64, 0, st>>>(AM, BC);
-  else if (d == 64) vda_solve_kernel<64><<<nframes, 128, 0, st>>>(AM, BC);
-  else vda_solve_kernel<128><<<nframes, 256, 0, st>>>(AM, BC);
+  if (d == 32) vda_solve_kernel<32><<<nframes, 64, 0, st>>>(AM);
+  else if (d == 64) vda_solve_kernel<64><<<nframes, 128, 0, st>>>(AM);
+  else vda_solve_kernel<128><<<nframes, 256, 0, st>>>(AM);
   return hipGetLastError();
 }
 
-hipError_t launch_vda_scan(int d, const float* M, const float* Cm, const float* gamma,
+hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float* gamma,
                            float* states, bf16* split, int BH, int T, hipStream_t st) {
   if (BH == 0) return hipSuccess;
   const int64_t bhtdd = (int64_t)BH * T * d * d;
+  if (d == 128) {
+    const int total = BH * 8;   // 4 row blocks x 2 directions per (batch, head)
+    vda_scan_d128_kernel<<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
+    return hipGetLastError();
+  }
   dim3 grid(d / kScanRows, BH, 2);
-  if (d == 32) vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
-  else if (d == 64) vda_scan_kernel<64, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
-  else vda_scan_kernel<128, kScanRows><<<grid, 256, 0, st>>>(M, Cm, gamma, states, split, T, bhtdd);
+  if (d == 32) vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd);
+  else vda_scan_kernel<64, kScanRows><<<grid, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd);
   return hipGetLastError();
 }
 

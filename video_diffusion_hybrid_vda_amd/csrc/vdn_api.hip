@@ -270,7 +270,7 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda gram launch");
   ph = phase_begin(kPhSolve, st);
-  e = launch_vda_solve(d, am, bc, nframes, st);
+  e = launch_vda_solve(d, am, nframes, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda solve launch");
   ph = phase_begin(kPhScan, st);

@@ -62,8 +62,8 @@ hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t
 hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st);
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
                            float* A, float* Bm, int nframes, int N, hipStream_t st);
-hipError_t launch_vda_solve(int d, float* AM, float* BC, int nframes, hipStream_t st);
-hipError_t launch_vda_scan(int d, const float* M, const float* Cm, const float* gamma,
+hipError_t launch_vda_solve(int d, float* AM, int nframes, hipStream_t st);   // AM: A in, M^T out
+hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float* gamma,
                            float* states, __bf16* split, int BH, int T, hipStream_t st);
 hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
                               const __bf16* split, const float* rms_w, const void* gate,
