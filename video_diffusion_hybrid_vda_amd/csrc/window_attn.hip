@@ -424,16 +424,18 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   // make every later LDS read wait for it (it cannot tell the stages apart);
   // the loop below waits for each tile's loads explicitly (vmcnt) before the
   // barrier that publishes the tile.
-  auto issue = [&](unsigned char* sb) {
+  auto issue = [&](int st) {
     const int base = lk0 * ROWB;
-    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)sb;
+    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
 #pragma unroll
     for (int i = 0; i < BLK; ++i) {
       const int blk = wave * BLK + i;
       const int voff = base + lane_off[i];
-      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk), "{m0}"(lds + blk * 1024)
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk),
+                   "{m0}"(lds + st * TILEB + blk * 1024)
                    : "memory");
-      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv), "{m0}"(lds + TILEB + blk * 1024)
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv),
+                   "{m0}"(lds + (STAGES + st) * TILEB + blk * 1024)
                    : "memory");
     }
     lk0 += BN;
@@ -448,9 +450,9 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
 
   // ring of four 64-key stages: tiles t+1 .. t+3 resident or in flight while
   // tile t is consumed
-  if (ntiles > 0) issue(ring);
-  if (ntiles > 1) issue(ring + STAGEB);
-  if (ntiles > 2) issue(ring + 2 * STAGEB);
+  if (ntiles > 0) issue(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds Q[query l32][16 ks + 8 h .. +7]
   bf16x8 qf[QT][8];
@@ -511,24 +513,41 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   f32x16 sa[QT], sb[QT];
   float mtile[QT];
 
-  // K fragment of 16-column step ks, rows 32 kt + l32
-  auto load_k = [&](const unsigned char* stage, int kt, int ks) {
-    const int row = kt * 32 + l32;
-    return *reinterpret_cast<const bf16x8*>(stage + row * ROWB + swz(row, 2 * ks + h) * 16);
-  };
-  // V^T fragments of 16-key step s4 of the tile for the four 32-wide column blocks
-  auto load_v = [&](bf16x8 (&vf)[4], const unsigned char* stage, int s4) {
-    const unsigned char* vb = stage + TILEB;
-    const int rowA = 16 * s4 + 4 * (g >> 1) + (j16 >> 2);
-    const int rowB = rowA + 8;
+  // Fragment reads.  The ring keeps the K tiles of the four stages in its
+  // first 64 KB and the V tiles in the second, so every read is a per-lane
+  // base register (fixed for the kernel) plus a constant below 64 KB (stage,
+  // half tile, key step) that the LDS instruction carries in its offset field.
+  // The swizzle depends on row % 16 only, and the constants move whole
+  // 16-row groups.
+  int koff[8], voffA[4], voffB[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    koff[ks] = l32 * ROWB + swz(l32, 2 * ks + h) * 16;
+    pin(koff[ks]);
+  }
+  {
+    const int rA = 4 * (g >> 1) + (j16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
       const int cch = dcol >> 3, off = (dcol & 7) * 2;
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + rowA * ROWB + swz(rowA, cch) * 16 + off));
-      const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vb + rowB * ROWB + swz(rowB, cch) * 16 + off));
+      voffA[dt] = STAGES * TILEB + rA * ROWB + swz(rA, cch) * 16 + off;
+      voffB[dt] = STAGES * TILEB + (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
+      pin(voffA[dt]);
+      pin(voffB[dt]);
+    }
+  }
+  // K fragment of 16-column step ks, rows 32 kt + l32 of stage st
+  auto load_k = [&](int st, int kt, int ks) {
+    return *reinterpret_cast<const bf16x8*>(ring + koff[ks] + st * TILEB + kt * 32 * ROWB);
+  };
+  // V^T fragments of 16-key step s4 of stage st for the four 32-wide column blocks
+  auto load_v = [&](bf16x8 (&vf)[4], int st, int s4) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int c = st * TILEB + s4 * 16 * ROWB;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ring + voffA[dt] + c));
+      const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ring + voffB[dt] + c));
       vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
@@ -599,8 +618,8 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   // score chunks carry p of the first 16 keys, the first P V chunk p of the
   // other 16, the second P V chunk the max of the next scores.  p is rounded
   // to bf16 for the products.
-  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], const unsigned char* sst, int skt,
-                       const unsigned char* pst, int pkt) {
+  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], int sst, int skt, int pst,
+                       int pkt) __attribute__((always_inline)) {
     bf16x8 kf[3], vf[2][4], pk[QT][2];
     // p of register r of query tile qt (16-key step r / 8)
     auto soft1 = [&](int qt, int r) {
@@ -666,13 +685,11 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
     chunk_fence();
   };
 
-  // stage offsets of tiles t .. t+3
-  int st0 = 0, st1 = STAGEB, st2 = 2 * STAGEB, st3 = 3 * STAGEB;
   int kn = min(BN, cke - ck0);   // keys of tile t
   if (ntiles > 0) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 kf = load_k(ring, 0, ks);
+      const bf16x8 kf = load_k(0, 0, ks);
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         if (ks == 0) mma_first(sa[qt], kf, qf[qt][ks]);
@@ -684,25 +701,31 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
     half_max(sa);
     boundary(sa, kn);
   }
-  // Each iteration runs the two halves of tile t; the second one computes
-  // the scores of the first half of tile t+1 (for the last tile they come
-  // from a stale stage and are never used).
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 3 < ntiles) issue(ring + st3);
-    half_step(sa, sb, ring + st0, 1, ring + st0, 0);
+  // One tile: its two halves; the second computes the scores of the first
+  // half of tile t+1 (for the last tile they come from a stale stage and are
+  // never used).  Tile t sits in ring stage t % 4; the loop is unrolled over
+  // the four stages so that every stage offset is a constant (it folds into
+  // the LDS instructions' offset field instead of costing an add per read).
+  auto tile = [&](int t, int s0, int s1, int s3) __attribute__((always_inline)) {
+    if (t + 3 < ntiles) issue(s3);
+    half_step(sa, sb, s0, 1, s0, 0);
     boundary(sb, kn - 32);
-    half_step(sb, sa, ring + st1, 0, ring + st0, 1);
+    half_step(sb, sa, s1, 0, s0, 1);
     advance();
     kn = min(BN, cke - ck0);
     if (t + 3 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm8);
     else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (t + 1 < ntiles) boundary(sa, kn);
-    const int sf = st0;
-    st0 = st1;
-    st1 = st2;
-    st2 = st3;
-    st3 = sf;
+  };
+  for (int t = 0; t < ntiles; t += 4) {
+    tile(t, 0, 1, 3);
+    if (t + 1 >= ntiles) break;
+    tile(t + 1, 1, 2, 0);
+    if (t + 2 >= ntiles) break;
+    tile(t + 2, 2, 3, 1);
+    if (t + 3 >= ntiles) break;
+    tile(t + 3, 3, 0, 2);
   }
 
   // ---- epilogue: o[dt][qt][r] = O(query 32 qt + l32, dim 32 dt + 8(r/4) + 4h + r%4)
