@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_w4_kernel(const bf16* __rest
   }
 }
 
-constexpr bool kGemmFourWaves = true;
+constexpr bool kGemmFourWaves = false;   // the eight-wave kernel measures faster on the layer shapes
 
 // the big-tile kernel's shape contract: bf16, K a multiple of 32, N of 8, 16-byte
 // aligned rows, and every operand tile's byte range below 2^31
