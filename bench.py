@@ -86,6 +86,66 @@ def window_traffic(cfg_name):
     return WINDOW_TRAFFIC_BYTES if h.hexdigest()[:16] == WINDOW_TRAFFIC_SHA else None
 
 
+def phase_rooflines(cfg, phases):
+    """Achieved rate of each hot-path kernel against its own roofline, from the library's per-phase
+    HIP-event times: algorithmic bytes (HBM-bound kernels) or flops (MFMA-bound kernels) per call."""
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    L, D = T * N, cfg.model_dim
+    es = 2 if cfg.dtype == "bf16" else 4
+    frames = B * H * T
+    tok = B * L * D * es                       # one [B, L, D] activation tensor
+    dd4 = frames * d * d * 4                   # one fp32 d x d matrix per frame-head
+    out = {}
+
+    def ms(name):
+        n, tot = phases.get(name, (0, 0.0))
+        return tot / n if n else None
+
+    def hbm(name, nbytes):
+        t = ms(name)
+        if t:
+            gbs = nbytes / (t * 1e-3) / 1e9
+            out[name] = {"bound": "hbm", "algorithmic_gb": round(nbytes / 1e9, 3), "ms": round(t, 3),
+                         "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+    def mfma(name, flops):
+        t = ms(name)
+        if t:
+            tf = flops / (t * 1e-3) / 1e12
+            out[name] = {"bound": "mfma", "algorithmic_tflop": round(flops / 1e12, 3), "ms": round(t, 3),
+                         "achieved_tflops": round(tf, 1), "peak_tflops": PEAK_BF16_TFLOPS,
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    # K and V read once; A_t and B_t written (fp32)
+    hbm("vda_gram", 2 * tok + 2 * dd4)
+    # Q, gate and output once; both directions' states once per frame
+    hbm("vda_readout", 3 * tok + 2 * dd4)
+    mfma("gate_gemm", 2.0 * B * L * D * 2 * D)
+    mfma("out_gemm", 2.0 * B * L * 2 * D * D)
+    t = ms("vda_scan")
+    if t:
+        out["vda_scan"] = {"bound": "latency", "ms": round(t, 3), "frame_steps": T,
+                           "us_per_step": round(t * 1e3 / T, 2)}
+    t = ms("vda_solve")
+    if t:
+        out["vda_solve"] = {"bound": "latency", "ms": round(t, 3), "systems": frames,
+                            "us_per_system_per_cu": round(t * 1e3 * 256 / frames, 2)}
+    return out
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
 def timed_calls(fn, steps, warmup):
     """Run fn warmup times, then `steps` times with a torch (HIP) event pair
     around each call on the current stream; returns (wall ms per call,
@@ -221,7 +281,7 @@ def cpu_baseline(cfg, inp):
               f"of {Rs} tokens; scaled by exact token/head counts to the B{B} H{H} T{T} N{N} layer "
               f"(extrapolated layer time {total:.0f} s)")
     return {"value": B * L / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "host": host_info()}
 
 
 def main():
@@ -309,6 +369,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
                      "traffic": window_traffic(cfg.name)},
+        "kernel_rooflines": phase_rooflines(cfg, phases),
         "call_ms_median": round(median(call_ms), 3),
         "call_ms_min": round(min(call_ms), 3),
         "phases_ms": phase_ms,
