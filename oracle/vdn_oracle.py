@@ -46,6 +46,14 @@ the alternatives, in the repository's design notes):
     multiplies the output.  [P3 方法概述 parts 1 and 3]  Readings D-10..D-12.
   * Each branch has its own output projection; the two projections are
     summed.  [P3 方法概述 part 3; P1 关键模块]
+  * Context (text / audio) tokens: every interaction that involves one keeps
+    the full softmax, and the linear branch covers only video-to-video context.
+    [P3 方法概述 part 1, last sentence; P3 内容介绍 item 1; P1 方法 / 输入与整体流程]
+    Reading C-1: the sequence is the T*N video tokens followed by n_ctx
+    context tokens; a video query's one softmax runs over its allowed video
+    keys plus every context key; a context query attends every token; the
+    linear branch output of a context row is zero; gates and projections
+    treat context rows like video rows.
 
 Everything is computed in float64 from the (already rounded) inputs.
 """
@@ -58,7 +66,7 @@ __all__ = [
     "rms_norm", "vda_readout", "vda_branch",
     "allowed_frames", "key_frames", "window_attention",
     "sigmoid", "gates", "merge_heads", "hybrid_layer", "hybrid_layer_rows",
-    "dense_layer",
+    "dense_layer", "window_attention_ctx", "hybrid_layer_ctx",
 ]
 
 
@@ -344,3 +352,83 @@ def dense_layer(q, k, v, w_o, scale=None):
             oo, _ = window_attention(q[b, h], k[b, h], v[b, h], allowed, scale)
             o[b, h] = oo.reshape(T, N, d)
     return merge_heads(o) @ _f64(w_o)
+
+
+# --------------------------------------------------------------------------
+# Context (text / audio) tokens  [P3 方法概述 part 1; P1 方法 / 输入与整体流程] - reading C-1
+# --------------------------------------------------------------------------
+
+def window_attention_ctx(q, k, v, allowed, N, scale, rows=None):
+    """Softmax branch of one (batch, head) with context tokens, ungated.
+
+    q, k, v: [T*N + n_ctx, d] - the video tokens (frame-major) followed by
+    n_ctx context tokens; `allowed` is the [T, T] frame mask.  A video query
+    of frame t sees the key tokens of its allowed frames plus every context
+    token, under one softmax; a context query sees every token.  rows:
+    optional flat query indices (default all).  Returns (o [len(rows), d],
+    lse [len(rows)]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T = allowed.shape[0]
+    L = T * N
+    Ltot, d = q.shape
+    if rows is None:
+        rows = np.arange(Ltot)
+    rows = np.asarray(rows)
+    ctx_keys = np.arange(L, Ltot)
+    o = np.zeros((len(rows), d))
+    lse = np.zeros(len(rows))
+    for i, r in enumerate(rows):
+        if r < L:
+            t = r // N
+            frames = key_frames(allowed, int(t))
+            keys = np.concatenate([np.arange(f * N, (f + 1) * N) for f in frames] + [ctx_keys])
+        else:
+            keys = np.arange(Ltot)
+        logits = (k[keys] @ q[r]) * scale
+        m = logits.max()
+        p = np.exp(logits - m)
+        o[i] = (p @ v[keys]) / p.sum()
+        lse[i] = m + np.log(p.sum())
+    return o, lse
+
+
+def hybrid_layer_ctx(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol, N,
+                     chunk_frames=5, window_chunks=1, anchor_first=True,
+                     anchor_last=True, scale=None, eps=1e-6, rows=None):
+    """Hybrid attention forward with n_ctx context tokens after the video.
+
+    x: [B, T*N + n_ctx, D]; q, k, v: [B, H, T*N + n_ctx, d]; gamma, beta
+    [B, H, T].  The softmax branch follows window_attention_ctx; the linear
+    branch runs on the video tokens only and is zero on context rows; gates
+    and projections as in hybrid_layer.  rows: optional flat output rows
+    (default all); the linear branch's scans always cover every frame.
+    Returns out [B, len(rows), D].  [P3 方法概述 parts 1-3; reading C-1]
+    """
+    gamma, beta, rms_w = _f64(gamma), _f64(beta), _f64(rms_w)
+    B, H, Ltot, d = q.shape
+    T = gamma.shape[2]
+    L = T * N
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if rows is None:
+        rows = np.arange(Ltot)
+    rows = np.asarray(rows)
+    allowed = allowed_frames(T, chunk_frames, window_chunks, anchor_first, anchor_last)
+    R = len(rows)
+    y_s = np.zeros((B, R, H * d))
+    y_l = np.zeros((B, R, H * d))
+    g_s, g_l = gates(_f64(np.asarray(x)[:, rows, :]), _f64(w_gs), _f64(w_gl))
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+            o, _ = window_attention_ctx(qh, kh, vh, allowed, N, scale, rows)
+            y_s[b, :, h * d:(h + 1) * d] = o
+            kv = kh[:L].reshape(T, N, d), vh[:L].reshape(T, N, d)
+            sf, sb = vda_states(kv[0], kv[1], gamma[b, h], beta[b, h])
+            w_h = rms_w[h * d:(h + 1) * d]
+            for i, r in enumerate(rows):
+                if r < L:
+                    t = int(r) // N
+                    y_l[b, i, h * d:(h + 1) * d] = vda_readout(qh[r][None], sf[t], sb[t], w_h, eps)[0]
+    return (g_s * y_s) @ _f64(w_os) + (g_l * y_l) @ _f64(w_ol)

@@ -451,3 +451,90 @@ def test_linear_branch_matches_explicit_states():
             b_t = b[t] * v[t].T @ k[t]
             s = np.linalg.solve((np.eye(d) + a_t).T, (g[t] * s + b_t).T).T
             assert np.max(np.abs(parts["s_fwd"][0, h, t] - s)) < 1e-12
+
+
+# ---------------------------------------------------------------- context tokens (reading C-1)
+
+def _ctx_token_mask(T, N, n_ctx, **kw):
+    """Token-level mask built from the rule directly: video x video by frame
+    pairs, and every pair that involves a context token allowed."""
+    L = T * N
+    m = np.ones((L + n_ctx, L + n_ctx), dtype=bool)
+    m[:L, :L] = np.kron(O.allowed_frames(T, **kw), np.ones((N, N), dtype=bool))
+    return m
+
+
+@pytest.mark.parametrize("T,N,n_ctx,d,sharp", [(12, 3, 5, 8, False), (17, 2, 3, 4, True), (23, 1, 7, 6, True)])
+def test_context_softmax_equals_dense_masked_sdpa(T, N, n_ctx, d, sharp):
+    r = rng(100 + T)
+    Ltot = T * N + n_ctx
+    q = r.normal(size=(Ltot, d)) * (4.0 if sharp else 1.0)
+    k = r.normal(size=(Ltot, d))
+    if not sharp:
+        k = unit_rows(k)
+    v = r.normal(size=(Ltot, d))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = O.window_attention_ctx(q, k, v, O.allowed_frames(T), N, scale)
+    mask = _ctx_token_mask(T, N, n_ctx)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(mask)[None], scale=scale)[0].numpy()
+    assert np.max(np.abs(o - ref)) < 1e-12
+    logits = (q @ k.T) * scale
+    logits[~mask] = -np.inf
+    assert np.max(np.abs(lse - scipy.special.logsumexp(logits, axis=1))) < 1e-12
+    # a context query sees everything: plain full softmax
+    full = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[-1:])[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        scale=scale)[0].numpy()
+    assert np.max(np.abs(o[-1:] - full)) < 1e-12
+
+
+def test_context_softmax_without_context_is_window_attention():
+    q, k, v = _attn_inputs(5, 17, 2, 4)
+    ok = O.allowed_frames(17)
+    o, lse = O.window_attention(q, k, v, ok, 0.4)
+    o2, lse2 = O.window_attention_ctx(q.reshape(34, 4), k.reshape(34, 4), v.reshape(34, 4), ok, 2, 0.4)
+    assert np.max(np.abs(o - o2)) < 1e-14 and np.max(np.abs(lse - lse2)) < 1e-14
+
+
+def _ctx_layer(seed, B=1, H=2, T=12, N=3, n_ctx=4, d=8):
+    inp = _layer(seed, B=B, H=H, T=T, N=N, d=d)
+    r = rng(seed + 1000)
+    D = H * d
+    flat = {}
+    for name in ("q", "k", "v"):
+        extra = r.normal(size=(B, H, n_ctx, d))
+        if name == "k":
+            extra = unit_rows(extra)
+        flat[name] = np.concatenate([inp[name].reshape(B, H, T * N, d), extra], axis=2)
+    flat["x"] = np.concatenate([inp["x"], r.normal(size=(B, n_ctx, D))], axis=1)
+    return inp, {**inp, **flat}
+
+
+def test_context_layer_branches():
+    """Without context tokens the layer is hybrid_layer; with them the linear
+    branch's video rows are unchanged and its context rows are zero, and the
+    softmax branch is the gated dense-masked softmax."""
+    T, N, n_ctx, H, d = 12, 3, 4, 2, 8
+    base, inp = _ctx_layer(7, T=T, N=N, n_ctx=n_ctx, H=H, d=d)
+    L = T * N
+    out0 = O.hybrid_layer(**base)
+    flat0 = {**base, **{n: base[n].reshape(1, H, L, d) for n in ("q", "k", "v")}}
+    assert np.max(np.abs(O.hybrid_layer_ctx(**flat0, N=N) - out0)) < 1e-12
+    zero = np.zeros_like(inp["w_os"])
+    lin = O.hybrid_layer_ctx(**{**inp, "w_os": zero}, N=N)
+    lin_video = O.hybrid_layer(**{**base, "w_os": zero})
+    assert np.max(np.abs(lin[:, :L] - lin_video)) < 1e-12
+    assert np.max(np.abs(lin[:, L:])) == 0.0
+    sm = O.hybrid_layer_ctx(**{**inp, "w_ol": zero}, N=N)
+    mask = torch.from_numpy(_ctx_token_mask(T, N, n_ctx))[None]
+    cols = [torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(inp["q"][0, h])[None], torch.from_numpy(inp["k"][0, h])[None],
+        torch.from_numpy(inp["v"][0, h])[None], attn_mask=mask)[0].numpy() for h in range(H)]
+    g_s = scipy.special.expit(inp["x"] @ inp["w_gs"])
+    ref = (g_s * np.concatenate(cols, axis=1)[None]) @ inp["w_os"]
+    assert np.max(np.abs(sm - ref)) < 1e-11
+    full = O.hybrid_layer_ctx(**inp, N=N)
+    rows = np.array([0, 7, L - 1, L, L + n_ctx - 1])
+    assert np.max(np.abs(O.hybrid_layer_ctx(**inp, N=N, rows=rows) - full[:, rows])) < 1e-12
