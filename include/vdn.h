@@ -21,24 +21,36 @@
  *                   g_l = sigmoid(x W_gl) (part 3).
  *
  * Notation: B batch, H heads, d head_dim, T latent frames, N tokens per frame,
- * L = T*N tokens, D = H*d model width.  Token l = t*N + n.
+ * L = T*N video tokens, Nc = shape->context_tokens text/audio tokens after
+ * them, Lt = L + Nc, D = H*d model width.  Video token l = t*N + n; context
+ * token c is row L + c.
+ *
+ * Context tokens (10100.com article, 方法概述 part 1, last sentence; ai-feeds
+ * page, 方法 / 输入与整体流程): every interaction that involves a text or audio
+ * token keeps the full softmax and the linear branch covers only video
+ * context.  So a video query's softmax also covers every context key, a
+ * context query attends every token, and the linear branch is zero on
+ * context rows.  With Nc = 0 the layouts below are exactly those of a
+ * video-only layer.
  *
  * Layouts (all row-major, contiguous, element type = shape->dtype unless
  * stated otherwise):
- *   q, k, v           [B, H, T, N, d]   rows of k must be L2-normalised by the
- *                                       caller (the operator does not do it)
+ *   q, k, v           [B, H, Lt, d]     = [B, H, T, N, d] followed, per (b, h),
+ *                                       by Nc context rows; rows of k must be
+ *                                       L2-normalised by the caller (the
+ *                                       operator does not do it)
  *   gamma, beta       [B, H, T]         float32, per-frame decay / write strength
- *   x                 [B, L, D]         layer input the gates read
+ *   x                 [B, Lt, D]        layer input the gates read
  *   w_gs, w_gl,
  *   w_os, w_ol        [D, D]            y = x @ W (input dimension first)
  *   rms_w             [D]               float32 RMSNorm weight (head h uses
  *                                       rms_w[h*d .. h*d+d-1]); NULL = ones
- *   gate_s, gate_l    [B, L, D]         gate values already in (0,1); NULL = 1
- *   out               [B, L, D]
+ *   gate_s, gate_l    [B, Lt, D]        gate values already in (0,1); NULL = 1
+ *   out               [B, Lt, D]
  *   states            [2, B, H, T, d, d] float32; [0] forward-scan state after
  *                                       frame t, [1] backward-scan state after
  *                                       frame t; S is d_v x d_k (row = value dim)
- *   lse               [B, H, L]         float32 natural-log softmax denominator
+ *   lse               [B, H, Lt]        float32 natural-log softmax denominator
  *                                       of the scaled logits
  *
  * Ownership: the caller allocates and owns every buffer, including the device
@@ -104,6 +116,7 @@ typedef struct vdn_shape {
   float softmax_scale;      /* logit scale; <= 0 selects 1/sqrt(d) */
   float rms_eps;            /* RMSNorm epsilon (1e-6) */
   int32_t dtype;            /* enum vdn_dtype: storage of q,k,v,x,W,gates,out */
+  int32_t context_tokens;   /* Nc >= 0 text/audio tokens after the video tokens (0) */
 } vdn_shape;
 
 /* Bytes of device workspace `op` needs for `shape` (0 on an invalid shape,
@@ -125,7 +138,8 @@ int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q,
 /* Linear branch alone (10100.com article, 方法概述 part 2; forward-plus-
  * backward scan figure):
  *   out[b, t*N+n, h*d+i] = gate_l * (RMSNorm(S_fwd_t q) + RMSNorm(S_bwd_t q))_i
- * gate_l may be NULL (no gate); states may be NULL (kept in the workspace). */
+ * and zero on context rows.  gate_l may be NULL (no gate); states may be
+ * NULL (kept in the workspace). */
 int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
                  const void* v, const float* gamma, const float* beta,
                  const float* rms_w, const void* gate_l, void* out,

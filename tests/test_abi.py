@@ -58,7 +58,10 @@ def test_version_and_clean_error_state(vdn):
 
 
 def test_shape_struct_layout(vdn):
-    assert ctypes.sizeof(vdn.vdn_shape) == 12 * 4
+    """13 four-byte fields in the order of include/vdn.h; context_tokens last."""
+    assert ctypes.sizeof(vdn.vdn_shape) == 13 * 4
+    assert vdn.vdn_shape.context_tokens.offset == 12 * 4
+    assert vdn.vdn_shape.dtype.offset == 11 * 4
 
 
 def _shape(vdn, **kw):
@@ -71,7 +74,8 @@ def _shape(vdn, **kw):
     (dict(head_dim=48), -2), (dict(head_dim=256), -2), (dict(frames=0), -2),
     (dict(tokens_per_frame=0), -2), (dict(batch=0), -2), (dict(heads=-1), -2),
     (dict(chunk_frames=0), -2), (dict(window_chunks=-1), -2), (dict(dtype=7), -3),
-    (dict(rms_eps=-1.0), -2), (dict(anchor_first=2), -2),
+    (dict(rms_eps=-1.0), -2), (dict(anchor_first=2), -2), (dict(context_tokens=-1), -2),
+    (dict(frames=2 ** 16, tokens_per_frame=2 ** 14, context_tokens=1), -2),
 ])
 def test_bad_shapes_rejected_before_launch(vdn, kw, status):
     s = _shape(vdn, **kw)
@@ -188,3 +192,17 @@ def test_timing_session_without_launches(vdn):
     stats = vdn.vdn_timing_stop()
     assert "window_attn" in stats and "vda_scan" in stats
     assert all(n == 0 for n, _ in stats.values())
+
+
+def test_context_tokens_grow_the_workspace(vdn):
+    """Context rows add gate and branch-output rows to the layer workspace and
+    a dense query group (its key-split partials) to the softmax workspace."""
+    a = vdn.make_shape(1, 4, 42, 64, 64, "bf16")
+    b = vdn.make_shape(1, 4, 42, 64, 64, "bf16", context_tokens=100)
+    D = 4 * 64
+    for op in (vdn.VDN_OP_HYBRID, vdn.VDN_OP_WINDOW_ATTN, vdn.VDN_OP_DENSE_ATTN):
+        assert vdn.vdn_workspace_bytes(b, op) > vdn.vdn_workspace_bytes(a, op)
+    grow = vdn.vdn_workspace_bytes(b, vdn.VDN_OP_HYBRID) - vdn.vdn_workspace_bytes(a, vdn.VDN_OP_HYBRID)
+    assert grow >= 2 * 100 * 2 * D * 2      # gates and branch outputs, [rows, 2D] bf16 each
+    # the linear branch reads video rows only: its workspace does not change
+    assert vdn.vdn_workspace_bytes(b, vdn.VDN_OP_VDA_SCAN) == vdn.vdn_workspace_bytes(a, vdn.VDN_OP_VDA_SCAN)

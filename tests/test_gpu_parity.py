@@ -290,6 +290,91 @@ def test_param_range_check(vdn):
     torch.cuda.synchronize()
 
 
+# ---------------------------------------------------------------- context tokens
+# Text/audio tokens after the video tokens (reading C-1): a video query's one
+# softmax covers its allowed video keys plus every context key, a context
+# query attends every token, the linear branch is zero on context rows.
+
+CTX = [
+    ("T12_N20_ctx7_d32_f32", VdnConfig(1, 2, 32, 12, 20, dtype="f32", seed=81, context_tokens=7)),
+    ("T17_N70_ctx77_d128_bf16", VdnConfig(1, 2, 128, 17, 70, dtype="bf16", seed=82, context_tokens=77)),
+    ("B2_T23_N9_ctx300_d64_bf16", VdnConfig(2, 1, 64, 23, 9, dtype="bf16", seed=83, context_tokens=300)),
+    ("T9_N4_ctx1_noanchor_d32_f32", VdnConfig(1, 1, 32, 9, 4, dtype="f32", anchor_first=False,
+                                              anchor_last=False, seed=84, context_tokens=1)),
+    ("T40_N20_ctx33_split_d128_bf16", VdnConfig(1, 1, 128, 40, 20, dtype="bf16", seed=85, context_tokens=33)),
+    ("T31_N3_ctx600_C3_W2_d64_f32", VdnConfig(1, 1, 64, 31, 3, dtype="f32", chunk_frames=3, window_chunks=2,
+                                              seed=86, context_tokens=600)),
+]
+
+
+def ctx_oracle_softmax(cfg, inp, rows=None, heads=None):
+    """Ungated softmax branch and lse of the oracle, [B, R, H*d] and [B, H, R]."""
+    B, H, d, N = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens_per_frame
+    allowed = O.allowed_frames(cfg.frames, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
+                               cfg.anchor_last)
+    R = cfg.seq_len if rows is None else len(rows)
+    heads = range(H) if heads is None else heads
+    o = np.zeros((B, R, H * d))
+    lse = np.zeros((B, H, R))
+    for b in range(B):
+        for h in heads:
+            oo, ll = O.window_attention_ctx(np32(inp["q"][b, h]), np32(inp["k"][b, h]), np32(inp["v"][b, h]),
+                                            allowed, N, 1 / np.sqrt(d), rows)
+            o[b, :, h * d:(h + 1) * d] = oo
+            lse[b, h] = ll
+    return o, lse
+
+
+@pytest.mark.parametrize("name,cfg", CTX, ids=[t[0] for t in CTX])
+def test_context_hybrid(vdn, name, cfg):
+    log(f"[ctx hybrid] {name}")
+    inp = gpu_inputs(cfg)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
+    ref = O.hybrid_layer_ctx(*(np32(inp[k]) for k in ("x", "q", "k", "v", "gamma", "beta", "w_gs",
+                                                      "w_gl", "rms_w", "w_os", "w_ol")),
+                             cfg.tokens_per_frame, **oracle_kwargs(cfg))
+    err = rel_err(np32(out), ref)
+    exc = excess_err(np32(out), ref, cfg.dtype)
+    L = cfg.video_len
+    err_ctx = excess_err(np32(out[:, L:]), ref[:, L:], cfg.dtype)
+    log(f"  rel err {err:.3e} excess {exc:.3e} context rows {err_ctx:.3e} (tol {TOL[cfg.dtype]})")
+    assert exc <= TOL[cfg.dtype] and err_ctx <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name,cfg", CTX, ids=[t[0] for t in CTX])
+def test_context_branches(vdn, name, cfg):
+    """Each branch alone with context tokens: the softmax branch with a gate
+    and lse, the linear branch (states of the video frames, zero output on
+    context rows)."""
+    log(f"[ctx branches] {name}")
+    inp = gpu_inputs(cfg)
+    shape = vdn.shape_from_config(cfg)
+    B, H, d, L, Lt = cfg.batch, cfg.heads, cfg.head_dim, cfg.video_len, cfg.seq_len
+    gen = torch.Generator().manual_seed(cfg.seed + 5)
+    gate = torch.rand(B, Lt, H * d, generator=gen).to(synth.DTYPES[cfg.dtype]).cuda()
+    out_s, lse = vdn.window_attn(shape, inp, gate_s=gate, with_lse=True)
+    out_l, states = vdn.vda_scan(shape, inp, with_states=True)
+    torch.cuda.synchronize()
+    ref_s, ref_lse = ctx_oracle_softmax(cfg, inp)
+    e_s = excess_err(np32(out_s), np32(gate).astype(np.float64) * ref_s, cfg.dtype)
+    e_lse = float(np.max(np.abs(np32(lse) - ref_lse)))
+    T, N = cfg.frames, cfg.tokens_per_frame
+    vid = {k: inp[k][:, :, :L].reshape(B, H, T, N, d) for k in ("q", "k", "v")}
+    o_l, sf, sb = O.vda_branch(*(np32(x).astype(np.float64) for x in (vid["q"], vid["k"], vid["v"],
+                                                                      inp["gamma"], inp["beta"],
+                                                                      inp["rms_w"])), cfg.rms_eps)
+    st = np32(states)
+    e_st = max(rel_err(st[0], sf), rel_err(st[1], sb))
+    e_l = excess_err(np32(out_l[:, :L]), O.merge_heads(o_l), cfg.dtype)
+    nz = torch.count_nonzero(out_l[:, L:]).item()
+    log(f"  softmax {e_s:.3e} lse abs {e_lse:.3e} states {e_st:.3e} linear {e_l:.3e} ctx nonzeros {nz}")
+    assert e_s <= TOL[cfg.dtype] and e_lse <= (1e-4 if cfg.dtype == "f32" else 1e-2)
+    assert e_st <= STATE_TOL[cfg.dtype] and e_l <= TOL[cfg.dtype]
+    assert nz == 0
+
+
 # ---------------------------------------------------------------- full size
 
 def test_window_attn_config4_sampled(vdn):
@@ -407,3 +492,24 @@ def test_length_sweep_T42_batch2_sampled(vdn):
     err_d = rel_err(np32(dense[:, rows]), ref_d)
     log(f"  dense rel err {err_d:.3e} ({time.time() - t0:.1f}s)")
     assert err_d <= TOL["bf16"]
+
+
+def test_context_config3_sampled(vdn):
+    """42-frame layer (B1 H24 d128 N4032) with 512 context tokens, checked at
+    sampled video and context rows against the oracle."""
+    cfg = synth.CONFIGS[3].replace(context_tokens=512)
+    log(f"[ctx hybrid] {cfg.name} + 512 context tokens")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    rows = synth.sample_tokens(cfg, 10)
+    host = {k: np32(v) for k, v in inp.items()}
+    ref = O.hybrid_layer_ctx(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                             host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                             cfg.tokens_per_frame, rows=np.array(rows), **oracle_kwargs(cfg))
+    err = rel_err(np32(out[:, rows]), ref)
+    log(f"  rel err {err:.3e} over {len(rows)} rows ({time.time() - t0:.1f}s)")
+    assert err <= TOL["bf16"]

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
                                                        const T* __restrict__ v,
                                                        const float* __restrict__ beta,
                                                        float* __restrict__ A,
-                                                       float* __restrict__ Bm, int N) {
+                                                       float* __restrict__ Bm, int T_, int N, int Lt) {
   using MM = Mma<T>;
   constexpr int KP = MM::kPack, KS = MM::kStep;
   constexpr int EPC = 16 / sizeof(T);
@@ -41,8 +41,9 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
   __shared__ __attribute__((aligned(16))) T Sm[2 * D * LDT];   // [K^T | V^T]
 
   const int64_t f = blockIdx.x;
-  const T* kf = k + f * N * D;
-  const T* vf = v + f * N * D;
+  const int64_t row0 = (f / T_) * Lt + (f % T_) * N;   // first token row of frame f
+  const T* kf = k + row0 * D;
+  const T* vf = v + row0 * D;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane % 16, lg = lane / 16;
 
@@ -170,16 +171,18 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
                                                                  const bf16* __restrict__ v,
                                                                  const float* __restrict__ beta,
                                                                  float* __restrict__ A,
-                                                                 float* __restrict__ Bm, int N) {
+                                                                 float* __restrict__ Bm, int T_, int N,
+                                                                 int Lt) {
   using namespace gr;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int g = lane / 16, j16 = lane % 16;
   const int64_t f = blockIdx.x;
+  const int64_t row0 = (f / T_) * Lt + (f % T_) * N;   // first token row of frame f
   const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(k + f * N * D), (short)0, N * ROWB, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + row0 * D), (short)0, N * ROWB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(v + f * N * D), (short)0, N * ROWB, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + row0 * D), (short)0, N * ROWB, 0x00020000);
 
   // DMA: lane l of block b fills physical chunk l%16 of tile row 4b + l/16
   int lane_off[4];
@@ -514,7 +517,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void vda_readout_kernel(
     const T* __restrict__ q, const float* __restrict__ states, const bf16* __restrict__ split,
     const float* __restrict__ rms_w, const T* __restrict__ gate, int64_t ldg, T* __restrict__ out,
-    int64_t ldo, int H, int T_, int N, float eps, int tiles_per_frame, int64_t bhtdd) {
+    int64_t ldo, int H, int T_, int N, int Lt, float eps, int tiles_per_frame, int64_t bhtdd) {
   using MM = Mma<T>;
   constexpr bool kSplit = sizeof(T) == 2;
   constexpr int KP = MM::kPack, KS = MM::kStep;
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int n = n0 + rt * 16 + li;
-    const T* qrow = q + (fi * N + n) * D;
+    const T* qrow = q + (bh * Lt + (int64_t)t * N + n) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
       qa[rt][ks] = (n < N) ? MM::load(qrow + ks * KS + lg * KP) : MM::zero();
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
       }
     }
   __syncthreads();
-  const int64_t NL = (int64_t)T_ * N;
+  const int64_t NL = Lt;   // output rows per batch entry
   constexpr int CPRO = D / EPC;          // 16-byte chunks per output row
   for (int c = tid; c < kReadoutBT * CPRO; c += 256) {
     const int row = c / CPRO, cc = c % CPRO;
@@ -677,7 +680,7 @@ __device__ __forceinline__ void mma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
 __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ split, const float* __restrict__ rms_w,
     const bf16* __restrict__ gate, int64_t ldg, bf16* __restrict__ out, int64_t ldo, int H, int T_, int N,
-    float eps, int64_t bhtdd) {
+    int Lt, float eps, int64_t bhtdd) {
   using namespace ro;
   __shared__ __attribute__((aligned(1024))) unsigned char Sl[4 * MATB];   // [dir][hi, lo][row][chunk]
   __shared__ float wl[D];
@@ -711,8 +714,8 @@ __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
   }
   if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
 
-  const int64_t NL = (int64_t)T_ * N;
-  const bf16* qfr = q + fi * N * D;
+  const int64_t NL = Lt;   // rows per (batch, head) of q and per batch entry of out / gate
+  const bf16* qfr = q + (bh * Lt + (int64_t)t * N) * D;
   const int nblk = (N + SUB - 1) / SUB;
   // Q^T fragments of a block: lane holds q[token 32 tt + l32][16 ks + 8 h .. +7].
   // Token indices past the frame are clamped to its last token (loads stay
@@ -833,15 +836,15 @@ __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
 // ---------------------------------------------------------------------------
 template <typename T>
 static hipError_t gram_t(int d, const void* k, const void* v, const float* beta, float* A,
-                         float* Bm, int nframes, int N, hipStream_t st) {
+                         float* Bm, int nframes, int T_, int N, int Lt, hipStream_t st) {
   if (sizeof(T) == 2 && d == 128)
-    vda_gram_bf16_d128_kernel<<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, N);
+    vda_gram_bf16_d128_kernel<<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, T_, N, Lt);
   else if (d == 32)
-    vda_gram_kernel<T, 32><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, N);
+    vda_gram_kernel<T, 32><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, T_, N, Lt);
   else if (d == 64)
-    vda_gram_kernel<T, 64><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, N);
+    vda_gram_kernel<T, 64><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, T_, N, Lt);
   else
-    vda_gram_kernel<T, 128><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, N);
+    vda_gram_kernel<T, 128><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, T_, N, Lt);
   return hipGetLastError();
 }
 
@@ -866,10 +869,10 @@ hipError_t launch_param_check(const float* gamma, const float* beta, int n, int*
 }
 
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
-                           float* A, float* Bm, int nframes, int N, hipStream_t st) {
+                           float* A, float* Bm, int nframes, int T, int N, int Lt, hipStream_t st) {
   if (nframes == 0) return hipSuccess;
-  return dtype == 1 ? gram_t<bf16>(d, k, v, beta, A, Bm, nframes, N, st)
-                    : gram_t<float>(d, k, v, beta, A, Bm, nframes, N, st);
+  return dtype == 1 ? gram_t<bf16>(d, k, v, beta, A, Bm, nframes, T, N, Lt, st)
+                    : gram_t<float>(d, k, v, beta, A, Bm, nframes, T, N, Lt, st);
 }
 
 hipError_t launch_vda_solve(int d, float* AM, int nframes, hipStream_t st) {
@@ -898,13 +901,13 @@ hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float*
 template <typename T>
 static hipError_t readout_t(int d, const void* q, const float* states, const bf16* split,
                             const float* rms_w, const void* gate, int64_t ldg, void* out, int64_t ldo,
-                            int B, int H, int T_, int N, float eps, hipStream_t st) {
+                            int B, int H, int T_, int N, int Lt, float eps, hipStream_t st) {
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
   if (sizeof(T) == 2 && d == 128 && split) {
     const int64_t nb = (int64_t)B * H * T_;
     if (nb == 0) return hipSuccess;
     vda_readout_bf16_d128_kernel<<<(unsigned)nb, 256, 0, st>>>((const bf16*)q, split, rms_w, (const bf16*)gate,
-                                                               ldg, (bf16*)out, ldo, H, T_, N, eps, bhtdd);
+                                                               ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
     return hipGetLastError();
   }
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
@@ -912,8 +915,8 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
   if (blocks == 0) return hipSuccess;
 #define VDN_READOUT(DD)                                                                         \
   vda_readout_kernel<T, DD><<<(unsigned)blocks, 256, 0, st>>>(                                  \
-      (const T*)q, states, split, rms_w, (const T*)gate, ldg, (T*)out, ldo, H, T_, N, eps, tpf, \
-      bhtdd)
+      (const T*)q, states, split, rms_w, (const T*)gate, ldg, (T*)out, ldo, H, T_, N, Lt, eps, \
+      tpf, bhtdd)
   if (d == 32) VDN_READOUT(32);
   else if (d == 64) VDN_READOUT(64);
   else VDN_READOUT(128);
@@ -923,10 +926,32 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
 
 hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
                               const bf16* split, const float* rms_w, const void* gate, int64_t ldg,
-                              void* out, int64_t ldo, int B, int H, int T, int N, float eps,
+                              void* out, int64_t ldo, int B, int H, int T, int N, int Lt, float eps,
                               hipStream_t st) {
-  return dtype == 1 ? readout_t<bf16>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st)
-                    : readout_t<float>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, eps, st);
+  return dtype == 1 ? readout_t<bf16>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, Lt, eps, st)
+                    : readout_t<float>(d, q, states, split, rms_w, gate, ldg, out, ldo, B, H, T, N, Lt, eps, st);
+}
+
+// Zero `cols` elements of rows [row0, row0 + nrows) of every batch entry of a
+// row-major [B, rows_per_batch, ld] matrix: the linear branch's output on
+// context rows.  One thread per 4-byte word.
+__global__ __launch_bounds__(256) void zero_rows_kernel(uint32_t* __restrict__ base, int64_t rows_per_batch,
+                                                        int64_t row0, int64_t nrows, int64_t ld_words,
+                                                        int64_t words, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t w = i % words, rb = i / words;
+  const int64_t r = rb % nrows, b = rb / nrows;
+  base[(b * rows_per_batch + row0 + r) * ld_words + w] = 0u;
+}
+
+hipError_t launch_zero_rows(void* base, int B, int64_t rows_per_batch, int64_t row0, int64_t nrows,
+                            int64_t ld, int64_t cols, int es, hipStream_t st) {
+  const int64_t words = cols * es / 4, total = (int64_t)B * nrows * words;
+  if (total == 0) return hipSuccess;
+  zero_rows_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>((uint32_t*)base, rows_per_batch, row0, nrows,
+                                                                    ld * es / 4, words, total);
+  return hipGetLastError();
 }
 
 }  // namespace vdn

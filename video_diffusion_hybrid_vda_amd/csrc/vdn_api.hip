@@ -41,18 +41,23 @@ int check_shape(const vdn_shape* s) {
   if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
     return fail(VDN_ERR_BAD_SHAPE, "head_dim %d not in {32, 64, 128}", s->head_dim);
   if (s->chunk_frames < 1) return fail(VDN_ERR_BAD_SHAPE, "chunk_frames must be >= 1");
+  if (s->context_tokens < 0) return fail(VDN_ERR_BAD_SHAPE, "context_tokens must be >= 0");
   if (s->window_chunks < 0) return fail(VDN_ERR_BAD_SHAPE, "window_chunks must be >= 0");
   if ((s->anchor_first != 0 && s->anchor_first != 1) || (s->anchor_last != 0 && s->anchor_last != 1))
     return fail(VDN_ERR_BAD_SHAPE, "anchor_first / anchor_last must be 0 or 1");
   if (!(s->rms_eps >= 0.f) || !isfinite(s->rms_eps))
     return fail(VDN_ERR_BAD_SHAPE, "rms_eps must be finite and >= 0");
   if (!isfinite(s->softmax_scale)) return fail(VDN_ERR_BAD_SHAPE, "softmax_scale must be finite");
-  const int64_t L = (int64_t)s->frames * s->tokens_per_frame;
-  if (L > (1LL << 30)) return fail(VDN_ERR_BAD_SHAPE, "frames * tokens_per_frame exceeds 2^30");
+  const int64_t L = (int64_t)s->frames * s->tokens_per_frame + s->context_tokens;
+  if (L > (1LL << 30))
+    return fail(VDN_ERR_BAD_SHAPE, "frames * tokens_per_frame + context_tokens exceeds 2^30");
   const int64_t D = (int64_t)s->heads * s->head_dim;
   if (D > (1 << 20)) return fail(VDN_ERR_BAD_SHAPE, "heads * head_dim exceeds 2^20");
   if ((int64_t)s->batch * L > (1LL << 31) - 1)
-    return fail(VDN_ERR_BAD_SHAPE, "batch * frames * tokens_per_frame exceeds 2^31 - 1");
+    return fail(VDN_ERR_BAD_SHAPE, "batch * (frames * tokens_per_frame + context_tokens) exceeds 2^31 - 1");
+  // the kernels address one (batch, head)'s q/k/v rows with 32-bit byte offsets
+  if (L * s->head_dim * (s->dtype == VDN_BF16 ? 2 : 4) > (1LL << 31) - 1)
+    return fail(VDN_ERR_BAD_SHAPE, "one (batch, head) of q/k/v exceeds 2 GiB");
   return VDN_OK;
 }
 
@@ -69,6 +74,9 @@ AttnParams make_attn_params(const vdn_shape* s) {
   p.H = s->heads;
   p.T = T;
   p.N = N;
+  p.L = T * N;
+  p.ctx = s->context_tokens;
+  p.Lt = p.L + p.ctx;
   p.C = C;
   p.W = W;
   p.a0 = s->anchor_first;
@@ -84,22 +92,33 @@ AttnParams make_attn_params(const vdn_shape* s) {
     p.tilesL = tiles(T - p.a1 - (p.nC - 1) * C);
     p.n_window_tiles = p.tiles0 + (p.nC - 2) * p.tilesM + p.tilesL;
   }
-  p.nA = 0;
-  if (p.a0) p.anchor_frame[p.nA++] = 0;
-  if (p.a1 && !(p.a0 && T == 1)) p.anchor_frame[p.nA++] = T - 1;
-  p.tiles_per_anchor = (N + BM - 1) / BM;
-  const int64_t L = (int64_t)T * N;
-  const int64_t key_tiles = (L + BN - 1) / BN;
-  // Split anchor rows so each piece sees about as many keys as a window tile.
+  // dense query groups, in row order: first frame, last frame, context tokens
+  p.nG = 0;
+  auto add_group = [&](int row0, int rows) {
+    p.grp_row0[p.nG] = row0;
+    p.grp_rows[p.nG] = rows;
+    p.grp_tiles[p.nG] = (rows + BM - 1) / BM;
+    p.grp_part[p.nG] = p.dense_rows;
+    p.dense_rows += rows;
+    ++p.nG;
+  };
+  if (p.a0) add_group(0, N);
+  if (p.a1 && !(p.a0 && T == 1)) add_group((T - 1) * N, N);
+  if (p.ctx > 0) add_group(p.L, p.ctx);
+  const int64_t Lt = p.Lt;
+  const int64_t key_tiles = (Lt + BN - 1) / BN;
+  // Split dense rows so each piece sees about as many keys as a window tile.
   const int64_t win_frames = (int64_t)(2 * W + 1) * C + 2;
-  const int64_t win_keys = (win_frames < T ? win_frames : T) * N;
-  int64_t ns = p.nA ? (L + win_keys - 1) / win_keys : 1;
+  const int64_t win_keys = (win_frames < T ? win_frames : T) * N + p.ctx;
+  int64_t ns = p.nG ? (Lt + win_keys - 1) / win_keys : 1;
   if (ns < 1) ns = 1;
   if (ns > key_tiles) ns = key_tiles;
   const int64_t tiles_per_split = (key_tiles + ns - 1) / ns;
   p.keys_per_split = (int)(tiles_per_split * BN);
-  p.nsplit = (int)((L + p.keys_per_split - 1) / p.keys_per_split);
-  p.tiles_per_bh = p.n_window_tiles + p.nA * p.nsplit * p.tiles_per_anchor;
+  p.nsplit = (int)((Lt + p.keys_per_split - 1) / p.keys_per_split);
+  int dense_tiles = 0;
+  for (int g = 0; g < p.nG; ++g) dense_tiles += p.grp_tiles[g];
+  p.tiles_per_bh = p.n_window_tiles + p.nsplit * dense_tiles;
   p.total = p.B * p.H * p.tiles_per_bh;
   const float scale = s->softmax_scale > 0.f ? s->softmax_scale : 1.f / sqrtf((float)s->head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
@@ -131,7 +150,7 @@ struct AttnLayout {
 AttnLayout attn_layout(const vdn_shape* s, const AttnParams& p) {
   AttnLayout l;
   size_t off = 0;
-  const size_t rows = p.nsplit > 1 ? (size_t)p.nA * p.B * p.H * p.nsplit * p.N : 0;
+  const size_t rows = p.nsplit > 1 ? (size_t)p.B * p.H * p.nsplit * p.dense_rows : 0;
   l.part_o = off; off = align_up(off + rows * s->head_dim * 4);
   l.part_ml = off; off = align_up(off + rows * 2 * 4);
   l.total = off;
@@ -144,7 +163,7 @@ struct HybridLayout {
 HybridLayout hybrid_layout(const vdn_shape* s, const AttnParams& p) {
   const size_t es = elem_size(s->dtype);
   const size_t D = (size_t)s->heads * s->head_dim;
-  const size_t rows = (size_t)s->batch * s->frames * s->tokens_per_frame;
+  const size_t rows = (size_t)s->batch * ((size_t)s->frames * s->tokens_per_frame + s->context_tokens);
   HybridLayout l;
   size_t off = 0;
   l.wg = off; off = align_up(off + 2 * D * D * es);       // [W_gs^T ; W_gl^T]   [2D, D]
@@ -173,7 +192,7 @@ DenseLayout dense_layout(const vdn_shape* s) {
   const vdn_shape ds = dense_shape(s);
   const size_t es = elem_size(s->dtype);
   const size_t D = (size_t)s->heads * s->head_dim;
-  const size_t rows = (size_t)s->batch * s->frames * s->tokens_per_frame;
+  const size_t rows = (size_t)s->batch * ((size_t)s->frames * s->tokens_per_frame + s->context_tokens);
   DenseLayout l;
   size_t off = 0;
   l.wo = off; off = align_up(off + D * D * es);          // W_o^T  [D, D]
@@ -264,9 +283,16 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   __bf16* split = s->dtype == VDN_BF16 ? (__bf16*)(ws + l.split) : nullptr;
   const int d = s->head_dim;
   const int nframes = s->batch * s->heads * s->frames;
+  const int N = s->tokens_per_frame, L = s->frames * N, Lt = L + s->context_tokens;
   hipError_t e;
+  // the linear branch covers video tokens only: its output is zero on context rows
+  if (s->context_tokens > 0) {
+    e = launch_zero_rows(out, s->batch, Lt, L, s->context_tokens, ldo, (int64_t)s->heads * d,
+                         s->dtype == VDN_BF16 ? 2 : 4, st);
+    if (e != hipSuccess) return hip_fail(e, "zero fill launch");
+  }
   int ph = phase_begin(kPhGram, st);
-  e = launch_vda_gram(s->dtype, d, k, v, beta, am, bc, nframes, s->tokens_per_frame, st);
+  e = launch_vda_gram(s->dtype, d, k, v, beta, am, bc, nframes, s->frames, N, Lt, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda gram launch");
   ph = phase_begin(kPhSolve, st);
@@ -279,7 +305,7 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   if (e != hipSuccess) return hip_fail(e, "vda scan launch");
   ph = phase_begin(kPhReadout, st);
   e = launch_vda_readout(s->dtype, d, q, st_buf, split, rms_w, gate, ldg, out, ldo, s->batch,
-                         s->heads, s->frames, s->tokens_per_frame, s->rms_eps, st);
+                         s->heads, s->frames, N, Lt, s->rms_eps, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "vda readout launch");
   return VDN_OK;
@@ -399,7 +425,7 @@ int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q, co
   if (rc != VDN_OK) return rc;
   const size_t es = elem_size(shape->dtype);
   const int D = shape->heads * shape->head_dim;
-  const int rows = shape->batch * shape->frames * shape->tokens_per_frame;
+  const int rows = shape->batch * (shape->frames * shape->tokens_per_frame + shape->context_tokens);
   char* wg = w + l.wg;
   char* wo = w + l.wo;
   char* gates = w + l.gates;
@@ -451,7 +477,7 @@ int vdn_dense_attn_fwd(const vdn_shape* shape, const void* q, const void* k, con
   hipStream_t st = (hipStream_t)stream;
   char* w = (char*)ws;
   const int D = shape->heads * shape->head_dim;
-  const int rows = shape->batch * shape->frames * shape->tokens_per_frame;
+  const int rows = shape->batch * (shape->frames * shape->tokens_per_frame + shape->context_tokens);
   int ph = phase_begin(kPhTranspose, st);
   hipError_t e = launch_transpose(shape->dtype, w_o, w + l.wo, D, D, D, st);
   phase_end(ph, st);

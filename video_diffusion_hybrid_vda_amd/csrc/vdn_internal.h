@@ -22,27 +22,35 @@ constexpr int kReadoutBT = 128;
 constexpr int kScanRows = 16;
 
 // Work decomposition of the window/anchor softmax.  Per (batch, head) the
-// work items are: the query tiles of every chunk's non-anchor frames (key set
-// = the chunk window plus anchor frames outside it), then for each anchor
-// frame its query tiles times `nsplit` key splits of the whole sequence.
+// work items are: the query tiles of every chunk's non-anchor video frames
+// (key set = the chunk window, the anchor frames outside it, and the context
+// tokens), then for each dense query group - the first and the last frame
+// (anchors) and the context tokens, whose key set is the whole sequence - its
+// query tiles times `nsplit` key splits of that sequence.  Rows per (batch,
+// head): Lt = T*N video tokens followed by ctx context tokens.
+constexpr int kMaxDenseGroups = 3;
 struct AttnParams {
   const void* q;
   const void* k;
   const void* v;
   const void* gate;   // nullable, row stride ldg
   void* out;          // row stride ldo
-  float* lse;         // nullable, [B, H, L]
-  float* part_o;      // anchor partials [nA, B, H, nsplit, N, d] (nsplit > 1)
-  float* part_ml;     // anchor partial (max, sum) [nA, B, H, nsplit, N, 2]
+  float* lse;         // nullable, [B, H, Lt]
+  float* part_o;      // dense-row partials [B, H, nsplit, dense_rows, d] (nsplit > 1)
+  float* part_ml;     // dense-row partial (max, sum) [B, H, nsplit, dense_rows, 2]
   int64_t ldg, ldo;
   int B, H, T, N;
+  int L, ctx, Lt;     // video tokens, context tokens, rows per (batch, head)
   int C, W, a0, a1;
   int nC;
   int tiles0, tilesM, tilesL;
   int n_window_tiles;
-  int nA;
-  int anchor_frame[2];
-  int tiles_per_anchor;
+  int nG;                               // dense query groups
+  int grp_row0[kMaxDenseGroups];        // first row of the group
+  int grp_rows[kMaxDenseGroups];        // rows of the group
+  int grp_tiles[kMaxDenseGroups];       // query tiles of the group
+  int grp_part[kMaxDenseGroups];        // offset of the group's rows among the dense rows
+  int dense_rows;                       // rows of all dense groups
   int nsplit;
   int keys_per_split;
   int tiles_per_bh;
@@ -60,15 +68,22 @@ hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, voi
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st);
 hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st);
 hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st);
+// Frame f = bh*T + t of q/k/v starts at row (f / T) * Lt + (f % T) * N (Lt rows per (batch, head):
+// T*N video tokens, then context tokens the linear branch does not read).
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,
-                           float* A, float* Bm, int nframes, int N, hipStream_t st);
+                           float* A, float* Bm, int nframes, int T, int N, int Lt, hipStream_t st);
 hipError_t launch_vda_solve(int d, float* AM, int nframes, hipStream_t st);   // AM: A in, M^T out
 hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float* gamma,
                            float* states, __bf16* split, int BH, int T, hipStream_t st);
+// out/gate rows: b * Lt + t * N + n; rows of context tokens are not written.
 hipError_t launch_vda_readout(int dtype, int d, const void* q, const float* states,
                               const __bf16* split, const float* rms_w, const void* gate,
                               int64_t ldg, void* out, int64_t ldo, int B, int H, int T, int N,
-                              float eps, hipStream_t st);
+                              int Lt, float eps, hipStream_t st);
+// Zero rows [row0, row0 + nrows) of `cols` elements of every batch entry of a
+// [B, rows_per_batch, ld] matrix (element size es bytes).
+hipError_t launch_zero_rows(void* base, int B, int64_t rows_per_batch, int64_t row0, int64_t nrows,
+                            int64_t ld, int64_t cols, int es, hipStream_t st);
 // flag[0] = 1 if some beta[i] < 0 or gamma[i] outside [0, 1] (i < n), else 0.
 hipError_t launch_param_check(const float* gamma, const float* beta, int n, int* flag,
                               hipStream_t st);

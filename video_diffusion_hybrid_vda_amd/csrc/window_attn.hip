@@ -2,16 +2,21 @@
 // granularity with two-way boundary anchors (10100.com article on Video
 // DeltaNet, 方法概述 part 1).  A query frame in chunk c = t / C sees the key
 // frames of chunks c-W .. c+W plus the first and last frame; the first and
-// last frame see every frame.  One softmax runs over the union of allowed
-// keys; the output is multiplied by the branch gate.
+// last frame see every frame.  Context (text / audio) tokens, when present,
+// follow the video tokens: every interaction that involves one stays on the
+// full softmax (same article, part 1, last sentence), so a video query also
+// sees every context token and a context query sees everything.  One softmax
+// runs over the union of allowed keys; the output is multiplied by the
+// branch gate.
 //
 // Flash-style forward on MFMA.  Each wave owns 32 queries and computes
 // S^T = K Q^T so that every lane holds scores of a single query: the online
 // softmax statistics are per lane, and the bf16 P^T tile feeds the P V
 // product as the MFMA B operand without any register shuffle (the key order
 // inside one 32-key step is permuted identically for P^T and V^T).
-// Anchor query frames, whose key set is the whole sequence, are split along
-// the keys; a merge kernel combines the partial (max, sum, output) triples.
+// Dense query groups (the anchor frames and the context tokens), whose key
+// set is the whole sequence, are split along the keys; a merge kernel
+// combines the partial (max, sum, output) triples.
 #include <math.h>
 
 #include "vdn_common.h"
@@ -20,11 +25,13 @@
 namespace vdn {
 
 // One softmax work item: a tile of query tokens [qbeg, qend) of one (batch,
-// head) with up to three key-token intervals [kb, ke); pidx >= 0 marks one
-// key split of an anchor frame's rows (partials go to the merge kernel).
+// head) with up to four key-token intervals [kb, ke); split != 0 marks one
+// key split of a dense group's rows: its partials go to row pbase + query of
+// the partial buffers (read by the merge kernel).
 struct WorkItem {
-  int bh, b, h, qbeg, qend, nint, pidx, afr;
-  int kb[3], ke[3];
+  int bh, b, h, qbeg, qend, nint, split;
+  int64_t pbase;   // may be negative: only pbase + query row is an index
+  int kb[4], ke[4];
 };
 
 __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
@@ -34,10 +41,9 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
   const int w = lid - wi.bh * p.tiles_per_bh;
   wi.b = wi.bh / p.H;
   wi.h = wi.bh - wi.b * p.H;
-  const int NL = p.T * p.N;
   wi.nint = 0;
-  wi.pidx = -1;
-  wi.afr = 0;
+  wi.split = 0;
+  wi.pbase = 0;
   if (w < p.n_window_tiles) {
     int c, j;
     if (p.nC == 1 || w < p.tiles0) {
@@ -59,23 +65,33 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
     const int kf1 = min(p.T, (c + p.W + 1) * p.C);
     if (p.a0 && kf0 > 0) { wi.kb[wi.nint] = 0; wi.ke[wi.nint] = p.N; ++wi.nint; }
     wi.kb[wi.nint] = kf0 * p.N; wi.ke[wi.nint] = kf1 * p.N; ++wi.nint;
-    if (p.a1 && kf1 < p.T) { wi.kb[wi.nint] = (p.T - 1) * p.N; wi.ke[wi.nint] = NL; ++wi.nint; }
+    if (p.a1 && kf1 < p.T) { wi.kb[wi.nint] = (p.T - 1) * p.N; wi.ke[wi.nint] = p.L; ++wi.nint; }
+    if (p.ctx > 0) { wi.kb[wi.nint] = p.L; wi.ke[wi.nint] = p.Lt; ++wi.nint; }
   } else {
     int u = w - p.n_window_tiles;
-    const int per_anchor = p.nsplit * p.tiles_per_anchor;
-    const int a = u / per_anchor;
-    u -= a * per_anchor;
-    const int s = u / p.tiles_per_anchor;
-    const int j = u - s * p.tiles_per_anchor;
-    wi.afr = p.anchor_frame[a];
-    wi.qbeg = wi.afr * p.N + j * BM;
-    wi.qend = min(wi.qbeg + BM, (wi.afr + 1) * p.N);
+    int g = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxDenseGroups - 1; ++i)
+      if (g == i && i < p.nG - 1 && u >= p.nsplit * p.grp_tiles[i]) {
+        u -= p.nsplit * p.grp_tiles[i];
+        g = i + 1;
+      }
+    const int tiles_g = g == 0 ? p.grp_tiles[0] : (g == 1 ? p.grp_tiles[1] : p.grp_tiles[2]);
+    const int row0 = g == 0 ? p.grp_row0[0] : (g == 1 ? p.grp_row0[1] : p.grp_row0[2]);
+    const int rows = g == 0 ? p.grp_rows[0] : (g == 1 ? p.grp_rows[1] : p.grp_rows[2]);
+    const int part = g == 0 ? p.grp_part[0] : (g == 1 ? p.grp_part[1] : p.grp_part[2]);
+    const int s = u / tiles_g;
+    const int j = u - s * tiles_g;
+    wi.qbeg = row0 + j * BM;
+    wi.qend = min(wi.qbeg + BM, row0 + rows);
     wi.kb[0] = s * p.keys_per_split;
-    wi.ke[0] = min(wi.kb[0] + p.keys_per_split, NL);
+    wi.ke[0] = min(wi.kb[0] + p.keys_per_split, p.Lt);
     wi.nint = 1;
-    if (p.nsplit > 1) wi.pidx = ((a * p.B + wi.b) * p.H + wi.h) * p.nsplit + s;
+    wi.split = p.nsplit > 1;
+    if (wi.split)
+      wi.pbase = ((int64_t)wi.bh * p.nsplit + s) * p.dense_rows + part - row0;
   }
-  for (int i = wi.nint; i < 3; ++i) { wi.kb[i] = 0; wi.ke[i] = 0; }
+  for (int i = wi.nint; i < 4; ++i) { wi.kb[i] = 0; wi.ke[i] = 0; }
   // Every field is uniform across the workgroup; the runtime integer divisions
   // above run on the vector unit, so pin the results to scalar registers.
   wi.bh = __builtin_amdgcn_readfirstlane(wi.bh);
@@ -84,10 +100,12 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
   wi.qbeg = __builtin_amdgcn_readfirstlane(wi.qbeg);
   wi.qend = __builtin_amdgcn_readfirstlane(wi.qend);
   wi.nint = __builtin_amdgcn_readfirstlane(wi.nint);
-  wi.pidx = __builtin_amdgcn_readfirstlane(wi.pidx);
-  wi.afr = __builtin_amdgcn_readfirstlane(wi.afr);
+  wi.split = __builtin_amdgcn_readfirstlane(wi.split);
+  const int plo = __builtin_amdgcn_readfirstlane((int)(wi.pbase & 0xffffffff));
+  const int phi = __builtin_amdgcn_readfirstlane((int)(wi.pbase >> 32));
+  wi.pbase = ((int64_t)phi << 32) | (uint32_t)plo;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 4; ++i) {
     wi.kb[i] = __builtin_amdgcn_readfirstlane(wi.kb[i]);
     wi.ke[i] = __builtin_amdgcn_readfirstlane(wi.ke[i]);
   }
@@ -117,11 +135,12 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
   // ---- decode the work item
   const WorkItem wi = decode_work(p, BM);
   const int bh = wi.bh, b = wi.b, h = wi.h, qbeg = wi.qbeg, qend = wi.qend, nint = wi.nint;
-  const int pidx = wi.pidx, afr = wi.afr;
-  const int NL = p.T * p.N;
-  int kb[3], ke[3];
+  const int64_t pbase = wi.pbase;
+  const int split = wi.split;
+  const int NL = p.Lt;   // rows per (batch, head)
+  int kb[4], ke[4];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) { kb[i] = wi.kb[i]; ke[i] = wi.ke[i]; }
+  for (int i = 0; i < 4; ++i) { kb[i] = wi.kb[i]; ke[i] = wi.ke[i]; }
 
   const T* Qb = (const T*)p.q + (int64_t)bh * NL * D;
   const T* Kb = (const T*)p.k + (int64_t)bh * NL * D;
@@ -262,7 +281,7 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
     l += __shfl_xor(l, 32);
     const int qrow = qbeg + wave * QW + j * 16 + li;
     if (qrow >= qend) continue;
-    if (pidx < 0) {
+    if (!split) {
       const float inv = 1.f / l;
       const int64_t orow = (int64_t)b * NL + qrow;
 #pragma unroll
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
         }
       if (p.lse && lg == 0) p.lse[(int64_t)bh * NL + qrow] = (mrun[j] + log2f(l)) * kLn2;
     } else {
-      const int64_t prow = (int64_t)pidx * p.N + (qrow - afr * p.N);
+      const int64_t prow = pbase + qrow;
 #pragma unroll
       for (int di = 0; di < DT; ++di)
 #pragma unroll
@@ -391,14 +410,14 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
 
   const WorkItem wi = decode_work(p, BM);
-  const int NL = p.T * p.N;
+  const int NL = p.Lt;   // rows per (batch, head)
   const bf16* Qb = (const bf16*)p.q + (int64_t)wi.bh * NL * D;
   const bf16* Kb = (const bf16*)p.k + (int64_t)wi.bh * NL * D;
   const bf16* Vb = (const bf16*)p.v + (int64_t)wi.bh * NL * D;
 
   int ntiles = 0;
 #pragma unroll
-  for (int iv = 0; iv < 3; ++iv)
+  for (int iv = 0; iv < 4; ++iv)
     if (iv < wi.nint) ntiles += (wi.ke[iv] - wi.kb[iv] + BN - 1) / BN;
 
   // Loader.  One buffer descriptor per tensor covering this (batch, head):
@@ -413,10 +432,10 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
     lane_off[i] = row * ROWB + swz(row, lane % 16) * 16;
   }
   // interval bounds picked without dynamic indexing, as wave-uniform scalars
-  const int kb0 = wi.kb[0], kb1 = wi.kb[1], kb2 = wi.kb[2];
-  const int ke0 = wi.ke[0], ke1 = wi.ke[1], ke2 = wi.ke[2];
-  auto kb_of = [&](int i) { return i == 0 ? kb0 : (i == 1 ? kb1 : kb2); };
-  auto ke_of = [&](int i) { return i == 0 ? ke0 : (i == 1 ? ke1 : ke2); };
+  const int kb0 = wi.kb[0], kb1 = wi.kb[1], kb2 = wi.kb[2], kb3 = wi.kb[3];
+  const int ke0 = wi.ke[0], ke1 = wi.ke[1], ke2 = wi.ke[2], ke3 = wi.ke[3];
+  auto kb_of = [&](int i) { return i == 0 ? kb0 : (i == 1 ? kb1 : (i == 2 ? kb2 : kb3)); };
+  auto ke_of = [&](int i) { return i == 0 ? ke0 : (i == 1 ? ke1 : (i == 2 ? ke2 : ke3)); };
   int liv = 0, lk0 = kb_of(0), lke = ke_of(0);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, NL * ROWB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, NL * ROWB, 0x00020000);
@@ -736,7 +755,7 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
     const float lt = lsum[qt][0];
     const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
     if (qrow >= wi.qend) continue;
-    if (wi.pidx < 0) {
+    if (!wi.split) {
       const float inv = 1.f / lt;
       const int64_t orow = (int64_t)wi.b * NL + qrow;
 #pragma unroll
@@ -756,7 +775,7 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
         }
       if (p.lse && h == 0) p.lse[(int64_t)wi.bh * NL + qrow] = (mrun[qt] + log2f(lt)) * kLn2;
     } else {
-      const int64_t prow = (int64_t)wi.pidx * p.N + (qrow - wi.afr * p.N);
+      const int64_t prow = wi.pbase + qrow;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -773,38 +792,39 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   }
 }
 
-// Combine the key splits of the anchor query rows: out = sum_s 2^(m_s - M) O_s
-// / sum_s 2^(m_s - M) l_s, then gate.  One thread per (query, quarter of d).
+// Combine the key splits of the dense query rows (anchor frames, context
+// tokens): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, then gate.
+// One thread per (dense row, quarter of d).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  const int nqb = (p.N + 63) / 64;
+  const int nqb = (p.dense_rows + 63) / 64;
   const int qb = blockIdx.x % nqb;
-  const int abh = blockIdx.x / nqb;             // (a*B + b)*H + h
-  const int h = abh % p.H;
-  const int ab = abh / p.H;
-  const int b = ab % p.B, a = ab / p.B;
-  const int n = qb * 64 + threadIdx.x / 4;
-  if (n >= p.N) return;
+  const int bh = blockIdx.x / nqb;             // b*H + h
+  const int h = bh % p.H, b = bh / p.H;
+  const int n = qb * 64 + threadIdx.x / 4;     // index among the dense rows
+  if (n >= p.dense_rows) return;
+  // the group holding dense row n (groups are stored in row order)
+  const int g = (p.nG > 2 && n >= p.grp_part[2]) ? 2 : ((p.nG > 1 && n >= p.grp_part[1]) ? 1 : 0);
+  const int qrow = (g == 0 ? p.grp_row0[0] : (g == 1 ? p.grp_row0[1] : p.grp_row0[2])) + n -
+                   (g == 0 ? p.grp_part[0] : (g == 1 ? p.grp_part[1] : p.grp_part[2]));
   const int dq = threadIdx.x % 4;
   constexpr int DQ = D / 4;
   float M = -INFINITY;
   for (int s = 0; s < p.nsplit; ++s)
-    M = fmaxf(M, p.part_ml[((int64_t)(abh * p.nsplit + s) * p.N + n) * 2]);
+    M = fmaxf(M, p.part_ml[(((int64_t)bh * p.nsplit + s) * p.dense_rows + n) * 2]);
   float L = 0.f;
   float acc[DQ];
 #pragma unroll
   for (int x = 0; x < DQ; ++x) acc[x] = 0.f;
   for (int s = 0; s < p.nsplit; ++s) {
-    const int64_t prow = (int64_t)(abh * p.nsplit + s) * p.N + n;
+    const int64_t prow = ((int64_t)bh * p.nsplit + s) * p.dense_rows + n;
     const float wgt = fast_exp2(p.part_ml[prow * 2] - M);
     L += wgt * p.part_ml[prow * 2 + 1];
 #pragma unroll
     for (int x = 0; x < DQ; ++x) acc[x] += wgt * p.part_o[prow * D + dq * DQ + x];
   }
   const float inv = 1.f / L;
-  const int NL = p.T * p.N;
-  const int qrow = p.anchor_frame[a] * p.N + n;
-  const int64_t orow = (int64_t)b * NL + qrow;
+  const int64_t orow = (int64_t)b * p.Lt + qrow;
   const T* gate = (const T*)p.gate;
   T* out = (T*)p.out;
 #pragma unroll
@@ -814,7 +834,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
     if (gate) val *= to_f32(gate[orow * p.ldg + h * D + dd]);
     out[orow * p.ldo + h * D + dd] = from_f32<T>(val);
   }
-  if (p.lse && dq == 0) p.lse[(int64_t)(b * p.H + h) * NL + qrow] = (M + log2f(L)) * kLn2;
+  if (p.lse && dq == 0) p.lse[(int64_t)bh * p.Lt + qrow] = (M + log2f(L)) * kLn2;
 }
 
 template <typename T, int D>
@@ -830,8 +850,8 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
 
 template <typename T, int D>
 static hipError_t launch_merge_t(const AttnParams& p, hipStream_t st) {
-  if (p.nsplit > 1 && p.nA > 0) {
-    const int blocks = p.nA * p.B * p.H * ((p.N + 63) / 64);
+  if (p.nsplit > 1 && p.nG > 0) {
+    const int blocks = p.B * p.H * ((p.dense_rows + 63) / 64);
     attn_merge_kernel<T, D><<<blocks, 256, 0, st>>>(p);
   }
   return hipGetLastError();

@@ -47,6 +47,7 @@ class VdnConfig:
     rms_eps: float = 1e-6
     seed: int = 0
     name: str = ""
+    context_tokens: int = 0      # text/audio tokens after the video tokens
 
     @property
     def model_dim(self) -> int:
@@ -54,6 +55,11 @@ class VdnConfig:
 
     @property
     def seq_len(self) -> int:
+        """Rows per (batch, head): video tokens, then context tokens."""
+        return self.frames * self.tokens_per_frame + self.context_tokens
+
+    @property
+    def video_len(self) -> int:
         return self.frames * self.tokens_per_frame
 
     def replace(self, **kw) -> "VdnConfig":
@@ -79,9 +85,11 @@ CONFIGS = {
 def make_inputs(cfg: VdnConfig, device="cpu", with_layer: bool = True) -> dict:
     """Draw every input of one hybrid-attention call.
 
-    Returns a dict of torch tensors on `device`: q, k, v (cfg.dtype),
-    gamma, beta (float32), and when `with_layer`: x, w_gs, w_gl, w_os, w_ol
-    (cfg.dtype) and rms_w (float32).  Random numbers are drawn in float32 from
+    Returns a dict of torch tensors on `device`: q, k, v (cfg.dtype) of shape
+    [B, H, T, N, d], or [B, H, T*N + n_ctx, d] when cfg.context_tokens > 0
+    (context rows after the video rows, drawn like them), gamma, beta
+    (float32), and when `with_layer`: x [B, T*N + n_ctx, D], w_gs, w_gl, w_os,
+    w_ol (cfg.dtype) and rms_w (float32).  Random numbers are drawn in float32 from
     a torch.Generator seeded with cfg.seed on `device`, then rounded once to
     the storage dtype (round to nearest even for bf16).
     """
@@ -101,12 +109,13 @@ def make_inputs(cfg: VdnConfig, device="cpu", with_layer: bool = True) -> dict:
         return t.mul_(hi - lo).add_(lo)
 
     out = {}
-    out["q"] = randn(B, H, T, N, d).to(dt)
-    k = randn(B, H, T, N, d)
+    qkv_shape = (B, H, T, N, d) if cfg.context_tokens == 0 else (B, H, L, d)
+    out["q"] = randn(*qkv_shape).to(dt)
+    k = randn(*qkv_shape)
     k = k / k.norm(dim=-1, keepdim=True).clamp_min(1e-12)
     out["k"] = k.to(dt)
     del k
-    out["v"] = randn(B, H, T, N, d).to(dt)
+    out["v"] = randn(*qkv_shape).to(dt)
     x = randn(B, L, D).to(dt) if with_layer else None
     out["beta"] = uniform(cfg.beta_lo, cfg.beta_hi, B, H, T).contiguous()
     out["gamma"] = uniform(cfg.gamma_lo, cfg.gamma_hi, B, H, T).contiguous()
@@ -120,7 +129,8 @@ def make_inputs(cfg: VdnConfig, device="cpu", with_layer: bool = True) -> dict:
 
 def sample_tokens(cfg: VdnConfig, count: int, seed: int = 1234) -> list:
     """Query tokens to check at full size: the first/last token of every
-    anchor frame and chunk edge, the ragged last chunk, plus random ones."""
+    anchor frame and chunk edge, the ragged last chunk, random video tokens,
+    and the first, middle and last context token if there are any."""
     T, N, C = cfg.frames, cfg.tokens_per_frame, cfg.chunk_frames
     picks = {0, N - 1, N, T * N - 1, (T - 1) * N, (T - 1) * N - 1}
     for c in range(0, T, C):
@@ -129,4 +139,7 @@ def sample_tokens(cfg: VdnConfig, count: int, seed: int = 1234) -> list:
     g = torch.Generator().manual_seed(seed)
     extra = torch.randint(0, T * N, (max(count - len(picks), 0),), generator=g).tolist()
     picks.update(extra)
-    return sorted(p for p in picks if 0 <= p < T * N)
+    if cfg.context_tokens > 0:   # first, middle and last context token
+        L = T * N
+        picks.update({L, L + cfg.context_tokens // 2, L + cfg.context_tokens - 1})
+    return sorted(p for p in picks if 0 <= p < cfg.seq_len)

@@ -37,7 +37,13 @@ class vdn_shape(ctypes.Structure):
         ("chunk_frames", ctypes.c_int32), ("window_chunks", ctypes.c_int32),
         ("anchor_first", ctypes.c_int32), ("anchor_last", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("context_tokens", ctypes.c_int32),
     ]
+
+    @property
+    def total_tokens(self) -> int:
+        """Rows per (batch, head): video tokens, then context tokens."""
+        return self.frames * self.tokens_per_frame + self.context_tokens
 
     @property
     def torch_dtype(self):
@@ -46,17 +52,17 @@ class vdn_shape(ctypes.Structure):
 
 def make_shape(batch, heads, frames, tokens_per_frame, head_dim, dtype="bf16", chunk_frames=5,
                window_chunks=1, anchor_first=True, anchor_last=True, softmax_scale=0.0,
-               rms_eps=1e-6) -> vdn_shape:
+               rms_eps=1e-6, context_tokens=0) -> vdn_shape:
     dt = {"f32": VDN_F32, "bf16": VDN_BF16, torch.float32: VDN_F32, torch.bfloat16: VDN_BF16}.get(dtype, dtype)
     return vdn_shape(batch, heads, frames, tokens_per_frame, head_dim, chunk_frames, window_chunks,
-                     int(anchor_first), int(anchor_last), softmax_scale, rms_eps, dt)
+                     int(anchor_first), int(anchor_last), softmax_scale, rms_eps, dt, context_tokens)
 
 
 def shape_from_config(cfg) -> vdn_shape:
     """vdn_shape of a synth.VdnConfig."""
     return make_shape(cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim,
                       cfg.dtype, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
-                      cfg.anchor_last, 0.0, cfg.rms_eps)
+                      cfg.anchor_last, 0.0, cfg.rms_eps, cfg.context_tokens)
 
 
 class vdn_phase_stat(ctypes.Structure):
@@ -189,7 +195,7 @@ def vdn_set_param_check(on: bool) -> bool:
 # ---- convenience wrappers: allocate outputs and workspace through torch, then call
 
 def hybrid_attn(shape, inp: dict, ws=None, stream=None) -> torch.Tensor:
-    B, L = shape.batch, shape.frames * shape.tokens_per_frame
+    B, L = shape.batch, shape.total_tokens
     D = shape.heads * shape.head_dim
     out = torch.empty(B, L, D, dtype=shape.torch_dtype, device=inp["q"].device)
     ws = workspace(shape, VDN_OP_HYBRID, inp["q"].device) if ws is None else ws
@@ -201,7 +207,7 @@ def hybrid_attn(shape, inp: dict, ws=None, stream=None) -> torch.Tensor:
 
 def vda_scan(shape, inp: dict, gate_l=None, with_states=False, ws=None, stream=None):
     B, H, T, d = shape.batch, shape.heads, shape.frames, shape.head_dim
-    L = T * shape.tokens_per_frame
+    L = shape.total_tokens
     dev = inp["q"].device
     out = torch.empty(B, L, H * d, dtype=shape.torch_dtype, device=dev)
     states = torch.empty(2, B, H, T, d, d, dtype=torch.float32, device=dev) if with_states else None
@@ -213,7 +219,7 @@ def vda_scan(shape, inp: dict, gate_l=None, with_states=False, ws=None, stream=N
 
 def window_attn(shape, inp: dict, gate_s=None, with_lse=False, ws=None, stream=None):
     B, H, d = shape.batch, shape.heads, shape.head_dim
-    L = shape.frames * shape.tokens_per_frame
+    L = shape.total_tokens
     dev = inp["q"].device
     out = torch.empty(B, L, H * d, dtype=shape.torch_dtype, device=dev)
     lse = torch.empty(B, H, L, dtype=torch.float32, device=dev) if with_lse else None
@@ -223,7 +229,7 @@ def window_attn(shape, inp: dict, gate_s=None, with_lse=False, ws=None, stream=N
 
 
 def dense_attn(shape, inp: dict, w_o, ws=None, stream=None) -> torch.Tensor:
-    B, L = shape.batch, shape.frames * shape.tokens_per_frame
+    B, L = shape.batch, shape.total_tokens
     D = shape.heads * shape.head_dim
     dev = inp["q"].device
     out = torch.empty(B, L, D, dtype=shape.torch_dtype, device=dev)
