@@ -19,6 +19,9 @@
 // combines the partial (max, sum, output) triples.
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
@@ -34,6 +37,19 @@ struct WorkItem {
   int kb[4], ke[4];
 };
 
+// append interval [b, e) to the item's list; the slot is picked by comparing
+// with constants so that the item stays in registers (a store at a runtime
+// index would put it in memory)
+__device__ __forceinline__ void push(WorkItem& wi, int b, int e) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i == wi.nint) {
+      wi.kb[i] = b;
+      wi.ke[i] = e;
+    }
+  ++wi.nint;
+}
+
 __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
   WorkItem wi;
   const int lid = xcd_remap(blockIdx.x, p.total);
@@ -42,6 +58,8 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
   wi.b = wi.bh / p.H;
   wi.h = wi.bh - wi.b * p.H;
   wi.nint = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { wi.kb[i] = 0; wi.ke[i] = 0; }
   wi.split = 0;
   wi.pbase = 0;
   if (w < p.n_window_tiles) {
@@ -63,10 +81,10 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
     wi.qend = min(wi.qbeg + BM, qf1 * p.N);
     const int kf0 = max(0, (c - p.W) * p.C);
     const int kf1 = min(p.T, (c + p.W + 1) * p.C);
-    if (p.a0 && kf0 > 0) { wi.kb[wi.nint] = 0; wi.ke[wi.nint] = p.N; ++wi.nint; }
-    wi.kb[wi.nint] = kf0 * p.N; wi.ke[wi.nint] = kf1 * p.N; ++wi.nint;
-    if (p.a1 && kf1 < p.T) { wi.kb[wi.nint] = (p.T - 1) * p.N; wi.ke[wi.nint] = p.L; ++wi.nint; }
-    if (p.ctx > 0) { wi.kb[wi.nint] = p.L; wi.ke[wi.nint] = p.Lt; ++wi.nint; }
+    if (p.a0 && kf0 > 0) push(wi, 0, p.N);
+    push(wi, kf0 * p.N, kf1 * p.N);
+    if (p.a1 && kf1 < p.T) push(wi, (p.T - 1) * p.N, p.L);
+    if (p.ctx > 0) push(wi, p.L, p.Lt);
   } else {
     int u = w - p.n_window_tiles;
     int g = 0;
@@ -91,7 +109,6 @@ __device__ __forceinline__ WorkItem decode_work(const AttnParams& p, int BM) {
     if (wi.split)
       wi.pbase = ((int64_t)wi.bh * p.nsplit + s) * p.dense_rows + part - row0;
   }
-  for (int i = wi.nint; i < 4; ++i) { wi.kb[i] = 0; wi.ke[i] = 0; }
   // Every field is uniform across the workgroup; the runtime integer divisions
   // above run on the vector unit, so pin the results to scalar registers.
   wi.bh = __builtin_amdgcn_readfirstlane(wi.bh);
@@ -311,47 +328,80 @@ __global__ __launch_bounds__(256) void window_attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 // bf16, head_dim 128: the production kernel for the workload shapes.
 //
-// 256 queries per workgroup: 4 waves x 64 queries (one wave per SIMD, the
-// default) or 8 waves x 32 queries (two per SIMD); both measure the same on
-// the workload.  64-key tiles; 32x32x16 MFMA.  K and V tiles are copied global -> LDS by the
-// direct-to-LDS DMA path (a buffer load with the lds modifier: lane l writes
-// bytes [16 l, 16 l + 16) of a 1 KB block) through a four-stage ring, so
-// tiles t+1 .. t+3 stream in while tile t is consumed; one barrier per tile.
-// Both tiles stay row-major in LDS with the 16-byte chunks of each row
-// XOR-swizzled; K fragments are plain 16-byte LDS reads, V fragments are
-// ds_read_b64_tr_b16 transpose reads.  Within a group of 16 lanes that
-// instruction hands lane i the element i%4 of the 8-byte loads of lanes i/4,
-// 4+i/4, 8+i/4, 12+i/4, so a group that loads a 4-key x 16-dim block of
-// row-major V receives, per lane, four consecutive keys of one dimension:
-// the MFMA A operand of O^T = V^T P^T.
+// 256 queries per workgroup: 4 waves x 64 queries, one wave per SIMD.  64-key
+// tiles.  K and V tiles are copied global -> LDS by the direct-to-LDS DMA path
+// (a buffer load with the lds modifier: lane l writes bytes [16 l, 16 l + 16)
+// of a 1 KB block) through a four-stage ring, so tiles t+1 .. t+3 stream in
+// while tile t is consumed; one barrier per tile.  Both tiles stay row-major
+// in LDS with the 16-byte chunks of each row XOR-swizzled; K fragments are
+// plain 16-byte LDS reads, V fragments ds_read_b64_tr_b16 transpose reads.
+// Within a group of 16 lanes that instruction hands lane i the element i%4 of
+// the 8-byte loads of lanes i/4, 4+i/4, 8+i/4, 12+i/4, so a group that loads a
+// 4-key x 16-dim block of row-major V receives, per lane, four consecutive
+// keys of one dimension: the MFMA A operand of O^T = V^T P^T.
 //
-// With one wave per SIMD the vector work of the softmax only overlaps the
-// matrix work if the wave's own instruction stream interleaves them, so the
-// loop is software-pipelined over half tiles of 32 keys: while the matrix
-// unit computes the scores of half tile j+1 and then P V of half tile j, the
-// vector unit computes the exponentials of half tile j and then the max of
-// half tile j+1.  Scores are produced in vector registers (the softmax reads
-// them there), O, Q and the row sums live in the accumulator registers; the
-// row sums are ones^T P^T on the matrix unit, because the vector unit is the
-// busier one.
+// The wave computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16, Q resident in the
+// accumulator registers), so each lane holds scores of one query: the softmax
+// statistics are per lane, and the bf16 P^T tile is already laid out as the B
+// operand of O^T = V^T P^T (the key order inside each 16-key step is permuted
+// identically for P and V).  The row sums are sel^T P^T on a 16x16x32 MFMA,
+// where sel picks, for rows 0 and 1, the lanes that hold queries 0-15 and
+// 16-31 of the 32-query tile.
+//
+// Software pipeline over half tiles of 32 keys.  One half step issues 36
+// matrix products - the 16 score products of half tile j+1, the 16 P V
+// products and 4 row-sum products of half tile j - and, beside them on the
+// vector unit, the 32 exponentials of half tile j (p = 2^(s c - m), rounded
+// to bf16 in pairs) and the max of half tile j+1's scores.  With one wave per
+// SIMD the two units only overlap if the wave's own instruction stream
+// alternates them, so the half step is a fixed list of slots, each one matrix
+// product followed by its share of vector work and LDS fragment reads, every
+// instruction an asm statement so that the compiler keeps the order.  Score
+// fragments are read 6 slots ahead and V fragments 6-9 slots ahead, each
+// product preceded by an explicit lgkmcnt wait for exactly the reads it
+// needs; the next tile's DMA loads are spread over the second half of the
+// first half step.  A probe of this instruction mix (36 products, 112 vector
+// instructions, 24 LDS reads, 8 DMA loads and a barrier per 72 products)
+// measured 1250 cycles per half step against 1156 for the products alone.
 //
 // The running max is refreshed lazily: the output accumulators are rescaled
 // only when some row max of the wave grows by more than 1 in log2 units, so
 // probabilities stay <= 2.  On the near-uniform softmax of unit-norm keys this
 // never triggers after the first tile; on peaked softmax it keeps the
 // dominant probability at (or next to) 1, as exact as a strict running max.
-namespace v2 {
+namespace v3 {
 constexpr int BM = 256, BN = 64, D = 128, STAGES = 4;
-constexpr int kAttnQT = 2;          // query tiles of 32 per wave: 8 / kAttnQT waves per workgroup
+constexpr int NW = 4, WQ = 64, QT = 2, BLK = 4;   // waves, queries per wave, 32-query tiles, DMA blocks
 constexpr int ROWB = D * 2;          // bytes per K/V row
 constexpr int TILEB = BN * ROWB;     // 16 KB
-constexpr int STAGEB = 2 * TILEB;    // K tile then V tile
+constexpr int VBASE = STAGES * TILEB;   // V tiles follow the four K tiles
 constexpr float kRescaleSlack = 1.f;
-constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt not waited for)
-constexpr int kWaitVm8 = 0x0F78;   // s_waitcnt vmcnt(8): at most the last 8 DMA loads outstanding
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<B>{}), f(IC<B + 1>{}), ..., f(IC<E - 1>{}): every index a compile-time constant
+template <int B, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<B + I>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (E > B) static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+
+// Vector work of a half step, in units: unit 3 j + k of pair j (the two
+// exponentials of p words (qt, 16-key step s4, word w), j = 8 s4 + 2 w + qt)
+// is its first value (k = 0), the conversion of pair j - 1 (k = 1) or its
+// second value (k = 2); unit 48 converts the last pair.  36 units (pairs
+// 0-11) run beside the 16 score products, the other 13 beside the first five
+// P V products.
+constexpr int units_before(int m) {
+  return m <= 16 ? (36 * m + 8) / 16 : (m <= 21 ? 36 + (13 * (m - 16) + 2) / 5 : 49);
+}
 
 // Physical 16-byte chunk of logical chunk c in row r.  For 16 consecutive
 // rows at a fixed chunk (K reads) the 16 results are distinct; for 8 aligned
@@ -359,34 +409,73 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // two passes over the 64 banks, the minimum for 512 bytes.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
-__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// LDS offset of K fragment (stage st, half kt) relative to the lane's base for
+// its score step; of V fragment (stage st, half pt, 16-key step s4) relative
+// to the lane's base for its 32-dim block
+constexpr int koffc(int st, int kt) { return st * TILEB + kt * 32 * ROWB; }
+constexpr int voffc(int st, int pt, int s4) { return st * TILEB + (2 * pt + s4) * 16 * ROWB; }
 
-// Scheduling fences.  pin(x) makes x look redefined at this point, so code
-// that produces x stays above it and code that consumes x stays below it;
-// chunk_fence() keeps memory operations on their side and ends a machine
-// scheduling region.  Both emit no instructions.
-template <typename T>
-__device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
-template <typename T>
-__device__ __forceinline__ void pin_acc(T& x) { asm volatile("" : "+a"(x)); }   // same, in the accumulator file
-__device__ __forceinline__ void chunk_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// ---- the instructions of a slot, each its own asm statement so that their
+// order is kept.  Hazards the hardware does not interlock are respected by
+// construction: a product's scores are read by the vector unit six or more
+// products later, p words are read by a product four or more slots after the
+// conversion that writes them, and a conversion never directly follows the
+// exponential it reads.
 
-// Score products written out so that their results land in vector registers
-// (where the softmax reads them) while O stays in the accumulator file.  The
-// first step of a chain starts from zero, later steps accumulate in place
-// (back-to-back accumulation into the same registers needs no wait states);
-// the vector unit reads a score buffer only eight or more MFMAs after its last
-// write.
-__device__ __forceinline__ void mma_first(f32x16& d, bf16x8 a, bf16x8 b) {
+// score product chain in vector registers; Q (b) in the accumulator file
+__device__ __forceinline__ void mma_s0(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
 }
-__device__ __forceinline__ void mma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+__device__ __forceinline__ void mma_s(f32x16& d, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// P V product into the accumulator file
+__device__ __forceinline__ void mma_o(f32x16& o, bf16x8 v, bf16x8 p) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+}
+// row sums: rows 0 and 1 of sel^T P^T
+__device__ __forceinline__ void mma_l(f32x4& l, bf16x8 sel, bf16x8 p) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(l) : "v"(sel), "v"(p));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_k(bf16x8& d, int addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr(i16x4& d, int addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// t = 2^(s c2 - m)
+__device__ __forceinline__ void fma_exp(float& t, float s, float c2, float negm) {
+  asm volatile("v_fma_f32 %0, %1, %2, %3\n\tv_exp_f32 %0, %0" : "=&v"(t) : "v"(s), "s"(c2), "v"(negm));
+}
+__device__ __forceinline__ void cvt_pk(unsigned& w, float a, float b) {
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void max3(float& m, float a, float b, float c) {
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(a), "v"(b), "v"(c));
+}
+__device__ __forceinline__ void max3_acc(float& m, float b, float c) {
+  asm volatile("v_max3_f32 %0, %0, %1, %2" : "+v"(m) : "v"(b), "v"(c));
+}
+__device__ __forceinline__ void max_acc(float& m, float b) {
+  asm volatile("v_max_f32 %0, %0, %1" : "+v"(m) : "v"(b));
+}
+// m = c2 * max(m over lanes i and i ^ 32)
+__device__ __forceinline__ void halves_max_scaled(float& m, float c2) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mul_f32 %0, %2, %0"
+      : "+v"(m), "=&v"(t)
+      : "s"(c2));
 }
 
 // max of x over lanes i and i ^ 32 (the swap exchanges the upper half of the
@@ -395,15 +484,11 @@ __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-}  // namespace v2
+}  // namespace v3
 
-template <int QT>
-__global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnParams p) {
-  using namespace v2;
-  constexpr int NW = 8 / QT;          // waves per workgroup
-  constexpr int WQ = 32 * QT;         // queries per wave
-  constexpr int BLK = 16 / NW;        // 1 KB DMA blocks per wave and operand of a tile
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
+__global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p) {
+  using namespace v3;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * 2 * TILEB];
 
   // wave index as a scalar: the DMA's LDS destination (M0) must be wave-uniform
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -439,39 +524,44 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
   int liv = 0, lk0 = kb_of(0), lke = ke_of(0);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, NL * ROWB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, NL * ROWB, 0x00020000);
-  // The DMA is written as an opaque instruction: the compiler would otherwise
-  // make every later LDS read wait for it (it cannot tell the stages apart);
-  // the loop below waits for each tile's loads explicitly (vmcnt) before the
-  // barrier that publishes the tile.
-  auto issue = [&](int st) {
-    const int base = lk0 * ROWB;
-    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
-#pragma unroll
-    for (int i = 0; i < BLK; ++i) {
-      const int blk = wave * BLK + i;
-      const int voff = base + lane_off[i];
+  const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  // Load i of a tile (i < BLK: K block i of this wave, else V block i - BLK);
+  // the last one moves the load cursor to the next tile.  The DMA is an
+  // opaque instruction: the loop waits for each tile's loads explicitly
+  // (vmcnt) before the barrier that publishes the tile.  Past the last tile
+  // the cursor keeps moving: those loads read other keys or zeros into the
+  // stage of an already consumed tile that is never read again.
+  auto issue_one = [&](int st, int i) {
+    const int b = i % BLK, blk = wave * BLK + b;
+    const int voff = lk0 * ROWB + lane_off[b];
+    if (i < BLK)
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk),
-                   "{m0}"(lds + st * TILEB + blk * 1024)
+                   "{m0}"(lds0 + st * TILEB + blk * 1024)
                    : "memory");
+    else
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv),
-                   "{m0}"(lds + (STAGES + st) * TILEB + blk * 1024)
+                   "{m0}"(lds0 + VBASE + st * TILEB + blk * 1024)
                    : "memory");
-    }
-    lk0 += BN;
-    if (lk0 >= lke) {
-      ++liv;
-      if (liv < wi.nint) {
-        lk0 = kb_of(liv);
-        lke = ke_of(liv);
+    if (i == 2 * BLK - 1) {
+      lk0 += BN;
+      if (lk0 >= lke) {
+        ++liv;
+        if (liv < wi.nint) {
+          lk0 = kb_of(liv);
+          lke = ke_of(liv);
+        }
       }
+      lk0 = __builtin_amdgcn_readfirstlane(lk0);
+      lke = __builtin_amdgcn_readfirstlane(lke);
     }
   };
 
   // ring of four 64-key stages: tiles t+1 .. t+3 resident or in flight while
   // tile t is consumed
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+#pragma unroll
+    for (int i = 0; i < 2 * BLK; ++i) issue_one(st, i);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds Q[query l32][16 ks + 8 h .. +7]
   bf16x8 qf[QT][8];
@@ -488,23 +578,33 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) pin_acc(qf[qt][ks]);
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+a"(qf[qt][ks]));
 
-  // O^T accumulators and the row sums of p: lsum[qt] = ones^T P^T on the
-  // matrix unit, so every register of a lane holds the full row sum of its
-  // query (of the bf16 p, the weights the P V product uses)
-  f32x16 o[4][QT], lsum[QT];
-  float mrun[QT];
+  // O^T accumulators (32x32 layout) and the row sums (16x16 layout: lanes 0-15
+  // hold rows 0 and 1, the sums of queries l and l + 16)
+  f32x16 o[4][QT];
+  f32x4 lsum[QT];
+  float mrun[QT], negm[QT], mtile[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     mrun[qt] = -INFINITY;
-    lsum[qt] = f32x16{};
+    negm[qt] = INFINITY;
+    lsum[qt] = f32x4{};
+    asm volatile("" : "+a"(lsum[qt]));
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt][qt] = f32x16{};
+    for (int dt = 0; dt < 4; ++dt) {
+      o[dt][qt] = f32x16{};
+      asm volatile("" : "+a"(o[dt][qt]));
+    }
   }
-  bf16x8 ones;
+  // row-sum selector: A operand of the 16x16x32 product; lane l holds row l%16,
+  // k = 8 (l/16) .. +7; row 0 takes the k groups of queries 0-15, row 1 those of 16-31
+  bf16x8 sel;
+  {
+    const bf16 one = (bf16)(((j16 == 0) && !(g & 1)) || ((j16 == 1) && (g & 1)) ? 1.f : 0.f);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.f;
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
   const float c2 = p.scale_log2;
   // compute cursor: first key and interval end of the tile whose scores are
   // the most recent ones
@@ -518,58 +618,32 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
         cke = ke_of(civ);
       }
     }
+    ck0 = __builtin_amdgcn_readfirstlane(ck0);
+    cke = __builtin_amdgcn_readfirstlane(cke);
   };
 
-  // Q and the first three tiles resident; no vector-memory load is pending
-  // anywhere in the loop except the DMA the loop itself waits for
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-
-  // The softmax runs on half tiles of 32 keys.  Scores of two half tiles are
-  // live at once: the current one (read by the softmax) and the next one
-  // (written by the matrix unit meanwhile).  sc[qt] register r holds the
-  // score of key 8(r/4) + 4h + r%4 of the half tile for query 32 qt + l32.
-  f32x16 sa[QT], sb[QT];
-  float mtile[QT];
-
-  // Fragment reads.  The ring keeps the K tiles of the four stages in its
+  // Fragment addresses.  The ring keeps the K tiles of the four stages in its
   // first 64 KB and the V tiles in the second, so every read is a per-lane
-  // base register (fixed for the kernel) plus a constant below 64 KB (stage,
-  // half tile, key step) that the LDS instruction carries in its offset field.
-  // The swizzle depends on row % 16 only, and the constants move whole
-  // 16-row groups.
+  // base register plus a constant below 64 KB (stage, half tile, key step)
+  // that the LDS instruction carries in its offset field.  The swizzle
+  // depends on row % 16 only, and the constants move whole 16-row groups.
   int koff[8], voffA[4], voffB[4];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    koff[ks] = l32 * ROWB + swz(l32, 2 * ks + h) * 16;
-    pin(koff[ks]);
-  }
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = lds0 + l32 * ROWB + swz(l32, 2 * ks + h) * 16;
   {
     const int rA = 4 * (g >> 1) + (j16 >> 2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
       const int cch = dcol >> 3, off = (dcol & 7) * 2;
-      voffA[dt] = STAGES * TILEB + rA * ROWB + swz(rA, cch) * 16 + off;
-      voffB[dt] = STAGES * TILEB + (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
-      pin(voffA[dt]);
-      pin(voffB[dt]);
+      voffA[dt] = lds0 + VBASE + rA * ROWB + swz(rA, cch) * 16 + off;
+      voffB[dt] = lds0 + VBASE + (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
     }
   }
-  // K fragment of 16-column step ks, rows 32 kt + l32 of stage st
-  auto load_k = [&](int st, int kt, int ks) {
-    return *reinterpret_cast<const bf16x8*>(ring + koff[ks] + st * TILEB + kt * 32 * ROWB);
-  };
-  // V^T fragments of 16-key step s4 of stage st for the four 32-wide column blocks
-  auto load_v = [&](bf16x8 (&vf)[4], int st, int s4) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int c = st * TILEB + s4 * 16 * ROWB;
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ring + voffA[dt] + c));
-      const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ring + voffB[dt] + c));
-      vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
+  // offset of K fragment (stage st, half kt, step ks) relative to koff[ks];
+  // of V fragment (stage st, half pt, 16-key step s4) relative to voffA/B
+
+
   // keys >= lim of a half tile get score -inf
   auto mask = [&](f32x16 (&sc)[QT], int lim) {
     const int l = lim - 4 * h;
@@ -579,31 +653,6 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
       for (int r = 0; r < 16; ++r)
         if (8 * (r / 4) + (r % 4) >= l) sc[qt][r] = -INFINITY;
   };
-  // raise the running max to the tile max if it outruns it by more than the
-  // slack, rescaling O and the row sums
-  auto refresh = [&]() {
-    bool up = false;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) up |= mtile[qt] > mrun[qt] + kRescaleSlack;
-    if (__any(up)) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float mnew = fmaxf(mrun[qt], mtile[qt]);
-        const float alpha = fast_exp2(mrun[qt] - mnew);
-        mrun[qt] = mnew;
-        pin_acc(lsum[qt]);
-        lsum[qt] *= alpha;
-        pin_acc(lsum[qt]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          pin_acc(o[dt][qt]);   // O is copied out here, not on the common path
-          o[dt][qt] *= alpha;
-          pin_acc(o[dt][qt]);
-        }
-      }
-    }
-  };
-
   // per-query max of a half tile's scores (scaled, base 2) in mtile; the two
   // half-waves hold the two key halves of each query
   auto half_max = [&](const f32x16 (&sc)[QT]) {
@@ -613,146 +662,227 @@ __global__ __launch_bounds__(512 / QT) void window_attn_bf16_d128_kernel(AttnPar
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qt][r]);
       mtile[qt] = halves_max(mx) * c2;
-      pin(mtile[qt]);
+    }
+  };
+  // raise the running max to the tile max if it outruns it by more than the
+  // slack, rescaling O and the row sums (a path the compiler schedules: it
+  // waits out the products' results first and leaves wait states after)
+  auto refresh = [&]() {
+    bool up = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) up |= mtile[qt] > mrun[qt] + kRescaleSlack;
+    if (__any(up)) {
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mnew = fmaxf(mrun[qt], mtile[qt]);
+        const float alpha = fast_exp2(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        negm[qt] = -mnew;
+        // lsum rows 0 / 1 of lane l < 16 belong to queries l / l + 16
+        const float a_hi = __shfl(alpha, (lane & 15) + 16);   // lanes 0-15: alpha of query l + 16
+        asm volatile("" : "+a"(lsum[qt]));
+        lsum[qt][0] *= alpha;
+        lsum[qt][1] *= a_hi;
+        asm volatile("" : "+a"(lsum[qt]));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          asm volatile("" : "+a"(o[dt][qt]));
+          o[dt][qt] *= alpha;
+          asm volatile("" : "+a"(o[dt][qt]));
+        }
+      }
+      asm volatile("s_nop 4" ::: "memory");
     }
   };
   // between half steps: mask a partial half tile (keys >= lim), then raise
   // the running max if needed; neither happens on most half tiles
   auto boundary = [&](f32x16 (&sc)[QT], int lim) {
     if (lim < 32) {
-      asm volatile("");   // a real branch: the masking stays off the common path
       mask(sc, lim);
       half_max(sc);
     }
     refresh();
   };
 
-  // One half step: the softmax and P V of the current half tile (scores in
-  // cur, half pkt of the tile in stage pst) run beside the scores of the next
-  // half tile (half skt of the tile in stage sst), which are then reduced to
-  // their max; the matrix unit works while the vector unit does the
-  // exponentials.  It is laid out as chunks (one 16-column step of the scores
-  // or one 16-key step of P V, each with its share of vector work and the
-  // operand reads of a later chunk) that are fenced against each other: the
-  // score chunks carry p of the first 16 keys, the first P V chunk p of the
-  // other 16, the second P V chunk the max of the next scores.  p is rounded
-  // to bf16 for the products.
-  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], int sst, int skt, int pst,
-                       int pkt) __attribute__((always_inline)) {
-    bf16x8 kf[3], vf[2][4], pk[QT][2];
-    // p of register r of query tile qt (16-key step r / 8)
-    auto soft1 = [&](int qt, int r) {
-      pk[qt][r >> 3][r & 7] = (bf16)fast_exp2(fmaf(cur[qt][r], c2, -mrun[qt]));
+  f32x16 sa[QT], sb[QT];     // scores of the current and of the next half tile
+  bf16x8 kf[4];              // K fragments of score steps ks, ks + 4 share kf[ks % 4]
+  i16x4 vfa[2][4], vfb[2][4];   // V^T fragments (two halves) of the two 16-key steps
+  unsigned pw[QT][2][4];     // p of the current half tile as bf16 pairs: [qt][16-key step][word]
+  float tt[4];               // exponentials in flight
+
+  // One half step (see above).  cur: scores of half tile j (stage PST, half
+  // PKT); nxt: scores of half tile j+1 (stage SST, half SKT), whose K
+  // fragments 0-2 were read by the previous half step; NST/NKT: the half tile
+  // after that, whose K fragments 0-2 this one reads; DST >= 0: issue the
+  // loads of a tile into that stage.
+  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], auto SST, auto SKT, auto PST, auto PKT,
+                       auto NST, auto NKT, int dst) __attribute__((always_inline)) {
+    constexpr int ks_off = koffc(decltype(SST)::value, decltype(SKT)::value);
+    constexpr int kn_off = koffc(decltype(NST)::value, decltype(NKT)::value);
+    constexpr int v0_off = voffc(decltype(PST)::value, decltype(PKT)::value, 0);
+    constexpr int v1_off = voffc(decltype(PST)::value, decltype(PKT)::value, 1);
+    auto val = [&](auto J, int e) {
+      constexpr int j = decltype(J)::value, s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
+      fma_exp(tt[(2 * j + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
     };
-    kf[0] = load_k(sst, skt, 0);
-    kf[1] = load_k(sst, skt, 1);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      chunk_fence();
-      if (ks < 6) kf[(ks + 2) % 3] = load_k(sst, skt, ks + 2);
-      if (ks == 6) load_v(vf[0], pst, 2 * pkt);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (ks == 0) mma_first(nxt[qt], kf[ks % 3], qf[qt][ks]);
-        else mma_acc(nxt[qt], kf[ks % 3], qf[qt][ks]);
+    auto cvt = [&](auto J) {
+      constexpr int j = decltype(J)::value, s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
+      cvt_pk(pw[qt][s4][w], tt[(2 * j) % 4], tt[(2 * j + 1) % 4]);
+    };
+    auto unit = [&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if constexpr (u == 48) {
+        cvt(IC<15>{});
+      } else {
+        constexpr int j = u / 3, k = u % 3;
+        if constexpr (k == 0) val(IC<j>{}, 0);
+        else if constexpr (k == 1) {
+          if constexpr (j > 0) cvt(IC<j - 1>{});
+        } else {
+          val(IC<j>{}, 1);
+        }
       }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        soft1(qt, ks);
-        pin(pk[qt][0]);
+    };
+    auto pk = [&](int qt, int s4) {
+      const u32x4 w = {pw[qt][s4][0], pw[qt][s4][1], pw[qt][s4][2], pw[qt][s4][3]};
+      return __builtin_bit_cast(bf16x8, w);
+    };
+    auto vf = [&](int s4, int dt) {
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vfa[s4][dt], vfb[s4][dt], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    float mx[QT];
+
+    auto slot = [&](auto M) {
+      constexpr int m = decltype(M)::value;
+      // ---- wait for this slot's operands, then its product
+      if constexpr (m < 16) {
+        constexpr int ks = m / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<(m <= 8 ? 2 : (m == 10 ? 3 : (m == 12 ? 4 : 5)))>();
+        if constexpr (ks == 0) mma_s0(nxt[qt], kf[ks % 4], qf[qt][ks]);
+        else mma_s(nxt[qt], kf[ks % 4], qf[qt][ks]);
+      } else if constexpr (m < 24) {
+        constexpr int dt = (m - 16) / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<5>();
+        mma_o(o[dt][qt], vf(0, dt), pk(qt, 0));
+      } else if constexpr (m < 26) {
+        mma_l(lsum[m - 24], sel, pk(m - 24, 0));
+      } else if constexpr (m < 34) {
+        constexpr int dt = (m - 26) / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<(dt == 0 ? 6 : (dt == 1 ? 4 : (dt == 2 ? 3 : 2)))>();
+        mma_o(o[dt][qt], vf(1, dt), pk(qt, 1));
+      } else {
+        mma_l(lsum[m - 34], sel, pk(m - 34, 1));
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      // ---- LDS fragment reads issued in this slot
+      if constexpr (m <= 8 && m % 2 == 0) {
+        constexpr int ks = 3 + m / 2;   // K fragments 3..7 of this half step
+        ds_k<ks_off>(kf[ks % 4], koff[ks]);
       }
-    }
-    chunk_fence();
-    load_v(vf[1], pst, 2 * pkt + 1);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[0][dt], pk[qt][0], o[dt][qt]);
-      lsum[qt] = mma(ones, pk[qt][0], lsum[qt]);
-    }
-#pragma unroll
-    for (int r = 8; r < 16; ++r)
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) soft1(qt, r);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) pin(pk[qt][1]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 5 * QT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    chunk_fence();
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][qt] = mma(vf[1][dt], pk[qt][1], o[dt][qt]);
-      lsum[qt] = mma(ones, pk[qt][1], lsum[qt]);
-    }
-    half_max(nxt);
-#pragma unroll
-    for (int i = 0; i < 5 * QT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-    chunk_fence();
+      if constexpr (m >= 9 && m <= 24) {
+        constexpr int i = m - 9, s4 = i / 8, dt = (i % 8) / 2, ab = i % 2;
+        constexpr int off = s4 == 0 ? v0_off : v1_off;
+        if constexpr (ab == 0) ds_tr<off>(vfa[s4][dt], voffA[dt]);
+        else ds_tr<off>(vfb[s4][dt], voffB[dt]);
+      }
+      if constexpr (m >= 28 && m <= 32 && m % 2 == 0) {
+        constexpr int ks = (m - 28) / 2;   // K fragments 0..2 of the next half step
+        ds_k<kn_off>(kf[ks % 4], koff[ks]);
+      }
+      // ---- DMA of a later tile
+      if constexpr (m >= 25 && m < 25 + 2 * BLK) {
+        if (dst >= 0) issue_one(dst, m - 25);
+      }
+      // ---- vector work
+      if constexpr (m <= 20) static_for<units_before(m), units_before(m + 1)>(unit);
+      // max of the next scores: the score chains end in slots 14 / 15
+      if constexpr (m == 21) {
+        max3(mx[0], nxt[0][0], nxt[0][1], nxt[0][2]);
+        max3(mx[1], nxt[1][0], nxt[1][1], nxt[1][2]);
+      }
+      if constexpr (m >= 22 && m <= 28) {
+        constexpr int r = 3 + 2 * (m - 22);   // 3, 5, .., 15
+        if constexpr (r < 15) {
+          max3_acc(mx[0], nxt[0][r], nxt[0][r + 1]);
+          max3_acc(mx[1], nxt[1][r], nxt[1][r + 1]);
+        } else {
+          max_acc(mx[0], nxt[0][15]);
+          max_acc(mx[1], nxt[1][15]);
+        }
+      }
+      if constexpr (m == 29) halves_max_scaled(mx[0], c2);
+      if constexpr (m == 30) halves_max_scaled(mx[1], c2);
+    };
+    static_for<0, 36>(slot);
+    mtile[0] = mx[0];
+    mtile[1] = mx[1];
   };
 
+  // Q and the first three tiles resident
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
   int kn = min(BN, cke - ck0);   // keys of tile t
-  if (ntiles > 0) {
+  // first half tile's scores (stage 0, half 0), then K fragments 0-2 of the
+  // first half step (stage 0, half 1)
+  asm volatile("s_nop 4" ::: "memory");   // Q was just written to the accumulator file
+  static_for<0, 8>([&](auto KS) {
+    constexpr int ks = decltype(KS)::value;
+    ds_k<koffc(0, 0)>(kf[ks % 4], koff[ks]);
+    wait_lgkm<0>();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 kf = load_k(0, 0, ks);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (ks == 0) mma_first(sa[qt], kf, qf[qt][ks]);
-        else mma_acc(sa[qt], kf, qf[qt][ks]);
-      }
+    for (int qt = 0; qt < QT; ++qt) {
+      if constexpr (ks == 0) mma_s0(sa[qt], kf[0], qf[qt][0]);
+      else mma_s(sa[qt], kf[ks % 4], qf[qt][ks]);
     }
-    // the vector unit reads the scores next: wait for the last products
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    half_max(sa);
-    boundary(sa, kn);
-  }
+  });
+  // the vector unit reads the scores next: wait for the last products
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  half_max(sa);
+  boundary(sa, kn);
+  ds_k<koffc(0, 1)>(kf[0], koff[0]);
+  ds_k<koffc(0, 1)>(kf[1], koff[1]);
+  ds_k<koffc(0, 1)>(kf[2], koff[2]);
+
   // One tile: its two halves; the second computes the scores of the first
   // half of tile t+1 (for the last tile they come from a stale stage and are
   // never used).  Tile t sits in ring stage t % 4; the loop is unrolled over
-  // the four stages so that every stage offset is a constant (it folds into
-  // the LDS instructions' offset field instead of costing an add per read).
-  auto tile = [&](int t, int s0, int s1, int s3) __attribute__((always_inline)) {
-    if (t + 3 < ntiles) issue(s3);
-    half_step(sa, sb, s0, 1, s0, 0);
+  // the four stages so that every stage offset is a constant.
+  auto tile = [&](int t, auto S0, auto S1, int s3) __attribute__((always_inline)) {
+    half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3);
     boundary(sb, kn - 32);
-    half_step(sb, sa, s1, 0, s0, 1);
+    half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1);
     advance();
     kn = min(BN, cke - ck0);
-    if (t + 3 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm8);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    // tile t+2's loads (issued one tile ago) are complete once at most the 8
+    // of tile t+3 are outstanding; the barrier publishes tile t+2 and frees
+    // the stage of tile t for the next tile's loads
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    __builtin_amdgcn_s_barrier();
     if (t + 1 < ntiles) boundary(sa, kn);
   };
   for (int t = 0; t < ntiles; t += 4) {
-    tile(t, 0, 1, 3);
+    tile(t, IC<0>{}, IC<1>{}, 3);
     if (t + 1 >= ntiles) break;
-    tile(t + 1, 1, 2, 0);
+    tile(t + 1, IC<1>{}, IC<2>{}, 0);
     if (t + 2 >= ntiles) break;
-    tile(t + 2, 2, 3, 1);
+    tile(t + 2, IC<2>{}, IC<3>{}, 1);
     if (t + 3 >= ntiles) break;
-    tile(t + 3, 3, 0, 2);
+    tile(t + 3, IC<3>{}, IC<0>{}, 2);
   }
+  // no load may still write this workgroup's LDS when it exits; the last
+  // products' results are read next
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // ---- epilogue: o[dt][qt][r] = O(query 32 qt + l32, dim 32 dt + 8(r/4) + 4h + r%4)
   const bf16* gate = (const bf16*)p.gate;
   bf16* out = (bf16*)p.out;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float lt = lsum[qt][0];
+    // row sum of query l32: row 0 of lane l32 (l32 < 16) or row 1 of lane l32 - 16
+    const float r0 = __shfl(lsum[qt][0], l32 & 15), r1 = __shfl(lsum[qt][1], l32 & 15);
+    const float lt = l32 < 16 ? r0 : r1;
     const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
     if (qrow >= wi.qend) continue;
     if (!wi.split) {
@@ -841,7 +971,7 @@ template <typename T, int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
   if (p.total > 0) {
     if (attn_uses_v2(sizeof(T) == 2 ? 1 : 0, D))
-      window_attn_bf16_d128_kernel<v2::kAttnQT><<<p.total, 512 / v2::kAttnQT, 0, st>>>(p);
+      window_attn_bf16_d128_kernel<<<p.total, 256, 0, st>>>(p);
     else
       window_attn_kernel<T, D><<<p.total, 256, 0, st>>>(p);
   }
