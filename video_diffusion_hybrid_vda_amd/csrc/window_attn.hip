@@ -403,6 +403,70 @@ constexpr int units_before(int m) {
   return m <= 16 ? (36 * m + 8) / 16 : (m <= 21 ? 36 + (13 * (m - 16) + 2) / 5 : 49);
 }
 
+// Issue slots of a half step's LDS fragment reads and of a tile's DMA loads.
+// K fragment ks of a half step is read in slot kIssueK[ks] of it or, when
+// negative, in slot 36 + kIssueK[ks] of the half step before; V half-fragment
+// i = 8 s4 + 2 dt + ab (16-key step s4, 32-dim block dt, rows 0-7 / 8-15) in
+// slot kIssueV[i]; DMA load i of the next tile in slot kIssueD[i] of the first
+// half step of a tile.  Within a slot, K reads come before V reads.
+constexpr int kIssueK[8] = {-8, -6, -4, 0, 2, 4, 6, 8};
+constexpr int kIssueV[16] = {9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24};
+constexpr int kIssueD[8] = {25, 26, 27, 28, 29, 30, 31, 32};
+// issue order keys
+constexpr int key_k(int ks) { return kIssueK[ks] * 64 + ks; }
+constexpr int key_v(int i) { return kIssueV[i] * 64 + 16 + i; }
+// LDS reads issued after the one with key a and before the wait point of
+// slot m: this half step's reads, the next half step's K reads issued in this
+// one, and the previous half step's reads shifted by one half step.  A wait
+// for at most that many outstanding reads completes the read with key a
+// (reads complete in order); counting fewer would only wait longer.
+constexpr int younger(int a, int m) {
+  int n = 0;
+  for (int sh = -1; sh <= 0; ++sh) {
+    for (int ks = 0; ks < 8; ++ks) {
+      const int k = key_k(ks) + sh * 36 * 64;
+      if (k > a && k < 64 * m) ++n;
+      if (kIssueK[ks] < 0) {   // read in the half step before its own
+        const int kn = (kIssueK[ks] + 36) * 64 + ks + sh * 36 * 64;
+        if (kn > a && kn < 64 * m && sh == 0) ++n;
+      }
+    }
+    for (int i = 0; i < 16; ++i) {
+      const int k = key_v(i) + sh * 36 * 64;
+      if (k > a && k < 64 * m) ++n;
+    }
+  }
+  return n < 15 ? n : 15;
+}
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// lgkmcnt before the first score product of step ks (slot 2 ks) and before
+// the first P V product of 16-key step s4, block dt (slot 16 + 10 s4 + 2 dt)
+constexpr int wait_s(int ks) { return younger(key_k(ks), 2 * ks); }
+constexpr int wait_p(int s4, int dt) {
+  return younger(cmax(key_v(8 * s4 + 2 * dt), key_v(8 * s4 + 2 * dt + 1)), 16 + 10 * s4 + 2 * dt);
+}
+// every read is consumed in its own half step and issued before the next
+// half step's first K read; reads that feed products are issued before them;
+// a K fragment buffer (kf[ks % 4]) is rewritten only after its last product
+constexpr bool schedule_ok() {
+  for (int ks = 0; ks < 8; ++ks) {
+    if (kIssueK[ks] >= 2 * ks) return false;
+    if (ks >= 4 && kIssueK[ks] <= 2 * (ks - 4) + 1) return false;
+    if (kIssueK[ks] >= 0 && kIssueK[ks] >= 36 + kIssueK[0]) return false;
+  }
+  for (int ks = 0; ks < 3; ++ks)
+    if (kIssueK[ks] < 0 && 36 + kIssueK[ks] <= 2 * (ks + 4) + 1) return false;
+  for (int i = 0; i < 16; ++i) {
+    const int s4 = i / 8, dt = (i % 8) / 2;
+    if (kIssueV[i] >= 16 + 10 * s4 + 2 * dt) return false;
+    if (kIssueV[i] >= 36 + kIssueK[0]) return false;
+    // the previous half step's use of the same registers is over
+    if (kIssueV[i] < 0) return false;
+  }
+  return true;
+}
+static_assert(schedule_ok(), "LDS read schedule violates its order constraints");
+
 // Physical 16-byte chunk of logical chunk c in row r.  For 16 consecutive
 // rows at a fixed chunk (K reads) the 16 results are distinct; for 8 aligned
 // rows x 4 aligned chunks (V transpose reads) each value appears twice, i.e.
@@ -464,6 +528,20 @@ __device__ __forceinline__ void max3_acc(float& m, float b, float c) {
 }
 __device__ __forceinline__ void max_acc(float& m, float b) {
   asm volatile("v_max_f32 %0, %0, %1" : "+v"(m) : "v"(b));
+}
+// lanes where max(m0 - r0, m1 - r1) > 1: a row max outran the running max
+// by more than the rescale slack (1 in log2 units)
+__device__ __forceinline__ unsigned long long grow_mask(float m0, float r0, float m1, float r1) {
+  unsigned long long mask;
+  float t0, t1;
+  asm volatile(
+      "v_sub_f32 %1, %3, %4\n\t"
+      "v_sub_f32 %2, %5, %6\n\t"
+      "v_max_f32 %1, %1, %2\n\t"
+      "v_cmp_lt_f32_e64 %0, 1.0, %1"
+      : "=s"(mask), "=&v"(t0), "=&v"(t1)
+      : "v"(m0), "v"(r0), "v"(m1), "v"(r1));
+  return mask;
 }
 // m = c2 * max(m over lanes i and i ^ 32)
 __device__ __forceinline__ void halves_max_scaled(float& m, float c2) {
@@ -664,45 +742,51 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       mtile[qt] = halves_max(mx) * c2;
     }
   };
-  // raise the running max to the tile max if it outruns it by more than the
-  // slack, rescaling O and the row sums (a path the compiler schedules: it
-  // waits out the products' results first and leaves wait states after)
-  auto refresh = [&]() {
+  // raise the running max to the tile max, rescaling O and the row sums (a
+  // path the compiler schedules: it waits out the products' results first and
+  // leaves wait states after)
+  auto rescale = [&]() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mnew = fmaxf(mrun[qt], mtile[qt]);
+      const float alpha = fast_exp2(mrun[qt] - mnew);
+      mrun[qt] = mnew;
+      negm[qt] = -mnew;
+      // lsum rows 0 / 1 of lane l < 16 belong to queries l / l + 16
+      const float a_hi = __shfl(alpha, (lane & 15) + 16);
+      asm volatile("" : "+a"(lsum[qt]));
+      lsum[qt][0] *= alpha;
+      lsum[qt][1] *= a_hi;
+      asm volatile("" : "+a"(lsum[qt]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        asm volatile("" : "+a"(o[dt][qt]));
+        o[dt][qt] *= alpha;
+        asm volatile("" : "+a"(o[dt][qt]));
+      }
+    }
+    asm volatile("s_nop 4" ::: "memory");
+  };
+  // ... if some row max outruns it by more than the slack
+  static_assert(kRescaleSlack == 1.f, "grow_mask compares against 1.0");
+  auto outran = [&]() {
     bool up = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) up |= mtile[qt] > mrun[qt] + kRescaleSlack;
-    if (__any(up)) {
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float mnew = fmaxf(mrun[qt], mtile[qt]);
-        const float alpha = fast_exp2(mrun[qt] - mnew);
-        mrun[qt] = mnew;
-        negm[qt] = -mnew;
-        // lsum rows 0 / 1 of lane l < 16 belong to queries l / l + 16
-        const float a_hi = __shfl(alpha, (lane & 15) + 16);   // lanes 0-15: alpha of query l + 16
-        asm volatile("" : "+a"(lsum[qt]));
-        lsum[qt][0] *= alpha;
-        lsum[qt][1] *= a_hi;
-        asm volatile("" : "+a"(lsum[qt]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          asm volatile("" : "+a"(o[dt][qt]));
-          o[dt][qt] *= alpha;
-          asm volatile("" : "+a"(o[dt][qt]));
-        }
-      }
-      asm volatile("s_nop 4" ::: "memory");
-    }
+    return __any(up);
   };
-  // between half steps: mask a partial half tile (keys >= lim), then raise
-  // the running max if needed; neither happens on most half tiles
-  auto boundary = [&](f32x16 (&sc)[QT], int lim) {
+  // between half steps: mask a partial half tile (keys >= lim) and recompute
+  // its max, then raise the running max if needed; grow is the half step's
+  // own verdict for a full half tile.  Neither happens on most half tiles.
+  auto boundary = [&](f32x16 (&sc)[QT], int lim, unsigned long long grow) {
+    bool up = grow != 0;
     if (lim < 32) {
       mask(sc, lim);
       half_max(sc);
+      up = outran();
     }
-    refresh();
+    if (up) rescale();
   };
 
   f32x16 sa[QT], sb[QT];     // scores of the current and of the next half tile
@@ -752,47 +836,50 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vfa[s4][dt], vfb[s4][dt], 0, 1, 2, 3, 4, 5, 6, 7));
     };
     float mx[QT];
+    unsigned long long grow = 0;
 
     auto slot = [&](auto M) {
       constexpr int m = decltype(M)::value;
       // ---- wait for this slot's operands, then its product
       if constexpr (m < 16) {
         constexpr int ks = m / 2, qt = m % 2;
-        if constexpr (qt == 0) wait_lgkm<(m <= 8 ? 2 : (m == 10 ? 3 : (m == 12 ? 4 : 5)))>();
+        if constexpr (qt == 0) wait_lgkm<wait_s(ks)>();
         if constexpr (ks == 0) mma_s0(nxt[qt], kf[ks % 4], qf[qt][ks]);
         else mma_s(nxt[qt], kf[ks % 4], qf[qt][ks]);
       } else if constexpr (m < 24) {
         constexpr int dt = (m - 16) / 2, qt = m % 2;
-        if constexpr (qt == 0) wait_lgkm<5>();
+        if constexpr (qt == 0) wait_lgkm<wait_p(0, dt)>();
         mma_o(o[dt][qt], vf(0, dt), pk(qt, 0));
       } else if constexpr (m < 26) {
         mma_l(lsum[m - 24], sel, pk(m - 24, 0));
       } else if constexpr (m < 34) {
         constexpr int dt = (m - 26) / 2, qt = m % 2;
-        if constexpr (qt == 0) wait_lgkm<(dt == 0 ? 6 : (dt == 1 ? 4 : (dt == 2 ? 3 : 2)))>();
+        if constexpr (qt == 0) wait_lgkm<wait_p(1, dt)>();
         mma_o(o[dt][qt], vf(1, dt), pk(qt, 1));
       } else {
         mma_l(lsum[m - 34], sel, pk(m - 34, 1));
       }
-      // ---- LDS fragment reads issued in this slot
-      if constexpr (m <= 8 && m % 2 == 0) {
-        constexpr int ks = 3 + m / 2;   // K fragments 3..7 of this half step
-        ds_k<ks_off>(kf[ks % 4], koff[ks]);
-      }
-      if constexpr (m >= 9 && m <= 24) {
-        constexpr int i = m - 9, s4 = i / 8, dt = (i % 8) / 2, ab = i % 2;
+      // ---- LDS fragment reads issued in this slot: K, then V
+      static_for<0, 8>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (kIssueK[ks] == m) ds_k<ks_off>(kf[ks % 4], koff[ks]);
+        if constexpr (kIssueK[ks] + 36 == m) ds_k<kn_off>(kf[ks % 4], koff[ks]);
+      });
+      static_for<0, 16>([&](auto I) {
+        constexpr int i = decltype(I)::value, s4 = i / 8, dt = (i % 8) / 2, ab = i % 2;
         constexpr int off = s4 == 0 ? v0_off : v1_off;
-        if constexpr (ab == 0) ds_tr<off>(vfa[s4][dt], voffA[dt]);
-        else ds_tr<off>(vfb[s4][dt], voffB[dt]);
-      }
-      if constexpr (m >= 28 && m <= 32 && m % 2 == 0) {
-        constexpr int ks = (m - 28) / 2;   // K fragments 0..2 of the next half step
-        ds_k<kn_off>(kf[ks % 4], koff[ks]);
-      }
+        if constexpr (kIssueV[i] == m) {
+          if constexpr (ab == 0) ds_tr<off>(vfa[s4][dt], voffA[dt]);
+          else ds_tr<off>(vfb[s4][dt], voffB[dt]);
+        }
+      });
       // ---- DMA of a later tile
-      if constexpr (m >= 25 && m < 25 + 2 * BLK) {
-        if (dst >= 0) issue_one(dst, m - 25);
-      }
+      static_for<0, 2 * BLK>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (kIssueD[i] == m) {
+          if (dst >= 0) issue_one(dst, i);
+        }
+      });
       // ---- vector work
       if constexpr (m <= 20) static_for<units_before(m), units_before(m + 1)>(unit);
       // max of the next scores: the score chains end in slots 14 / 15
@@ -812,10 +899,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       }
       if constexpr (m == 29) halves_max_scaled(mx[0], c2);
       if constexpr (m == 30) halves_max_scaled(mx[1], c2);
+      if constexpr (m == 32) grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
     };
     static_for<0, 36>(slot);
     mtile[0] = mx[0];
     mtile[1] = mx[1];
+    return grow;
   };
 
   // Q and the first three tiles resident
@@ -839,7 +928,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // the vector unit reads the scores next: wait for the last products
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   half_max(sa);
-  boundary(sa, kn);
+  boundary(sa, kn, outran() ? 1ull : 0ull);
   ds_k<koffc(0, 1)>(kf[0], koff[0]);
   ds_k<koffc(0, 1)>(kf[1], koff[1]);
   ds_k<koffc(0, 1)>(kf[2], koff[2]);
@@ -849,9 +938,9 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // never used).  Tile t sits in ring stage t % 4; the loop is unrolled over
   // the four stages so that every stage offset is a constant.
   auto tile = [&](int t, auto S0, auto S1, int s3) __attribute__((always_inline)) {
-    half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3);
-    boundary(sb, kn - 32);
-    half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1);
+    const unsigned long long g1 = half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3);
+    boundary(sb, kn - 32, g1);
+    const unsigned long long g2 = half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1);
     advance();
     kn = min(BN, cke - ck0);
     // tile t+2's loads (issued one tile ago) are complete once at most the 8
@@ -859,7 +948,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     // the stage of tile t for the next tile's loads
     __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
     __builtin_amdgcn_s_barrier();
-    if (t + 1 < ntiles) boundary(sa, kn);
+    if (t + 1 < ntiles) boundary(sa, kn, g2);
   };
   for (int t = 0; t < ntiles; t += 4) {
     tile(t, IC<0>{}, IC<1>{}, 3);
