@@ -41,9 +41,9 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy calibration
 # (profiles/window_attn_T102_hbm_counters.md).  Valid only for the kernel sources they were
 # taken on: reported as null once those sources change.
-WINDOW_TRAFFIC_BYTES = 241727528539
+WINDOW_TRAFFIC_BYTES = 263079702784
 WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
-WINDOW_TRAFFIC_SHA = "d62587074027fd51"
+WINDOW_TRAFFIC_SHA = "debdaecfe3038c24"
 
 
 def frame_key_counts(T, C, W, a0, a1):
