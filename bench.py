@@ -43,7 +43,7 @@ PEAK_HBM_GBS = 8000.0
 # taken on: reported as null once those sources change.
 WINDOW_TRAFFIC_BYTES = 263079702784
 WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
-WINDOW_TRAFFIC_SHA = "debdaecfe3038c24"
+WINDOW_TRAFFIC_SHA = "1fab0ec6af7b2293"
 
 
 def frame_key_counts(T, C, W, a0, a1):

@@ -456,6 +456,29 @@ def test_hybrid_full_sampled(vdn, cfg_id):
     assert err <= TOL["bf16"]
 
 
+def test_hybrid_ragged_projection_tiles_sampled(vdn):
+    """Nine heads of 128 (D = 1152) over 40 frames of 1000 tokens: the
+    projections' output tiles are ragged in rows (40000 = 156.25 x 256) and,
+    for the output projection, in columns (1152 = 4.5 x 256), and there are
+    several tiles per workgroup of the persistent GEMM.  Sampled tokens
+    against the oracle."""
+    cfg = VdnConfig(1, 9, 128, 40, 1000, dtype="bf16", seed=21)
+    log("[hybrid] B1 H9 d128 T40 N1000")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
+    rows = synth.sample_tokens(cfg, 24)
+    host = {k: np32(v) for k, v in inp.items()}
+    ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                              host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                              rows, **oracle_kwargs(cfg))
+    err = rel_err(np32(out[:, rows]), ref)
+    log(f"  rel err {err:.3e} ({time.time() - t0:.1f}s)")
+    assert err <= TOL["bf16"]
+
+
 def test_length_sweep_T42_batch2_sampled(vdn):
     """Batch-2 layer of the length sweep at 42 latent frames (B2 H24 d128
     N4032): the hybrid layer and the dense baseline on the same inputs, both

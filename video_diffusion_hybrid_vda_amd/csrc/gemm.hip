@@ -5,6 +5,10 @@
 // C[m][n] = epi(sum_k A[m][k] * Bt[n][k]) with both operands k-contiguous, so
 // MFMA fragments come straight from LDS rows.  Weights arrive as [D_in, D_out]
 // and are transposed once per call into the workspace (a few MB).
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
@@ -582,6 +586,282 @@ __global__ __launch_bounds__(512) void gemm_bf16_nt_k64_kernel(const bf16* __res
   }
 }
 
+// bf16, K a multiple of 128: the layer's two projections.  256x256 output
+// tile, four waves (one per SIMD) of 128x128, v_mfma_f32_32x32x16_bf16 with
+// 256 accumulator registers per wave.  K advances in 64-wide slabs through a
+// two-stage LDS ring filled by the direct-to-LDS DMA.  As in the softmax
+// kernel, a slab is a fixed list of 64 slots, one product each, every
+// instruction its own asm statement so that the order holds: the 8 fragment
+// reads of K step ks+1 go out in every other slot of step ks (each product
+// waits, with an explicit lgkmcnt, for exactly the reads it needs), and the
+// slab after next's 16 DMA loads go out one per slot of the last step.  The
+// barrier that retires a slab sits before its last step: that step's
+// fragments are already in registers, so its products run while the next
+// slab's first fragments are read and the slab after it streams into the
+// freed stage.  The kernel is persistent (one workgroup per compute unit):
+// the slab stream runs on from one output tile into the next, so a tile's
+// epilogue overlaps the next tile's first loads instead of a fresh
+// workgroup's start-up.
+namespace gemm_s {
+constexpr int BM = 256, BN = 256, BK = 64, ROWB = BK * 2;   // 128-byte slab rows
+constexpr int TILEB = BM * ROWB;                              // 32 KB per operand and stage
+constexpr int BBASE = 2 * TILEB;                              // A slabs of both stages, then Bt slabs
+constexpr int GROUP_M = 8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// chunk c of row r at c ^ ((r >> 1) & 7): the sixteen rows of a 16-lane
+// fragment read cover all 64 banks
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+template <int V>
+using IC = std::integral_constant<int, V>;
+template <int B, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<B + I>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (E > B) static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+// Fragment reads of a step, in issue order: Bt tile 0, A tiles 0-3, Bt tiles
+// 1-3; read r goes out in slot 2 r of the step before, or in slot r when
+// that step is the one before a barrier (early), so that its reads are in
+// when the barrier's lgkmcnt(0) comes.  Product (jn, im) is slot 4 jn + im.
+// The first product that uses read r waits until at most (7 - r) reads of
+// its own step plus the next step's reads issued before slot s are
+// outstanding.
+constexpr bool first_use(int s) { return s <= 4 || s == 8 || s == 12; }
+constexpr int first_use_read(int s) { return s == 0 ? 1 : s <= 4 ? s + 1 : s == 8 ? 6 : 7; }
+constexpr int reads_before(int s, bool early) { return early ? (s < 8 ? s : 8) : (s + 1) / 2; }
+constexpr int first_use_wait(int s, bool early) { return 7 - first_use_read(s) + reads_before(s, early); }
+static_assert(first_use_wait(0, false) == 6 && first_use_wait(2, false) == 5 && first_use_wait(12, false) == 6 &&
+              first_use_wait(8, true) == 9 && first_use_wait(12, true) == 8, "lgkmcnt table");
+__device__ __forceinline__ void mma(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_frag(bf16x8& d, int addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+// the first product of a tile: C operand zero, so no accumulator is cleared
+__device__ __forceinline__ void mma_zero(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(bf16)lo, (bf16)hi};
+  return __builtin_bit_cast(unsigned, v);
+}
+}  // namespace gemm_s
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __restrict__ A,
+                                                                const bf16* __restrict__ Bt,
+                                                                bf16* __restrict__ C, int M, int N, int K,
+                                                                int64_t lda, int64_t ldb, int64_t ldc,
+                                                                int tiles_m, int tiles_n) {
+  using namespace gemm_s;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[4 * TILEB];
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l32 = lane % 32, h = lane / 32;
+  const int wm = wave >> 1, wn = wave & 1;   // 128-row block of A, 128-row block of Bt
+
+  // Persistent: workgroup b takes logical tiles r G + xcd_remap(b, G), r = 0, 1, ...,
+  // so that in every round the workgroups of one XCD hold consecutive tiles
+  // of the grouped order below and share their A and Bt slabs in that L2.
+  const int total = tiles_m * tiles_n, G = gridDim.x;
+  auto coords = [&](int l, int& tm, int& tn) {
+    const int group = l / (GROUP_M * tiles_n);
+    const int first_m = group * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int in_group = l - group * GROUP_M * tiles_n;
+    tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsize);
+    tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+  };
+  // Rows past M (N) read as zero through the descriptors' ranges.
+  auto rsrc_a = [&](int tm) {
+    const int64_t m0 = (int64_t)tm * BM;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * lda), (short)0,
+                                             (int)(min((int64_t)BM, M - m0) * lda * 2), 0x00020000);
+  };
+  auto rsrc_b = [&](int tn) {
+    const int64_t n0 = (int64_t)tn * BN;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(Bt + n0 * ldb), (short)0,
+                                             (int)(min((int64_t)BN, N - n0) * ldb * 2), 0x00020000);
+  };
+
+  // DMA: wave w fills rows 64 w .. 64 w + 63 of each operand's slab, eight
+  // 8-row blocks; lane l of block i loads row 64 w + 8 i + l/8, the global
+  // chunk that lands at physical chunk l % 8.
+  const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  int offa[8], offb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + lane / 8;
+    const int c = swz(row, lane % 8);
+    offa[i] = (int)(row * lda * 2) + 16 * c;
+    offb[i] = (int)(row * ldb * 2) + 16 * c;
+  }
+  // load i (0..15) of the slab at byte column kb into stage st: i < 8 A
+  // block i, else Bt block i - 8
+  auto issue_one = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kb, int st, int i) {
+    if (i < 8)
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offa[i]), "s"(ra), "s"(kb),
+                   "{m0}"(lds0 + st * TILEB + (8 * wave + i) * 1024)
+                   : "memory");
+    else
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offb[i - 8]), "s"(rb), "s"(kb),
+                   "{m0}"(lds0 + BBASE + st * TILEB + (8 * wave + i - 8) * 1024)
+                   : "memory");
+  };
+  // fragment addresses (stage 0) of A tile im and Bt tile jn at step ks
+  int adA[4][4], adB[4][4];
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int rA = 128 * wm + 32 * t4 + l32, rB = 128 * wn + 32 * t4 + l32;
+      adA[t4][ks] = lds0 + rA * ROWB + 16 * swz(rA, 2 * ks + h);
+      adB[t4][ks] = lds0 + BBASE + rB * ROWB + 16 * swz(rB, 2 * ks + h);
+    }
+
+  int li = xcd_remap(blockIdx.x, G);
+  int tm, tn;
+  coords(li, tm, tn);
+  __amdgpu_buffer_rsrc_t ra = rsrc_a(tm), rb = rsrc_b(tn);
+  const int nk = K / BK;   // even
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_one(ra, rb, 0, 0, i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_one(ra, rb, ROWB, 1, i);
+  __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): slab 0 landed
+  asm volatile("s_barrier" ::: "memory");
+
+  f32x16 acc[4][4];            // [Bt tile jn][A tile im]: C^T tile
+  bf16x8 fa[2][4], fb[2][4];   // fragments of two steps: [step parity][tile]
+  // read r of step (stage ST, ks KS) into fragment set P
+  auto read = [&](auto ST, auto KS, auto P, auto R) {
+    constexpr int st = decltype(ST)::value, ks = decltype(KS)::value, p = decltype(P)::value;
+    constexpr int r = decltype(R)::value;
+    if constexpr (r == 0) ds_frag<st * TILEB>(fb[p][0], adB[0][ks]);
+    else if constexpr (r <= 4) ds_frag<st * TILEB>(fa[p][r - 1], adA[r - 1][ks]);
+    else ds_frag<st * TILEB>(fb[p][r - 4], adB[r - 4][ks]);
+  };
+  static_for<0, 8>([&](auto R) { read(IC<0>{}, IC<0>{}, IC<0>{}, R); });
+
+  // The slab stream runs on across tiles: the last two slabs of a tile load
+  // the next tile's first two, and the last step of a tile reads the next
+  // tile's first fragments, so only the epilogue separates two tiles.
+  for (;;) {
+    const int lnext = li + G;
+    const bool has_next = lnext < total;
+    int ntm = tm, ntn = tn;   // past the last tile: reload this tile's first slabs (never read)
+    if (has_next) coords(lnext, ntm, ntn);
+    const __amdgpu_buffer_rsrc_t nra = rsrc_a(ntm), nrb = rsrc_b(ntn);
+
+    // One step: 16 products on fragment set P (the first step of a tile
+    // starts them from zero), the next step's reads (stage NST, step NKS)
+    // into set P ^ 1, and on the last step of a slab the DMA of the slab two
+    // ahead into stage DST.
+    auto step = [&](auto P, auto NST, auto NKS, auto ZERO, auto DMA, auto EARLY, __amdgpu_buffer_rsrc_t da,
+                    __amdgpu_buffer_rsrc_t db, int dkb, int dst) __attribute__((always_inline)) {
+      constexpr int p = decltype(P)::value;
+      static_for<0, 16>([&](auto S) {
+        constexpr int sl = decltype(S)::value, jn = sl / 4, im = sl % 4;
+        if constexpr (first_use(sl)) wait_lgkm<first_use_wait(sl, decltype(EARLY)::value)>();
+        if constexpr (decltype(ZERO)::value) mma_zero(acc[jn][im], fb[p][jn], fa[p][im]);
+        else mma(acc[jn][im], fb[p][jn], fa[p][im]);
+        if constexpr (decltype(EARLY)::value) {
+          if constexpr (sl < 8) read(NST, NKS, IC<1 - p>{}, IC<sl>{});
+        } else if constexpr (sl % 2 == 0) {
+          read(NST, NKS, IC<1 - p>{}, IC<sl / 2>{});
+        }
+        if constexpr (decltype(DMA)::value) issue_one(da, db, dkb, dst, sl);
+      });
+    };
+    // Slab kt in stage ST: steps 0-2, then the barrier that publishes the
+    // next slab and frees stage ST, then step 3 (its fragments are in
+    // registers) with the DMA of the slab two ahead into stage ST.
+    auto slab = [&](int kt, auto ST, auto FIRST) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      step(IC<0>{}, ST, IC<1>{}, FIRST, IC<0>{}, IC<0>{}, ra, rb, 0, 0);
+      step(IC<1>{}, ST, IC<2>{}, IC<0>{}, IC<0>{}, IC<0>{}, ra, rb, 0, 0);
+      step(IC<0>{}, ST, IC<3>{}, IC<0>{}, IC<0>{}, IC<1>{}, ra, rb, 0, 0);
+      const bool wrap = kt + 2 >= nk;
+      const int dkb = (wrap ? kt + 2 - nk : kt + 2) * ROWB;
+      wait_lgkm<0>();
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next slab landed
+      asm volatile("s_barrier" ::: "memory");
+      step(IC<1>{}, IC<1 - st>{}, IC<0>{}, IC<0>{}, IC<1>{}, IC<0>{}, wrap ? nra : ra, wrap ? nrb : rb, dkb, st);
+    };
+    slab(0, IC<0>{}, IC<1>{});
+    slab(1, IC<1>{}, IC<0>{});
+    for (int kt = 2; kt < nk; kt += 2) {
+      slab(kt, IC<0>{}, IC<0>{});
+      slab(kt + 1, IC<1>{}, IC<0>{});
+    }
+    // the last products' results are read by vector instructions below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // Epilogue: acc[jn][im][4 r4 + e] = C[m0 + 128 wm + 32 im + l32][n0 + 128 wn + 32 jn + 8 r4 + 4 h + e].
+    // Swapping the upper half-wave of the r4 = 2 q pair with the lower half
+    // of r4 = 2 q + 1 gives every lane eight consecutive columns,
+    // 32 jn + 16 q + 8 h + (0..7): one 16-byte store.  Rows past M fall
+    // outside the descriptor's range and columns past N get an offset past
+    // it, so the hardware drops both.
+    {
+      const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(C + m0 * ldc), (short)0, (int)(min((int64_t)BM, M - m0) * ldc * 2), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * wm + 32 * i + l32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // one accumulator block at a time: reading them all first would
+          // push the loop's address registers to scratch
+          asm volatile("" : "+a"(acc[j][i]));
+          unsigned pk[4][2];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              float x0 = acc[j][i][4 * r4 + 2 * e2], x1 = acc[j][i][4 * r4 + 2 * e2 + 1];
+              if (EPI == kEpiSigmoid) { x0 = sigmoidf(x0); x1 = sigmoidf(x1); }
+              pk[r4][e2] = pack_bf16x2(x0, x1);
+            }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * q][e2], pk[2 * q + 1][e2], false, false);
+              pk[2 * q][e2] = sw[0];
+              pk[2 * q + 1][e2] = sw[1];
+            }
+            const int64_t col = n0 + 128 * wn + 32 * j + 16 * q + 8 * h;
+            const int off = col < N ? (int)((row * ldc + col) * 2) : int(0x80000000u);
+            const u32x4 v = {pk[2 * q][0], pk[2 * q][1], pk[2 * q + 1][0], pk[2 * q + 1][1]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+          }
+        }
+      }
+    }
+    if (!has_next) break;
+    li = lnext;
+    tm = ntm;
+    tn = ntn;
+    ra = nra;
+    rb = nrb;
+  }
+  // no load may still write this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+}
+
+constexpr bool kGemmSlot = true;
 constexpr bool kGemmK64 = true;
 constexpr bool kGemmFourWaves = false;   // the eight-wave kernel measures faster on the layer shapes
 
@@ -594,6 +874,19 @@ static bool gemm_big_ok(int dtype, int M, int N, int K, int64_t lda, int64_t ldb
   if (((uintptr_t)A | (uintptr_t)Bt | (uintptr_t)C) & 15) return false;
   if (256 * lda * 2 >= (int64_t(1) << 31) || 256 * ldb * 2 >= (int64_t(1) << 31)) return false;
   return true;
+}
+
+// compute units of the current device, looked up once per device
+static int compute_units() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
@@ -610,7 +903,16 @@ hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, voi
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st) {
   if (gemm_big_ok(dtype, M, N, K, lda, ldb, ldc, A, Bt, C)) {
     const int tm = (M + 255) / 256, tn = (N + 255) / 256;
-    if (kGemmK64 && K % 64 == 0) {
+    if (kGemmSlot && K % 128 == 0 && 256 * ldc * 2 < (int64_t(1) << 31)) {
+      // persistent: one workgroup per compute unit (its 128 KB of LDS allows no second)
+      const int grid = std::min(tm * tn, compute_units());
+      if (epi == kEpiSigmoid)
+        gemm_bf16_nt_slot_kernel<kEpiSigmoid><<<grid, 256, 0, st>>>(
+            (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
+      else
+        gemm_bf16_nt_slot_kernel<kEpiStore><<<grid, 256, 0, st>>>(
+            (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
+    } else if (kGemmK64 && K % 64 == 0) {
       if (epi == kEpiSigmoid)
         gemm_bf16_nt_k64_kernel<kEpiSigmoid><<<tm * tn, 512, 0, st>>>(
             (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
