@@ -117,6 +117,8 @@ typedef struct vdn_shape {
   float rms_eps;            /* RMSNorm epsilon (1e-6) */
   int32_t dtype;            /* enum vdn_dtype: storage of q,k,v,x,W,gates,out */
   int32_t context_tokens;   /* Nc >= 0 text/audio tokens after the video tokens (0) */
+  int32_t softmax_mxfp8;    /* 1: softmax-branch scores from MXFP8 q and k (below);
+                               needs dtype VDN_BF16 and head_dim 128 (0) */
 } vdn_shape;
 
 /* Bytes of device workspace `op` needs for `shape` (0 on an invalid shape,
@@ -153,6 +155,44 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
                            const void* k, const void* v, const void* gate_s,
                            void* out, float* lse, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* MXFP8 mode of the softmax branch.  The 10100.com article (实验结果, the
+ * paragraph on scaling with sequence length) runs the denoiser in MXFP8
+ * without saying which operations; here q and k of the softmax branch are
+ * MXFP8 and the scores q . k come from them, while the softmax, P V, v, the
+ * gates, the linear branch and the projections stay as in the bf16 path.
+ * Format: OCP Microscaling (MX) v1.0 MXFP8, i.e. blocks of 32 consecutive
+ * elements (along head_dim) in OCP FP8 E4M3 (bias 7, largest finite 448)
+ * sharing one E8M0 scale 2^(code - 127).  With shape->softmax_mxfp8 = 1,
+ * vdn_hybrid_attn_fwd, window_anchor_attn_fwd and vdn_dense_attn_fwd quantise
+ * their bf16 q and k into the workspace (vdn_workspace_bytes grows by
+ * 2 * B*H*Lt*(d + d/32) bytes) and use these scores. */
+
+/* MXFP8 quantisation of n_elems bf16 values x (n_elems a non-negative
+ * multiple of 32), block i = x[32 i .. 32 i + 31]: scales[i] = clamp(
+ * floor(log2 max|x|) - 8, -127, 127) + 127 (0 for an all-zero block) and
+ * codes[32 i + j] = x / 2^(scales[i] - 127) rounded to the nearest E4M3
+ * value, ties to the even code, magnitudes >= 448 saturating to 448, sign
+ * bit = sign of x.  For a [rows, d] tensor (d a multiple of 32) this gives
+ * codes [rows, d] and scales [rows, d / 32].  x and codes 16-byte aligned,
+ * scales any alignment; all device pointers, caller-owned.  Non-finite
+ * inputs give unspecified codes.  Errors: VDN_ERR_INVALID_ARG (NULL or
+ * misaligned pointer), VDN_ERR_BAD_SHAPE (n_elems). */
+int vdn_mxfp8_quantize(const void* x, int64_t n_elems, void* codes,
+                       void* scales, void* stream);
+
+/* Softmax branch (10100.com article, 方法概述 part 1) with scores from
+ * MXFP8 q and k given as codes [B, H, Lt, 128] (uint8 E4M3) and scales
+ * [B, H, Lt, 4] (uint8 E8M0), as vdn_mxfp8_quantize writes them; v, gate_s,
+ * out and lse as window_anchor_attn_fwd.  shape->dtype must be VDN_BF16 and
+ * head_dim 128 (VDN_ERR_DTYPE / VDN_ERR_BAD_SHAPE otherwise); the
+ * softmax_mxfp8 field is ignored.  Workspace: vdn_workspace_bytes(shape,
+ * VDN_OP_WINDOW_ATTN) of the shape with softmax_mxfp8 = 0 suffices. */
+int window_anchor_attn_mxfp8_fwd(const vdn_shape* shape, const void* q_codes,
+                                 const void* q_scales, const void* k_codes,
+                                 const void* k_scales, const void* v,
+                                 const void* gate_s, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Dense full-softmax baseline layer, the cost reference of the length sweep
  * (10100.com article, 实验结果 / 效率阶梯: softmax density and backbone

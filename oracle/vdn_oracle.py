@@ -74,6 +74,12 @@ __all__ = [
 # Linear branch: Video Delta Attention  [P3 方法概述 part 2]
 # --------------------------------------------------------------------------
 
+
+def mxfp8_values(x):
+    """Values of the MXFP8 encoding of x along its last axis (oracle.mxfp8)."""
+    from oracle import mxfp8
+    return mxfp8.dequantize(*mxfp8.quantize(x))
+
 def frame_stats(k_t: np.ndarray, v_t: np.ndarray, beta_t: float):
     """Frame statistics of one frame and head.
 
@@ -299,13 +305,17 @@ def hybrid_layer(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
 
 def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
                       rows, chunk_frames=5, window_chunks=1, anchor_first=True,
-                      anchor_last=True, scale=None, eps=1e-6, states=None):
+                      anchor_last=True, scale=None, eps=1e-6, states=None,
+                      softmax_mxfp8=False):
     """hybrid_layer restricted to the output tokens `rows` (flat t*N + n) of
     every batch entry, for workloads too large to evaluate whole.
 
     The linear branch still needs every frame's state (full scans); the
     softmax branch, gates and projections are evaluated only at `rows`.
     `states` may carry precomputed (s_fwd, s_bwd) of shape [B, H, T, d, d].
+    softmax_mxfp8: the softmax branch scores the MXFP8 values of q and k
+    (oracle.mxfp8: OCP MXFP8 along head_dim; [P3] 实验结果 runs the denoiser
+    in MXFP8), the linear branch keeps q and k as given.
     Returns out [B, len(rows), D].
     """
     # q, k, v are converted to float64 one (batch, head) slice at a time so that
@@ -324,7 +334,10 @@ def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
     for b in range(B):
         for h in range(H):
             qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
-            o, _ = window_attention(qh, kh, vh, allowed, scale, rows)
+            if softmax_mxfp8:
+                o, _ = window_attention(mxfp8_values(qh), mxfp8_values(kh), vh, allowed, scale, rows)
+            else:
+                o, _ = window_attention(qh, kh, vh, allowed, scale, rows)
             y_s[b, :, h * d:(h + 1) * d] = o
             if states is None:
                 sf, sb = vda_states(kh, vh, gamma[b, h], beta[b, h])

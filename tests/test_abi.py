@@ -58,9 +58,10 @@ def test_version_and_clean_error_state(vdn):
 
 
 def test_shape_struct_layout(vdn):
-    """13 four-byte fields in the order of include/vdn.h; context_tokens last."""
-    assert ctypes.sizeof(vdn.vdn_shape) == 13 * 4
+    """14 four-byte fields in the order of include/vdn.h; softmax_mxfp8 last."""
+    assert ctypes.sizeof(vdn.vdn_shape) == 14 * 4
     assert vdn.vdn_shape.context_tokens.offset == 12 * 4
+    assert vdn.vdn_shape.softmax_mxfp8.offset == 13 * 4
     assert vdn.vdn_shape.dtype.offset == 11 * 4
 
 
@@ -76,6 +77,7 @@ def _shape(vdn, **kw):
     (dict(chunk_frames=0), -2), (dict(window_chunks=-1), -2), (dict(dtype=7), -3),
     (dict(rms_eps=-1.0), -2), (dict(anchor_first=2), -2), (dict(context_tokens=-1), -2),
     (dict(frames=2 ** 16, tokens_per_frame=2 ** 14, context_tokens=1), -2),
+    (dict(softmax_mxfp8=True), -2), (dict(head_dim=128, dtype="f32", softmax_mxfp8=True), -3),
 ])
 def test_bad_shapes_rejected_before_launch(vdn, kw, status):
     s = _shape(vdn, **kw)
@@ -206,3 +208,45 @@ def test_context_tokens_grow_the_workspace(vdn):
     assert grow >= 2 * 100 * 2 * D * 2      # gates and branch outputs, [rows, 2D] bf16 each
     # the linear branch reads video rows only: its workspace does not change
     assert vdn.vdn_workspace_bytes(b, vdn.VDN_OP_VDA_SCAN) == vdn.vdn_workspace_bytes(a, vdn.VDN_OP_VDA_SCAN)
+
+
+def test_mxfp8_quantize_rejects_bad_arguments(vdn):
+    fake = 1 << 20
+    assert vdn._lib.vdn_mxfp8_quantize(None, 32, fake, fake, None) == -1
+    assert vdn._lib.vdn_mxfp8_quantize(fake, 32, None, fake, None) == -1
+    assert vdn._lib.vdn_mxfp8_quantize(fake + 4, 32, fake, fake, None) == -1
+    assert "aligned" in vdn.vdn_last_error()
+    assert vdn._lib.vdn_mxfp8_quantize(fake, 33, fake, fake, None) == -2
+    assert vdn._lib.vdn_mxfp8_quantize(fake, -32, fake, fake, None) == -2
+
+
+def test_mxfp8_window_entry_rejects_bad_arguments(vdn):
+    fake = 1 << 20
+    ok = _shape(vdn, head_dim=128)
+    call = lambda s, *a: vdn._lib.window_anchor_attn_mxfp8_fwd(ctypes.byref(s), *a)
+    args = [fake] * 8 + [fake, 1 << 40, None]
+    assert call(_shape(vdn, head_dim=64), *args) == -2           # head_dim 128 only
+    assert call(_shape(vdn, head_dim=128, dtype="f32"), *args) == -3
+    for i in (0, 1, 2, 3, 4, 6):                                  # codes, scales, v, out
+        a = list(args)
+        a[i] = None
+        assert call(ok, *a) == -1
+    a = list(args)
+    a[1] = fake + 8                                               # misaligned scales
+    assert call(ok, *a) == -1
+    a = list(args)
+    a[8] = None   # no workspace: the anchor rows of 102 frames are split over keys, their partials need one
+    assert call(vdn.make_shape(1, 2, 102, 4032, 128, "bf16"), *a) == -4
+
+
+def test_mxfp8_mode_grows_the_workspace(vdn):
+    """With softmax_mxfp8 the softmax-branch workspace also holds the codes and
+    scales of q and k: 2 * B*H*Lt*(d + d/32) bytes (plus alignment)."""
+    B, H, T, N, d = 1, 24, 102, 4032, 128
+    plain = vdn.make_shape(B, H, T, N, d, "bf16")
+    mx = vdn.make_shape(B, H, T, N, d, "bf16", softmax_mxfp8=True)
+    extra = 2 * B * H * T * N * (d + d // 32)
+    for op in (0, 2, 3):
+        grow = vdn.vdn_workspace_bytes(mx, op) - vdn.vdn_workspace_bytes(plain, op)
+        assert extra <= grow <= extra + 4 * 256, (op, grow)
+    assert vdn.vdn_workspace_bytes(mx, 1) == vdn.vdn_workspace_bytes(plain, 1)

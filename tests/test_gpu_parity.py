@@ -536,3 +536,160 @@ def test_context_config3_sampled(vdn):
     err = rel_err(np32(out[:, rows]), ref)
     log(f"  rel err {err:.3e} over {len(rows)} rows ({time.time() - t0:.1f}s)")
     assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- MXFP8 mode
+# The softmax branch's scores from MXFP8 q and k (OCP MXFP8 along head_dim;
+# the 10100.com article's 实验结果 runs the denoiser in MXFP8).  The oracle
+# quantises q and k itself (oracle/mxfp8.py, pinned against the OCP formats)
+# and runs the fp64 softmax on the decoded values, so the bar is the bf16
+# one; the codes and scales themselves must match bit for bit.
+
+from oracle import mxfp8 as MX
+
+
+def mx_values(a):
+    return O.mxfp8_values(np.asarray(a, dtype=np.float64))
+
+
+def test_mxfp8_quantize_bit_exact(vdn):
+    """Random rows spanning 2^-40 .. 2^40, plus rows of zeros, a lone value,
+    bf16 subnormals, values near the top of the bf16 range, saturating
+    blocks and exact ties, every row's blocks checked bit for bit."""
+    log("[mxfp8] quantize")
+    g = torch.Generator().manual_seed(51)
+    x = torch.randn(300, 128, generator=g) * torch.exp2(torch.randint(-40, 41, (300, 4), generator=g)
+                                                        .float()).repeat_interleave(32, 1)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 77] = -3.0
+    x[2] = torch.randn(128, generator=g) * 2.0 ** -130          # bf16 subnormals (scale clamped)
+    x[3] = torch.randn(128, generator=g) * 2.0 ** 125
+    x[4, :32] = torch.tensor([448.0, 1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9, -1.0625] + [0.5] * 26)
+    x[4, 32:64] = torch.tensor([1.99 * 256, -1.99 * 256] + [3.0] * 30)   # 509 > 448: saturates
+    x[5] = -x[5].abs()
+    xb = x.to(torch.bfloat16)
+    codes, scales = vdn.mxfp8_quantize(xb.cuda())
+    torch.cuda.synchronize()
+    c_ref, s_ref = MX.quantize(xb.float().numpy())
+    bad_s = np.count_nonzero(scales.cpu().numpy() != s_ref)
+    bad_c = np.count_nonzero(codes.cpu().numpy() != c_ref)
+    log(f"  scale mismatches {bad_s}, code mismatches {bad_c} of {x.numel()}")
+    assert bad_s == 0 and bad_c == 0
+
+
+def test_mxfp8_quantize_config4_q_sampled(vdn):
+    """Q of the 102-frame layer (B1 H24 T102 N4032 d128, 1.26e9 values)
+    quantised at once; 4096 sampled rows checked bit for bit."""
+    log("[mxfp8] quantize 102-frame Q")
+    cfg = synth.CONFIGS[4]
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    q = inp["q"].reshape(-1, cfg.head_dim)
+    codes, scales = vdn.mxfp8_quantize(q)
+    torch.cuda.synchronize()
+    rows = torch.randint(0, q.shape[0], (4096,), generator=torch.Generator().manual_seed(52)).cuda()
+    c_ref, s_ref = MX.quantize(q[rows].float().cpu().numpy())
+    assert np.array_equal(scales[rows].cpu().numpy(), s_ref)
+    assert np.array_equal(codes[rows].cpu().numpy(), c_ref)
+
+
+MXCASES = [
+    ("H2_T17_N130", VdnConfig(1, 2, 128, 17, 130, dtype="bf16", seed=61), 0.0),
+    ("B2_T12_N33", VdnConfig(2, 1, 128, 12, 33, dtype="bf16", seed=62), 0.0),
+    ("T23_N40_noanchor_W0", VdnConfig(1, 1, 128, 23, 40, dtype="bf16", window_chunks=0,
+                                      anchor_first=False, anchor_last=False, seed=63), 0.0),
+    ("T40_N20_C3_W2_split", VdnConfig(1, 2, 128, 40, 20, dtype="bf16", chunk_frames=3, window_chunks=2,
+                                      seed=64), 0.0),
+    ("T13_N70_sharp4", VdnConfig(1, 1, 128, 13, 70, dtype="bf16", seed=65), 4.0),
+    ("T17_N70_ctx77", VdnConfig(1, 2, 128, 17, 70, dtype="bf16", seed=66, context_tokens=77), 0.0),
+]
+
+
+@pytest.mark.parametrize("name,cfg,sharp", MXCASES, ids=[t[0] for t in MXCASES])
+def test_window_attn_mxfp8(vdn, name, cfg, sharp):
+    """Softmax branch with MXFP8 scores, gated and ungated, with lse; the same
+    result through the entry point that takes codes and scales."""
+    log(f"[mxfp8 window] {name}")
+    inp = gpu_inputs(cfg, with_layer=False, sharp=sharp)
+    shape = vdn.shape_from_config(cfg, softmax_mxfp8=True)
+    B, H, d, N, Lt = cfg.batch, cfg.heads, cfg.head_dim, cfg.tokens_per_frame, cfg.seq_len
+    gen = torch.Generator().manual_seed(cfg.seed + 5)
+    gate = torch.rand(B, Lt, H * d, generator=gen).to(torch.bfloat16).cuda()
+    out, lse = vdn.window_attn(shape, inp, gate_s=gate, with_lse=True)
+    out_ng = vdn.window_attn(shape, inp)
+    qc, qs = vdn.mxfp8_quantize(inp["q"].contiguous())
+    kc, ks = vdn.mxfp8_quantize(inp["k"].contiguous())
+    out_pre = vdn.window_attn_mxfp8(shape, qc, qs, kc, ks, inp["v"], gate_s=gate)
+    torch.cuda.synchronize()
+    allowed = O.allowed_frames(cfg.frames, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
+                               cfg.anchor_last)
+    ref = np.zeros((B, Lt, H * d))
+    ref_lse = np.zeros((B, H, Lt))
+    for b in range(B):
+        for h in range(H):
+            q8 = mx_values(np32(inp["q"][b, h]))
+            k8 = mx_values(np32(inp["k"][b, h]))
+            v = np32(inp["v"][b, h]).astype(np.float64)
+            if cfg.context_tokens:
+                o, l = O.window_attention_ctx(q8, k8, v, allowed, N, 1 / np.sqrt(d))
+            else:
+                o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d))
+            ref[b, :, h * d:(h + 1) * d] = o.reshape(Lt, d)
+            ref_lse[b, h] = l
+    g = np32(gate).astype(np.float64)
+    e1 = excess_err(np32(out), g * ref, "bf16")
+    e2 = excess_err(np32(out_ng), ref, "bf16")
+    e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
+    same = torch.equal(out, out_pre)
+    log(f"  gated {e1:.3e} ungated {e2:.3e} (plain {rel_err(np32(out_ng), ref):.3e}) lse abs {e3:.3e} "
+        f"codes entry identical {same}")
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"] and e3 <= 1e-2
+    assert same
+
+
+def test_hybrid_mxfp8(vdn):
+    """Whole layer with the softmax branch in MXFP8 (the linear branch keeps
+    bf16 q and k), every output row against the oracle."""
+    cfg = VdnConfig(1, 2, 128, 17, 130, dtype="bf16", seed=67)
+    log("[mxfp8 hybrid] H2 T17 N130")
+    inp = gpu_inputs(cfg)
+    out = vdn.hybrid_attn(vdn.shape_from_config(cfg, softmax_mxfp8=True), inp)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.frames * cfg.tokens_per_frame)
+    host = {k: np32(v) for k, v in inp.items()}
+    ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                              host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                              rows, softmax_mxfp8=True, **oracle_kwargs(cfg))
+    err = rel_err(np32(out), ref)
+    log(f"  rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_window_attn_mxfp8_T102_two_heads_sampled(vdn):
+    """Softmax branch in MXFP8 at the 102-frame length (B1 H2 T102 N4032):
+    every tile, the anchor rows' key splits and the merge; sampled query
+    tokens of both heads against the oracle."""
+    cfg = synth.CONFIGS[4].replace(heads=2)
+    log("[mxfp8 window] B1 H2 T102 N4032")
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg, softmax_mxfp8=True)
+    out, lse = vdn.window_attn(shape, inp, with_lse=True)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    rows = np.array(synth.sample_tokens(cfg, 12))
+    T, N, d = cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+    worst = 0.0
+    for h in range(cfg.heads):
+        q8 = inp["q"][0, h].float().cpu().numpy().astype(np.float64)
+        q8.reshape(-1, d)[rows] = mx_values(q8.reshape(-1, d)[rows])   # only the sampled queries are read
+        k8 = mx_values(inp["k"][0, h].float().cpu().numpy())
+        v = inp["v"][0, h].float().cpu().numpy().astype(np.float64)
+        o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d), rows)
+        e = rel_err(np32(out[0, rows, h * d:(h + 1) * d]), o)
+        el = float(np.max(np.abs(np32(lse[0, h, rows]) - l)))
+        log(f"  head {h}: rel err {e:.3e} lse abs {el:.3e} ({time.time() - t0:.1f}s)")
+        worst = max(worst, e)
+        assert el <= 1e-2
+    assert worst <= TOL["bf16"]

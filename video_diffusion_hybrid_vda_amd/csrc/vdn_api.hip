@@ -48,6 +48,12 @@ int check_shape(const vdn_shape* s) {
   if (!(s->rms_eps >= 0.f) || !isfinite(s->rms_eps))
     return fail(VDN_ERR_BAD_SHAPE, "rms_eps must be finite and >= 0");
   if (!isfinite(s->softmax_scale)) return fail(VDN_ERR_BAD_SHAPE, "softmax_scale must be finite");
+  if (s->softmax_mxfp8 != 0 && s->softmax_mxfp8 != 1)
+    return fail(VDN_ERR_BAD_SHAPE, "softmax_mxfp8 must be 0 or 1");
+  if (s->softmax_mxfp8 && s->dtype != VDN_BF16)
+    return fail(VDN_ERR_DTYPE, "softmax_mxfp8 needs dtype VDN_BF16");
+  if (s->softmax_mxfp8 && s->head_dim != 128)
+    return fail(VDN_ERR_BAD_SHAPE, "softmax_mxfp8 needs head_dim 128");
   const int64_t L = (int64_t)s->frames * s->tokens_per_frame + s->context_tokens;
   if (L > (1LL << 30))
     return fail(VDN_ERR_BAD_SHAPE, "frames * tokens_per_frame + context_tokens exceeds 2^30");
@@ -145,14 +151,20 @@ VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
 }
 
 struct AttnLayout {
-  size_t part_o, part_ml, total;
+  size_t part_o, part_ml, qc, qs, kc, ks, total;
 };
+// with softmax_mxfp8, q and k quantised to MXFP8 (codes [B, H, Lt, d], scales [B, H, Lt, d / 32])
 AttnLayout attn_layout(const vdn_shape* s, const AttnParams& p) {
   AttnLayout l;
   size_t off = 0;
   const size_t rows = p.nsplit > 1 ? (size_t)p.B * p.H * p.nsplit * p.dense_rows : 0;
   l.part_o = off; off = align_up(off + rows * s->head_dim * 4);
   l.part_ml = off; off = align_up(off + rows * 2 * 4);
+  const size_t elems = s->softmax_mxfp8 ? (size_t)p.B * p.H * p.Lt * s->head_dim : 0;
+  l.qc = off; off = align_up(off + elems);
+  l.qs = off; off = align_up(off + elems / 32);
+  l.kc = off; off = align_up(off + elems);
+  l.ks = off; off = align_up(off + elems / 32);
   l.total = off;
   return l;
 }
@@ -226,11 +238,12 @@ int check_params(const vdn_shape* s, const float* gamma, const float* beta, char
 // ---- opt-in phase timing: HIP event pairs recorded around each phase
 enum Phase {
   kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhAnchorMerge, kPhGram, kPhSolve, kPhScan,
-  kPhReadout, kPhOutGemm, kNumPhases
+  kPhReadout, kPhOutGemm, kPhQuantize, kNumPhases
 };
 const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "window_attn",
                                              "anchor_merge",      "vda_gram",  "vda_solve",
-                                             "vda_scan",          "vda_readout", "out_gemm"};
+                                             "vda_scan",          "vda_readout", "out_gemm",
+                                             "mxfp8_quantize"};
 
 struct Timer {
   std::mutex mu;
@@ -311,8 +324,12 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   return VDN_OK;
 }
 
+// Softmax branch.  With s->softmax_mxfp8, q and k are quantised into the
+// workspace first, unless qs / ks already point at MXFP8 scales (then q and k
+// are the codes).
 int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, const void* gate,
-             int64_t ldg, void* out, int64_t ldo, float* lse, char* ws, hipStream_t st) {
+             int64_t ldg, void* out, int64_t ldo, float* lse, char* ws, hipStream_t st,
+             const void* qs = nullptr, const void* ks = nullptr) {
   AttnParams p = make_attn_params(s);
   const AttnLayout l = attn_layout(s, p);
   p.q = q;
@@ -325,8 +342,26 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
   p.ldo = ldo;
   p.part_o = (float*)(ws + l.part_o);
   p.part_ml = (float*)(ws + l.part_ml);
-  int ph = phase_begin(kPhWindowAttn, st);
-  hipError_t e = launch_window_attn(s->dtype, s->head_dim, p, st);
+  const bool mx = s->softmax_mxfp8 || qs;
+  hipError_t e;
+  int ph;
+  if (mx && !qs) {
+    const int64_t n = (int64_t)p.B * p.H * p.Lt * s->head_dim;
+    ph = phase_begin(kPhQuantize, st);
+    e = launch_mxfp8_quantize(q, n, ws + l.qc, ws + l.qs, st);
+    if (e == hipSuccess) e = launch_mxfp8_quantize(k, n, ws + l.kc, ws + l.ks, st);
+    phase_end(ph, st);
+    if (e != hipSuccess) return hip_fail(e, "mxfp8 quantize launch");
+    p.q = ws + l.qc;
+    p.qs = ws + l.qs;
+    p.k = ws + l.kc;
+    p.ks = ws + l.ks;
+  } else if (mx) {
+    p.qs = qs;
+    p.ks = ks;
+  }
+  ph = phase_begin(kPhWindowAttn, st);
+  e = mx ? launch_window_attn_mxfp8(p, st) : launch_window_attn(s->dtype, s->head_dim, p, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
   ph = phase_begin(kPhAnchorMerge, st);
@@ -398,6 +433,47 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q, const void* k,
                 need, ws ? ws_bytes : (size_t)0);
   const int64_t D = (int64_t)shape->heads * shape->head_dim;
   return run_attn(shape, q, k, v, gate_s, D, out, D, lse, (char*)ws, (hipStream_t)stream);
+}
+
+int vdn_mxfp8_quantize(const void* x, int64_t n_elems, void* codes, void* scales, void* stream) {
+  if (!x || !codes || !scales)
+    return fail(VDN_ERR_INVALID_ARG, "vdn_mxfp8_quantize: x, codes and scales must be non-NULL");
+  if (misaligned(x) || misaligned(codes))
+    return fail(VDN_ERR_INVALID_ARG, "vdn_mxfp8_quantize: x and codes must be 16-byte aligned");
+  if (n_elems < 0 || n_elems % 32)
+    return fail(VDN_ERR_BAD_SHAPE, "vdn_mxfp8_quantize: n_elems %lld is not a non-negative multiple of 32",
+                (long long)n_elems);
+  const hipError_t e = launch_mxfp8_quantize(x, n_elems, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp8 quantize launch");
+  return VDN_OK;
+}
+
+int window_anchor_attn_mxfp8_fwd(const vdn_shape* shape, const void* q_codes, const void* q_scales,
+                                 const void* k_codes, const void* k_scales, const void* v,
+                                 const void* gate_s, void* out, float* lse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (shape->dtype != VDN_BF16)
+    return fail(VDN_ERR_DTYPE, "window_anchor_attn_mxfp8_fwd: v, gate and out must be bf16");
+  if (shape->head_dim != 128)
+    return fail(VDN_ERR_BAD_SHAPE, "window_anchor_attn_mxfp8_fwd: head_dim must be 128");
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v || !out)
+    return fail(VDN_ERR_INVALID_ARG,
+                "window_anchor_attn_mxfp8_fwd: codes, scales, v and out must be non-NULL");
+  if (misaligned(q_codes) || misaligned(q_scales) || misaligned(k_codes) || misaligned(k_scales) ||
+      misaligned(v) || misaligned(out) || misaligned(gate_s) || misaligned(ws))
+    return fail(VDN_ERR_INVALID_ARG, "window_anchor_attn_mxfp8_fwd: device pointers must be 16-byte aligned");
+  vdn_shape s = *shape;
+  s.softmax_mxfp8 = 0;   // the codes are given: no quantisation buffers
+  const AttnParams p = make_attn_params(&s);
+  const size_t need = attn_layout(&s, p).total;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(VDN_ERR_WORKSPACE, "window_anchor_attn_mxfp8_fwd: workspace of %zu bytes needed, %zu given",
+                need, ws ? ws_bytes : (size_t)0);
+  const int64_t D = (int64_t)shape->heads * shape->head_dim;
+  return run_attn(&s, q_codes, k_codes, v, gate_s, D, out, D, lse, (char*)ws, (hipStream_t)stream,
+                  q_scales, k_scales);
 }
 
 int vdn_hybrid_attn_fwd(const vdn_shape* shape, const void* x, const void* q, const void* k,

@@ -1011,6 +1011,557 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Softmax branch with MXFP8 scores: head_dim 128, Q and K as MXFP8 (OCP E4M3
+// codes, one E8M0 scale per 32 elements of a row; [P3] 实验结果 runs the
+// denoiser in MXFP8), V, gate and output bf16.  The same work items, key
+// intervals, running-max softmax, P V and row-sum products and epilogue as
+// the bf16 kernel above; only the score product changes.
+//
+// S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4: 64 dims per product, so a
+// 32x32 score tile is 2 products of 64 cycles instead of 8 of 32.  The
+// product's K layout (probed): lane l of row i holds the 32 codes of dims
+// 16 (l / 32) .. +15 and 32 + 16 (l / 32) .. +15 of its 64-dim half, and the
+// scale of 32-dim block b of row i comes from lane i + 32 b.  So a lane reads
+// two 16-byte chunks of its row (K from LDS, Q from global once) and one
+// scale byte; the block order inside a half is the order of the dims.
+//
+// A half step is a fixed list of 24 slots, one product each: 4 score
+// products of half tile j+1 (slots 0-3), 8 P V products and 2 row sums for
+// each 16-key step of half tile j (slots 4-13 and 14-23).  The 32
+// exponentials and 16 conversions of half tile j run beside the score and
+// the first P V products (queries 0-31 of each step first, so the first P V
+// product's words are ready early); the max of half tile j+1 beside the
+// second P V step.  LDS reads: V of step 1 of half tile j in slots 0-7, the
+// K codes and scales of half tile j+2 in slots 8-13, V of step 0 of half
+// tile j+1 in slots 14-21; each product waits with an lgkmcnt computed from
+// these tables at compile time.
+namespace v8 {
+using namespace v3;
+constexpr int KROWB8 = D;                        // code bytes per K row
+constexpr int KTILEB8 = BN * KROWB8;             // 8 KB
+constexpr int VBASE8 = STAGES * KTILEB8;         // V tiles (bf16) after the K tiles
+constexpr int SBASE8 = VBASE8 + STAGES * TILEB;  // then the K scales
+constexpr int STILEB8 = BN * 4;                  // 4 scale bytes per key
+constexpr int LDSB8 = SBASE8 + STAGES * STILEB8;
+constexpr int KBLK8 = 2;                         // 1 KB K blocks per wave and tile
+constexpr int NLOAD8 = KBLK8 + BLK + 1;          // K, V and one scale load per wave and tile
+constexpr int NSLOT8 = 24;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 128-byte K rows cover 32 banks: chunk c of row r at c ^ ((r >> 1) & 7), so
+// a 16-lane read of one chunk in 16 consecutive rows covers all 64 banks
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
+// constant parts of the K code / scale read addresses: stage st, half tile kt
+constexpr int kcoff8(int st, int kt) { return st * KTILEB8 + kt * 32 * KROWB8; }
+constexpr int ksoff8(int st, int kt) { return st * STILEB8 + kt * 32 * 4; }
+
+// issue slots: K reads r = 3 kh + {codes 0-15, codes 16-31, scale} of the
+// half step after this one; V half-fragments i = 2 dt + ab of 16-key step s4
+constexpr int kIssueK8[6] = {8, 9, 10, 11, 12, 13};
+constexpr int kIssueV8[2][8] = {{14, 15, 16, 17, 18, 19, 20, 21}, {0, 1, 2, 3, 4, 5, 6, 7}};
+constexpr int kIssueD8[NLOAD8] = {4, 5, 6, 7, 8, 9, 10};
+constexpr int key8_k(int r) { return kIssueK8[r] * 64 + r; }
+constexpr int key8_v(int s4, int i) { return kIssueV8[s4][i] * 64 + 8 + 8 * s4 + i; }
+// reads issued after the one with key a (keys of the half step before are
+// shifted by one half step) and before the wait of slot m
+constexpr int younger8(int a, int m) {
+  int n = 0;
+  for (int sh = -1; sh <= 0; ++sh) {
+    for (int r = 0; r < 6; ++r) {
+      const int k = key8_k(r) + sh * NSLOT8 * 64;
+      if (k > a && k < 64 * m) ++n;
+    }
+    for (int s4 = 0; s4 < 2; ++s4)
+      for (int i = 0; i < 8; ++i) {
+        const int k = key8_v(s4, i) + sh * NSLOT8 * 64;
+        if (k > a && k < 64 * m) ++n;
+      }
+  }
+  return n < 15 ? n : 15;
+}
+// score products of dims half kh (slot 2 kh): K reads of the half step before
+constexpr int wait8_s(int kh) { return younger8(key8_k(3 * kh + 2) - NSLOT8 * 64, 2 * kh); }
+// P V of step 0 (slot 4 + 2 dt): V reads of the half step before; of step 1
+// (slot 14 + 2 dt): this half step's
+constexpr int wait8_p0(int dt) { return younger8(key8_v(0, 2 * dt + 1) - NSLOT8 * 64, 4 + 2 * dt); }
+constexpr int wait8_p1(int dt) { return younger8(key8_v(1, 2 * dt + 1), 14 + 2 * dt); }
+constexpr bool schedule8_ok() {
+  for (int r = 0; r < 6; ++r)
+    if (kIssueK8[r] < 4) return false;                      // after this half step's score products
+  for (int i = 0; i < 8; ++i) {
+    if (kIssueV8[0][i] < 12) return false;                  // after this half step's step-0 P V products
+    if (kIssueV8[1][i] >= 14 + 2 * (i / 2)) return false;   // before its own product
+  }
+  return true;
+}
+static_assert(schedule8_ok(), "MXFP8 LDS read schedule violates its order constraints");
+static_assert(wait8_s(0) == 11 && wait8_p1(0) == 12, "lgkmcnt tables");
+
+// exponential pairs in order of use: queries 0-31 (qt 0) of each 16-key step first
+constexpr int kPair8[16] = {0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15};
+// 26 units (pairs 0-7 of the order and the conversion of the eighth) beside
+// the 4 score products, the other 23 beside slots 4-13
+constexpr int units_before8(int m) {
+  return m <= 4 ? (26 * m + 2) / 4 : (m <= 14 ? 26 + (23 * (m - 4) + 5) / 10 : 49);
+}
+
+template <int SEL>   // Q scale byte (2 qt + kh)
+__device__ __forceinline__ void mma8_0(f32x16& d, i32x8 k, i32x8 q, int ks, int qs) {
+  asm volatile(
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[0,%5,0] op_sel_hi:[0,%6,0]"
+      : "=&v"(d)
+      : "v"(k), "a"(q), "v"(ks), "v"(qs), "n"(SEL & 1), "n"(SEL >> 1));
+}
+template <int SEL>
+__device__ __forceinline__ void mma8(f32x16& d, i32x8 k, i32x8 q, int ks, int qs) {
+  asm volatile(
+      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[0,%5,0] op_sel_hi:[0,%6,0]"
+      : "+v"(d)
+      : "v"(k), "a"(q), "v"(ks), "v"(qs), "n"(SEL & 1), "n"(SEL >> 1));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_c(i32x4& d, int addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_s(int& d, int addr) {
+  asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+}  // namespace v8
+
+__global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams p) {
+  using namespace v8;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[LDSB8];
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
+
+  const WorkItem wi = decode_work(p, BM);
+  const int NL = p.Lt;
+  const unsigned char* Qc = (const unsigned char*)p.q + (int64_t)wi.bh * NL * D;
+  const unsigned char* Qs = (const unsigned char*)p.qs + (int64_t)wi.bh * NL * 4;
+  const unsigned char* Kc = (const unsigned char*)p.k + (int64_t)wi.bh * NL * D;
+  const unsigned char* Ks = (const unsigned char*)p.ks + (int64_t)wi.bh * NL * 4;
+  const bf16* Vb = (const bf16*)p.v + (int64_t)wi.bh * NL * D;
+
+  int ntiles = 0;
+#pragma unroll
+  for (int iv = 0; iv < 4; ++iv)
+    if (iv < wi.nint) ntiles += (wi.ke[iv] - wi.kb[iv] + BN - 1) / BN;
+
+  // Loader: per tile and wave 2 K blocks (8 rows of 128 code bytes; lane l
+  // fills physical chunk l % 8 of row l / 8), 4 V blocks (as the bf16
+  // kernel) and one 256-byte load of the tile's 64 x 4 scale bytes (every
+  // wave loads the same bytes, so each wave issues the same loads).
+  int koff_lane[KBLK8], voff_lane[BLK];
+#pragma unroll
+  for (int i = 0; i < KBLK8; ++i) {
+    const int row = (wave * KBLK8 + i) * 8 + lane / 8;
+    koff_lane[i] = row * KROWB8 + swz8(row, lane % 8) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < BLK; ++i) {
+    const int row = (wave * BLK + i) * 4 + lane / 16;
+    voff_lane[i] = row * ROWB + swz(row, lane % 16) * 16;
+  }
+  const int kb0 = wi.kb[0], kb1 = wi.kb[1], kb2 = wi.kb[2], kb3 = wi.kb[3];
+  const int ke0 = wi.ke[0], ke1 = wi.ke[1], ke2 = wi.ke[2], ke3 = wi.ke[3];
+  auto kb_of = [&](int i) { return i == 0 ? kb0 : (i == 1 ? kb1 : (i == 2 ? kb2 : kb3)); };
+  auto ke_of = [&](int i) { return i == 0 ? ke0 : (i == 1 ? ke1 : (i == 2 ? ke2 : ke3)); };
+  int liv = 0, lk0 = kb_of(0), lke = ke_of(0);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)Kc, (short)0, NL * KROWB8, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)Ks, (short)0, NL * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, NL * ROWB, 0x00020000);
+  const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
+  auto issue8 = [&](int st, int i) {
+    if (i < KBLK8) {
+      const int voff = lk0 * KROWB8 + koff_lane[i];
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk),
+                   "{m0}"(lds0 + st * KTILEB8 + (wave * KBLK8 + i) * 1024)
+                   : "memory");
+    } else if (i < KBLK8 + BLK) {
+      const int b = i - KBLK8;
+      const int voff = lk0 * ROWB + voff_lane[b];
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rv),
+                   "{m0}"(lds0 + VBASE8 + st * TILEB + (wave * BLK + b) * 1024)
+                   : "memory");
+    } else {
+      const int voff = (lk0 + lane) * 4;
+      asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                   "{m0}"(lds0 + SBASE8 + st * STILEB8)
+                   : "memory");
+      lk0 += BN;
+      if (lk0 >= lke) {
+        ++liv;
+        if (liv < wi.nint) {
+          lk0 = kb_of(liv);
+          lke = ke_of(liv);
+        }
+      }
+      lk0 = __builtin_amdgcn_readfirstlane(lk0);
+      lke = __builtin_amdgcn_readfirstlane(lke);
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+#pragma unroll
+    for (int i = 0; i < NLOAD8; ++i) issue8(st, i);
+
+  // Q codes (B operand, in the accumulator file) and scales: lane holds
+  // query l32's codes of dims 64 kh + 16 h .. +15 and 64 kh + 32 + 16 h .. +15;
+  // byte 2 qt + kh of qsc is the scale of its block 2 kh + h
+  i32x8 qf8[QT][2];
+  int qsc = 0;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
+    const bool ok = qrow < wi.qend;
+    const unsigned sw = ok ? *reinterpret_cast<const unsigned*>(Qs + (int64_t)qrow * 4) : 0u;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const unsigned char* src = Qc + (int64_t)qrow * D + 64 * kh + 16 * h;
+      const i32x4 lo = ok ? *reinterpret_cast<const i32x4*>(src) : i32x4{};
+      const i32x4 hi = ok ? *reinterpret_cast<const i32x4*>(src + 32) : i32x4{};
+      qf8[qt][kh] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      qsc |= (int)(((sw >> (8 * (2 * kh + h))) & 0xFFu) << (8 * (2 * qt + kh)));
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) asm volatile("" : "+a"(qf8[qt][kh]));
+
+  f32x16 o[4][QT];
+  f32x4 lsum[QT];
+  float mrun[QT], negm[QT], mtile[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mrun[qt] = -INFINITY;
+    negm[qt] = INFINITY;
+    lsum[qt] = f32x4{};
+    asm volatile("" : "+a"(lsum[qt]));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      o[dt][qt] = f32x16{};
+      asm volatile("" : "+a"(o[dt][qt]));
+    }
+  }
+  bf16x8 sel;
+  {
+    const bf16 one = (bf16)(((j16 == 0) && !(g & 1)) || ((j16 == 1) && (g & 1)) ? 1.f : 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
+  const float c2 = p.scale_log2;
+  int civ = 0, ck0 = kb_of(0), cke = ke_of(0);
+  auto advance = [&]() {
+    ck0 += BN;
+    if (ck0 >= cke) {
+      ++civ;
+      if (civ < wi.nint) {
+        ck0 = kb_of(civ);
+        cke = ke_of(civ);
+      }
+    }
+    ck0 = __builtin_amdgcn_readfirstlane(ck0);
+    cke = __builtin_amdgcn_readfirstlane(cke);
+  };
+
+  // Fragment addresses: K codes and scales of row l32 of a half tile (chunks
+  // 4 kh + 2 part + h), V as the bf16 kernel
+  int kcoff[2][2], ksoff[2], voffA[4], voffB[4];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) kcoff[kh][pt] = lds0 + l32 * KROWB8 + swz8(l32, 4 * kh + 2 * pt + h) * 16;
+    ksoff[kh] = lds0 + SBASE8 + l32 * 4 + 2 * kh + h;
+  }
+  {
+    const int rA = 4 * (g >> 1) + (j16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+      const int cch = dcol >> 3, off = (dcol & 7) * 2;
+      voffA[dt] = lds0 + VBASE8 + rA * ROWB + swz(rA, cch) * 16 + off;
+      voffB[dt] = lds0 + VBASE8 + (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
+    }
+  }
+
+  auto mask = [&](f32x16 (&sc)[QT], int lim) {
+    const int l = lim - 4 * h;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) >= l) sc[qt][r] = -INFINITY;
+  };
+  auto half_max = [&](const f32x16 (&sc)[QT]) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = sc[qt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qt][r]);
+      mtile[qt] = halves_max(mx) * c2;
+    }
+  };
+  auto rescale = [&]() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mnew = fmaxf(mrun[qt], mtile[qt]);
+      const float alpha = fast_exp2(mrun[qt] - mnew);
+      mrun[qt] = mnew;
+      negm[qt] = -mnew;
+      const float a_hi = __shfl(alpha, (lane & 15) + 16);
+      asm volatile("" : "+a"(lsum[qt]));
+      lsum[qt][0] *= alpha;
+      lsum[qt][1] *= a_hi;
+      asm volatile("" : "+a"(lsum[qt]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        asm volatile("" : "+a"(o[dt][qt]));
+        o[dt][qt] *= alpha;
+        asm volatile("" : "+a"(o[dt][qt]));
+      }
+    }
+    asm volatile("s_nop 4" ::: "memory");
+  };
+  static_assert(kRescaleSlack == 1.f, "grow_mask compares against 1.0");
+  auto outran = [&]() {
+    bool up = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) up |= mtile[qt] > mrun[qt] + kRescaleSlack;
+    return __any(up);
+  };
+  auto boundary = [&](f32x16 (&sc)[QT], int lim, unsigned long long grow) {
+    bool up = grow != 0;
+    if (lim < 32) {
+      mask(sc, lim);
+      half_max(sc);
+      up = outran();
+    }
+    if (up) rescale();
+  };
+
+  f32x16 sa[QT], sb[QT];
+  i32x4 klo[2], khi[2];   // K codes of the next score products: [dims half][chunk pair part]
+  int ksc[2];             // their scales (byte 0)
+  i16x4 vfa[2][4], vfb[2][4];
+  unsigned pw[QT][2][4];
+  float tt[4];
+  auto kfrag = [&](int kh) { return __builtin_shufflevector(klo[kh], khi[kh], 0, 1, 2, 3, 4, 5, 6, 7); };
+
+  auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], auto SST, auto SKT, auto PST, auto PKT,
+                       auto NST, auto NKT, int dst) __attribute__((always_inline)) {
+    constexpr int kc_off = kcoff8(decltype(NST)::value, decltype(NKT)::value);
+    constexpr int ks_off = ksoff8(decltype(NST)::value, decltype(NKT)::value);
+    constexpr int v0_off = voffc(decltype(SST)::value, decltype(SKT)::value, 0);
+    constexpr int v1_off = voffc(decltype(PST)::value, decltype(PKT)::value, 1);
+    auto val = [&](auto I, int e) {
+      constexpr int i = decltype(I)::value, j = kPair8[i], s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
+      fma_exp(tt[(2 * i + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
+    };
+    auto cvt = [&](auto I) {
+      constexpr int i = decltype(I)::value, j = kPair8[i], s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
+      cvt_pk(pw[qt][s4][w], tt[(2 * i) % 4], tt[(2 * i + 1) % 4]);
+    };
+    auto unit = [&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if constexpr (u == 48) {
+        cvt(IC<15>{});
+      } else {
+        constexpr int i = u / 3, k = u % 3;
+        if constexpr (k == 0) val(IC<i>{}, 0);
+        else if constexpr (k == 1) {
+          if constexpr (i > 0) cvt(IC<i - 1>{});
+        } else {
+          val(IC<i>{}, 1);
+        }
+      }
+    };
+    auto pk = [&](int qt, int s4) {
+      const u32x4 w = {pw[qt][s4][0], pw[qt][s4][1], pw[qt][s4][2], pw[qt][s4][3]};
+      return __builtin_bit_cast(bf16x8, w);
+    };
+    auto vf = [&](int s4, int dt) {
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vfa[s4][dt], vfb[s4][dt], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    float mx[QT];
+    unsigned long long grow = 0;
+
+    auto slot = [&](auto M) {
+      constexpr int m = decltype(M)::value;
+      if constexpr (m < 4) {
+        constexpr int kh = m / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<wait8_s(kh)>();
+        if constexpr (kh == 0) mma8_0<2 * qt>(nxt[qt], kfrag(0), qf8[qt][0], ksc[0], qsc);
+        else mma8<2 * qt + 1>(nxt[qt], kfrag(1), qf8[qt][1], ksc[1], qsc);
+      } else if constexpr (m < 12) {
+        constexpr int dt = (m - 4) / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<wait8_p0(dt)>();
+        mma_o(o[dt][qt], vf(0, dt), pk(qt, 0));
+      } else if constexpr (m < 14) {
+        mma_l(lsum[m - 12], sel, pk(m - 12, 0));
+      } else if constexpr (m < 22) {
+        constexpr int dt = (m - 14) / 2, qt = m % 2;
+        if constexpr (qt == 0) wait_lgkm<wait8_p1(dt)>();
+        mma_o(o[dt][qt], vf(1, dt), pk(qt, 1));
+      } else {
+        mma_l(lsum[m - 22], sel, pk(m - 22, 1));
+      }
+      // LDS reads of this slot: K, then V
+      static_for<0, 6>([&](auto R) {
+        constexpr int r = decltype(R)::value, kh = r / 3, part = r % 3;
+        if constexpr (kIssueK8[r] == m) {
+          if constexpr (part == 0) ds_c<kc_off>(klo[kh], kcoff[kh][0]);
+          else if constexpr (part == 1) ds_c<kc_off>(khi[kh], kcoff[kh][1]);
+          else ds_s<ks_off>(ksc[kh], ksoff[kh]);
+        }
+      });
+      static_for<0, 16>([&](auto I) {
+        constexpr int s4 = decltype(I)::value / 8, i = decltype(I)::value % 8, dt = i / 2, ab = i % 2;
+        constexpr int off = s4 == 0 ? v0_off : v1_off;
+        if constexpr (kIssueV8[s4][i] == m) {
+          if constexpr (ab == 0) ds_tr<off>(vfa[s4][dt], voffA[dt]);
+          else ds_tr<off>(vfb[s4][dt], voffB[dt]);
+        }
+      });
+      static_for<0, NLOAD8>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (kIssueD8[i] == m) {
+          if (dst >= 0) issue8(dst, i);
+        }
+      });
+      if constexpr (m <= 13) static_for<units_before8(m), units_before8(m + 1)>(unit);
+      // max of the next scores (their products ended by slot 5)
+      if constexpr (m == 12) {
+        max3(mx[0], nxt[0][0], nxt[0][1], nxt[0][2]);
+        max3(mx[1], nxt[1][0], nxt[1][1], nxt[1][2]);
+      }
+      if constexpr (m >= 13 && m <= 19) {
+        constexpr int r = 3 + 2 * (m - 13);
+        if constexpr (r < 15) {
+          max3_acc(mx[0], nxt[0][r], nxt[0][r + 1]);
+          max3_acc(mx[1], nxt[1][r], nxt[1][r + 1]);
+        } else {
+          max_acc(mx[0], nxt[0][15]);
+          max_acc(mx[1], nxt[1][15]);
+        }
+      }
+      if constexpr (m == 20) halves_max_scaled(mx[0], c2);
+      if constexpr (m == 21) halves_max_scaled(mx[1], c2);
+      if constexpr (m == 22) grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
+    };
+    static_for<0, NSLOT8>(slot);
+    mtile[0] = mx[0];
+    mtile[1] = mx[1];
+    return grow;
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+
+  int kn = min(BN, cke - ck0);
+  // first half tile's scores (stage 0, half 0)
+  asm volatile("s_nop 4" ::: "memory");
+  ds_c<kcoff8(0, 0)>(klo[0], kcoff[0][0]);
+  ds_c<kcoff8(0, 0)>(khi[0], kcoff[0][1]);
+  ds_s<ksoff8(0, 0)>(ksc[0], ksoff[0]);
+  ds_c<kcoff8(0, 0)>(klo[1], kcoff[1][0]);
+  ds_c<kcoff8(0, 0)>(khi[1], kcoff[1][1]);
+  ds_s<ksoff8(0, 0)>(ksc[1], ksoff[1]);
+  wait_lgkm<0>();
+  mma8_0<0>(sa[0], kfrag(0), qf8[0][0], ksc[0], qsc);
+  mma8_0<2>(sa[1], kfrag(0), qf8[1][0], ksc[0], qsc);
+  mma8<1>(sa[0], kfrag(1), qf8[0][1], ksc[1], qsc);
+  mma8<3>(sa[1], kfrag(1), qf8[1][1], ksc[1], qsc);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  half_max(sa);
+  boundary(sa, kn, outran() ? 1ull : 0ull);
+  // the reads the first half step expects from a half step before it: K of
+  // half tile (stage 0, half 1), then V step 0 of half tile (stage 0, half 0)
+  ds_c<kcoff8(0, 1)>(klo[0], kcoff[0][0]);
+  ds_c<kcoff8(0, 1)>(khi[0], kcoff[0][1]);
+  ds_s<ksoff8(0, 1)>(ksc[0], ksoff[0]);
+  ds_c<kcoff8(0, 1)>(klo[1], kcoff[1][0]);
+  ds_c<kcoff8(0, 1)>(khi[1], kcoff[1][1]);
+  ds_s<ksoff8(0, 1)>(ksc[1], ksoff[1]);
+  static_for<0, 8>([&](auto I) {
+    constexpr int i = decltype(I)::value, dt = i / 2;
+    if constexpr (i % 2 == 0) ds_tr<voffc(0, 0, 0)>(vfa[0][dt], voffA[dt]);
+    else ds_tr<voffc(0, 0, 0)>(vfb[0][dt], voffB[dt]);
+  });
+
+  auto tile = [&](int t, auto S0, auto S1, int s3) __attribute__((always_inline)) {
+    const unsigned long long g1 = half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3);
+    boundary(sb, kn - 32, g1);
+    const unsigned long long g2 = half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1);
+    advance();
+    kn = min(BN, cke - ck0);
+    // tile t+2's loads are complete once at most the 7 of tile t+3 are outstanding
+    __builtin_amdgcn_s_waitcnt(0x0F77);   // vmcnt(7)
+    __builtin_amdgcn_s_barrier();
+    if (t + 1 < ntiles) boundary(sa, kn, g2);
+  };
+  for (int t = 0; t < ntiles; t += 4) {
+    tile(t, IC<0>{}, IC<1>{}, 3);
+    if (t + 1 >= ntiles) break;
+    tile(t + 1, IC<1>{}, IC<2>{}, 0);
+    if (t + 2 >= ntiles) break;
+    tile(t + 2, IC<2>{}, IC<3>{}, 1);
+    if (t + 3 >= ntiles) break;
+    tile(t + 3, IC<3>{}, IC<0>{}, 2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+  const bf16* gate = (const bf16*)p.gate;
+  bf16* out = (bf16*)p.out;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float r0 = __shfl(lsum[qt][0], l32 & 15), r1 = __shfl(lsum[qt][1], l32 & 15);
+    const float lt = l32 < 16 ? r0 : r1;
+    const int qrow = wi.qbeg + wave * WQ + qt * 32 + l32;
+    if (qrow >= wi.qend) continue;
+    if (!wi.split) {
+      const float inv = 1.f / lt;
+      const int64_t orow = (int64_t)wi.b * NL + qrow;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * h;
+          float v0 = o[dt][qt][4 * r4] * inv, v1 = o[dt][qt][4 * r4 + 1] * inv;
+          float v2 = o[dt][qt][4 * r4 + 2] * inv, v3 = o[dt][qt][4 * r4 + 3] * inv;
+          if (gate) {
+            const bf16x4 gv = *reinterpret_cast<const bf16x4*>(gate + orow * p.ldg + wi.h * D + d0);
+            v0 *= (float)gv[0]; v1 *= (float)gv[1]; v2 *= (float)gv[2]; v3 *= (float)gv[3];
+          }
+          bf16x4 ov;
+          ov[0] = (bf16)v0; ov[1] = (bf16)v1; ov[2] = (bf16)v2; ov[3] = (bf16)v3;
+          *reinterpret_cast<bf16x4*>(out + orow * p.ldo + wi.h * D + d0) = ov;
+        }
+      if (p.lse && h == 0) p.lse[(int64_t)wi.bh * NL + qrow] = (mrun[qt] + log2f(lt)) * kLn2;
+    } else {
+      const int64_t prow = wi.pbase + qrow;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = dt * 32 + 8 * r4 + 4 * h;
+          *reinterpret_cast<float4*>(p.part_o + prow * D + d0) =
+              make_float4(o[dt][qt][4 * r4], o[dt][qt][4 * r4 + 1], o[dt][qt][4 * r4 + 2], o[dt][qt][4 * r4 + 3]);
+        }
+      if (h == 0) {
+        p.part_ml[prow * 2] = mrun[qt];
+        p.part_ml[prow * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
 // Combine the key splits of the dense query rows (anchor frames, context
 // tokens): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, then gate.
 // One thread per (dense row, quarter of d).
@@ -1086,6 +1637,12 @@ hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t
   if (d == 32) return launch_attn_t<float, 32>(p, st);
   if (d == 64) return launch_attn_t<float, 64>(p, st);
   return launch_attn_t<float, 128>(p, st);
+}
+
+hipError_t launch_window_attn_mxfp8(const AttnParams& p, hipStream_t st) {
+  if (p.bm != attn_query_tile(1, 128)) return hipErrorInvalidValue;
+  if (p.total > 0) window_attn_mxfp8_d128_kernel<<<p.total, 256, 0, st>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st) {

@@ -37,7 +37,7 @@ class vdn_shape(ctypes.Structure):
         ("chunk_frames", ctypes.c_int32), ("window_chunks", ctypes.c_int32),
         ("anchor_first", ctypes.c_int32), ("anchor_last", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("context_tokens", ctypes.c_int32),
+        ("context_tokens", ctypes.c_int32), ("softmax_mxfp8", ctypes.c_int32),
     ]
 
     @property
@@ -52,17 +52,18 @@ class vdn_shape(ctypes.Structure):
 
 def make_shape(batch, heads, frames, tokens_per_frame, head_dim, dtype="bf16", chunk_frames=5,
                window_chunks=1, anchor_first=True, anchor_last=True, softmax_scale=0.0,
-               rms_eps=1e-6, context_tokens=0) -> vdn_shape:
+               rms_eps=1e-6, context_tokens=0, softmax_mxfp8=False) -> vdn_shape:
     dt = {"f32": VDN_F32, "bf16": VDN_BF16, torch.float32: VDN_F32, torch.bfloat16: VDN_BF16}.get(dtype, dtype)
     return vdn_shape(batch, heads, frames, tokens_per_frame, head_dim, chunk_frames, window_chunks,
-                     int(anchor_first), int(anchor_last), softmax_scale, rms_eps, dt, context_tokens)
+                     int(anchor_first), int(anchor_last), softmax_scale, rms_eps, dt, context_tokens,
+                     int(bool(softmax_mxfp8)))
 
 
-def shape_from_config(cfg) -> vdn_shape:
+def shape_from_config(cfg, softmax_mxfp8=False) -> vdn_shape:
     """vdn_shape of a synth.VdnConfig."""
     return make_shape(cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim,
                       cfg.dtype, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
-                      cfg.anchor_last, 0.0, cfg.rms_eps, cfg.context_tokens)
+                      cfg.anchor_last, 0.0, cfg.rms_eps, cfg.context_tokens, softmax_mxfp8)
 
 
 class vdn_phase_stat(ctypes.Structure):
@@ -83,6 +84,10 @@ def _load():
     lib.vda_scan_fwd.restype = I
     lib.window_anchor_attn_fwd.argtypes = [S] + [P] * 6 + [P, SZ, P]
     lib.window_anchor_attn_fwd.restype = I
+    lib.vdn_mxfp8_quantize.argtypes = [P, ctypes.c_int64, P, P, P]
+    lib.vdn_mxfp8_quantize.restype = I
+    lib.window_anchor_attn_mxfp8_fwd.argtypes = [S] + [P] * 8 + [P, SZ, P]
+    lib.window_anchor_attn_mxfp8_fwd.restype = I
     lib.vdn_dense_attn_fwd.argtypes = [S] + [P] * 6 + [SZ, P]
     lib.vdn_dense_attn_fwd.restype = I
     lib.vdn_set_param_check.argtypes = [I]
@@ -102,7 +107,7 @@ _lib = _load()
 
 EXPORTS = ("vdn_workspace_bytes", "vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
            "vdn_dense_attn_fwd", "vdn_set_param_check", "vdn_last_error", "vdn_version",
-           "vdn_timing_start", "vdn_timing_stop")
+           "vdn_timing_start", "vdn_timing_stop", "vdn_mxfp8_quantize", "window_anchor_attn_mxfp8_fwd")
 
 
 def _ptr(t):
@@ -181,6 +186,18 @@ def window_anchor_attn_fwd(shape, q, k, v, gate_s, out, lse, ws, stream=None) ->
         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def vdn_mxfp8_quantize(x, n_elems, codes, scales, stream=None) -> int:
+    return _check(_lib.vdn_mxfp8_quantize(_ptr(x), int(n_elems), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def window_anchor_attn_mxfp8_fwd(shape, q_codes, q_scales, k_codes, k_scales, v, gate_s, out, lse, ws,
+                                 stream=None) -> int:
+    return _check(_lib.window_anchor_attn_mxfp8_fwd(
+        ctypes.byref(shape), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v),
+        _ptr(gate_s), _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
 def vdn_dense_attn_fwd(shape, q, k, v, w_o, out, ws, stream=None) -> int:
     return _check(_lib.vdn_dense_attn_fwd(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(w_o), _ptr(out), _ptr(ws),
@@ -236,3 +253,28 @@ def dense_attn(shape, inp: dict, w_o, ws=None, stream=None) -> torch.Tensor:
     ws = workspace(shape, VDN_OP_DENSE_ATTN, dev) if ws is None else ws
     vdn_dense_attn_fwd(shape, inp["q"], inp["k"], inp["v"], w_o, out, ws, stream)
     return out
+
+
+def mxfp8_quantize(x: torch.Tensor, stream=None):
+    """MXFP8 of a bf16 tensor along its last axis (a multiple of 32):
+    (codes uint8 of x's shape, scales uint8 [..., last / 32])."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape[-1] % 32 == 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.uint8, device=x.device)
+    vdn_mxfp8_quantize(x, x.numel(), codes, scales, stream)
+    return codes, scales
+
+
+def window_attn_mxfp8(shape, q_codes, q_scales, k_codes, k_scales, v, gate_s=None, with_lse=False,
+                      ws=None, stream=None):
+    B, H, d = shape.batch, shape.heads, shape.head_dim
+    L = shape.total_tokens
+    dev = v.device
+    out = torch.empty(B, L, H * d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=dev) if with_lse else None
+    if ws is None:
+        plain = vdn_shape.from_buffer_copy(shape)
+        plain.softmax_mxfp8 = 0
+        ws = workspace(plain, VDN_OP_WINDOW_ATTN, dev)
+    window_anchor_attn_mxfp8_fwd(shape, q_codes, q_scales, k_codes, k_scales, v, gate_s, out, lse, ws, stream)
+    return (out, lse) if with_lse else out
