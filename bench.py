@@ -34,16 +34,18 @@ if ROOT not in sys.path:
 
 METRIC = "hybrid attn fwd tokens/s + ms/layer @102 latent frames; % MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch of the window/anchor softmax kernel on the 102-frame layer, from two
 # rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy calibration
-# (profiles/window_attn_T102_hbm_counters.md).  Valid only for the kernel sources they were
+# (profiles/window_attn_T102_counters.md).  Valid only for the kernel sources they were
 # taken on: reported as null once those sources change.
-WINDOW_TRAFFIC_BYTES = 263079702784
+WINDOW_TRAFFIC_BYTES = 260951900994
+WINDOW_MXFP8_TRAFFIC_BYTES = 185027972268   # the MXFP8-score kernel, same passes
 WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
-WINDOW_TRAFFIC_SHA = "1fab0ec6af7b2293"
+WINDOW_TRAFFIC_SHA = "50c25d3f51c8ff8b"
 
 
 def frame_key_counts(T, C, W, a0, a1):
@@ -73,7 +75,7 @@ def window_flops(cfg):
     return 4 * cfg.head_dim * cfg.batch * cfg.heads * pairs_per_head, pairs_per_head
 
 
-def window_traffic(cfg_name):
+def window_traffic(cfg_name, mxfp8=False):
     """Measured HBM bytes per window-kernel launch, or None if the workload or the kernel sources
     differ from the ones the counters were taken on."""
     import hashlib
@@ -83,7 +85,9 @@ def window_traffic(cfg_name):
     for f in WINDOW_TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "video_diffusion_hybrid_vda_amd", f), "rb") as fh:
             h.update(fh.read())
-    return WINDOW_TRAFFIC_BYTES if h.hexdigest()[:16] == WINDOW_TRAFFIC_SHA else None
+    if h.hexdigest()[:16] != WINDOW_TRAFFIC_SHA:
+        return None
+    return WINDOW_MXFP8_TRAFFIC_BYTES if mxfp8 else WINDOW_TRAFFIC_BYTES
 
 
 def phase_rooflines(cfg, phases):
@@ -118,6 +122,8 @@ def phase_rooflines(cfg, phases):
 
     # K and V read once; A_t and B_t written (fp32)
     hbm("vda_gram", 2 * tok + 2 * dd4)
+    # MXFP8 mode: q and k read (bf16), their codes (1 byte per element) and scales (1 per 32) written
+    hbm("mxfp8_quantize", 2 * tok + 2 * (tok // es) * (1 + 1 / 32))
     # Q, gate and output once; both directions' states once per frame
     hbm("vda_readout", 3 * tok + 2 * dd4)
     mfma("gate_gemm", 2.0 * B * L * D * 2 * D)
@@ -295,6 +301,10 @@ def main():
                     help="run the batch-2 hybrid-vs-dense length sweep instead of the single workload")
     ap.add_argument("--sweep-frames", type=int, nargs="+", default=[42, 62, 82, 102])
     ap.add_argument("--sweep-steps", type=int, default=3)
+    ap.add_argument("--softmax-mxfp8", action="store_true",
+                    help="time the layer with MXFP8 softmax-branch scores instead of bf16 ones")
+    ap.add_argument("--mxfp8-steps", type=int, default=3,
+                    help="after the bf16 measurement, also time this many calls in MXFP8 mode (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling HBM counters)")
@@ -315,15 +325,18 @@ def main():
     cfg = synth.CONFIGS[args.config]
     torch.cuda.set_device(0)
     inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
-    shape = vdn.shape_from_config(cfg)
+    shape = vdn.shape_from_config(cfg, softmax_mxfp8=args.softmax_mxfp8)
     ws = vdn.workspace(shape, vdn.VDN_OP_HYBRID)
     B, L, D = cfg.batch, cfg.seq_len, cfg.model_dim
     out = torch.empty(B, L, D, dtype=torch.bfloat16, device="cuda")
 
-    def step():
-        vdn.vdn_hybrid_attn_fwd(shape, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"],
+    def layer(sh, w):
+        vdn.vdn_hybrid_attn_fwd(sh, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"],
                                 inp["beta"], inp["w_gs"], inp["w_gl"], inp["rms_w"], inp["w_os"],
-                                inp["w_ol"], out, ws)
+                                inp["w_ol"], out, w)
+
+    def step():
+        layer(shape, ws)
 
     if args.calibrate_copy_mb > 0:
         src = torch.ones(args.calibrate_copy_mb << 20, dtype=torch.uint8, device="cuda")
@@ -347,6 +360,36 @@ def main():
     achieved = flops / (attn_avg_ms * 1e-3) / 1e12
     density = pairs / float(L) ** 2
     phase_ms = {k: round(v[1] / max(v[0], 1), 3) for k, v in phases.items() if v[0] > 0}
+    # MXFP8 scores: the q.k half of the window kernel's flops at the fp8 peak, the P V half at bf16
+    mx_peak = flops / (0.5 * flops / PEAK_FP8_TFLOPS + 0.5 * flops / PEAK_BF16_TFLOPS)
+
+    def mx_roofline(ms):
+        a = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": "window_attn_mxfp8", "achieved": round(a, 2),
+                "peak": round(mx_peak, 1), "unit": "TFLOP/s", "frac": round(a / mx_peak, 4),
+                "peak_note": "q.k half at the 5.0 PFLOP/s fp8 peak, P V half at the 2.5 PFLOP/s bf16 peak",
+                "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(ms, 3),
+                "traffic": window_traffic(cfg.name, mxfp8=True)}
+
+    mxfp8 = None
+    if not args.softmax_mxfp8 and args.mxfp8_steps > 0:
+        # the same layer with MXFP8 softmax-branch scores, timed after the bf16 region
+        shape8 = vdn.shape_from_config(cfg, softmax_mxfp8=True)
+        del ws
+        ws8 = vdn.workspace(shape8, vdn.VDN_OP_HYBRID)
+        layer(shape8, ws8)
+        torch.cuda.synchronize()
+        vdn.vdn_timing_start()
+        ms8, call8 = timed_calls(lambda: layer(shape8, ws8), args.mxfp8_steps, 0)
+        ph8 = vdn.vdn_timing_stop()
+        ph8_ms = {k: round(v[1] / max(v[0], 1), 3) for k, v in ph8.items() if v[0] > 0}
+        mxfp8 = {"mode": "softmax-branch scores from MXFP8 q and k (OCP E4M3, E8M0 per 32 elements); "
+                         "P V, gates, linear branch and projections bf16",
+                 "value": B * L / (ms8 * 1e-3), "unit": "tokens/s", "ms_per_step": ms8,
+                 "steps": args.mxfp8_steps, "call_ms_median": round(median(call8), 3),
+                 "roofline": mx_roofline(ph8_ms["window_attn"]), "phases_ms": ph8_ms,
+                 "kernel_rooflines": phase_rooflines(cfg, ph8)}
+        del ws8
 
     result = {
         "metric": METRIC,
@@ -359,13 +402,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+mxfp8 scores" if args.softmax_mxfp8 else "bf16",
         "data": "synthetic (seeded; Q,V,x ~ N(0,1), K rows unit-norm, beta ~ U(0.1,1), gamma ~ U(0.9,1), W ~ N(0,0.02^2))",
         "config": {"workload": cfg.name, "batch": B, "heads": cfg.heads, "head_dim": cfg.head_dim,
                    "frames": cfg.frames, "tokens_per_frame": cfg.tokens_per_frame, "tokens": B * L,
                    "chunk_frames": cfg.chunk_frames, "window_chunks": cfg.window_chunks,
                    "anchors": "first+last", "softmax_density": round(density, 5)},
-        "roofline": {"bound": "mfma", "kernel": "window_attn", "achieved": round(achieved, 2),
+        "roofline": mx_roofline(attn_avg_ms) if args.softmax_mxfp8 else
+                    {"bound": "mfma", "kernel": "window_attn", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
                      "traffic": window_traffic(cfg.name)},
@@ -374,6 +418,8 @@ def main():
         "call_ms_min": round(min(call_ms), 3),
         "phases_ms": phase_ms,
     }
+    if mxfp8 is not None:
+        result["mxfp8_softmax"] = mxfp8
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)
