@@ -130,8 +130,14 @@ def phase_rooflines(cfg, phases):
     mfma("out_gemm", 2.0 * B * L * 2 * D * D)
     t = ms("vda_scan")
     if t:
+        # per frame-head and direction: M_t and B_t read (fp32), S_t written as fp32 and (bf16 I/O)
+        # as hi/lo bf16 pairs
+        scan_bytes = 2 * frames * (2 * d * d * 4 + d * d * 4 + (2 * d * d * 2 if es == 2 else 0))
         out["vda_scan"] = {"bound": "latency", "ms": round(t, 3), "frame_steps": T,
-                           "us_per_step": round(t * 1e3 / T, 2)}
+                           "us_per_step": round(t * 1e3 / T, 2),
+                           "algorithmic_gb": round(scan_bytes / 1e9, 3),
+                           "achieved_gbs": round(scan_bytes / (t * 1e-3) / 1e9, 1),
+                           "frac_of_hbm_peak": round(scan_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     t = ms("vda_solve")
     if t:
         out["vda_solve"] = {"bound": "latency", "ms": round(t, 3), "systems": frames,
