@@ -75,10 +75,23 @@ __all__ = [
 # --------------------------------------------------------------------------
 
 
-def mxfp8_values(x):
-    """Values of the MXFP8 encoding of x along its last axis (oracle.mxfp8)."""
+def mxfp8_values(x, mul=None):
+    """Values of the MXFP8 encoding of x along its last axis (oracle.mxfp8);
+    with mul, of the fp32 product x * mul (rounded to nearest)."""
     from oracle import mxfp8
+    if mul is not None:
+        x = (np.asarray(x, dtype=np.float32) * np.float32(mul)).astype(np.float64)
     return mxfp8.dequantize(*mxfp8.quantize(x))
+
+
+def score_scale_log2_fp32(d, scale=None):
+    """The softmax scale in log2 units as an fp32 value, formed like the
+    path forms it: fp32(scale) * fp32(log2 e), scale = 1 / sqrt(d) in fp32
+    unless given.  Reading F-1: the MXFP8 mode multiplies q by it before the
+    encoding, so the products of the decoded q and k are logits in log2
+    units."""
+    s = np.float32(1.0) / np.sqrt(np.float32(d)) if scale is None else np.float32(scale)
+    return np.float32(s * np.float32(1.4426950408889634))
 
 def frame_stats(k_t: np.ndarray, v_t: np.ndarray, beta_t: float):
     """Frame statistics of one frame and head.
@@ -313,9 +326,10 @@ def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
     The linear branch still needs every frame's state (full scans); the
     softmax branch, gates and projections are evaluated only at `rows`.
     `states` may carry precomputed (s_fwd, s_bwd) of shape [B, H, T, d, d].
-    softmax_mxfp8: the softmax branch scores the MXFP8 values of q and k
-    (oracle.mxfp8: OCP MXFP8 along head_dim; [P3] 实验结果 runs the denoiser
-    in MXFP8), the linear branch keeps q and k as given.
+    softmax_mxfp8: the softmax branch scores the MXFP8 values of c * q
+    (c = score_scale_log2_fp32) and k (oracle.mxfp8: OCP MXFP8 along head_dim;
+    [P3] 实验结果 runs the denoiser in MXFP8), i.e. logits ln(2) * (q8 . k8);
+    the linear branch keeps q and k as given.
     Returns out [B, len(rows), D].
     """
     # q, k, v are converted to float64 one (batch, head) slice at a time so that
@@ -335,7 +349,8 @@ def hybrid_layer_rows(x, q, k, v, gamma, beta, w_gs, w_gl, rms_w, w_os, w_ol,
         for h in range(H):
             qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
             if softmax_mxfp8:
-                o, _ = window_attention(mxfp8_values(qh), mxfp8_values(kh), vh, allowed, scale, rows)
+                c = score_scale_log2_fp32(d, None if scale == 1.0 / np.sqrt(d) else scale)
+                o, _ = window_attention(mxfp8_values(qh, c), mxfp8_values(kh), vh, allowed, np.log(2.0), rows)
             else:
                 o, _ = window_attention(qh, kh, vh, allowed, scale, rows)
             y_s[b, :, h * d:(h + 1) * d] = o

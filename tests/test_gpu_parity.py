@@ -548,8 +548,8 @@ def test_context_config3_sampled(vdn):
 from oracle import mxfp8 as MX
 
 
-def mx_values(a):
-    return O.mxfp8_values(np.asarray(a, dtype=np.float64))
+def mx_values(a, mul=None):
+    return O.mxfp8_values(np.asarray(a, dtype=np.float64), mul)
 
 
 def test_mxfp8_quantize_bit_exact(vdn):
@@ -607,8 +607,9 @@ MXCASES = [
 
 @pytest.mark.parametrize("name,cfg,sharp", MXCASES, ids=[t[0] for t in MXCASES])
 def test_window_attn_mxfp8(vdn, name, cfg, sharp):
-    """Softmax branch with MXFP8 scores, gated and ungated, with lse; the same
-    result through the entry point that takes codes and scales."""
+    """Softmax branch with MXFP8 scores, gated and ungated, with lse: the mode
+    flag (q encoded as c * q, c the fp32 log2-unit scale) and the entry point
+    that takes the caller's codes of q and k, each against its own oracle."""
     log(f"[mxfp8 window] {name}")
     inp = gpu_inputs(cfg, with_layer=False, sharp=sharp)
     shape = vdn.shape_from_config(cfg, softmax_mxfp8=True)
@@ -623,28 +624,35 @@ def test_window_attn_mxfp8(vdn, name, cfg, sharp):
     torch.cuda.synchronize()
     allowed = O.allowed_frames(cfg.frames, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
                                cfg.anchor_last)
-    ref = np.zeros((B, Lt, H * d))
-    ref_lse = np.zeros((B, H, Lt))
-    for b in range(B):
-        for h in range(H):
-            q8 = mx_values(np32(inp["q"][b, h]))
-            k8 = mx_values(np32(inp["k"][b, h]))
-            v = np32(inp["v"][b, h]).astype(np.float64)
-            if cfg.context_tokens:
-                o, l = O.window_attention_ctx(q8, k8, v, allowed, N, 1 / np.sqrt(d))
-            else:
-                o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d))
-            ref[b, :, h * d:(h + 1) * d] = o.reshape(Lt, d)
-            ref_lse[b, h] = l
+    c = O.score_scale_log2_fp32(d)
+
+    def oracle(scaled):
+        ref = np.zeros((B, Lt, H * d))
+        ref_lse = np.zeros((B, H, Lt))
+        for b in range(B):
+            for h in range(H):
+                q8 = mx_values(np32(inp["q"][b, h]), c if scaled else None)
+                k8 = mx_values(np32(inp["k"][b, h]))
+                v = np32(inp["v"][b, h]).astype(np.float64)
+                sc = np.log(2.0) if scaled else 1 / np.sqrt(d)
+                if cfg.context_tokens:
+                    o, l = O.window_attention_ctx(q8, k8, v, allowed, N, sc)
+                else:
+                    o, l = O.window_attention(q8, k8, v, allowed, sc)
+                ref[b, :, h * d:(h + 1) * d] = o.reshape(Lt, d)
+                ref_lse[b, h] = l
+        return ref, ref_lse
+
+    ref, ref_lse = oracle(True)
     g = np32(gate).astype(np.float64)
     e1 = excess_err(np32(out), g * ref, "bf16")
     e2 = excess_err(np32(out_ng), ref, "bf16")
     e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
-    same = torch.equal(out, out_pre)
+    ref_pre, _ = oracle(False)
+    e4 = excess_err(np32(out_pre), g * ref_pre, "bf16")
     log(f"  gated {e1:.3e} ungated {e2:.3e} (plain {rel_err(np32(out_ng), ref):.3e}) lse abs {e3:.3e} "
-        f"codes entry identical {same}")
-    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"] and e3 <= 1e-2
-    assert same
+        f"codes entry {e4:.3e}")
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"] and e3 <= 1e-2 and e4 <= TOL["bf16"]
 
 
 def test_hybrid_mxfp8(vdn):
@@ -682,11 +690,12 @@ def test_window_attn_mxfp8_T102_two_heads_sampled(vdn):
     allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
     worst = 0.0
     for h in range(cfg.heads):
+        c = O.score_scale_log2_fp32(d)
         q8 = inp["q"][0, h].float().cpu().numpy().astype(np.float64)
-        q8.reshape(-1, d)[rows] = mx_values(q8.reshape(-1, d)[rows])   # only the sampled queries are read
+        q8.reshape(-1, d)[rows] = mx_values(q8.reshape(-1, d)[rows], c)   # only the sampled queries are read
         k8 = mx_values(inp["k"][0, h].float().cpu().numpy())
         v = inp["v"][0, h].float().cpu().numpy().astype(np.float64)
-        o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d), rows)
+        o, l = O.window_attention(q8, k8, v, allowed, np.log(2.0), rows)
         e = rel_err(np32(out[0, rows, h * d:(h + 1) * d]), o)
         el = float(np.max(np.abs(np32(lse[0, h, rows]) - l)))
         log(f"  head {h}: rel err {e:.3e} lse abs {el:.3e} ({time.time() - t0:.1f}s)")
