@@ -42,10 +42,10 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy calibration
 # (profiles/window_attn_T102_counters.md).  Valid only for the kernel sources they were
 # taken on: reported as null once those sources change.
-WINDOW_TRAFFIC_BYTES = 260951900994
-WINDOW_MXFP8_TRAFFIC_BYTES = 185027972268   # the MXFP8-score kernel, same passes
+WINDOW_TRAFFIC_BYTES = 257156886872
+WINDOW_MXFP8_TRAFFIC_BYTES = 184544936788   # the MXFP8-score kernel, same passes
 WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
-WINDOW_TRAFFIC_SHA = "50c25d3f51c8ff8b"
+WINDOW_TRAFFIC_SHA = "5df1ca28a90a17d6"
 
 
 def frame_key_counts(T, C, W, a0, a1):

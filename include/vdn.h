@@ -165,8 +165,9 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
  * elements (along head_dim) in OCP FP8 E4M3 (bias 7, largest finite 448)
  * sharing one E8M0 scale 2^(code - 127).  With shape->softmax_mxfp8 = 1,
  * vdn_hybrid_attn_fwd, window_anchor_attn_fwd and vdn_dense_attn_fwd quantise
- * their bf16 q and k into the workspace (vdn_workspace_bytes grows by
- * 2 * B*H*Lt*(d + d/32) bytes) and use these scores. */
+ * their bf16 k and c * q into the workspace, c = scale * log2(e) in fp32 (so
+ * the products are logits in log2 units; vdn_workspace_bytes grows by
+ * 2 * B*H*Lt*(d + d/32) bytes), and use these scores. */
 
 /* MXFP8 quantisation of n_elems bf16 values x (n_elems a non-negative
  * multiple of 32), block i = x[32 i .. 32 i + 31]: scales[i] = clamp(
@@ -182,7 +183,7 @@ int vdn_mxfp8_quantize(const void* x, int64_t n_elems, void* codes,
                        void* scales, void* stream);
 
 /* Softmax branch (10100.com article, 方法概述 part 1) with scores from
- * MXFP8 q and k given as codes [B, H, Lt, 128] (uint8 E4M3) and scales
+ * MXFP8 q and k (of q itself, not scaled) given as codes [B, H, Lt, 128] (uint8 E4M3) and scales
  * [B, H, Lt, 4] (uint8 E8M0), as vdn_mxfp8_quantize writes them; v, gate_s,
  * out and lse as window_anchor_attn_fwd.  shape->dtype must be VDN_BF16 and
  * head_dim 128 (VDN_ERR_DTYPE / VDN_ERR_BAD_SHAPE otherwise); the
