@@ -285,153 +285,6 @@ __global__ __launch_bounds__(512) void gemm_bf16_nt_big_kernel(const bf16* __res
   }
 }
 
-// Same tile, operands, ring and DMA as above with four waves (one per SIMD)
-// of 128 x 128: half the LDS fragment traffic per product (8 fragment reads
-// per 16 products instead of 6 per 8).  The 256 accumulator registers per
-// lane are fixed in the accumulator file by writing the products as inline
-// asm; fragment reads run half a slab ahead of their products.
-namespace gemm_w4 {
-using gemm_big::f32x16;
-constexpr int kWaitVm16 = 0x4F70;            // s_waitcnt vmcnt(16): the last two slabs' loads (8 per slab)
-__device__ __forceinline__ void mma(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-}  // namespace gemm_w4
-
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_nt_w4_kernel(const bf16* __restrict__ A,
-                                                              const bf16* __restrict__ Bt,
-                                                              bf16* __restrict__ C, int M, int N, int K,
-                                                              int64_t lda, int64_t ldb, int64_t ldc,
-                                                              int tiles_m, int tiles_n) {
-  using namespace gemm_big;
-  using gemm_w4::mma;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
-  const int tid = threadIdx.x, lane = tid % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int l32 = lane % 32, h = lane / 32;
-  const int wm = wave >> 1, wn = wave & 1;   // 128-row blocks of A and of Bt
-
-  const int total = tiles_m * tiles_n;
-  const int pid = xcd_remap(blockIdx.x, total);
-  const int group = pid / (GROUP_M * tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int in_group = pid - group * GROUP_M * tiles_n;
-  const int tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsize);
-  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
-  // DMA: wave w fills rows 64 w .. 64 w + 63 of each slab, four 16-row blocks
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + m0 * lda), (short)0, (int)(min((int64_t)BM, M - m0) * lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Bt + n0 * ldb), (short)0, (int)(min((int64_t)BN, N - n0) * ldb * 2), 0x00020000);
-  int offa[4], offb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 64 * wave + 16 * i + lane / 4;
-    const int c = swz(row, lane % 4);
-    offa[i] = (int)(row * lda * 2) + 16 * c;
-    offb[i] = (int)(row * ldb * 2) + 16 * c;
-  }
-  const int nk = K / BK;
-  auto issue = [&](int kt, int stage) {
-    const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)(ring + stage * STAGEB);
-    const int kb = kt * ROWB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * wave + i;
-      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offa[i]), "s"(ra), "s"(kb),
-                   "{m0}"(lds + blk * 1024)
-                   : "memory");
-      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offb[i]), "s"(rb), "s"(kb),
-                   "{m0}"(lds + TILEB + blk * 1024)
-                   : "memory");
-    }
-  };
-
-  f32x16 acc[4][4];   // acc[jn][im]: C^T block (n: 32 jn.., m: 32 im..) of this wave's 128 x 128
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x16{};
-  // the zeroed accumulators are read by the first products: fenced wait states
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 4");
-  __builtin_amdgcn_sched_barrier(0);
-
-  auto read_frags = [&](int stage, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
-    const unsigned char* sa = ring + stage * STAGEB;
-    const unsigned char* sb = sa + TILEB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rb_row = 128 * wn + 32 * i + l32;
-      fb[i] = *reinterpret_cast<const bf16x8*>(sb + rb_row * ROWB + 16 * swz(rb_row, 2 * ks + h));
-      const int ra_row = 128 * wm + 32 * i + l32;
-      fa[i] = *reinterpret_cast<const bf16x8*>(sa + ra_row * ROWB + 16 * swz(ra_row, 2 * ks + h));
-    }
-  };
-  auto products = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mma(acc[j][i], fb[j], fa[i]);
-  };
-  auto fence = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  for (int s = 0; s < 3; ++s)
-    if (s < nk) issue(s, s);
-  if (nk > 2) __builtin_amdgcn_s_waitcnt(gemm_w4::kWaitVm16);
-  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 3 < nk) issue(kt + 3, (kt + 3) % STAGES);
-    read_frags(kt % STAGES, 1, fa1, fb1);
-    fence();
-    products(fa0, fb0);
-    fence();
-    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(gemm_w4::kWaitVm16);
-    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (kt + 1 < nk) read_frags((kt + 1) % STAGES, 0, fa0, fb0);
-    fence();
-    products(fa1, fb1);
-  }
-  // the last products' results are read by vector instructions below
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-
-  // epilogue: acc[jn][im][4 r4 + e] = C[m0 + 128 wm + 32 im + l32][n0 + 128 wn + 32 jn + 8 r4 + 4 h + e]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + 128 * wm + 32 * i + l32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int64_t n = n0 + 128 * wn + 32 * j + 8 * r4 + 4 * h;
-        if (n >= N) continue;
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = acc[j][i][4 * r4 + e];
-          if (EPI == kEpiSigmoid) x = sigmoidf(x);
-          v[e] = (bf16)x;
-        }
-        *reinterpret_cast<bf16x4*>(C + m * ldc + n) = v;
-      }
-  }
-}
-
 // Eight waves as above with 64-wide K slabs in a two-stage ring (the same
 // 128 KB of LDS): half the barriers per product.  Rows of a slab are 128 bytes
 // (eight 16-byte chunks); chunk c of row r sits at c ^ ((r >> 1) & 7), so the
@@ -863,7 +716,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
 
 constexpr bool kGemmSlot = true;
 constexpr bool kGemmK64 = true;
-constexpr bool kGemmFourWaves = false;   // the eight-wave kernel measures faster on the layer shapes
 
 // the big-tile kernel's shape contract: bf16, K a multiple of 32, N of 8, 16-byte
 // aligned rows, and every operand tile's byte range below 2^31
@@ -918,13 +770,6 @@ hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, voi
             (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
       else
         gemm_bf16_nt_k64_kernel<kEpiStore><<<tm * tn, 512, 0, st>>>(
-            (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
-    } else if (kGemmFourWaves) {
-      if (epi == kEpiSigmoid)
-        gemm_bf16_nt_w4_kernel<kEpiSigmoid><<<tm * tn, 256, 0, st>>>(
-            (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
-      else
-        gemm_bf16_nt_w4_kernel<kEpiStore><<<tm * tn, 256, 0, st>>>(
             (const bf16*)A, (const bf16*)Bt, (bf16*)C, M, N, K, lda, ldb, ldc, tm, tn);
     } else {
       if (epi == kEpiSigmoid)
