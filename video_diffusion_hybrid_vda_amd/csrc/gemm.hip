@@ -6,6 +6,7 @@
 // MFMA fragments come straight from LDS rows.  Weights arrive as [D_in, D_out]
 // and are transposed once per call into the workspace (a few MB).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -728,17 +729,18 @@ static bool gemm_big_ok(int dtype, int M, int N, int K, int64_t lda, int64_t ldb
   return true;
 }
 
-// compute units of the current device, looked up once per device
+// compute units of the current device, looked up once per device (threads
+// that race on the first lookup store the same value)
 static int compute_units() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (!n) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t launch_transpose(int dtype, const void* src, void* dst, int rows, int cols,
