@@ -100,7 +100,8 @@ enum vdn_op {
   VDN_OP_HYBRID = 0,      /* vdn_hybrid_attn_fwd    */
   VDN_OP_VDA_SCAN = 1,    /* vda_scan_fwd           */
   VDN_OP_WINDOW_ATTN = 2, /* window_anchor_attn_fwd */
-  VDN_OP_DENSE_ATTN = 3   /* vdn_dense_attn_fwd     */
+  VDN_OP_DENSE_ATTN = 3,  /* vdn_dense_attn_fwd     */
+  VDN_OP_VDA_BWD = 4      /* vda_scan_bwd           */
 };
 
 typedef struct vdn_shape {
@@ -146,6 +147,26 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
                  const void* v, const float* gamma, const float* beta,
                  const float* rms_w, const void* gate_l, void* out,
                  float* states, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient of the linear branch (10100.com article, 方法概述 part 2, the
+ * delta rule, and part 3, RMSNorm per direction; the article's staged
+ * adaptation trains this branch).  For the ungated output
+ *   o[b, t*N+n, h*d+i] = (RMSNorm(S_fwd_t q) + RMSNorm(S_bwd_t q))_i
+ * of vda_scan_fwd (gate_l = NULL) and d_out = dLoss/do, the call writes
+ *   dq, dk, dv   [B, H, Lt, d]  dtype; zero on context rows
+ *   dgamma, dbeta [B, H, T]     float32
+ *   drms_w       [D]            float32 (may be NULL: not computed)
+ * d_out has the layout of out, [B, Lt, D] (its context rows are not read).
+ * The gradient is the derivative of the forward rule taken step by step in
+ * reverse (readout, both scans, the solve (I + A_t)^-1, the Gram products);
+ * the forward quantities are recomputed from q, k, v, gamma, beta in the
+ * workspace (op VDN_OP_VDA_BWD).  Arithmetic is fp32 throughout; rms_w may
+ * be NULL (ones).  batch * heads must not exceed 65535. */
+int vda_scan_bwd(const vdn_shape* shape, const void* q, const void* k,
+                 const void* v, const float* gamma, const float* beta,
+                 const float* rms_w, const void* d_out, void* dq, void* dk,
+                 void* dv, float* dgamma, float* dbeta, float* drms_w,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* Softmax branch alone (10100.com article, 方法概述 part 1):
  *   out[b, l, h*d+i] = gate_s * (softmax over allowed keys of

@@ -250,3 +250,41 @@ def test_mxfp8_mode_grows_the_workspace(vdn):
         grow = vdn.vdn_workspace_bytes(mx, op) - vdn.vdn_workspace_bytes(plain, op)
         assert extra <= grow <= extra + 4 * 256, (op, grow)
     assert vdn.vdn_workspace_bytes(mx, 1) == vdn.vdn_workspace_bytes(plain, 1)
+
+
+def test_vda_bwd_entry_rejects_bad_arguments(vdn):
+    fake = 1 << 20
+    ok = _shape(vdn)
+    need = vdn.vdn_workspace_bytes(ok, vdn.VDN_OP_VDA_BWD)
+    call = lambda s, *a: vdn._lib.vda_scan_bwd(ctypes.byref(s), *a)
+    # q k v gamma beta rms_w d_out dq dk dv dgamma dbeta drms_w | ws ws_bytes stream
+    args = [fake] * 13 + [fake, need, None]
+    for i in (0, 1, 2, 3, 4, 6, 7, 8, 9, 10, 11):                # rms_w and drms_w may be NULL
+        a = list(args)
+        a[i] = None
+        assert call(ok, *a) == -1, i
+    for i in (0, 5, 6, 12):
+        a = list(args)
+        a[i] = fake + 4                                           # misaligned
+        assert call(ok, *a) == -1, i
+    a = list(args)
+    a[14] = need - 1
+    assert call(ok, *a) == -4
+    a[13], a[14] = None, need
+    assert call(ok, *a) == -4
+    assert call(_shape(vdn, head_dim=48), *args) == -2
+    assert call(_shape(vdn, dtype=7), *args) == -3
+    assert call(vdn.make_shape(300, 300, 2, 4, 32, "bf16"), *args) == -2   # batch * heads > 65535
+
+
+def test_vda_bwd_workspace_holds_the_adjoint_buffers(vdn):
+    """The gradient's workspace holds 17 per-frame d x d fp32 matrices (recomputed
+    forward, both directions of the adjoint chain) and u / du of every token and
+    direction in fp32."""
+    B, H, T, N, d = 1, 24, 102, 4032, 128
+    s = vdn.make_shape(B, H, T, N, d, "bf16")
+    n = vdn.vdn_workspace_bytes(s, vdn.VDN_OP_VDA_BWD)
+    nf = B * H * T
+    low = 17 * nf * d * d * 4 + nf * 2 * N * d * 4
+    assert low <= n <= low + 32 * 256 + nf * (4 + 2 * d * 4) + 256
+    assert n % 256 == 0

@@ -1,0 +1,161 @@
+"""GPU parity of the linear-branch gradient (vda_scan_bwd) against the fp64
+oracle (oracle.vda_backward, pinned by finite differences of the forward
+oracle in test_vda_backward_oracle.py).
+
+Error measure, per output: max |gpu - oracle| / RMS(oracle), bounded by 2e-2
+for bf16 I/O and 1e-4 for fp32 I/O (fp32 arithmetic inside in both); for the
+bf16 outputs dq, dk, dv the bound applies to the error in excess of each
+element's own bf16 rounding (excess_err), as in the forward parity tests.  Small
+shapes are compared element by element for all six outputs; they span
+several 64-row product tiles with ragged tails (N = 70, 130, 100), head_dim
+32/64/128, batch > 1, frames with beta = 0, and context tokens (whose rows
+of dq, dk, dv must be zero).  The 102-frame headline shape is compared on
+whole heads: every gradient of one head depends on that head's inputs only.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.vda_backward import vda_branch_backward
+from video_diffusion_hybrid_vda_amd import synth
+from video_diffusion_hybrid_vda_amd.synth import VdnConfig
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vdn():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch: the HIP path cannot run")
+    from video_diffusion_hybrid_vda_amd import vdn as binding
+    return binding
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    """max |got - ref| / RMS(ref); where ref is exactly zero (dgamma of a single
+    frame: no previous state in either scan), max |got| itself."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    err = np.max(np.abs(got - ref))
+    return float(err / rms) if rms > 0 else float(err)
+
+
+def excess_err(got, ref, dtype):
+    """Error beyond each element's own bf16 rounding (half an ulp, 2^-9
+    relative) over RMS(ref); plain rel_err for fp32.  Gradients are heavy-
+    tailed (max/RMS near 10 at the headline shape), so the rounding of a
+    bf16 output alone reaches 2% of RMS."""
+    if dtype != "bf16":
+        return rel_err(got, ref)
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    exc = np.maximum(np.abs(got - ref) - 2.0 ** -9 * np.abs(ref), 0.0)
+    return float(np.max(exc) / np.sqrt(np.mean(ref * ref)))
+
+
+def grad_inputs(cfg, device):
+    """Seeded inputs of the linear branch plus an RMSNorm weight and an upstream
+    gradient d_out [B, Lt, D] of the output's dtype."""
+    inp = synth.make_inputs(cfg, device="cpu", with_layer=False)
+    B, H, d = cfg.batch, cfg.heads, cfg.head_dim
+    Lt = cfg.frames * cfg.tokens_per_frame + cfg.context_tokens
+    g = torch.Generator().manual_seed(cfg.seed + 77)
+    inp["rms_w"] = 0.5 + torch.rand(H * d, generator=g)
+    d_out = torch.randn(B, Lt, H * d, generator=g).to(synth.DTYPES[cfg.dtype])
+    return {k: v.to(device) for k, v in inp.items()}, d_out.to(device)
+
+
+def video(t, cfg):
+    """[B, H, Lt, d] -> the video rows as [B, H, T, N, d] (fp64)."""
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    return np64(t[:, :, :T * N]).reshape(B, H, T, N, d)
+
+
+def d_out_heads(d_out, cfg):
+    """[B, Lt, D] -> the video rows as [B, H, T, N, d] (fp64)."""
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    return np64(d_out[:, :T * N]).reshape(B, T, N, H, d).transpose(0, 3, 1, 2, 4)
+
+
+CASES = [
+    ("B2H2_T6_N6_d32_f32", VdnConfig(2, 2, 32, 6, 6, dtype="f32", seed=81)),
+    ("H2_T7_N70_d64_bf16", VdnConfig(1, 2, 64, 7, 70, dtype="bf16", seed=82)),
+    ("T5_N130_d128_bf16", VdnConfig(1, 1, 128, 5, 130, dtype="bf16", seed=83)),
+    ("T4_N100_d128_f32_beta0", VdnConfig(1, 1, 128, 4, 100, dtype="f32", beta_lo=0.0, seed=84)),
+    ("T1_N9_d64_f32", VdnConfig(1, 1, 64, 1, 9, dtype="f32", seed=85)),
+    ("H2_T6_N20_d32_ctx9_bf16", VdnConfig(1, 2, 32, 6, 20, dtype="bf16", context_tokens=9, seed=86)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_vda_backward_small(vdn, name, cfg):
+    log(f"[vda bwd] {name}")
+    inp, d_out = grad_inputs(cfg, "cuda")
+    if "beta0" in name:
+        inp["beta"][0, 0, 1] = 0.0
+    shape = vdn.shape_from_config(cfg)
+    got = vdn.vda_scan_grad(shape, inp, d_out)
+    torch.cuda.synchronize()
+    ref = vda_branch_backward(video(inp["q"], cfg), video(inp["k"], cfg), video(inp["v"], cfg),
+                              np64(inp["gamma"]), np64(inp["beta"]), np64(inp["rms_w"]), cfg.rms_eps,
+                              d_out_heads(d_out, cfg))
+    tol = TOL[cfg.dtype]
+    errs = {}
+    for n in ("q", "k", "v"):
+        errs[n] = excess_err(video(got[n], cfg), ref["d" + n], cfg.dtype)
+        if cfg.context_tokens:
+            L = cfg.frames * cfg.tokens_per_frame
+            assert torch.count_nonzero(got[n][:, :, L:]).item() == 0, n
+    errs["gamma"] = rel_err(np64(got["gamma"]), ref["dgamma"])
+    errs["beta"] = rel_err(np64(got["beta"]), ref["dbeta"])
+    errs["rms_w"] = rel_err(np64(got["rms_w"]), ref["drms_w"])
+    log("  " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    if "beta0" in name:
+        assert torch.count_nonzero(got["k"][0, 0, 100:200]).item() == 0
+        assert torch.count_nonzero(got["v"][0, 0, 100:200]).item() == 0
+
+
+def test_vda_backward_headline_two_heads(vdn):
+    """B1 H24 d128 T102 N4032 bf16, the launch the benchmark times: every
+    gradient of heads 0 and 23 against the oracle."""
+    cfg = synth.CONFIGS[4]
+    log(f"[vda bwd] {cfg.name}")
+    t0 = time.time()
+    inp, d_out = grad_inputs(cfg, "cuda")
+    shape = vdn.shape_from_config(cfg)
+    got = vdn.vda_scan_grad(shape, inp, d_out)
+    torch.cuda.synchronize()
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    T, N, d = cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    dh = d_out_heads(d_out, cfg)
+    for h in (0, 23):
+        sl = lambda t: np64(t[0:1, h:h + 1]).reshape(1, 1, T, N, d)
+        ref = vda_branch_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), np64(inp["gamma"][0:1, h:h + 1]),
+                                  np64(inp["beta"][0:1, h:h + 1]), np64(inp["rms_w"][h * d:(h + 1) * d]),
+                                  cfg.rms_eps, dh[0:1, h:h + 1])
+        plain = {n: rel_err(sl(got[n]), ref["d" + n]) for n in ("q", "k", "v")}
+        errs = {n: excess_err(sl(got[n]), ref["d" + n], "bf16") for n in ("q", "k", "v")}
+        errs["gamma"] = rel_err(np64(got["gamma"][0, h]), ref["dgamma"][0, 0])
+        errs["beta"] = rel_err(np64(got["beta"][0, h]), ref["dbeta"][0, 0])
+        errs["rms_w"] = rel_err(np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"])
+        log(f"  head {h}: " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items())
+            + " (plain " + " ".join(f"d{n} {e:.2e}" for n, e in plain.items()) + f") ({time.time() - t0:.1f}s)")
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (h, n, e)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdn.so")
-SOURCES = ["vdn_api.hip", "gemm.hip", "window_attn.hip", "vda.hip", "mxfp8.hip"]
+SOURCES = ["vdn_api.hip", "gemm.hip", "window_attn.hip", "vda.hip", "mxfp8.hip", "vda_bwd.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

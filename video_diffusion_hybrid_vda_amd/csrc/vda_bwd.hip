@@ -1,0 +1,461 @@
+// Gradient of the VDA linear branch (10100.com article on Video DeltaNet,
+// 方法概述 part 2: the frame-level delta rule; part 3: RMSNorm per direction
+// and the staged adaptation that trains this branch).  The pages give the
+// forward rule only; the kernels below evaluate its derivative, step by step
+// in reverse:
+//   readout  u = S_t q, r = u / rho, o = w (r_f + r_b):
+//            du = (w do - r mean(w do r)) / rho,  dq = S_f^T du_f + S_b^T du_b,
+//            dS_t = sum over the frame's tokens of du q^T,  dw = sum (r_f + r_b) do
+//   scan     S_t = X_t M_t, X_t = gamma_t S_prev + B_t:  G_t = dS_t + gamma_next dX_next,
+//            dX_t = G_t M_t^T,  dM_t = sum_dir X_t^T G_t,  dB_t = sum_dir dX_t,
+//            dgamma_t = sum_dir <dX_t, S_prev>
+//   solve    M_t = (I + A_t)^-1:  dA_t = -M_t^T dM_t M_t^T
+//   Gram     dK_t = beta_t (K_t (dA_t + dA_t^T) + V_t dB_t),  dV_t = beta_t K_t dB_t^T,
+//            dbeta_t = <dA_t, K_t^T K_t> + <dB_t, V_t^T K_t>
+//
+// Kernels:
+//   bgemm        batched fp32-accumulate product with strided, two-segment
+//                operands: every contraction above (token-side products and the
+//                per-frame d x d products)
+//   rms_bwd      per token and direction: du from u (in place) and partial dw
+//   scan_bwd     per (batch, head, direction, 16 state rows): the T-step adjoint chain
+//   frame_bwd    per frame: X_t of both directions, dB_t and dgamma_t
+//   sym_dbeta    per frame: dA_t + dA_t^T next to dB_t, and dbeta_t
+//   dw_reduce    sum of the partial RMSNorm-weight gradients
+#include <math.h>
+
+#include "vda_bwd.h"
+#include "vdn_common.h"
+
+namespace vdn {
+
+// ---------------------------------------------------------------------------
+// bgemm: C[z] = alpha * alpha_z[z] * sum_k A[z](m, k) B[z](k, n)  (+ C[z] if accumulate)
+// 64 x 64 output tile per workgroup of 256 threads (4 x 4 outputs per thread,
+// spread 16 apart so that LDS reads are conflict-free and each row of the
+// store is 16 consecutive elements), 16-deep k slabs staged through LDS in
+// fp32, the next slab loaded into registers while the current one is used.
+// Operand elements are fetched along the operand's unit-stride axis.
+namespace bg {
+constexpr int BM = 64, BN = 64, BK = 16, LDT = 64 + 4;
+}
+
+__device__ __forceinline__ void batch_index(const BGemm& p, int64_t z, int64_t& z0, int64_t& z1,
+                                            int64_t& z2) {
+  z0 = z % p.n0;
+  z1 = (z / p.n0) % p.n1;
+  z2 = z / ((int64_t)p.n0 * p.n1);
+}
+
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
+  using namespace bg;
+  __shared__ float As[BK][LDT];
+  __shared__ float Bs[BK][LDT];
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
+  const int64_t z = blockIdx.x / tiles;
+  const int tile = blockIdx.x % tiles;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  int64_t z0, z1, z2;
+  batch_index(p, z, z0, z1, z2);
+  const int64_t oa = z0 * p.sa[0] + z1 * p.sa[1] + z2 * p.sa[2];
+  const int64_t ob = z0 * p.sb[0] + z1 * p.sb[1] + z2 * p.sb[2];
+  const int64_t oc = z0 * p.sc[0] + z1 * p.sc[1] + z2 * p.sc[2];
+  const TA* a0 = (const TA*)p.a0 + oa;
+  const TA* a1 = (const TA*)(p.a1 ? p.a1 : p.a0) + oa;
+  const TB* b0 = (const TB*)p.b0 + ob;
+  const TB* b1 = (const TB*)(p.b1 ? p.b1 : p.b0) + ob;
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+
+  // element r of this thread's share of a slab: (row of the tile, k in the slab)
+  auto a_pos = [&](int r, int& mm, int& kk) {
+    const int e = tid + 256 * r;
+    if (p.a_kfast) { kk = e % BK; mm = e / BK; } else { mm = e % BM; kk = e / BM; }
+  };
+  auto b_pos = [&](int r, int& nn, int& kk) {
+    const int e = tid + 256 * r;
+    if (p.b_nfast) { nn = e % BN; kk = e / BN; } else { kk = e % BK; nn = e / BK; }
+  };
+  float ra[4], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int mm, kk;
+      a_pos(r, mm, kk);
+      const int m = m0 + mm, k = k0 + kk;
+      float x = 0.f;
+      if (m < p.M && k < p.K) {
+        const bool s1 = k >= p.ks;
+        x = to_f32((s1 ? a1 : a0)[m * p.sam + (s1 ? k - p.ks : k) * p.sak]);
+      }
+      ra[r] = x;
+      int nn;
+      b_pos(r, nn, kk);
+      const int n = n0 + nn, kb = k0 + kk;
+      float y = 0.f;
+      if (n < p.N && kb < p.K) {
+        const bool s1 = kb >= p.ks;
+        y = to_f32((s1 ? b1 : b0)[(s1 ? kb - p.ks : kb) * p.sbk + n * p.sbn]);
+      }
+      rb[r] = y;
+    }
+  };
+
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+  load(0);
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+    __syncthreads();   // the previous slab has been read
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int mm, kk;
+      a_pos(r, mm, kk);
+      As[kk][mm] = ra[r];
+      int nn;
+      b_pos(r, nn, kk);
+      Bs[kk][nn] = rb[r];
+    }
+    __syncthreads();
+    if (k0 + BK < p.K) load(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+  }
+
+  const float alpha = p.alpha * (p.alpha_z ? p.alpha_z[z] : 1.f);
+  TC* c = (TC*)p.c + oc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n >= p.N) continue;
+      const int64_t idx = m * p.ldc + n;
+      float val = alpha * acc[i][j];
+      if (p.accumulate) val += to_f32(c[idx]);
+      c[idx] = from_f32<TC>(val);
+    }
+  }
+}
+
+hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st) {
+  if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
+  if (p.ks <= 0) p.ks = p.K;
+  p.a_kfast = p.sak == 1;
+  p.b_nfast = p.sbn == 1;
+  const int64_t tiles = (int64_t)((p.M + bg::BM - 1) / bg::BM) * ((p.N + bg::BN - 1) / bg::BN);
+  const int64_t blocks = tiles * p.batch;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+#define VDN_BG(A, B, C) bgemm_kernel<A, B, C><<<(unsigned)blocks, 256, 0, st>>>(p)
+  // the combinations the gradient uses: bf16 or fp32 tokens against fp32 matrices
+  if (ta == 1 && tb == 0 && tc == 0) VDN_BG(bf16, float, float);
+  else if (ta == 0 && tb == 1 && tc == 0) VDN_BG(float, bf16, float);
+  else if (ta == 0 && tb == 0 && tc == 1) VDN_BG(float, float, bf16);
+  else if (ta == 1 && tb == 0 && tc == 1) VDN_BG(bf16, float, bf16);
+  else if (ta == 0 && tb == 0 && tc == 0) VDN_BG(float, float, float);
+  else return hipErrorInvalidValue;
+#undef VDN_BG
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sum over a workgroup of 256 threads (four waves); every thread gets the sum.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+  x = wave_sum(x);
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------------------
+// fill and per-frame scaling of the recomputed Gram products:
+// A_t = beta_t (K^T K)_t, B_t = beta_t (V^T K)_t
+__global__ __launch_bounds__(256) void fill_kernel(float* x, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = v;
+}
+
+__global__ __launch_bounds__(256) void scale_frames_kernel(const float* __restrict__ kk,
+                                                           const float* __restrict__ vk,
+                                                           const float* __restrict__ beta,
+                                                           float* __restrict__ am, float* __restrict__ bm,
+                                                           int64_t dd, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const float b = beta[i / dd];
+  am[i] = b * kk[i];
+  bm[i] = b * vk[i];
+}
+
+// ---------------------------------------------------------------------------
+// rms_bwd: workgroup (frame f, direction) walks the frame's N tokens, one wave
+// per token.  U holds u = S_t q on entry and du on exit, [frame][dir][N][D].
+// dw_part[f][dir][i] = sum over the frame's tokens of r_i do_i.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rms_bwd_kernel(float* __restrict__ U, const T* __restrict__ d_out,
+                                                      int64_t ldo, const float* __restrict__ rms_w,
+                                                      float* __restrict__ dw_part, int H, int T_, int N,
+                                                      int Lt, float eps) {
+  constexpr int PL = (D + kWave - 1) / kWave;   // elements per lane
+  __shared__ float red[4][D];
+  const int64_t f = blockIdx.x / 2;
+  const int dir = blockIdx.x % 2;
+  const int64_t bh = f / T_;
+  const int t = (int)(f % T_);
+  const int64_t b = bh / H;
+  const int h = (int)(bh % H);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  float w[PL], dw[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) {
+    const int c = lane + kWave * e;
+    w[e] = c < D ? (rms_w ? rms_w[h * D + c] : 1.f) : 0.f;
+    dw[e] = 0.f;
+  }
+  for (int n = wave; n < N; n += 4) {
+    float* u = U + ((f * 2 + dir) * N + n) * D;
+    const T* dor = d_out + (b * Lt + (int64_t)t * N + n) * ldo + (int64_t)h * D;
+    float uv[PL], dv[PL];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+      const int c = lane + kWave * e;
+      uv[e] = c < D ? u[c] : 0.f;
+      dv[e] = c < D ? to_f32(dor[c]) : 0.f;
+      ss += uv[e] * uv[e];
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / D + eps);
+    float gr = 0.f;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) gr += w[e] * dv[e] * uv[e] * inv;
+    const float mgr = wave_sum(gr) / D;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+      const int c = lane + kWave * e;
+      const float r = uv[e] * inv;
+      dw[e] += r * dv[e];
+      if (c < D) u[c] = (w[e] * dv[e] - r * mgr) * inv;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PL; ++e) {
+    const int c = lane + kWave * e;
+    if (c < D) red[wave][c] = dw[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 256)
+    dw_part[(f * 2 + dir) * D + c] = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+}
+
+// ---------------------------------------------------------------------------
+// scan_bwd: rows of G are independent given the M_t, as in the forward scan.
+// Workgroup (row block, batch-head, direction) walks the frames against the
+// direction that scan wrote them in.  dsg holds dS_t on entry and G_t on exit;
+// dx receives dX_t = G_t M_t^T; both [frame][dir][D][D].  Mt holds M_t^T.
+template <int D, int R>
+__global__ __launch_bounds__(256) void scan_bwd_kernel(const float* __restrict__ Mt,
+                                                       const float* __restrict__ gamma,
+                                                       float* __restrict__ dsg, float* __restrict__ dx,
+                                                       int T_) {
+  constexpr int TPR = 256 / R;     // threads per row
+  constexpr int CPT = D / TPR;     // columns per thread
+  __shared__ float Gs[R][D + 4];
+  const int tid = threadIdx.x;
+  const int row = tid / TPR, col0 = (tid % TPR) * CPT;
+  const int r0 = blockIdx.x * R;
+  const int64_t bh = blockIdx.y;
+  const int dir = blockIdx.z;
+  float carry[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) carry[c] = 0.f;
+  for (int step = 0; step < T_; ++step) {
+    const int t = dir ? step : T_ - 1 - step;
+    const int64_t f = bh * T_ + t;
+    const int64_t off = ((f * 2 + dir) * D + r0 + row) * D + col0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const float g = dsg[off + c] + carry[c];
+      dsg[off + c] = g;
+      Gs[row][col0 + c] = g;
+    }
+    __syncthreads();
+    const float* mt = Mt + f * D * D + col0;
+    float acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+    for (int j = 0; j < D; ++j) {
+      const float gj = Gs[row][j];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(gj, mt[j * D + c], acc[c]);
+    }
+    const float gm = gamma[f];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      dx[off + c] = acc[c];
+      carry[c] = gm * acc[c];
+    }
+    __syncthreads();   // Gs is rewritten by the next frame
+  }
+}
+
+// ---------------------------------------------------------------------------
+// frame_bwd: per frame f, X_t = gamma_t S_prev + B_t for both directions
+// (S_prev = S_{t-1} forward, S_{t+1} backward, zero past the ends), into
+// xs[f][dir]; dB_t = dX_f + dX_b into cdb[f][1]; dgamma_t.
+__global__ __launch_bounds__(256) void frame_bwd_kernel(const float* __restrict__ states,
+                                                        const float* __restrict__ bm,
+                                                        const float* __restrict__ gamma,
+                                                        const float* __restrict__ dx, float* __restrict__ xs,
+                                                        float* __restrict__ cdb, float* __restrict__ dgamma,
+                                                        int T_, int64_t nf, int64_t dd) {
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x;
+  const int t = (int)(f % T_);
+  const float g = gamma[f];
+  const float* sf = t > 0 ? states + (f - 1) * dd : nullptr;
+  const float* sb = t < T_ - 1 ? states + (nf + f + 1) * dd : nullptr;
+  float part = 0.f;
+  for (int64_t e = threadIdx.x; e < dd; e += 256) {
+    const float xf = dx[(f * 2) * dd + e], xb = dx[(f * 2 + 1) * dd + e];
+    const float pf = sf ? sf[e] : 0.f, pb = sb ? sb[e] : 0.f;
+    const float bt = bm[f * dd + e];
+    xs[(f * 2) * dd + e] = g * pf + bt;
+    xs[(f * 2 + 1) * dd + e] = g * pb + bt;
+    cdb[(f * 2 + 1) * dd + e] = xf + xb;
+    part += xf * pf + xb * pb;
+  }
+  part = block_sum(part, red);
+  if (threadIdx.x == 0) dgamma[f] = part;
+}
+
+// ---------------------------------------------------------------------------
+// sym_dbeta: per frame, cdb[f][0] = dA_t + dA_t^T and
+// dbeta_t = <dA_t, K^T K> + <dB_t, V^T K> (kk, vk: the Gram products without beta).
+template <int D>
+__global__ __launch_bounds__(256) void sym_dbeta_kernel(const float* __restrict__ dA,
+                                                        const float* __restrict__ kk,
+                                                        const float* __restrict__ vk,
+                                                        float* __restrict__ cdb, float* __restrict__ dbeta) {
+  constexpr int DD = D * D;
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x;
+  const float* a = dA + f * DD;
+  float part = 0.f;
+  for (int e = threadIdx.x; e < DD; e += 256) {
+    const int i = e / D, j = e % D;
+    const float x = a[e];
+    cdb[(f * 2) * DD + e] = x + a[j * D + i];
+    part += x * kk[f * DD + e] + cdb[(f * 2 + 1) * DD + e] * vk[f * DD + e];
+  }
+  part = block_sum(part, red);
+  if (threadIdx.x == 0) dbeta[f] = part;
+}
+
+// dw_reduce: drms_w[h*D + i] = sum over batch, frame and direction of dw_part.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
+                                                        float* __restrict__ drms_w, int B, int H, int T_,
+                                                        int D) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H * D) return;
+  const int h = idx / D, i = idx % D;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T_; ++t) {
+      const int64_t f = ((int64_t)b * H + h) * T_ + t;
+      s += part[(f * 2) * D + i] + part[(f * 2 + 1) * D + i];
+    }
+  drms_w[idx] = s;
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_fill(float* x, float v, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_frames(const float* kk, const float* vk, const float* beta, float* am,
+                               float* bm, int64_t nf, int64_t dd, hipStream_t st) {
+  const int64_t total = nf * dd;
+  if (total <= 0) return hipSuccess;
+  scale_frames_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(kk, vk, beta, am, bm, dd, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_bwd(int dtype, int d, float* U, const void* d_out, int64_t ldo,
+                          const float* rms_w, float* dw_part, int64_t nf, int H, int T, int N, int Lt,
+                          float eps, hipStream_t st) {
+  if (nf <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)(nf * 2);
+#define VDN_RB(TT, DD) \
+  rms_bwd_kernel<TT, DD><<<blocks, 256, 0, st>>>(U, (const TT*)d_out, ldo, rms_w, dw_part, H, T, N, Lt, eps)
+  if (dtype == 1) {
+    if (d == 32) VDN_RB(bf16, 32); else if (d == 64) VDN_RB(bf16, 64); else VDN_RB(bf16, 128);
+  } else {
+    if (d == 32) VDN_RB(float, 32); else if (d == 64) VDN_RB(float, 64); else VDN_RB(float, 128);
+  }
+#undef VDN_RB
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd(int d, const float* Mt, const float* gamma, float* dsg, float* dx, int BH,
+                           int T, hipStream_t st) {
+  if (BH <= 0) return hipSuccess;
+  constexpr int R = 16;
+  dim3 grid(d / R, BH, 2);
+  if (d == 32) scan_bwd_kernel<32, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
+  else if (d == 64) scan_bwd_kernel<64, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
+  else scan_bwd_kernel<128, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_bwd(const float* states, const float* bm, const float* gamma, const float* dx,
+                            float* xs, float* cdb, float* dgamma, int T, int64_t nf, int d,
+                            hipStream_t st) {
+  if (nf <= 0) return hipSuccess;
+  frame_bwd_kernel<<<(unsigned)nf, 256, 0, st>>>(states, bm, gamma, dx, xs, cdb, dgamma, T, nf,
+                                                 (int64_t)d * d);
+  return hipGetLastError();
+}
+
+hipError_t launch_sym_dbeta(int d, const float* dA, const float* kk, const float* vk, float* cdb,
+                            float* dbeta, int64_t nf, hipStream_t st) {
+  if (nf <= 0) return hipSuccess;
+  if (d == 32) sym_dbeta_kernel<32><<<(unsigned)nf, 256, 0, st>>>(dA, kk, vk, cdb, dbeta);
+  else if (d == 64) sym_dbeta_kernel<64><<<(unsigned)nf, 256, 0, st>>>(dA, kk, vk, cdb, dbeta);
+  else sym_dbeta_kernel<128><<<(unsigned)nf, 256, 0, st>>>(dA, kk, vk, cdb, dbeta);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const float* part, float* drms_w, int B, int H, int T, int d,
+                            hipStream_t st) {
+  const int n = H * d;
+  dw_reduce_kernel<<<(n + 255) / 256, 256, 0, st>>>(part, drms_w, B, H, T, d);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

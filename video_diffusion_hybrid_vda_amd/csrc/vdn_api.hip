@@ -10,6 +10,7 @@
 #include <mutex>
 #include <vector>
 
+#include "vda_bwd.h"
 #include "vdn.h"
 #include "vdn_internal.h"
 
@@ -150,6 +151,39 @@ VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   return l;
 }
 
+// Gradient of the linear branch: recomputed forward quantities, the adjoint
+// chain's per-frame matrices ([frame][direction][d][d] where both directions
+// are kept) and the token-side buffer U = S q, then du, [frame][direction][N][d].
+struct VdaBwdLayout {
+  size_t ones, kk, vk, am, bm, states, dsg, dx, xs, dm, p, da, cdb, u, dwp, flag, total;
+};
+VdaBwdLayout vda_bwd_layout(const vdn_shape* s) {
+  const size_t d = s->head_dim, dd = d * d;
+  const size_t nf = (size_t)s->batch * s->heads * s->frames;
+  const size_t N = s->tokens_per_frame;
+  VdaBwdLayout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  l.ones = take(nf * 4);             // beta = 1 for the recomputed Gram products
+  l.kk = take(nf * dd * 4);          // K^T K
+  l.vk = take(nf * dd * 4);          // V^T K
+  l.am = take(nf * dd * 4);          // A_t, then M_t^T
+  l.bm = take(nf * dd * 4);          // B_t
+  l.states = take(2 * nf * dd * 4);  // S_t of both scans, [dir][frame]
+  l.dsg = take(2 * nf * dd * 4);     // dS_t, then G_t
+  l.dx = take(2 * nf * dd * 4);      // dX_t
+  l.xs = take(2 * nf * dd * 4);      // X_t
+  l.dm = take(nf * dd * 4);          // dM_t
+  l.p = take(nf * dd * 4);           // M_t^T dM_t
+  l.da = take(nf * dd * 4);          // dA_t
+  l.cdb = take(2 * nf * dd * 4);     // [dA_t + dA_t^T, dB_t]
+  l.u = take(nf * 2 * N * d * 4);    // u, then du
+  l.dwp = take(nf * 2 * d * 4);      // partial RMSNorm-weight gradients
+  l.flag = take(kAlign);
+  l.total = off;
+  return l;
+}
+
 struct AttnLayout {
   size_t part_o, part_ml, qc, qs, kc, ks, total;
 };
@@ -238,12 +272,16 @@ int check_params(const vdn_shape* s, const float* gamma, const float* beta, char
 // ---- opt-in phase timing: HIP event pairs recorded around each phase
 enum Phase {
   kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhAnchorMerge, kPhGram, kPhSolve, kPhScan,
-  kPhReadout, kPhOutGemm, kPhQuantize, kNumPhases
+  kPhReadout, kPhOutGemm, kPhQuantize, kPhBwdRecompute, kPhBwdU, kPhBwdRms, kPhBwdDq, kPhBwdDs,
+  kPhBwdScan, kPhBwdFrame, kPhBwdKv, kPhBwdDw, kNumPhases
 };
 const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "window_attn",
                                              "anchor_merge",      "vda_gram",  "vda_solve",
                                              "vda_scan",          "vda_readout", "out_gemm",
-                                             "mxfp8_quantize"};
+                                             "mxfp8_quantize", "bwd_recompute", "bwd_u_gemm",
+                                             "bwd_rms",        "bwd_dq_gemm", "bwd_ds_gemm",
+                                             "bwd_scan",       "bwd_frame",   "bwd_kv_gemm",
+                                             "bwd_dw"};
 
 struct Timer {
   std::mutex mu;
@@ -324,6 +362,155 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   return VDN_OK;
 }
 
+// Gradient of the linear branch on already validated arguments: the forward
+// quantities are recomputed (Gram products without beta, then scaled), then
+// the adjoint runs readout -> scans -> solve -> Gram.
+int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v, const float* gamma,
+                const float* beta, const float* rms_w, const void* d_out, void* dq, void* dk, void* dv,
+                float* dgamma, float* dbeta, float* drms_w, char* ws, hipStream_t st) {
+  const VdaBwdLayout l = vda_bwd_layout(s);
+  float* ones = (float*)(ws + l.ones);
+  float* kk = (float*)(ws + l.kk);
+  float* vk = (float*)(ws + l.vk);
+  float* am = (float*)(ws + l.am);
+  float* bm = (float*)(ws + l.bm);
+  float* states = (float*)(ws + l.states);
+  float* dsg = (float*)(ws + l.dsg);
+  float* dx = (float*)(ws + l.dx);
+  float* xs = (float*)(ws + l.xs);
+  float* dm = (float*)(ws + l.dm);
+  float* pm = (float*)(ws + l.p);
+  float* da = (float*)(ws + l.da);
+  float* cdb = (float*)(ws + l.cdb);
+  float* u = (float*)(ws + l.u);
+  float* dwp = (float*)(ws + l.dwp);
+  const int dt = s->dtype, d = s->head_dim, H = s->heads, T = s->frames, N = s->tokens_per_frame;
+  const int L = T * N, Lt = L + s->context_tokens, BH = s->batch * H;
+  const int64_t nf = (int64_t)BH * T, dd = (int64_t)d * d, Nd = (int64_t)N * d, Ltd = (int64_t)Lt * d;
+  const int es = dt == VDN_BF16 ? 2 : 4;
+  hipError_t e = hipSuccess;
+  auto step = [&](int phase, const char* what, auto&& body) -> int {
+    const int ph = phase_begin(phase, st);
+    e = body();
+    phase_end(ph, st);
+    return e == hipSuccess ? VDN_OK : hip_fail(e, what);
+  };
+  int rc;
+  if (s->context_tokens > 0) {
+    // the linear branch does not read context rows: their gradient is zero
+    for (void* g : {dq, dk, dv}) {
+      e = launch_zero_rows(g, BH, Lt, L, s->context_tokens, d, d, es, st);
+      if (e != hipSuccess) return hip_fail(e, "zero fill launch");
+    }
+  }
+  rc = step(kPhBwdRecompute, "vda_bwd recompute", [&] {
+    hipError_t r = launch_fill(ones, 1.f, nf, st);
+    if (r == hipSuccess) r = launch_vda_gram(dt, d, k, v, ones, kk, vk, (int)nf, T, N, Lt, st);
+    if (r == hipSuccess) r = launch_scale_frames(kk, vk, beta, am, bm, nf, dd, st);
+    if (r == hipSuccess) r = launch_vda_solve(d, am, (int)nf, st);
+    if (r == hipSuccess) r = launch_vda_scan(d, am, bm, gamma, states, nullptr, BH, T, st);
+    return r;
+  });
+  if (rc != VDN_OK) return rc;
+
+  // U[f][dir] = Q_t S_dir,t^T
+  BGemm g;
+  g.a0 = q; g.b0 = states; g.c = u;
+  g.M = N; g.N = d; g.K = d;
+  g.sam = d; g.sak = 1; g.sbk = 1; g.sbn = d; g.ldc = d;
+  g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
+  g.sa[0] = 0; g.sa[1] = Nd; g.sa[2] = Ltd;
+  g.sb[0] = nf * dd; g.sb[1] = dd; g.sb[2] = T * dd;
+  g.sc[0] = Nd; g.sc[1] = 2 * Nd; g.sc[2] = T * 2 * Nd;
+  rc = step(kPhBwdU, "vda_bwd u launch", [&] { return launch_bgemm(dt, 0, 0, g, st); });
+  if (rc != VDN_OK) return rc;
+  rc = step(kPhBwdRms, "vda_bwd rms launch", [&] {
+    return launch_rms_bwd(dt, d, u, d_out, (int64_t)H * d, rms_w, dwp, nf, H, T, N, Lt, s->rms_eps, st);
+  });
+  if (rc != VDN_OK) return rc;
+
+  // dq = du_f S_f + du_b S_b (K = 2d over the two directions)
+  g = BGemm();
+  g.a0 = u; g.a1 = u + Nd; g.b0 = states; g.b1 = states + nf * dd; g.c = dq;
+  g.M = N; g.N = d; g.K = 2 * d; g.ks = d;
+  g.sam = d; g.sak = 1; g.sbk = d; g.sbn = 1; g.ldc = d;
+  g.batch = nf; g.n0 = T; g.n1 = 1;
+  g.sa[0] = 2 * Nd; g.sa[2] = T * 2 * Nd;
+  g.sb[0] = dd; g.sb[2] = T * dd;
+  g.sc[0] = Nd; g.sc[2] = Ltd;
+  rc = step(kPhBwdDq, "vda_bwd dq launch", [&] { return launch_bgemm(0, 0, dt, g, st); });
+  if (rc != VDN_OK) return rc;
+
+  // dS[f][dir] = du^T Q_t (sum over the frame's tokens)
+  g = BGemm();
+  g.a0 = u; g.b0 = q; g.c = dsg;
+  g.M = d; g.N = d; g.K = N;
+  g.sam = 1; g.sak = d; g.sbk = d; g.sbn = 1; g.ldc = d;
+  g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
+  g.sa[0] = Nd; g.sa[1] = 2 * Nd; g.sa[2] = T * 2 * Nd;
+  g.sb[0] = 0; g.sb[1] = Nd; g.sb[2] = Ltd;
+  g.sc[0] = dd; g.sc[1] = 2 * dd; g.sc[2] = T * 2 * dd;
+  rc = step(kPhBwdDs, "vda_bwd dS launch", [&] { return launch_bgemm(0, dt, 0, g, st); });
+  if (rc != VDN_OK) return rc;
+
+  rc = step(kPhBwdScan, "vda_bwd scan launch", [&] { return launch_scan_bwd(d, am, gamma, dsg, dx, BH, T, st); });
+  if (rc != VDN_OK) return rc;
+
+  rc = step(kPhBwdFrame, "vda_bwd frame launch", [&] {
+    hipError_t r = launch_frame_bwd(states, bm, gamma, dx, xs, cdb, dgamma, T, nf, d, st);
+    // dM = sum_dir X^T G (K = 2d over the stacked directions)
+    BGemm m;
+    m.a0 = xs; m.b0 = dsg; m.c = dm;
+    m.M = d; m.N = d; m.K = 2 * d;
+    m.sam = 1; m.sak = d; m.sbk = d; m.sbn = 1; m.ldc = d;
+    m.batch = nf; m.n0 = T; m.n1 = 1;
+    m.sa[0] = 2 * dd; m.sa[2] = T * 2 * dd;
+    m.sb[0] = 2 * dd; m.sb[2] = T * 2 * dd;
+    m.sc[0] = dd; m.sc[2] = T * dd;
+    if (r == hipSuccess) r = launch_bgemm(0, 0, 0, m, st);
+    // P = M^T dM, then dA = -P M^T (am holds M^T)
+    m = BGemm();
+    m.a0 = am; m.b0 = dm; m.c = pm;
+    m.M = d; m.N = d; m.K = d;
+    m.sam = d; m.sak = 1; m.sbk = d; m.sbn = 1; m.ldc = d;
+    m.batch = nf; m.n0 = T; m.n1 = 1;
+    m.sa[0] = dd; m.sa[2] = T * dd;
+    m.sb[0] = dd; m.sb[2] = T * dd;
+    m.sc[0] = dd; m.sc[2] = T * dd;
+    if (r == hipSuccess) r = launch_bgemm(0, 0, 0, m, st);
+    m.a0 = pm; m.b0 = am; m.c = da; m.alpha = -1.f;
+    if (r == hipSuccess) r = launch_bgemm(0, 0, 0, m, st);
+    if (r == hipSuccess) r = launch_sym_dbeta(d, da, kk, vk, cdb, dbeta, nf, st);
+    return r;
+  });
+  if (rc != VDN_OK) return rc;
+
+  rc = step(kPhBwdKv, "vda_bwd dk/dv launch", [&] {
+    // dK = beta (K (dA + dA^T) + V dB)  (K = 2d over [K | V] and [dA + dA^T ; dB])
+    BGemm m;
+    m.a0 = k; m.a1 = v; m.b0 = cdb; m.b1 = cdb + dd; m.c = dk;
+    m.M = N; m.N = d; m.K = 2 * d; m.ks = d;
+    m.sam = d; m.sak = 1; m.sbk = d; m.sbn = 1; m.ldc = d;
+    m.batch = nf; m.n0 = T; m.n1 = 1;
+    m.sa[0] = Nd; m.sa[2] = Ltd;
+    m.sb[0] = 2 * dd; m.sb[2] = T * 2 * dd;
+    m.sc[0] = Nd; m.sc[2] = Ltd;
+    m.alpha_z = beta;
+    hipError_t r = launch_bgemm(dt, 0, dt, m, st);
+    // dV = beta K dB^T
+    m.a1 = nullptr; m.b0 = cdb + dd; m.b1 = nullptr; m.c = dv;
+    m.K = d; m.ks = 0; m.sbk = 1; m.sbn = d;
+    if (r == hipSuccess) r = launch_bgemm(dt, 0, dt, m, st);
+    return r;
+  });
+  if (rc != VDN_OK) return rc;
+  if (drms_w) {
+    rc = step(kPhBwdDw, "vda_bwd dw launch", [&] { return launch_dw_reduce(dwp, drms_w, s->batch, H, T, d, st); });
+    if (rc != VDN_OK) return rc;
+  }
+  return VDN_OK;
+}
+
 // Softmax branch.  With s->softmax_mxfp8, q and k are quantised into the
 // workspace first, unless qs / ks already point at MXFP8 scales (then q and k
 // are the codes).
@@ -388,6 +575,7 @@ size_t vdn_workspace_bytes(const vdn_shape* shape, int op) {
     case VDN_OP_VDA_SCAN: n = vda_layout(shape, true).total; break;
     case VDN_OP_WINDOW_ATTN: n = attn_layout(shape, p).total; break;
     case VDN_OP_DENSE_ATTN: n = dense_layout(shape).total; break;
+    case VDN_OP_VDA_BWD: n = vda_bwd_layout(shape).total; break;
     default: fail(VDN_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
   // Never 0 for a valid request, so that 0 always signals an error.
@@ -414,6 +602,31 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k, const voi
   const int64_t D = (int64_t)shape->heads * shape->head_dim;
   return run_vda(shape, q, k, v, gamma, beta, rms_w, gate_l, D, out, D, states, (char*)ws,
                  (hipStream_t)stream);
+}
+
+int vda_scan_bwd(const vdn_shape* shape, const void* q, const void* k, const void* v,
+                 const float* gamma, const float* beta, const float* rms_w, const void* d_out,
+                 void* dq, void* dk, void* dv, float* dgamma, float* dbeta, float* drms_w, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!q || !k || !v || !gamma || !beta || !d_out || !dq || !dk || !dv || !dgamma || !dbeta)
+    return fail(VDN_ERR_INVALID_ARG,
+                "vda_scan_bwd: q, k, v, gamma, beta, d_out, dq, dk, dv, dgamma and dbeta must be non-NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(d_out) || misaligned(dq) ||
+      misaligned(dk) || misaligned(dv) || misaligned(ws) || misaligned(gamma) || misaligned(beta) ||
+      misaligned(rms_w) || misaligned(dgamma) || misaligned(dbeta) || misaligned(drms_w))
+    return fail(VDN_ERR_INVALID_ARG, "vda_scan_bwd: device pointers must be 16-byte aligned");
+  if ((int64_t)shape->batch * shape->heads > 65535)
+    return fail(VDN_ERR_BAD_SHAPE, "vda_scan_bwd: batch * heads exceeds 65535");
+  const size_t need = vda_bwd_layout(shape).total;
+  if (!ws || ws_bytes < need)
+    return fail(VDN_ERR_WORKSPACE, "vda_scan_bwd: workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  rc = check_params(shape, gamma, beta, (char*)ws + vda_bwd_layout(shape).flag, (hipStream_t)stream);
+  if (rc != VDN_OK) return rc;
+  return run_vda_bwd(shape, q, k, v, gamma, beta, rms_w, d_out, dq, dk, dv, dgamma, dbeta, drms_w,
+                     (char*)ws, (hipStream_t)stream);
 }
 
 int window_anchor_attn_fwd(const vdn_shape* shape, const void* q, const void* k, const void* v,

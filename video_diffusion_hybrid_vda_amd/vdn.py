@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libvdn.so")
 
 VDN_F32, VDN_BF16 = 0, 1
-VDN_OP_HYBRID, VDN_OP_VDA_SCAN, VDN_OP_WINDOW_ATTN, VDN_OP_DENSE_ATTN = 0, 1, 2, 3
+VDN_OP_HYBRID, VDN_OP_VDA_SCAN, VDN_OP_WINDOW_ATTN, VDN_OP_DENSE_ATTN, VDN_OP_VDA_BWD = 0, 1, 2, 3, 4
 STATUS = {0: "VDN_OK", -1: "VDN_ERR_INVALID_ARG", -2: "VDN_ERR_BAD_SHAPE", -3: "VDN_ERR_DTYPE",
           -4: "VDN_ERR_WORKSPACE", -5: "VDN_ERR_HIP", -6: "VDN_ERR_PARAM_RANGE"}
 _TORCH_DTYPE = {VDN_F32: torch.float32, VDN_BF16: torch.bfloat16}
@@ -82,6 +82,8 @@ def _load():
     lib.vdn_hybrid_attn_fwd.restype = I
     lib.vda_scan_fwd.argtypes = [S] + [P] * 9 + [P, SZ, P]
     lib.vda_scan_fwd.restype = I
+    lib.vda_scan_bwd.argtypes = [S] + [P] * 13 + [P, SZ, P]
+    lib.vda_scan_bwd.restype = I
     lib.window_anchor_attn_fwd.argtypes = [S] + [P] * 6 + [P, SZ, P]
     lib.window_anchor_attn_fwd.restype = I
     lib.vdn_mxfp8_quantize.argtypes = [P, ctypes.c_int64, P, P, P]
@@ -107,7 +109,8 @@ _lib = _load()
 
 EXPORTS = ("vdn_workspace_bytes", "vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
            "vdn_dense_attn_fwd", "vdn_set_param_check", "vdn_last_error", "vdn_version",
-           "vdn_timing_start", "vdn_timing_stop", "vdn_mxfp8_quantize", "window_anchor_attn_mxfp8_fwd")
+           "vdn_timing_start", "vdn_timing_stop", "vdn_mxfp8_quantize", "window_anchor_attn_mxfp8_fwd",
+           "vda_scan_bwd")
 
 
 def _ptr(t):
@@ -146,8 +149,8 @@ def vdn_timing_start() -> int:
 
 def vdn_timing_stop() -> dict:
     """{phase name: (launches, total ms)} of the phases recorded since start."""
-    stats = (vdn_phase_stat * 16)()
-    n = _lib.vdn_timing_stop(stats, 16)
+    stats = (vdn_phase_stat * 32)()
+    n = _lib.vdn_timing_stop(stats, 32)
     if n < 0:
         raise VdnError(n, vdn_last_error())
     return {stats[i].name.decode(): (stats[i].launches, stats[i].total_ms) for i in range(n)}
@@ -177,6 +180,14 @@ def vda_scan_fwd(shape, q, k, v, gamma, beta, rms_w, gate_l, out, states, ws, st
     return _check(_lib.vda_scan_fwd(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(rms_w),
         _ptr(gate_l), _ptr(out), _ptr(states), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vda_scan_bwd(shape, q, k, v, gamma, beta, rms_w, d_out, dq, dk, dv, dgamma, dbeta, drms_w, ws,
+                 stream=None) -> int:
+    return _check(_lib.vda_scan_bwd(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(rms_w),
+        _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgamma), _ptr(dbeta), _ptr(drms_w), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -232,6 +243,21 @@ def vda_scan(shape, inp: dict, gate_l=None, with_states=False, ws=None, stream=N
     vda_scan_fwd(shape, inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], inp.get("rms_w"),
                  gate_l, out, states, ws, stream)
     return (out, states) if with_states else out
+
+
+def vda_scan_grad(shape, inp: dict, d_out, ws=None, stream=None) -> dict:
+    """Gradient of <d_out, ungated linear-branch output> with respect to q, k, v, gamma, beta and
+    the RMSNorm weight (d_out [B, Lt, D] like the forward output)."""
+    B, H, T, d = shape.batch, shape.heads, shape.frames, shape.head_dim
+    dev = inp["q"].device
+    g = {n: torch.empty_like(inp[n]) for n in ("q", "k", "v")}
+    g["gamma"] = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    g["beta"] = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    g["rms_w"] = torch.empty(H * d, dtype=torch.float32, device=dev)
+    ws = workspace(shape, VDN_OP_VDA_BWD, dev) if ws is None else ws
+    vda_scan_bwd(shape, inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], inp.get("rms_w"), d_out,
+                 g["q"], g["k"], g["v"], g["gamma"], g["beta"], g["rms_w"], ws, stream)
+    return g
 
 
 def window_attn(shape, inp: dict, gate_s=None, with_lse=False, ws=None, stream=None):
