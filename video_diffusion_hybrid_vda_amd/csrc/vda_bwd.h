@@ -27,10 +27,13 @@ struct BGemm {
   const float* alpha_z = nullptr;
   int accumulate = 0;
   int a_kfast = 0, b_nfast = 0;   // set by launch_bgemm
+  int vec = 0;                    // set by launch_bgemm: 16-byte vector loads allowed
 };
 
-// ta, tb, tc: 0 = fp32, 1 = bf16 element type of A, B, C
-hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st);
+// ta, tb, tc: 0 = fp32, 1 = bf16 element type of A, B, C.  mfma: run on bf16
+// MFMA with fp32 operands split into hi + lo bf16 (one operand must be bf16 or
+// C bf16); otherwise fp32 FMA.
+hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st, bool mfma = false);
 hipError_t launch_fill(float* x, float v, int64_t n, hipStream_t st);
 // am = beta_f kk, bm = beta_f vk over nf frames of dd elements
 hipError_t launch_scale_frames(const float* kk, const float* vk, const float* beta, float* am,

@@ -16,13 +16,17 @@
 // Kernels:
 //   bgemm        batched fp32-accumulate product with strided, two-segment
 //                operands: every contraction above (token-side products and the
-//                per-frame d x d products)
+//                per-frame d x d products); fp32 FMA
+//   bgemm_mfma   the same on bf16 MFMA with fp32 operands split into hi + lo
+//                bf16: the token-side products of bf16 I/O
 //   rms_bwd      per token and direction: du from u (in place) and partial dw
 //   scan_bwd     per (batch, head, direction, 16 state rows): the T-step adjoint chain
 //   frame_bwd    per frame: X_t of both directions, dB_t and dgamma_t
 //   sym_dbeta    per frame: dA_t + dA_t^T next to dB_t, and dbeta_t
 //   dw_reduce    sum of the partial RMSNorm-weight gradients
 #include <math.h>
+
+#include <type_traits>
 
 #include "vda_bwd.h"
 #include "vdn_common.h"
@@ -154,7 +158,258 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
   }
 }
 
-hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// bgemm_mfma: the same product on bf16 MFMA (v_mfma_f32_16x16x32_bf16) for the
+// token-side contractions of bf16 I/O.  An fp32 operand enters as the
+// unevaluated pair hi + lo of bf16 values (hi = bf16(x), lo = bf16(x - hi),
+// ~16 significant bits); a bf16 operand is exact.  Each product sums
+// hi*hi, and hi*lo / lo*hi for each split operand (lo*lo, ~2^-16 relative, is
+// dropped).  64 x BN output tile per workgroup (BN = 128 when the output is
+// that wide, so that each token row is read once), four waves of 32 x BN/2,
+// 64-deep k slabs staged in LDS as [row][k] bf16 (k contiguous,
+// rows padded to 144 bytes) so that each lane's 8-element fragment is one
+// 16-byte read; the next slab is loaded into registers while the current one
+// is multiplied.
+namespace bm {
+constexpr int BM = 64, BK = 64, LDK = BK + 8;   // output tile BM x BN, BN = 64 or 128
+}
+
+template <typename TA, typename TB, typename TC, int BN>
+__global__ __launch_bounds__(256) void bgemm_mfma_kernel(BGemm p) {
+  using bm::BM;
+  using bm::BK;
+  using bm::LDK;
+  constexpr int JT = BN / 32;   // 16-column MFMA tiles per wave (a wave covers BN / 2 columns)
+  constexpr int RB = BN / 64;   // 16-element runs of the B slab per thread
+  constexpr bool SA = sizeof(TA) == 4, SB = sizeof(TB) == 4;   // fp32 operands are split
+  // operand slabs; after the last slab the same bytes hold the fp32 output tile
+  constexpr int kOpBytes = (BM * LDK + BN * LDK + (SA ? BM * LDK : 0) + (SB ? BN * LDK : 0)) * 2;
+  constexpr int LDC = BN + 4;
+  constexpr int kCBytes = BM * LDC * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kOpBytes > kCBytes ? kOpBytes : kCBytes];
+  bf16* Ah = reinterpret_cast<bf16*>(smem);
+  bf16* Bh = Ah + BM * LDK;
+  bf16* Al = Bh + BN * LDK;
+  bf16* Bl = Al + (SA ? BM * LDK : 0);
+  float* Cs = reinterpret_cast<float*>(smem);
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
+  const int64_t z = blockIdx.x / tiles;
+  const int tile = blockIdx.x % tiles;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  int64_t z0, z1, z2;
+  batch_index(p, z, z0, z1, z2);
+  const int64_t oa = z0 * p.sa[0] + z1 * p.sa[1] + z2 * p.sa[2];
+  const int64_t ob = z0 * p.sb[0] + z1 * p.sb[1] + z2 * p.sb[2];
+  const int64_t oc = z0 * p.sc[0] + z1 * p.sc[1] + z2 * p.sc[2];
+  const TA* a0 = (const TA*)p.a0 + oa;
+  const TA* a1 = (const TA*)(p.a1 ? p.a1 : p.a0) + oa;
+  const TB* b0 = (const TB*)p.b0 + ob;
+  const TB* b1 = (const TB*)(p.b1 ? p.b1 : p.b0) + ob;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+
+  // element j < 16 of this thread's share of a slab: 16 consecutive elements
+  // along the operand's unit-stride axis
+  auto a_pos = [&](int j, int& mm, int& kk) {
+    if (p.a_kfast) { mm = tid / 4; kk = (tid % 4) * 16 + j; } else { kk = tid / 4; mm = (tid % 4) * 16 + j; }
+  };
+  // run u of the B slab: along n (BN / 16 runs per k) or along k (4 runs per n)
+  auto b_run = [&](int u, int& nn, int& kk) {
+    if (p.b_nfast) { kk = u / (BN / 16); nn = (u % (BN / 16)) * 16; } else { nn = u / 4; kk = (u % 4) * 16; }
+  };
+  float ra[16], rb[RB][16];
+  // 16 consecutive elements from p[0..15] (16-byte aligned; checked on the host)
+  auto vload = [](const auto* ptr, float (&r)[16]) {
+    if constexpr (sizeof(*ptr) == 4) {
+      const float4* v = reinterpret_cast<const float4*>(ptr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = v[i];
+        r[4 * i] = x.x; r[4 * i + 1] = x.y; r[4 * i + 2] = x.z; r[4 * i + 3] = x.w;
+      }
+    } else {
+      const bf16x8* v = reinterpret_cast<const bf16x8*>(ptr);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 x = v[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[8 * i + e] = (float)x[e];
+      }
+    }
+  };
+  auto load = [&](int k0) {
+    // A: the thread's run is along k (a_kfast) or along m
+    {
+      const int mm = p.a_kfast ? tid / 4 : (tid % 4) * 16;
+      const int kk = p.a_kfast ? (tid % 4) * 16 : tid / 4;
+      const int m = m0 + mm, k = k0 + kk;
+      const bool s1 = k >= p.ks;
+      const int kl = s1 ? k - p.ks : k;
+      const bool whole = p.vec && (p.a_kfast ? (m < p.M && k + 16 <= p.K && (s1 || k + 16 <= p.ks))
+                                             : (k < p.K && m + 16 <= p.M));
+      if (whole) {
+        vload((s1 ? a1 : a0) + m * p.sam + kl * p.sak, ra);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          int jm, jk;
+          a_pos(j, jm, jk);
+          const int mj = m0 + jm, kj = k0 + jk;
+          float x = 0.f;
+          if (mj < p.M && kj < p.K) {
+            const bool t1 = kj >= p.ks;
+            x = to_f32((t1 ? a1 : a0)[mj * p.sam + (t1 ? kj - p.ks : kj) * p.sak]);
+          }
+          ra[j] = x;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      int nn, kk;
+      b_run(tid + 256 * rr, nn, kk);
+      const int n = n0 + nn, k = k0 + kk;
+      const bool s1 = k >= p.ks;
+      const int kl = s1 ? k - p.ks : k;
+      const bool whole = p.vec && (p.b_nfast ? (k < p.K && n + 16 <= p.N)
+                                             : (n < p.N && k + 16 <= p.K && (s1 || k + 16 <= p.ks)));
+      if (whole) {
+        vload((s1 ? b1 : b0) + kl * p.sbk + n * p.sbn, rb[rr]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int nj = n + (p.b_nfast ? j : 0), kj = k + (p.b_nfast ? 0 : j);
+          float y = 0.f;
+          if (nj < p.N && kj < p.K) {
+            const bool t1 = kj >= p.ks;
+            y = to_f32((t1 ? b1 : b0)[(t1 ? kj - p.ks : kj) * p.sbk + nj * p.sbn]);
+          }
+          rb[rr][j] = y;
+        }
+      }
+    }
+  };
+
+  f32x4 acc[2][JT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < JT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  for (int k0 = 0; k0 < p.K; k0 += BK) {
+    __syncthreads();   // the previous slab has been read
+    // runs along k go to LDS as two 16-byte stores, runs along m / n element by element
+    auto put = [&](const float (&r)[16], bool kfast, int row, int kk, bf16* hi, bf16* lo, auto split) {
+      if (kfast) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 vh, vl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            vh[e] = (bf16)r[8 * h + e];
+            if constexpr (decltype(split)::value) vl[e] = (bf16)(r[8 * h + e] - (float)vh[e]);
+          }
+          *reinterpret_cast<bf16x8*>(&hi[row * LDK + kk + 8 * h]) = vh;
+          if constexpr (decltype(split)::value) *reinterpret_cast<bf16x8*>(&lo[row * LDK + kk + 8 * h]) = vl;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const bf16 h = (bf16)r[j];
+          hi[(row + j) * LDK + kk] = h;
+          if constexpr (decltype(split)::value) lo[(row + j) * LDK + kk] = (bf16)(r[j] - (float)h);
+        }
+      }
+    };
+    put(ra, p.a_kfast, p.a_kfast ? tid / 4 : (tid % 4) * 16, p.a_kfast ? (tid % 4) * 16 : tid / 4, Ah, Al,
+        std::integral_constant<bool, SA>());
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      int nn, kk;
+      b_run(tid + 256 * rr, nn, kk);
+      put(rb[rr], !p.b_nfast, nn, kk, Bh, Bl, std::integral_constant<bool, SB>());
+    }
+    __syncthreads();
+    if (k0 + BK < p.K) load(k0 + BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int kof = ks * 32 + (lane / 16) * 8;
+      bf16x8 ah[2], al[2], bh[JT], bl[JT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 32 + i * 16 + lane % 16;
+        ah[i] = *reinterpret_cast<const bf16x8*>(&Ah[row * LDK + kof]);
+        if constexpr (SA) al[i] = *reinterpret_cast<const bf16x8*>(&Al[row * LDK + kof]);
+      }
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const int col = wn * (BN / 2) + j * 16 + lane % 16;
+        bh[j] = *reinterpret_cast<const bf16x8*>(&Bh[col * LDK + kof]);
+        if constexpr (SB) bl[j] = *reinterpret_cast<const bf16x8*>(&Bl[col * LDK + kof]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+          if constexpr (SB) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+          if constexpr (SA) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  // acc[i][j][r] = C[wm*32 + i*16 + (lane/16)*4 + r][wn*BN/2 + j*16 + lane%16]: through
+  // LDS, then each thread writes 16-byte row chunks
+  const float alpha = p.alpha * (p.alpha_z ? p.alpha_z[z] : 1.f);
+  __syncthreads();   // every wave is done with the operand slabs
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < JT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Cs[(wm * 32 + i * 16 + (lane / 16) * 4 + r) * LDC + wn * (BN / 2) + j * 16 + lane % 16] =
+            alpha * acc[i][j][r];
+  __syncthreads();
+  TC* c = (TC*)p.c + oc;
+  constexpr int CH = 16 / sizeof(TC);   // elements per 16-byte chunk
+  for (int u = tid; u < BM * (BN / CH); u += 256) {
+    const int mm = u / (BN / CH), nn = (u % (BN / CH)) * CH;
+    const int m = m0 + mm, n = n0 + nn;
+    if (m >= p.M) continue;
+    const float* cs = Cs + mm * LDC + nn;
+    TC* dst = c + m * p.ldc + n;
+    if (p.vec && n + CH <= p.N) {
+      float v[CH];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) v[e] = cs[e];
+      if constexpr (sizeof(TC) == 4) {
+        float4 o = make_float4(v[0], v[1], v[2], v[3]);
+        if (p.accumulate) {
+          const float4 x = *reinterpret_cast<const float4*>(dst);
+          o.x += x.x; o.y += x.y; o.z += x.z; o.w += x.w;
+        }
+        *reinterpret_cast<float4*>(dst) = o;
+      } else {
+        bf16x8 o;
+        const bf16x8 x = p.accumulate ? *reinterpret_cast<const bf16x8*>(dst) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < CH; ++e) o[e] = (bf16)(v[e] + (p.accumulate ? (float)x[e] : 0.f));
+        *reinterpret_cast<bf16x8*>(dst) = o;
+      }
+    } else {
+      for (int e = 0; e < CH && n + e < p.N; ++e) {
+        float val = cs[e];
+        if (p.accumulate) val += to_f32(dst[e]);
+        dst[e] = from_f32<TC>(val);
+      }
+    }
+  }
+}
+
+hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st, bool mfma) {
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
   if (p.ks <= 0) p.ks = p.K;
   p.a_kfast = p.sak == 1;
@@ -162,6 +417,32 @@ hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st) {
   const int64_t tiles = (int64_t)((p.M + bg::BM - 1) / bg::BM) * ((p.N + bg::BN - 1) / bg::BN);
   const int64_t blocks = tiles * p.batch;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  if (mfma) {
+    // 16-element runs load as 16-byte vectors when every base pointer and every
+    // non-unit stride keeps them 16-byte aligned (8 elements covers both types)
+    auto al16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+    bool vec = al16(p.a0) && al16(p.b0) && al16(p.c) && (!p.a1 || al16(p.a1)) && (!p.b1 || al16(p.b1)) &&
+               p.ks % 16 == 0 && (p.sak == 1 || p.sam == 1) && (p.sbn == 1 || p.sbk == 1);
+    for (int64_t x : {p.sam, p.sak, p.sbk, p.sbn, p.sa[0], p.sa[1], p.sa[2], p.sb[0], p.sb[1], p.sb[2], p.ldc,
+                      p.sc[0], p.sc[1], p.sc[2]})
+      vec = vec && (x == 1 || x % 8 == 0);
+    p.vec = vec;
+    // 128-column tiles when the output is that wide: each token row of A is then read once
+    const bool wide = p.N > 64;
+    const int bn = wide ? 128 : 64;
+    const int64_t mtiles = (int64_t)((p.M + bm::BM - 1) / bm::BM) * ((p.N + bn - 1) / bn) * p.batch;
+    if (mtiles > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+#define VDN_BM(A, B, C)                                                                  \
+  (wide ? bgemm_mfma_kernel<A, B, C, 128><<<(unsigned)mtiles, 256, 0, st>>>(p)         \
+        : bgemm_mfma_kernel<A, B, C, 64><<<(unsigned)mtiles, 256, 0, st>>>(p))
+    if (ta == 1 && tb == 0 && tc == 0) VDN_BM(bf16, float, float);
+    else if (ta == 0 && tb == 1 && tc == 0) VDN_BM(float, bf16, float);
+    else if (ta == 0 && tb == 0 && tc == 1) VDN_BM(float, float, bf16);
+    else if (ta == 1 && tb == 0 && tc == 1) VDN_BM(bf16, float, bf16);
+    else return hipErrorInvalidValue;
+#undef VDN_BM
+    return hipGetLastError();
+  }
 #define VDN_BG(A, B, C) bgemm_kernel<A, B, C><<<(unsigned)blocks, 256, 0, st>>>(p)
   // the combinations the gradient uses: bf16 or fp32 tokens against fp32 matrices
   if (ta == 1 && tb == 0 && tc == 0) VDN_BG(bf16, float, float);

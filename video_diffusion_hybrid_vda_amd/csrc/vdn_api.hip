@@ -388,6 +388,8 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   const int L = T * N, Lt = L + s->context_tokens, BH = s->batch * H;
   const int64_t nf = (int64_t)BH * T, dd = (int64_t)d * d, Nd = (int64_t)N * d, Ltd = (int64_t)Lt * d;
   const int es = dt == VDN_BF16 ? 2 : 4;
+  // bf16 I/O: token-side products on bf16 MFMA (fp32 operands split hi + lo)
+  const bool mfma = dt == VDN_BF16;
   hipError_t e = hipSuccess;
   auto step = [&](int phase, const char* what, auto&& body) -> int {
     const int ph = phase_begin(phase, st);
@@ -422,7 +424,7 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   g.sa[0] = 0; g.sa[1] = Nd; g.sa[2] = Ltd;
   g.sb[0] = nf * dd; g.sb[1] = dd; g.sb[2] = T * dd;
   g.sc[0] = Nd; g.sc[1] = 2 * Nd; g.sc[2] = T * 2 * Nd;
-  rc = step(kPhBwdU, "vda_bwd u launch", [&] { return launch_bgemm(dt, 0, 0, g, st); });
+  rc = step(kPhBwdU, "vda_bwd u launch", [&] { return launch_bgemm(dt, 0, 0, g, st, mfma); });
   if (rc != VDN_OK) return rc;
   rc = step(kPhBwdRms, "vda_bwd rms launch", [&] {
     return launch_rms_bwd(dt, d, u, d_out, (int64_t)H * d, rms_w, dwp, nf, H, T, N, Lt, s->rms_eps, st);
@@ -438,7 +440,7 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   g.sa[0] = 2 * Nd; g.sa[2] = T * 2 * Nd;
   g.sb[0] = dd; g.sb[2] = T * dd;
   g.sc[0] = Nd; g.sc[2] = Ltd;
-  rc = step(kPhBwdDq, "vda_bwd dq launch", [&] { return launch_bgemm(0, 0, dt, g, st); });
+  rc = step(kPhBwdDq, "vda_bwd dq launch", [&] { return launch_bgemm(0, 0, dt, g, st, mfma); });
   if (rc != VDN_OK) return rc;
 
   // dS[f][dir] = du^T Q_t (sum over the frame's tokens)
@@ -450,7 +452,7 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   g.sa[0] = Nd; g.sa[1] = 2 * Nd; g.sa[2] = T * 2 * Nd;
   g.sb[0] = 0; g.sb[1] = Nd; g.sb[2] = Ltd;
   g.sc[0] = dd; g.sc[1] = 2 * dd; g.sc[2] = T * 2 * dd;
-  rc = step(kPhBwdDs, "vda_bwd dS launch", [&] { return launch_bgemm(0, dt, 0, g, st); });
+  rc = step(kPhBwdDs, "vda_bwd dS launch", [&] { return launch_bgemm(0, dt, 0, g, st, mfma); });
   if (rc != VDN_OK) return rc;
 
   rc = step(kPhBwdScan, "vda_bwd scan launch", [&] { return launch_scan_bwd(d, am, gamma, dsg, dx, BH, T, st); });
@@ -496,11 +498,11 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
     m.sb[0] = 2 * dd; m.sb[2] = T * 2 * dd;
     m.sc[0] = Nd; m.sc[2] = Ltd;
     m.alpha_z = beta;
-    hipError_t r = launch_bgemm(dt, 0, dt, m, st);
+    hipError_t r = launch_bgemm(dt, 0, dt, m, st, mfma);
     // dV = beta K dB^T
     m.a1 = nullptr; m.b0 = cdb + dd; m.b1 = nullptr; m.c = dv;
     m.K = d; m.ks = 0; m.sbk = 1; m.sbn = d;
-    if (r == hipSuccess) r = launch_bgemm(dt, 0, dt, m, st);
+    if (r == hipSuccess) r = launch_bgemm(dt, 0, dt, m, st, mfma);
     return r;
   });
   if (rc != VDN_OK) return rc;
