@@ -14,7 +14,10 @@ dominant kernel's roofline fraction (window softmax, MFMA bf16) from HIP
 events recorded in the timed region, per-phase milliseconds, and the fp64 CPU
 oracle timed on a bounded sample of the same workload on this host.
 
-    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+After the forward, the same line carries `vda_backward`: the linear-branch
+gradient (vda_scan_bwd) timed on the same workload, per phase against HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline] [--bwd-steps 3]
 
 With --sweep it instead runs the batch-2 length sweep (B2 H24 d128 N4032,
 T = 42, 62, 82, 102 latent frames): the hybrid layer and the dense
@@ -296,6 +299,58 @@ def cpu_baseline(cfg, inp):
             "sample": sample, "host": host_info()}
 
 
+def time_backward(cfg, inp, vdn, torch, steps):
+    """Time the linear-branch gradient (vda_scan_bwd) on the workload: gradient of
+    <d_out, ungated linear-branch output> with respect to q, k, v, gamma, beta and
+    the RMSNorm weight, d_out seeded N(0, 1) in bf16.  Each token-side phase is
+    reported against HBM with its algorithmic bytes (every tensor it must read or
+    write once); the dominant phase (dK and dV) is the roofline entry."""
+    B, H, d, T, N = cfg.batch, cfg.heads, cfg.head_dim, cfg.frames, cfg.tokens_per_frame
+    L, D = cfg.seq_len, cfg.model_dim
+    shape = vdn.shape_from_config(cfg)
+    ws = vdn.workspace(shape, vdn.VDN_OP_VDA_BWD)
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 4242)
+    d_out = torch.randn(B, L, D, device="cuda", generator=g).to(torch.bfloat16)
+    grads = {n: torch.empty_like(inp[n]) for n in ("q", "k", "v")}
+    dgamma = torch.empty(B, H, T, dtype=torch.float32, device="cuda")
+    dbeta = torch.empty_like(dgamma)
+    drms = torch.empty(D, dtype=torch.float32, device="cuda")
+
+    def call():
+        vdn.vda_scan_bwd(shape, inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], inp["rms_w"], d_out,
+                         grads["q"], grads["k"], grads["v"], dgamma, dbeta, drms, ws)
+
+    call()
+    torch.cuda.synchronize()
+    vdn.vdn_timing_start()
+    ms, calls = timed_calls(call, steps, 0)
+    ph = vdn.vdn_timing_stop()
+    ph_ms = {k: round(v[1] / max(v[0], 1), 3) for k, v in ph.items() if v[0] > 0}
+    tok = B * H * L * d          # elements of one [B, H, L, d] token tensor
+    nbytes = {                   # algorithmic HBM bytes per call of each phase (bf16 tokens, fp32 u / du)
+        "bwd_u_gemm": tok * 2 + 2 * tok * 4,                 # read q, write u of both directions
+        "bwd_rms": 2 * tok * 4 * 2 + tok * 2,                # read u, write du (both directions), read d_out
+        "bwd_dq_gemm": 2 * tok * 4 + tok * 2,                # read du, write dq
+        "bwd_ds_gemm": 2 * tok * 4 + tok * 2,                # read du and q
+        "bwd_kv_gemm": 4 * tok * 2,                          # read k, v; write dk, dv
+    }
+    kern = {}
+    for k, b in nbytes.items():
+        if k in ph_ms:
+            gbs = b / (ph_ms[k] * 1e-3) / 1e9
+            kern[k] = {"bound": "hbm", "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                       "algorithmic_GB": round(b / 1e9, 3), "avg_ms": ph_ms[k]}
+    dom = max(nbytes, key=lambda k: ph_ms.get(k, 0.0))
+    del ws
+    return {"mode": "gradient of the ungated linear-branch output w.r.t. q, k, v, gamma, beta and the "
+                    "RMSNorm weight (vda_scan_bwd; forward quantities recomputed inside)",
+            "value": B * L / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
+            "call_ms_median": round(median(calls), 3), "phases_ms": ph_ms,
+            "roofline": dict(kern[dom], kernel=dom + " (bgemm_mfma)", peak=PEAK_HBM_GBS, unit="GB/s",
+                             achieved=kern[dom]["achieved_GBps"], traffic=None),
+            "kernel_rooflines": kern}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +366,9 @@ def main():
                     help="time the layer with MXFP8 softmax-branch scores instead of bf16 ones")
     ap.add_argument("--mxfp8-steps", type=int, default=3,
                     help="after the bf16 measurement, also time this many calls in MXFP8 mode (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=3,
+                    help="after the forward measurement, also time this many calls of the linear-branch "
+                         "gradient (vda_scan_bwd) on the same workload (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling HBM counters)")
@@ -397,6 +455,10 @@ def main():
                  "kernel_rooflines": phase_rooflines(cfg, ph8)}
         del ws8
 
+    backward = None
+    if args.bwd_steps > 0:
+        backward = time_backward(cfg, inp, vdn, torch, args.bwd_steps)
+
     result = {
         "metric": METRIC,
         "value": B * L / (ms_per_step * 1e-3),
@@ -426,6 +488,8 @@ def main():
     }
     if mxfp8 is not None:
         result["mxfp8_softmax"] = mxfp8
+    if backward is not None:
+        result["vda_backward"] = backward
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)
