@@ -159,3 +159,27 @@ def test_vda_backward_headline_two_heads(vdn):
             + " (plain " + " ".join(f"d{n} {e:.2e}" for n, e in plain.items()) + f") ({time.time() - t0:.1f}s)")
         for n, e in errs.items():
             assert e <= TOL["bf16"], (h, n, e)
+
+
+def test_vda_backward_scan_workload_two_heads(vdn):
+    """B1 H8 d64 T42 N1560 bf16 (the linear-branch scan workload): every gradient
+    of heads 0 and 7, whole, against the oracle."""
+    cfg = synth.CONFIGS[2]
+    log(f"[vda bwd] {cfg.name}")
+    inp, d_out = grad_inputs(cfg, "cuda")
+    got = vdn.vda_scan_grad(vdn.shape_from_config(cfg), inp, d_out)
+    torch.cuda.synchronize()
+    T, N, d = cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    dh = d_out_heads(d_out, cfg)
+    for h in (0, 7):
+        sl = lambda t: np64(t[0:1, h:h + 1]).reshape(1, 1, T, N, d)
+        ref = vda_branch_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), np64(inp["gamma"][0:1, h:h + 1]),
+                                  np64(inp["beta"][0:1, h:h + 1]), np64(inp["rms_w"][h * d:(h + 1) * d]),
+                                  cfg.rms_eps, dh[0:1, h:h + 1])
+        errs = {n: excess_err(sl(got[n]), ref["d" + n], "bf16") for n in ("q", "k", "v")}
+        errs["gamma"] = rel_err(np64(got["gamma"][0, h]), ref["dgamma"][0, 0])
+        errs["beta"] = rel_err(np64(got["beta"][0, h]), ref["dbeta"][0, 0])
+        errs["rms_w"] = rel_err(np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"])
+        log(f"  head {h}: " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (h, n, e)
