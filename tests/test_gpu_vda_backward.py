@@ -183,3 +183,39 @@ def test_vda_backward_scan_workload_two_heads(vdn):
         log(f"  head {h}: " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()))
         for n, e in errs.items():
             assert e <= TOL["bf16"], (h, n, e)
+
+
+def test_vda_backward_repeatable_and_range_checked(vdn):
+    """Two calls on one workspace give bit-identical gradients (no atomics:
+    every reduction has a fixed order); with the opt-in range check on,
+    beta < 0 or gamma > 1 is rejected with VDN_ERR_PARAM_RANGE (-6) and the
+    outputs are left untouched, and valid parameters pass unchanged."""
+    cfg = VdnConfig(1, 2, 64, 6, 50, dtype="bf16", seed=87)
+    inp, d_out = grad_inputs(cfg, "cuda")
+    shape = vdn.shape_from_config(cfg)
+    ws = vdn.workspace(shape, vdn.VDN_OP_VDA_BWD)
+    g1 = vdn.vda_scan_grad(shape, inp, d_out, ws=ws)
+    g2 = vdn.vda_scan_grad(shape, inp, d_out, ws=ws)
+    torch.cuda.synchronize()
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
+    prev = vdn.vdn_set_param_check(True)
+    try:
+        g3 = vdn.vda_scan_grad(shape, inp, d_out, ws=ws)
+        torch.cuda.synchronize()
+        for n in g1:
+            assert torch.equal(g1[n], g3[n]), n
+        for key, val in (("beta", -0.5), ("gamma", 1.5)):
+            bad = dict(inp)
+            bad[key] = inp[key].clone()
+            bad[key][0, 1, 3] = val
+            sentinel = torch.full_like(g1["q"], 7.0)
+            with pytest.raises(vdn.VdnError) as ei:
+                vdn.vda_scan_bwd(shape, bad["q"], bad["k"], bad["v"], bad["gamma"], bad["beta"], bad["rms_w"],
+                                 d_out, sentinel, torch.empty_like(sentinel), torch.empty_like(sentinel),
+                                 torch.empty_like(g1["gamma"]), torch.empty_like(g1["beta"]), None, ws)
+            assert ei.value.status == -6, key
+            torch.cuda.synchronize()
+            assert torch.all(sentinel == 7.0).item(), key
+    finally:
+        vdn.vdn_set_param_check(prev)
