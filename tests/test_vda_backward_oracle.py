@@ -121,3 +121,34 @@ def test_frame_reversal_swaps_the_directions():
     for name in ("dq", "dk", "dv", "dgamma", "dbeta"):
         np.testing.assert_allclose(g1[name], flip(g0[name]), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g1["drms_w"], g0["drms_w"], rtol=1e-10, atol=1e-12)
+
+
+def test_all_zero_beta_closed_form():
+    """beta = 0 in every frame: every state is zero, so dq, dk, dv and dgamma
+    vanish exactly.  dbeta_t has a closed form.  Frame t's write
+    Btil_t = V_t^T K_t reaches frame s of the forward scan (s >= t) scaled by
+    gamma_{t+1} ... gamma_s, and frame s <= t of the backward scan scaled by
+    gamma_s ... gamma_{t-1}.  The readout at zero state is linear,
+    r = u / sqrt(eps).  So
+        dbeta_t = sum over both scans and reached frames s of
+                  (gamma product) * sum_n <w * do_{s,n}, Btil_t q_{s,n}> / sqrt(eps),
+    a direct sum, not the adjoint recursion."""
+    eps = 1e-4
+    x, d_o = _inputs(18, B=1, H=1, T=5, N=3, d=4)
+    x["beta"][:] = 0.0
+    gr = _grads(x, d_o, eps)
+    for name in ("dq", "dk", "dv", "dgamma"):
+        assert np.all(gr[name] == 0.0), name
+    q, k, v, gam, w = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], x["gamma"][0, 0], x["rms_w"]
+    do = d_o[0, 0]
+    T = q.shape[0]
+    want = np.zeros(T)
+    for t in range(T):
+        btil = v[t].T @ k[t]
+        for s in range(T):
+            if s >= t:      # forward scan
+                want[t] += np.prod(gam[t + 1:s + 1]) * np.sum((w * do[s]) * (q[s] @ btil.T))
+            if s <= t:      # backward scan
+                want[t] += np.prod(gam[s:t]) * np.sum((w * do[s]) * (q[s] @ btil.T))
+    want /= np.sqrt(eps)
+    np.testing.assert_allclose(gr["dbeta"][0, 0], want, rtol=1e-12, atol=1e-12)
