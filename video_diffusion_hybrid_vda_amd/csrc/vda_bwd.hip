@@ -409,6 +409,193 @@ __global__ __launch_bounds__(256) void bgemm_mfma_kernel(BGemm p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bgemm_mfma_resident: the bf16-MFMA product for outputs 128 columns wide with
+// K = KK (128 or 256): the whole K x 128 B operand (a frame's d x d matrices)
+// is staged into LDS once, as hi/lo bf16 pairs, and `tiles_per_wg` consecutive
+// 64-row tiles of A stream through it, 64-deep k slabs at a time.  Staging B
+// once per tile is what bounds the tiled kernel above.
+namespace br {
+constexpr int BM = 64, BN = 128, BK = 64, LDK = BK + 8;
+}
+
+template <typename TA, typename TB, typename TC, int KK>
+__global__ __launch_bounds__(256) void bgemm_mfma_resident_kernel(BGemm p, int tiles_per_wg) {
+  using namespace br;
+  constexpr bool SA = sizeof(TA) == 4, SB = sizeof(TB) == 4;
+  constexpr int LDB = KK + 8;   // B row pitch in LDS (bf16): 16-byte multiple
+  __shared__ __attribute__((aligned(16))) bf16 Bh[BN * LDB];
+  __shared__ __attribute__((aligned(16))) bf16 Bl[SB ? BN * LDB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 Ah[BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Al[SA ? BM * LDK : 8];
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int chunks = (tiles_m + tiles_per_wg - 1) / tiles_per_wg;
+  const int64_t z = blockIdx.x / chunks;
+  const int tm0 = (int)(blockIdx.x % chunks) * tiles_per_wg;
+  int64_t z0, z1, z2;
+  batch_index(p, z, z0, z1, z2);
+  const int64_t oa = z0 * p.sa[0] + z1 * p.sa[1] + z2 * p.sa[2];
+  const int64_t ob = z0 * p.sb[0] + z1 * p.sb[1] + z2 * p.sb[2];
+  const int64_t oc = z0 * p.sc[0] + z1 * p.sc[1] + z2 * p.sc[2];
+  const TA* a0 = (const TA*)p.a0 + oa;
+  const TA* a1 = (const TA*)(p.a1 ? p.a1 : p.a0) + oa;
+  const TB* b0 = (const TB*)p.b0 + ob;
+  const TB* b1 = (const TB*)(p.b1 ? p.b1 : p.b0) + ob;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+
+  auto vload = [](const auto* ptr, float (&r)[16]) {
+    if constexpr (sizeof(*ptr) == 4) {
+      const float4* v = reinterpret_cast<const float4*>(ptr);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = v[i];
+        r[4 * i] = x.x; r[4 * i + 1] = x.y; r[4 * i + 2] = x.z; r[4 * i + 3] = x.w;
+      }
+    } else {
+      const bf16x8* v = reinterpret_cast<const bf16x8*>(ptr);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 x = v[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[8 * i + e] = (float)x[e];
+      }
+    }
+  };
+  // runs along k go to LDS as two 16-byte stores, runs along m / n element by element
+  auto put = [](const float (&r)[16], bool kfast, int row, int kk, int pitch, bf16* hi, bf16* lo, auto split) {
+    if (kfast) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 vh, vl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          vh[e] = (bf16)r[8 * h + e];
+          if constexpr (decltype(split)::value) vl[e] = (bf16)(r[8 * h + e] - (float)vh[e]);
+        }
+        *reinterpret_cast<bf16x8*>(&hi[row * pitch + kk + 8 * h]) = vh;
+        if constexpr (decltype(split)::value) *reinterpret_cast<bf16x8*>(&lo[row * pitch + kk + 8 * h]) = vl;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bf16 h = (bf16)r[j];
+        hi[(row + j) * pitch + kk] = h;
+        if constexpr (decltype(split)::value) lo[(row + j) * pitch + kk] = (bf16)(r[j] - (float)h);
+      }
+    }
+  };
+
+  // the whole B operand: KK x 128 in runs of 16 along its unit-stride axis
+  for (int u = tid; u < KK * BN / 16; u += 256) {
+    int nn, kk;
+    if (p.b_nfast) { kk = u / (BN / 16); nn = (u % (BN / 16)) * 16; } else { nn = u / (KK / 16); kk = (u % (KK / 16)) * 16; }
+    const bool s1 = kk >= p.ks;
+    const int kl = s1 ? kk - p.ks : kk;
+    float rb[16];
+    const bool whole = p.vec && (p.b_nfast ? (nn + 16 <= p.N) : (nn < p.N && (s1 || kk + 16 <= p.ks)));
+    if (whole) {
+      vload((s1 ? b1 : b0) + kl * p.sbk + nn * p.sbn, rb);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int nj = nn + (p.b_nfast ? j : 0), kj = kk + (p.b_nfast ? 0 : j);
+        float y = 0.f;
+        if (nj < p.N && kj < p.K) {
+          const bool t1 = kj >= p.ks;
+          y = to_f32((t1 ? b1 : b0)[(t1 ? kj - p.ks : kj) * p.sbk + nj * p.sbn]);
+        }
+        rb[j] = y;
+      }
+    }
+    put(rb, !p.b_nfast, nn, kk, LDB, Bh, Bl, std::integral_constant<bool, SB>());
+  }
+
+  const float alpha = p.alpha * (p.alpha_z ? p.alpha_z[z] : 1.f);
+  TC* c = (TC*)p.c + oc;
+  const int amm = p.a_kfast ? tid / 4 : (tid % 4) * 16;   // this thread's A run in a slab
+  const int akk = p.a_kfast ? (tid % 4) * 16 : tid / 4;
+  float ra[16];
+  for (int ti = 0; ti < tiles_per_wg; ++ti) {
+    const int tm = tm0 + ti;
+    if (tm >= tiles_m) break;
+    const int m0 = tm * BM;
+    auto load = [&](int k0) {
+      const int m = m0 + amm, k = k0 + akk;
+      const bool s1 = k >= p.ks;
+      const int kl = s1 ? k - p.ks : k;
+      const bool whole = p.vec && (p.a_kfast ? (m < p.M && (s1 || k + 16 <= p.ks)) : (m + 16 <= p.M));
+      if (whole) {
+        vload((s1 ? a1 : a0) + m * p.sam + kl * p.sak, ra);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int mj = m + (p.a_kfast ? 0 : j), kj = k + (p.a_kfast ? j : 0);
+          float x = 0.f;
+          if (mj < p.M && kj < p.K) {
+            const bool t1 = kj >= p.ks;
+            x = to_f32((t1 ? a1 : a0)[mj * p.sam + (t1 ? kj - p.ks : kj) * p.sak]);
+          }
+          ra[j] = x;
+        }
+      }
+    };
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0);
+    for (int k0 = 0; k0 < KK; k0 += BK) {
+      __syncthreads();   // B staged (first slab) / the previous A slab has been read
+      put(ra, p.a_kfast, amm, akk, LDK, Ah, Al, std::integral_constant<bool, SA>());
+      __syncthreads();
+      if (k0 + BK < KK) load(k0 + BK);
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int kof = ks * 32 + (lane / 16) * 8;
+        bf16x8 ah[2], al[2], bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = wm * 32 + i * 16 + lane % 16;
+          ah[i] = *reinterpret_cast<const bf16x8*>(&Ah[row * LDK + kof]);
+          if constexpr (SA) al[i] = *reinterpret_cast<const bf16x8*>(&Al[row * LDK + kof]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = wn * 64 + j * 16 + lane % 16;
+          bh[j] = *reinterpret_cast<const bf16x8*>(&Bh[col * LDB + k0 + kof]);
+          if constexpr (SB) bl[j] = *reinterpret_cast<const bf16x8*>(&Bl[col * LDB + k0 + kof]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+            if constexpr (SB) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+            if constexpr (SA) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+    // acc[i][j][r] = C[wm*32 + i*16 + (lane/16)*4 + r][wn*64 + j*16 + lane%16]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 64 + j * 16 + lane % 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 32 + i * 16 + (lane / 16) * 4 + r;
+          if (m >= p.M || n >= p.N) continue;
+          const int64_t idx = m * p.ldc + n;
+          float val = alpha * acc[i][j][r];
+          if (p.accumulate) val += to_f32(c[idx]);
+          c[idx] = from_f32<TC>(val);
+        }
+      }
+  }
+}
+
 hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st, bool mfma) {
   if (p.M <= 0 || p.N <= 0 || p.batch <= 0) return hipSuccess;
   if (p.ks <= 0) p.ks = p.K;
@@ -427,6 +614,23 @@ hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st, bool mf
                       p.sc[0], p.sc[1], p.sc[2]})
       vec = vec && (x == 1 || x % 8 == 0);
     p.vec = vec;
+    if (p.vec && p.N == 128 && (p.K == 128 || p.K == 256)) {
+      // the B operand resident in LDS, eight 64-row tiles of A per workgroup
+      constexpr int kTilesPerWg = 8;
+      const int64_t tm = (p.M + br::BM - 1) / br::BM;
+      const int64_t wgs = (tm + kTilesPerWg - 1) / kTilesPerWg * p.batch;
+      if (wgs > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+#define VDN_BR(A, B, C)                                                                               \
+  (p.K == 128 ? bgemm_mfma_resident_kernel<A, B, C, 128><<<(unsigned)wgs, 256, 0, st>>>(p, kTilesPerWg) \
+              : bgemm_mfma_resident_kernel<A, B, C, 256><<<(unsigned)wgs, 256, 0, st>>>(p, kTilesPerWg))
+      if (ta == 1 && tb == 0 && tc == 0) VDN_BR(bf16, float, float);
+      else if (ta == 0 && tb == 1 && tc == 0) VDN_BR(float, bf16, float);
+      else if (ta == 0 && tb == 0 && tc == 1) VDN_BR(float, float, bf16);
+      else if (ta == 1 && tb == 0 && tc == 1) VDN_BR(bf16, float, bf16);
+      else return hipErrorInvalidValue;
+#undef VDN_BR
+      return hipGetLastError();
+    }
     // 128-column tiles when the output is that wide: each token row of A is then read once
     const bool wide = p.N > 64;
     const int bn = wide ? 128 : 64;
