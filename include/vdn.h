@@ -160,8 +160,13 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
  * The gradient is the derivative of the forward rule taken step by step in
  * reverse (readout, both scans, the solve (I + A_t)^-1, the Gram products);
  * the forward quantities are recomputed from q, k, v, gamma, beta in the
- * workspace (op VDN_OP_VDA_BWD).  Arithmetic is fp32 throughout; rms_w may
- * be NULL (ones).  batch * heads must not exceed 65535. */
+ * workspace (op VDN_OP_VDA_BWD).  Precision: fp32 accumulation throughout;
+ * with fp32 I/O every product is fp32, with bf16 I/O the token-side products
+ * (S q, the readout adjoint, dq, dS, dK, dV) run on bf16 matrix cores with
+ * each fp32 operand split into a bf16 high and low half (the low-by-low term
+ * dropped, about 16 significant bits per operand), and the d x d products,
+ * scans and solve adjoints stay fp32.  rms_w may be NULL (ones).
+ * batch * heads must not exceed 65535. */
 int vda_scan_bwd(const vdn_shape* shape, const void* q, const void* k,
                  const void* v, const float* gamma, const float* beta,
                  const float* rms_w, const void* d_out, void* dq, void* dk,
@@ -179,16 +184,18 @@ int window_anchor_attn_fwd(const vdn_shape* shape, const void* q,
 
 /* MXFP8 mode of the softmax branch.  The 10100.com article (实验结果, the
  * paragraph on scaling with sequence length) runs the denoiser in MXFP8
- * without saying which operations; here q and k of the softmax branch are
- * MXFP8 and the scores q . k come from them, while the softmax, P V, v, the
- * gates, the linear branch and the projections stay as in the bf16 path.
+ * without saying which operations.  Read here: the two operands of the
+ * softmax branch's score product, q and k as the layer receives them, are
+ * MXFP8, and the softmax scales their product as usual,
+ * logit = scale * (q8 . k8); the softmax, P V, v, the gates, the linear
+ * branch (which reads the unquantised q and k) and the projections stay as in
+ * the bf16 path.
  * Format: OCP Microscaling (MX) v1.0 MXFP8, i.e. blocks of 32 consecutive
  * elements (along head_dim) in OCP FP8 E4M3 (bias 7, largest finite 448)
  * sharing one E8M0 scale 2^(code - 127).  With shape->softmax_mxfp8 = 1,
  * vdn_hybrid_attn_fwd, window_anchor_attn_fwd and vdn_dense_attn_fwd quantise
- * their bf16 k and c * q into the workspace, c = scale * log2(e) in fp32 (so
- * the products are logits in log2 units; vdn_workspace_bytes grows by
- * 2 * B*H*Lt*(d + d/32) bytes), and use these scores. */
+ * their bf16 q and k into the workspace (vdn_workspace_bytes grows by
+ * 2 * B*H*Lt*(d + d/32) bytes) and take the scores from them. */
 
 /* MXFP8 quantisation of n_elems bf16 values x (n_elems a non-negative
  * multiple of 32), block i = x[32 i .. 32 i + 31]: scales[i] = clamp(
@@ -204,7 +211,7 @@ int vdn_mxfp8_quantize(const void* x, int64_t n_elems, void* codes,
                        void* scales, void* stream);
 
 /* Softmax branch (10100.com article, 方法概述 part 1) with scores from
- * MXFP8 q and k (of q itself, not scaled) given as codes [B, H, Lt, 128] (uint8 E4M3) and scales
+ * MXFP8 q and k given as codes [B, H, Lt, 128] (uint8 E4M3) and scales
  * [B, H, Lt, 4] (uint8 E8M0), as vdn_mxfp8_quantize writes them; v, gate_s,
  * out and lse as window_anchor_attn_fwd.  shape->dtype must be VDN_BF16 and
  * head_dim 128 (VDN_ERR_DTYPE / VDN_ERR_BAD_SHAPE otherwise); the

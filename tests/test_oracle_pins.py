@@ -538,3 +538,178 @@ def test_context_layer_branches():
     full = O.hybrid_layer_ctx(**inp, N=N)
     rows = np.array([0, 7, L - 1, L, L + n_ctx - 1])
     assert np.max(np.abs(O.hybrid_layer_ctx(**inp, N=N, rows=rows) - full[:, rows])) < 1e-12
+
+
+# ---------------------------------------------------------------- RMSNorm, gates, head merge, dense baseline
+
+def test_rms_norm_eps_closed_form():
+    """eps sits inside the square root, next to the mean of squares, and the
+    weight multiplies after the normalisation: a constant vector c gives
+    c / sqrt(c^2 + eps) exactly, (a, -a, 0, 0) gives a / sqrt(a^2 / 2 + eps)."""
+    c, eps = 1e-3, 1e-6
+    u = np.full((2, 8), c)
+    w = np.array([1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0])
+    got = O.rms_norm(u, w, eps)
+    assert np.allclose(got, w * (c / np.sqrt(c * c + eps)), rtol=1e-14, atol=0)
+    assert abs(got[0, 0] - 1.0 / np.sqrt(2.0)) < 1e-12       # c^2 = eps
+    a = 3e-3
+    got = O.rms_norm(np.array([[a, -a, 0.0, 0.0]]), np.ones(4), eps)
+    want = a / np.sqrt(a * a / 2 + eps)
+    assert np.allclose(got, [[want, -want, 0.0, 0.0]], rtol=1e-14, atol=0)
+    assert np.all(O.rms_norm(np.zeros((1, 4)), np.ones(4), eps) == 0.0)
+
+
+def test_gates_closed_form():
+    """sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly in closed form; the
+    gate of output channel j reads column j of W (y = x W)."""
+    D = 4
+    x = np.eye(D)[[1, 3]]                  # token 0 = e_1, token 1 = e_3
+    w_s = np.zeros((D, D))
+    w_l = np.zeros((D, D))
+    w_s[1, 2] = np.log(3.0)                # token 0, channel 2 of the softmax gate
+    w_l[3, 0] = -np.log(3.0)               # token 1, channel 0 of the linear gate
+    g_s, g_l = O.gates(x, w_s, w_l)
+    want_s = np.full((2, D), 0.5)
+    want_s[0, 2] = 0.75
+    want_l = np.full((2, D), 0.5)
+    want_l[1, 0] = 0.25
+    assert np.max(np.abs(g_s - want_s)) < 1e-15 and np.max(np.abs(g_l - want_l)) < 1e-15
+
+
+def test_merge_heads_index_map():
+    """[B, H, T, N, d] -> [B, T*N, H*d]: element (b, h, t, n, j) lands at row
+    t*N + n, column h*d + j."""
+    B, H, T, N, d = 2, 3, 4, 5, 6
+    o = np.zeros((B, H, T, N, d))
+    for idx in np.ndindex(o.shape):
+        o[idx] = float("".join(str(i) for i in idx))
+    m = O.merge_heads(o)
+    assert m.shape == (B, T * N, H * d)
+    for b, h, t, n, j in np.ndindex(o.shape):
+        assert m[b, t * N + n, h * d + j] == o[b, h, t, n, j]
+
+
+def test_dense_layer_equals_unmasked_sdpa_and_projection():
+    """The dense baseline: a library softmax attention with no mask per head,
+    heads concatenated along channels, one projection, no gates."""
+    r = rng(31)
+    B, H, T, N, d = 2, 2, 13, 3, 4
+    q = r.normal(size=(B, H, T, N, d)) * 2.0
+    k = r.normal(size=(B, H, T, N, d))
+    v = r.normal(size=(B, H, T, N, d))
+    w_o = r.normal(size=(H * d, H * d))
+    got = O.dense_layer(q, k, v, w_o)
+    for b in range(B):
+        cols = [torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b, h].reshape(T * N, d))[None], torch.from_numpy(k[b, h].reshape(T * N, d))[None],
+            torch.from_numpy(v[b, h].reshape(T * N, d))[None])[0].numpy() for h in range(H)]
+        ref = np.concatenate(cols, axis=1) @ w_o
+        assert np.max(np.abs(got[b] - ref)) < 1e-12
+    # with 13 frames the hybrid mask is not dense: the baseline must differ from
+    # the windowed softmax
+    ok = O.allowed_frames(T)
+    assert not ok.all()
+
+
+# ---------------------------------------------------------------- MXFP8 scores (reading F-1)
+
+def _mx_layer(seed, T=7, N=3, H=2, d=32):
+    inp = _layer(seed, T=T, N=N, H=H, d=d)
+    return {**inp, "w_gs": inp["w_gs"] * 0.1, "w_os": inp["w_os"] * 0.1}
+
+
+def _grid_values(r, shape, se):
+    """Random values exactly on the MXFP8 grid of blocks with shared exponent
+    se: random E4M3 codes (no NaN) times 2^se, one element per block at the
+    largest code 0x7E (448) so that the block's exponent is se again."""
+    from oracle import mxfp8 as MX
+    codes = r.integers(0, 0x7F, size=shape) | (r.integers(0, 2, size=shape) << 7)
+    vals = np.array([MX.e4m3_value(c) for c in codes.ravel()]).reshape(shape)
+    vals[..., ::32] = 448.0 * np.sign(vals[..., ::32] + 0.5)
+    return np.ldexp(vals, se)
+
+
+def test_mxfp8_layer_is_plain_layer_on_grid_values():
+    """q and k already on the MXFP8 grid: the encoding changes nothing, so the
+    MXFP8-score layer equals the plain layer (same scale, same softmax)."""
+    inp = _mx_layer(41)
+    r = rng(42)
+    inp["q"] = _grid_values(r, inp["q"].shape, -9)
+    inp["k"] = _grid_values(r, inp["k"].shape, -10)
+    rows = np.arange(7 * 3)
+    plain = O.hybrid_layer_rows(**inp, rows=rows)
+    mx = O.hybrid_layer_rows(**inp, rows=rows, softmax_mxfp8=True)
+    assert np.max(np.abs(mx - plain)) < 1e-12 * np.max(np.abs(plain))
+    # either operand off the grid alone changes the scores: both are encoded
+    off = _mx_layer(46)
+    for name in ("q", "k"):
+        one = {**inp, name: off[name]}
+        d1 = O.hybrid_layer_rows(**one, rows=rows, softmax_mxfp8=True) - O.hybrid_layer_rows(**one, rows=rows)
+        assert np.max(np.abs(d1)) > 1e-6 * np.max(np.abs(plain)), name
+
+
+def test_mxfp8_layer_keeps_linear_branch_unquantised():
+    """Only the softmax branch's scores use MXFP8: with the softmax projection
+    zero the two modes agree exactly, and with it nonzero they differ."""
+    inp = _mx_layer(43)
+    rows = np.arange(7 * 3)
+    zero = np.zeros_like(inp["w_os"])
+    a = O.hybrid_layer_rows(**{**inp, "w_os": zero}, rows=rows)
+    b = O.hybrid_layer_rows(**{**inp, "w_os": zero}, rows=rows, softmax_mxfp8=True)
+    assert np.array_equal(a, b)
+    full = O.hybrid_layer_rows(**inp, rows=rows)
+    full_mx = O.hybrid_layer_rows(**inp, rows=rows, softmax_mxfp8=True)
+    assert np.max(np.abs(full - full_mx)) > 1e-6 * np.max(np.abs(full))
+
+
+def _mx_elem_bound(x):
+    """Bound on |MXFP8(x) - x| from the format alone: blocks of 32 along the
+    last axis with X = 2^(floor(log2 max|x|) - 8); half an E4M3 ulp (2^-4 of
+    |x|) in the normal range, 2^-10 X below it, and saturation at 448 X."""
+    xb = x.reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.max(np.abs(xb), axis=-1, keepdims=True)
+    X = 2.0 ** (np.floor(np.log2(amax)) - 8)
+    e = np.maximum(np.maximum(2.0 ** -4 * np.abs(xb), 2.0 ** -10 * X), np.abs(xb) - 448 * X)
+    return e.reshape(x.shape)
+
+
+def test_mxfp8_layer_within_the_format_error_bound():
+    """The MXFP8 layer differs from the plain layer by no more than the
+    format's error bound carried through the softmax: a logit moves by at most
+    Delta = scale * sum_c (e_q|k| + |q|e_k + e_q e_k), a probability by a factor
+    within exp(+-2 Delta), so each softmax output channel by at most
+    (exp(2 Delta) - 1) max|v|, and the projected output accordingly."""
+    inp = _mx_layer(44)
+    B, H, T, N, d = inp["q"].shape
+    rows = np.arange(T * N)
+    diff = (O.hybrid_layer_rows(**inp, rows=rows, softmax_mxfp8=True) -
+            O.hybrid_layer_rows(**inp, rows=rows))
+    scale = 1.0 / np.sqrt(d)
+    g_s = 1.0 / (1.0 + np.exp(-(inp["x"] @ inp["w_gs"])))
+    bound_o = np.zeros((B, T * N, H * d))
+    for b in range(B):
+        for h in range(H):
+            q = inp["q"][b, h].reshape(T * N, d)
+            k = inp["k"][b, h].reshape(T * N, d)
+            v = inp["v"][b, h].reshape(T * N, d)
+            eq, ek = _mx_elem_bound(q), _mx_elem_bound(k)
+            delta = scale * (eq @ np.abs(k).T + np.abs(q) @ ek.T + eq @ ek.T)   # [queries, keys]
+            dmax = delta.max(axis=1)
+            bound_o[b, :, h * d:(h + 1) * d] = np.expm1(2 * dmax)[:, None] * np.abs(v).max(axis=0)[None]
+    bound = (np.abs(g_s) * bound_o) @ np.abs(inp["w_os"])
+    assert np.all(np.abs(diff) <= bound * (1 + 1e-9))
+    assert np.max(np.abs(diff)) > 0
+
+
+def test_mxfp8_layer_power_of_two_invariance():
+    """Scaling q by 2^k and the softmax scale by 2^-k leaves the MXFP8 layer
+    unchanged at eps = 0: MXFP8 codes are invariant under powers of two (the
+    block scale absorbs them) and the linear branch's RMSNorm is scale-free."""
+    inp = _mx_layer(45)
+    d = inp["q"].shape[-1]
+    rows = np.arange(7 * 3)
+    base = O.hybrid_layer_rows(**inp, rows=rows, eps=0.0, scale=1.0 / np.sqrt(d), softmax_mxfp8=True)
+    for k in (-7, 5):
+        got = O.hybrid_layer_rows(**{**inp, "q": np.ldexp(inp["q"], k)}, rows=rows, eps=0.0,
+                                  scale=np.ldexp(1.0 / np.sqrt(d), -k), softmax_mxfp8=True)
+        assert np.max(np.abs(got - base)) < 1e-12 * np.max(np.abs(base))

@@ -10,9 +10,6 @@
 // rounded to the nearest E4M3 value, ties to the even code, saturating at 448,
 // with the sign bit of x.
 //
-// x may be multiplied by a factor (fp32, rounded to nearest) before it is
-// encoded: the softmax branch folds its log2-unit score scale into q.
-//
 // One thread per block: 64 bytes in, 32 code bytes and one scale byte out.
 // The scaling is an exact ldexp; the rounding works on the fp32 bit pattern
 // (normal range) or on a * 2^9 (subnormal range, rint is ties-to-even).
@@ -33,7 +30,7 @@ __device__ __forceinline__ unsigned e4m3_magnitude(float a) {
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16* __restrict__ x,
                                                              unsigned char* __restrict__ codes,
                                                              unsigned char* __restrict__ scales,
-                                                             int64_t nblocks, float mul) {
+                                                             int64_t nblocks) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
   const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
@@ -44,8 +41,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16* __restr
     const unsigned u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[8 * i + 2 * j] = __uint_as_float(u[j] << 16) * mul;
-      v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u) * mul;
+      v[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
     }
   }
   float amax = 0.f;
@@ -72,11 +69,11 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16* __restr
 }
 
 hipError_t launch_mxfp8_quantize(const void* x, int64_t n_elems, void* codes, void* scales,
-                                 hipStream_t st, float mul) {
+                                 hipStream_t st) {
   const int64_t nblocks = n_elems / 32;
   if (nblocks == 0) return hipSuccess;
   mxfp8_quantize_kernel<<<(unsigned)((nblocks + 255) / 256), 256, 0, st>>>(
-      (const bf16*)x, (unsigned char*)codes, (unsigned char*)scales, nblocks, mul);
+      (const bf16*)x, (unsigned char*)codes, (unsigned char*)scales, nblocks);
   return hipGetLastError();
 }
 

@@ -537,7 +537,7 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
   if (mx && !qs) {
     const int64_t n = (int64_t)p.B * p.H * p.Lt * s->head_dim;
     ph = phase_begin(kPhQuantize, st);
-    e = launch_mxfp8_quantize(q, n, ws + l.qc, ws + l.qs, st, p.scale_log2);
+    e = launch_mxfp8_quantize(q, n, ws + l.qc, ws + l.qs, st);
     if (e == hipSuccess) e = launch_mxfp8_quantize(k, n, ws + l.kc, ws + l.ks, st);
     phase_end(ph, st);
     if (e != hipSuccess) return hip_fail(e, "mxfp8 quantize launch");
@@ -550,7 +550,7 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
     p.ks = ks;
   }
   ph = phase_begin(kPhWindowAttn, st);
-  e = mx ? launch_window_attn_mxfp8(p, qs == nullptr, st) : launch_window_attn(s->dtype, s->head_dim, p, st);
+  e = mx ? launch_window_attn_mxfp8(p, st) : launch_window_attn(s->dtype, s->head_dim, p, st);
   phase_end(ph, st);
   if (e != hipSuccess) return hip_fail(e, "window attention launch");
   ph = phase_begin(kPhAnchorMerge, st);

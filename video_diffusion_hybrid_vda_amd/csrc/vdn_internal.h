@@ -70,14 +70,11 @@ hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, voi
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st);
 hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st);
 hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st);
-// head_dim 128, bf16 v / gate / out; p.q, p.k E4M3 codes with scales p.qs, p.ks.
-// q_scaled: q was multiplied by p.scale_log2 before its encoding (the scores
-// then come out in log2 units)
-hipError_t launch_window_attn_mxfp8(const AttnParams& p, bool q_scaled, hipStream_t st);
-// MXFP8 (E4M3 codes, one E8M0 scale per 32 consecutive elements) of n_elems bf16
-// values, each first multiplied by mul (fp32)
+// head_dim 128, bf16 v / gate / out; p.q, p.k E4M3 codes with scales p.qs, p.ks
+hipError_t launch_window_attn_mxfp8(const AttnParams& p, hipStream_t st);
+// MXFP8 (E4M3 codes, one E8M0 scale per 32 consecutive elements) of n_elems bf16 values
 hipError_t launch_mxfp8_quantize(const void* x, int64_t n_elems, void* codes, void* scales,
-                                 hipStream_t st, float mul = 1.f);
+                                 hipStream_t st);
 // Frame f = bh*T + t of q/k/v starts at row (f / T) * Lt + (f % T) * N (Lt rows per (batch, head):
 // T*N video tokens, then context tokens the linear branch does not read).
 hipError_t launch_vda_gram(int dtype, int d, const void* k, const void* v, const float* beta,

@@ -1114,18 +1114,6 @@ __device__ __forceinline__ void mma8_0(f32x16& d, i32x8 k, i32x8 q, int ks, int 
       : "=&v"(d)
       : "v"(k), "a"(q), "v"(ks), "v"(qs), "n"(SEL & 1), "n"(SEL >> 1));
 }
-// the first product of a score chain started from the tile c (-m of each query)
-template <int SEL>
-__device__ __forceinline__ void mma8_c(f32x16& d, i32x8 k, i32x8 q, const f32x16& c, int ks, int qs) {
-  asm volatile(
-      "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %3, %4, %5 op_sel:[0,%6,0] op_sel_hi:[0,%7,0]"
-      : "=&v"(d)
-      : "v"(k), "a"(q), "v"(c), "v"(ks), "v"(qs), "n"(SEL & 1), "n"(SEL >> 1));
-}
-// t = 2^s
-__device__ __forceinline__ void exp2_v(float& t, float s) {
-  asm volatile("v_exp_f32 %0, %1" : "=&v"(t) : "v"(s));
-}
 template <int SEL>
 __device__ __forceinline__ void mma8(f32x16& d, i32x8 k, i32x8 q, int ks, int qs) {
   asm volatile(
@@ -1143,12 +1131,8 @@ __device__ __forceinline__ void ds_s(int& d, int addr) {
 }
 }  // namespace v8
 
-// QS: q was multiplied by p.scale_log2 before its encoding, so a product is
-// already in the exponent's units; each query's score chain starts from -m
-// (the tile nt) and the exponential of a score is v_exp_f32 alone.  A rescale
-// also shifts the pending half tile's scores by the change of m.  Otherwise
-// (codes given by the caller) scores are scaled on the way into v_exp_f32.
-template <bool QS>
+// Scores are the products of the decoded q and k; each is scaled into log2
+// units on its way into v_exp_f32 (one v_fma_f32 with the running maximum).
 __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams p) {
   using namespace v8;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[LDSB8];
@@ -1254,13 +1238,10 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
   f32x16 o[4][QT];
   f32x4 lsum[QT];
   float mrun[QT], negm[QT], mtile[QT];
-  f32x16 nt[QT];   // QS: -m of the lane's query in every element
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = QS ? 0.f : -INFINITY;
-    negm[qt] = QS ? 0.f : INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nt[qt][r] = 0.f;
+    mrun[qt] = -INFINITY;
+    negm[qt] = INFINITY;
     lsum[qt] = f32x4{};
     asm volatile("" : "+a"(lsum[qt]));
 #pragma unroll
@@ -1276,8 +1257,6 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
     for (int e = 0; e < 8; ++e) sel[e] = one;
   }
   const float c2 = p.scale_log2;
-  const float cs = QS ? 1.f : c2;   // factor from a product to log2 units
-  const float zero = 0.f;
   int civ = 0, ck0 = kb_of(0), cke = ke_of(0);
   auto advance = [&]() {
     ck0 += BN;
@@ -1326,7 +1305,7 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
       float mx = sc[qt][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[qt][r]);
-      mtile[qt] = QS ? halves_max(mx) + mrun[qt] : halves_max(mx) * c2;
+      mtile[qt] = halves_max(mx) * c2;
     }
   };
   auto rescale = [&](f32x16 (&sc)[QT]) {
@@ -1335,14 +1314,6 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
     for (int qt = 0; qt < QT; ++qt) {
       const float mnew = fmaxf(mrun[qt], mtile[qt]);
       const float alpha = fast_exp2(mrun[qt] - mnew);
-      if constexpr (QS) {
-        const float shift = mrun[qt] - mnew;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[qt][r] += shift;
-          nt[qt][r] = -mnew;
-        }
-      }
       mrun[qt] = mnew;
       negm[qt] = -mnew;
       const float a_hi = __shfl(alpha, (lane & 15) + 16);
@@ -1392,8 +1363,7 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
     constexpr int v1_off = voffc(decltype(PST)::value, decltype(PKT)::value, 1);
     auto val = [&](auto I, int e) {
       constexpr int i = decltype(I)::value, j = kPair8[i], s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
-      if constexpr (QS) exp2_v(tt[(2 * i + e) % 4], cur[qt][8 * s4 + 2 * w + e]);
-      else fma_exp(tt[(2 * i + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
+      fma_exp(tt[(2 * i + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
     };
     auto cvt = [&](auto I) {
       constexpr int i = decltype(I)::value, j = kPair8[i], s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
@@ -1428,8 +1398,7 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
       if constexpr (m < 4) {
         constexpr int kh = m / 2, qt = m % 2;
         if constexpr (qt == 0) wait_lgkm<wait8_s(kh)>();
-        if constexpr (kh == 0 && QS) mma8_c<2 * qt>(nxt[qt], kfrag(0), qf8[qt][0], nt[qt], ksc[0], qsc);
-        else if constexpr (kh == 0) mma8_0<2 * qt>(nxt[qt], kfrag(0), qf8[qt][0], ksc[0], qsc);
+        if constexpr (kh == 0) mma8_0<2 * qt>(nxt[qt], kfrag(0), qf8[qt][0], ksc[0], qsc);
         else mma8<2 * qt + 1>(nxt[qt], kfrag(1), qf8[qt][1], ksc[1], qsc);
       } else if constexpr (m < 12) {
         constexpr int dt = (m - 4) / 2, qt = m % 2;
@@ -1483,16 +1452,13 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
           max_acc(mx[1], nxt[1][15]);
         }
       }
-      if constexpr (m == 20) halves_max_scaled(mx[0], cs);
-      if constexpr (m == 21) halves_max_scaled(mx[1], cs);
-      if constexpr (m == 22) {
-        if constexpr (QS) grow = grow_mask(mx[0], zero, mx[1], zero);   // maxima relative to m
-        else grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
-      }
+      if constexpr (m == 20) halves_max_scaled(mx[0], c2);
+      if constexpr (m == 21) halves_max_scaled(mx[1], c2);
+      if constexpr (m == 22) grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
     };
     static_for<0, NSLOT8>(slot);
-    mtile[0] = QS ? mx[0] + mrun[0] : mx[0];
-    mtile[1] = QS ? mx[1] + mrun[1] : mx[1];
+    mtile[0] = mx[0];
+    mtile[1] = mx[1];
     return grow;
   };
 
@@ -1514,26 +1480,8 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
   mma8<1>(sa[0], kfrag(1), qf8[0][1], ksc[1], qsc);
   mma8<3>(sa[1], kfrag(1), qf8[1][1], ksc[1], qsc);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  if constexpr (QS) {
-    // the running max starts as this half tile's max (m = 0 so far: the
-    // products are the scores themselves); no keys at all leaves m = 0
-    if (kn < 32) mask(sa, kn);
-    half_max(sa);
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float m0 = mtile[qt] > -INFINITY ? mtile[qt] : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sa[qt][r] -= m0;
-        nt[qt][r] = -m0;
-      }
-      mrun[qt] = m0;
-      negm[qt] = -m0;
-    }
-  } else {
-    half_max(sa);
-    boundary(sa, kn, outran() ? 1ull : 0ull);
-  }
+  half_max(sa);
+  boundary(sa, kn, outran() ? 1ull : 0ull);
   // the reads the first half step expects from a half step before it: K of
   // half tile (stage 0, half 1), then V step 0 of half tile (stage 0, half 0)
   ds_c<kcoff8(0, 1)>(klo[0], kcoff[0][0]);
@@ -1693,12 +1641,9 @@ hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t
   return launch_attn_t<float, 128>(p, st);
 }
 
-hipError_t launch_window_attn_mxfp8(const AttnParams& p, bool q_scaled, hipStream_t st) {
+hipError_t launch_window_attn_mxfp8(const AttnParams& p, hipStream_t st) {
   if (p.bm != attn_query_tile(1, 128)) return hipErrorInvalidValue;
-  if (p.total > 0) {
-    if (q_scaled) window_attn_mxfp8_d128_kernel<true><<<p.total, 256, 0, st>>>(p);
-    else window_attn_mxfp8_d128_kernel<false><<<p.total, 256, 0, st>>>(p);
-  }
+  if (p.total > 0) window_attn_mxfp8_d128_kernel<<<p.total, 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
