@@ -1,17 +1,19 @@
 """GPU parity: every C-ABI entry point against the fp64 oracle on the same
 seeded inputs.
 
-Error measure: max |gpu - oracle| / RMS(oracle), bounded by 2e-2 for bf16
-I/O with fp32 accumulation and by 1e-4 for the fp32 path.  The workload
-configurations use this measure as it stands.  Stress inputs (random gates,
-RMSNorm weights, sharpened softmax) give outputs with max/RMS near 10, where
-the bf16 rounding of the output itself (half an ulp, 2^-9 relative) already
-reaches 2%; for those the same bar applies to the error in excess of each
-element's own half-ulp (`excess_err`), which any bf16-output implementation
-incurs.  Small shapes are compared element by element; they span several
-query/key tiles, ragged tails, every mask regime (dense, banded, anchors
-on/off, split anchor rows) and head_dim 32/64/128.  Full-size shapes are
-compared on sampled tokens and heads, plus invariants that hold at any size.
+Error measure (tests/measure.py): max |gpu - oracle| / RMS(oracle), bounded
+by 2e-2 for bf16 I/O with fp32 accumulation and by 1e-4 for the fp32 path.
+Every case drawn from the workload recipe is held to it as it stands.  Named
+stress inputs (random gates, random RMSNorm weights, a sharpened softmax) may
+use the error beyond each element's own bf16 rounding instead, and only where
+their output's max/RMS is at least 5; they log both figures.  A layer with
+context tokens is measured per row class (video rows, context rows), each
+against its own RMS: context rows carry no linear-branch output and are far
+smaller than video rows, so one RMS over both would mostly measure the mix.
+Small shapes are compared element by element; they span several query/key
+tiles, ragged tails, every mask regime (dense, banded, anchors on/off, split
+anchor rows) and head_dim 32/64/128.  Full-size shapes are compared on sampled
+tokens and heads, plus invariants that hold at any size.
 """
 import os
 import sys
@@ -21,13 +23,13 @@ import numpy as np
 import pytest
 import torch
 
+from measure import TOL, check, rel_err
 from oracle import vdn_oracle as O
 from video_diffusion_hybrid_vda_amd import synth
 from video_diffusion_hybrid_vda_amd.synth import VdnConfig
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
 # states are fp32 in both paths (bf16 inputs are exact in fp32)
 STATE_TOL = {"f32": 1e-4, "bf16": 1e-3}
 
@@ -47,20 +49,6 @@ def vdn():
 
 def np32(t):
     return t.detach().float().cpu().numpy()
-
-
-def rel_err(got, ref):
-    ref = np.asarray(ref, dtype=np.float64)
-    got = np.asarray(got, dtype=np.float64)
-    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
-
-
-def excess_err(got, ref, dtype):
-    """max(|got - ref| - ulp/2(ref), 0) / RMS(ref); plain rel_err for fp32."""
-    ref = np.asarray(ref, dtype=np.float64)
-    got = np.asarray(got, dtype=np.float64)
-    slack = 2.0 ** -9 * np.abs(ref) if dtype == "bf16" else 0.0
-    return float(np.max(np.maximum(np.abs(got - ref) - slack, 0.0)) / np.sqrt(np.mean(ref * ref)))
 
 
 def gpu_inputs(cfg, with_layer=True, sharp=0.0):
@@ -106,12 +94,7 @@ def test_hybrid_tiny(vdn, name, cfg):
     ref = O.hybrid_layer(*(np32(inp[k]) for k in ("x", "q", "k", "v", "gamma", "beta", "w_gs",
                                                   "w_gl", "rms_w", "w_os", "w_ol")),
                          **oracle_kwargs(cfg))
-    err = rel_err(np32(out), ref)
-    exc = excess_err(np32(out), ref, cfg.dtype)
-    log(f"  rel err {err:.3e} excess {exc:.3e} (tol {TOL[cfg.dtype]})")
-    if name.startswith("config"):
-        assert err <= TOL[cfg.dtype]
-    assert exc <= TOL[cfg.dtype]
+    check(log, "layer", np32(out), ref, cfg.dtype)
 
 
 # sharp: q scale with unnormalised keys (logit std = sharp); 0 = the configs' recipe.
@@ -149,11 +132,10 @@ def test_window_attn(vdn, name, cfg, sharp):
             ref[b, h], ref_lse[b, h] = o, l
     ref_tok = np.transpose(ref, (0, 2, 1, 3)).reshape(B, T * N, H * d)
     g = np32(gate).astype(np.float64)
-    e1 = excess_err(np32(out), g * ref_tok, cfg.dtype)
-    e2 = excess_err(np32(out_ng), ref_tok, cfg.dtype)
+    check(log, "gated (random gate)", np32(out), g * ref_tok, cfg.dtype, stress=True)
+    check(log, "ungated", np32(out_ng), ref_tok, cfg.dtype, stress=sharp > 0)
     e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
-    log(f"  gated {e1:.3e} ungated {e2:.3e} (plain {rel_err(np32(out_ng), ref_tok):.3e}) lse abs {e3:.3e}")
-    assert e1 <= TOL[cfg.dtype] and e2 <= TOL[cfg.dtype]
+    log(f"  lse abs {e3:.3e}")
     assert e3 <= (1e-4 if cfg.dtype == "f32" else 1e-2)
 
 
@@ -176,16 +158,18 @@ def test_vda_scan(vdn, name, cfg):
     inp["rms_w"] = (0.5 + torch.rand(H * d, generator=gen)).cuda()
     gate = torch.rand(B, T * N, H * d, generator=gen).to(synth.DTYPES[cfg.dtype]).cuda()
     out, states = vdn.vda_scan(shape, inp, gate_l=gate, with_states=True)
+    out1 = vdn.vda_scan(shape, dict(inp, rms_w=None))
     torch.cuda.synchronize()
-    o_l, sf, sb = O.vda_branch(*(np32(inp[k]).astype(np.float64) for k in ("q", "k", "v", "gamma", "beta", "rms_w")),
-                               cfg.rms_eps)
+    qkv = [np32(inp[k]).astype(np.float64) for k in ("q", "k", "v", "gamma", "beta")]
+    o_l, sf, sb = O.vda_branch(*qkv, np32(inp["rms_w"]).astype(np.float64), cfg.rms_eps)
     ref = np32(gate).astype(np.float64) * O.merge_heads(o_l)
     st = np32(states)
     es = max(rel_err(st[0], sf), rel_err(st[1], sb))
-    eo = excess_err(np32(out), ref, cfg.dtype)
-    log(f"  states {es:.3e} out {eo:.3e} (plain {rel_err(np32(out), ref):.3e})")
+    log(f"  states {es:.3e}")
     assert es <= STATE_TOL[cfg.dtype]
-    assert eo <= TOL[cfg.dtype]
+    check(log, "out (random gate and RMSNorm weight)", np32(out), ref, cfg.dtype, stress=True)
+    o_1, _, _ = O.vda_branch(*qkv, np.ones(H * d), cfg.rms_eps)
+    check(log, "out (ungated, unit RMSNorm weight)", np32(out1), O.merge_heads(o_1), cfg.dtype)
 
 
 def test_vda_config2_full(vdn):
@@ -247,10 +231,7 @@ def test_dense_layer(vdn, name, cfg):
     out = vdn.dense_attn(shape, inp, inp["w_os"])
     torch.cuda.synchronize()
     ref = O.dense_layer(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(inp["w_os"]))
-    err = rel_err(np32(out), ref)
-    exc = excess_err(np32(out), ref, cfg.dtype)
-    log(f"  rel err {err:.3e} excess {exc:.3e}")
-    assert exc <= TOL[cfg.dtype]
+    check(log, "dense layer", np32(out), ref, cfg.dtype)
 
 
 def test_param_range_check(vdn):
@@ -335,12 +316,12 @@ def test_context_hybrid(vdn, name, cfg):
     ref = O.hybrid_layer_ctx(*(np32(inp[k]) for k in ("x", "q", "k", "v", "gamma", "beta", "w_gs",
                                                       "w_gl", "rms_w", "w_os", "w_ol")),
                              cfg.tokens_per_frame, **oracle_kwargs(cfg))
-    err = rel_err(np32(out), ref)
-    exc = excess_err(np32(out), ref, cfg.dtype)
     L = cfg.video_len
-    err_ctx = excess_err(np32(out[:, L:]), ref[:, L:], cfg.dtype)
-    log(f"  rel err {err:.3e} excess {exc:.3e} context rows {err_ctx:.3e} (tol {TOL[cfg.dtype]})")
-    assert exc <= TOL[cfg.dtype] and err_ctx <= TOL[cfg.dtype]
+    g = np32(out)
+    log(f"  one RMS over both row classes: rel err {rel_err(g, ref):.3e} (RMS context / RMS video rows "
+        f"{np.sqrt(np.mean(ref[:, L:] ** 2) / np.mean(ref[:, :L] ** 2)):.3f})")
+    check(log, "video rows", g[:, :L], ref[:, :L], cfg.dtype)
+    check(log, "context rows", g[:, L:], ref[:, L:], cfg.dtype)
 
 
 @pytest.mark.parametrize("name,cfg", CTX, ids=[t[0] for t in CTX])
@@ -358,7 +339,11 @@ def test_context_branches(vdn, name, cfg):
     out_l, states = vdn.vda_scan(shape, inp, with_states=True)
     torch.cuda.synchronize()
     ref_s, ref_lse = ctx_oracle_softmax(cfg, inp)
-    e_s = excess_err(np32(out_s), np32(gate).astype(np.float64) * ref_s, cfg.dtype)
+    g_s = np32(gate).astype(np.float64)
+    check(log, "softmax video rows (random gate)", np32(out_s[:, :L]), g_s[:, :L] * ref_s[:, :L], cfg.dtype,
+          stress=True)
+    check(log, "softmax context rows (random gate)", np32(out_s[:, L:]), g_s[:, L:] * ref_s[:, L:], cfg.dtype,
+          stress=True)
     e_lse = float(np.max(np.abs(np32(lse) - ref_lse)))
     T, N = cfg.frames, cfg.tokens_per_frame
     vid = {k: inp[k][:, :, :L].reshape(B, H, T, N, d) for k in ("q", "k", "v")}
@@ -367,11 +352,11 @@ def test_context_branches(vdn, name, cfg):
                                                                       inp["rms_w"])), cfg.rms_eps)
     st = np32(states)
     e_st = max(rel_err(st[0], sf), rel_err(st[1], sb))
-    e_l = excess_err(np32(out_l[:, :L]), O.merge_heads(o_l), cfg.dtype)
+    check(log, "linear video rows", np32(out_l[:, :L]), O.merge_heads(o_l), cfg.dtype)
     nz = torch.count_nonzero(out_l[:, L:]).item()
-    log(f"  softmax {e_s:.3e} lse abs {e_lse:.3e} states {e_st:.3e} linear {e_l:.3e} ctx nonzeros {nz}")
-    assert e_s <= TOL[cfg.dtype] and e_lse <= (1e-4 if cfg.dtype == "f32" else 1e-2)
-    assert e_st <= STATE_TOL[cfg.dtype] and e_l <= TOL[cfg.dtype]
+    log(f"  lse abs {e_lse:.3e} states {e_st:.3e} ctx nonzeros {nz}")
+    assert e_lse <= (1e-4 if cfg.dtype == "f32" else 1e-2)
+    assert e_st <= STATE_TOL[cfg.dtype]
     assert nz == 0
 
 
@@ -479,42 +464,68 @@ def test_hybrid_ragged_projection_tiles_sampled(vdn):
     assert err <= TOL["bf16"]
 
 
-def test_length_sweep_T42_batch2_sampled(vdn):
-    """Batch-2 layer of the length sweep at 42 latent frames (B2 H24 d128
-    N4032): the hybrid layer and the dense baseline on the same inputs, both
-    checked at sampled tokens of both batch entries."""
-    cfg = synth.CONFIGS[5].replace(frames=42)
-    log("[sweep] B2 T42 hybrid + dense")
+def _sweep_rows(cfg):
+    """Rows checked in the batch-2 sweep layers (every row in both batch
+    entries): both anchor frames' first and last tokens, chunk edges at the
+    start and at the end, the ragged last chunk, random tokens."""
+    T, N = cfg.frames, cfg.tokens_per_frame
+    picks = {0, N - 1, N, 5 * N - 1, 5 * N, (T // 2) * N + 7, (T - 3) * N - 1, (T - 2) * N,
+             (T - 1) * N - 1, (T - 1) * N, T * N - 1}
+    g = torch.Generator().manual_seed(cfg.frames)
+    picks.update(torch.randint(0, T * N, (6,), generator=g).tolist())
+    return np.array(sorted(picks))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("frames", [42, 102])
+def test_length_sweep_batch2_sampled(vdn, frames):
+    """Batch-2 layer of the length sweep (B2 H24 d128 N4032) at 42 and 102
+    latent frames: the hybrid layer and the dense baseline on the same inputs,
+    both checked at sampled tokens of both batch entries.  At 102 frames each
+    of q, k, v, x and out holds 2.53e9 elements, so the rows of batch entry 1
+    sit past element 2^31 of every tensor."""
+    cfg = synth.CONFIGS[5].replace(frames=frames)
+    log(f"[sweep] B2 T{frames} hybrid + dense")
     t0 = time.time()
     inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
     shape = vdn.shape_from_config(cfg)
     out = vdn.hybrid_attn(shape, inp)
+    torch.cuda.synchronize()
     dense = vdn.dense_attn(shape, inp, inp["w_os"])
     torch.cuda.synchronize()
     log(f"  gpu done {time.time() - t0:.1f}s")
-    rows = synth.sample_tokens(cfg, 10)
-    host = {k: np32(v) for k, v in inp.items() if k not in ("q", "k", "v")}
+    rows = _sweep_rows(cfg)
+    out_r = np32(out[:, rows])
+    dense_r = np32(dense[:, rows])
+    del out, dense
+    host = {k: np32(v) for k, v in inp.items() if k not in ("q", "k", "v", "x")}
+    host["x"] = np32(inp["x"][:, rows])
     for k in ("q", "k", "v"):
         host[k] = inp[k].float().cpu().numpy()
-    ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+    del inp
+    torch.cuda.empty_cache()
+    x_rows = np.zeros((cfg.batch, cfg.seq_len, cfg.model_dim), dtype=np.float32)
+    x_rows[:, rows] = host["x"]          # hybrid_layer_rows reads x at `rows` only
+    ref = O.hybrid_layer_rows(x_rows, host["q"], host["k"], host["v"], host["gamma"], host["beta"],
                               host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
                               rows, **oracle_kwargs(cfg))
-    err = rel_err(np32(out[:, rows]), ref)
-    log(f"  hybrid rel err {err:.3e} ({time.time() - t0:.1f}s)")
-    assert err <= TOL["bf16"]
+    log(f"  oracle hybrid done ({time.time() - t0:.1f}s)")
+    for b in range(cfg.batch):
+        check(log, f"hybrid, batch entry {b}", out_r[b], ref[b], "bf16")
     B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    drows = rows[[0, len(rows) - 1]]        # frame 0 and the last token (past 2^31 in entry 1)
     allowed = np.ones((T, T), dtype=bool)
-    o = np.zeros((B, len(rows), H * d))
+    o = np.zeros((B, len(drows), H * d))
     for b in range(B):
         for h in range(H):
-            oo, _ = O.window_attention(host["q"][b, h].astype(np.float64), host["k"][b, h].astype(np.float64),
-                                       host["v"][b, h].astype(np.float64), allowed, 1 / np.sqrt(d),
-                                       np.array(rows))
+            oo, _ = O.window_attention(host["q"][b, h], host["k"][b, h], host["v"][b, h], allowed,
+                                       1 / np.sqrt(d), drows)
             o[b, :, h * d:(h + 1) * d] = oo
     ref_d = o @ host["w_os"].astype(np.float64)
-    err_d = rel_err(np32(dense[:, rows]), ref_d)
-    log(f"  dense rel err {err_d:.3e} ({time.time() - t0:.1f}s)")
-    assert err_d <= TOL["bf16"]
+    sel = np.searchsorted(rows, drows)
+    for b in range(B):
+        check(log, f"dense, batch entry {b} (rows {drows.tolist()})", dense_r[b][sel], ref_d[b], "bf16")
+    log(f"  ({time.time() - t0:.1f}s)")
 
 
 def test_context_config3_sampled(vdn):
@@ -542,14 +553,15 @@ def test_context_config3_sampled(vdn):
 # The softmax branch's scores from MXFP8 q and k (OCP MXFP8 along head_dim;
 # the 10100.com article's 实验结果 runs the denoiser in MXFP8).  The oracle
 # quantises q and k itself (oracle/mxfp8.py, pinned against the OCP formats)
-# and runs the fp64 softmax on the decoded values, so the bar is the bf16
-# one; the codes and scales themselves must match bit for bit.
+# and runs the fp64 softmax, with the usual scale, on the decoded values, so
+# the bar is the bf16 one; the codes and scales themselves must match bit for
+# bit.
 
 from oracle import mxfp8 as MX
 
 
-def mx_values(a, mul=None):
-    return O.mxfp8_values(np.asarray(a, dtype=np.float64), mul)
+def mx_values(a):
+    return O.mxfp8_values(np.asarray(a, dtype=np.float64))
 
 
 def test_mxfp8_quantize_bit_exact(vdn):
@@ -608,8 +620,8 @@ MXCASES = [
 @pytest.mark.parametrize("name,cfg,sharp", MXCASES, ids=[t[0] for t in MXCASES])
 def test_window_attn_mxfp8(vdn, name, cfg, sharp):
     """Softmax branch with MXFP8 scores, gated and ungated, with lse: the mode
-    flag (q encoded as c * q, c the fp32 log2-unit scale) and the entry point
-    that takes the caller's codes of q and k, each against its own oracle."""
+    flag (the library encodes q and k) and the entry point that takes the
+    caller's codes, both against the oracle's softmax of the decoded q and k."""
     log(f"[mxfp8 window] {name}")
     inp = gpu_inputs(cfg, with_layer=False, sharp=sharp)
     shape = vdn.shape_from_config(cfg, softmax_mxfp8=True)
@@ -618,41 +630,33 @@ def test_window_attn_mxfp8(vdn, name, cfg, sharp):
     gate = torch.rand(B, Lt, H * d, generator=gen).to(torch.bfloat16).cuda()
     out, lse = vdn.window_attn(shape, inp, gate_s=gate, with_lse=True)
     out_ng = vdn.window_attn(shape, inp)
+    out_bf16 = vdn.window_attn(vdn.shape_from_config(cfg), inp)
     qc, qs = vdn.mxfp8_quantize(inp["q"].contiguous())
     kc, ks = vdn.mxfp8_quantize(inp["k"].contiguous())
     out_pre = vdn.window_attn_mxfp8(shape, qc, qs, kc, ks, inp["v"], gate_s=gate)
     torch.cuda.synchronize()
     allowed = O.allowed_frames(cfg.frames, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first,
                                cfg.anchor_last)
-    c = O.score_scale_log2_fp32(d)
-
-    def oracle(scaled):
-        ref = np.zeros((B, Lt, H * d))
-        ref_lse = np.zeros((B, H, Lt))
-        for b in range(B):
-            for h in range(H):
-                q8 = mx_values(np32(inp["q"][b, h]), c if scaled else None)
-                k8 = mx_values(np32(inp["k"][b, h]))
-                v = np32(inp["v"][b, h]).astype(np.float64)
-                sc = np.log(2.0) if scaled else 1 / np.sqrt(d)
-                if cfg.context_tokens:
-                    o, l = O.window_attention_ctx(q8, k8, v, allowed, N, sc)
-                else:
-                    o, l = O.window_attention(q8, k8, v, allowed, sc)
-                ref[b, :, h * d:(h + 1) * d] = o.reshape(Lt, d)
-                ref_lse[b, h] = l
-        return ref, ref_lse
-
-    ref, ref_lse = oracle(True)
+    ref = np.zeros((B, Lt, H * d))
+    ref_lse = np.zeros((B, H, Lt))
+    for b in range(B):
+        for h in range(H):
+            q8 = mx_values(np32(inp["q"][b, h]))
+            k8 = mx_values(np32(inp["k"][b, h]))
+            v = np32(inp["v"][b, h]).astype(np.float64)
+            if cfg.context_tokens:
+                o, l = O.window_attention_ctx(q8, k8, v, allowed, N, 1 / np.sqrt(d))
+            else:
+                o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d))
+            ref[b, :, h * d:(h + 1) * d] = o.reshape(Lt, d)
+            ref_lse[b, h] = l
     g = np32(gate).astype(np.float64)
-    e1 = excess_err(np32(out), g * ref, "bf16")
-    e2 = excess_err(np32(out_ng), ref, "bf16")
+    check(log, "gated (random gate)", np32(out), g * ref, "bf16", stress=True)
+    check(log, "ungated", np32(out_ng), ref, "bf16", stress=sharp > 0)
+    check(log, "codes entry point, gated", np32(out_pre), g * ref, "bf16", stress=True)
     e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
-    ref_pre, _ = oracle(False)
-    e4 = excess_err(np32(out_pre), g * ref_pre, "bf16")
-    log(f"  gated {e1:.3e} ungated {e2:.3e} (plain {rel_err(np32(out_ng), ref):.3e}) lse abs {e3:.3e} "
-        f"codes entry {e4:.3e}")
-    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"] and e3 <= 1e-2 and e4 <= TOL["bf16"]
+    log(f"  lse abs {e3:.3e}; MXFP8 against bf16 scores on the GPU: {rel_err(np32(out_ng), np32(out_bf16)):.3e}")
+    assert e3 <= 1e-2
 
 
 def test_hybrid_mxfp8(vdn):
@@ -668,9 +672,11 @@ def test_hybrid_mxfp8(vdn):
     ref = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
                               host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
                               rows, softmax_mxfp8=True, **oracle_kwargs(cfg))
-    err = rel_err(np32(out), ref)
-    log(f"  rel err {err:.3e}")
-    assert err <= TOL["bf16"]
+    check(log, "layer", np32(out), ref, "bf16")
+    ref_bf16 = O.hybrid_layer_rows(host["x"], host["q"], host["k"], host["v"], host["gamma"], host["beta"],
+                                   host["w_gs"], host["w_gl"], host["rms_w"], host["w_os"], host["w_ol"],
+                                   rows, **oracle_kwargs(cfg))
+    log(f"  the oracle's MXFP8 layer against its bf16-score layer: {rel_err(ref, ref_bf16):.3e}")
 
 
 def test_window_attn_mxfp8_T102_two_heads_sampled(vdn):
@@ -690,12 +696,11 @@ def test_window_attn_mxfp8_T102_two_heads_sampled(vdn):
     allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
     worst = 0.0
     for h in range(cfg.heads):
-        c = O.score_scale_log2_fp32(d)
         q8 = inp["q"][0, h].float().cpu().numpy().astype(np.float64)
-        q8.reshape(-1, d)[rows] = mx_values(q8.reshape(-1, d)[rows], c)   # only the sampled queries are read
+        q8.reshape(-1, d)[rows] = mx_values(q8.reshape(-1, d)[rows])   # only the sampled queries are read
         k8 = mx_values(inp["k"][0, h].float().cpu().numpy())
         v = inp["v"][0, h].float().cpu().numpy().astype(np.float64)
-        o, l = O.window_attention(q8, k8, v, allowed, np.log(2.0), rows)
+        o, l = O.window_attention(q8, k8, v, allowed, 1 / np.sqrt(d), rows)
         e = rel_err(np32(out[0, rows, h * d:(h + 1) * d]), o)
         el = float(np.max(np.abs(np32(lse[0, h, rows]) - l)))
         log(f"  head {h}: rel err {e:.3e} lse abs {el:.3e} ({time.time() - t0:.1f}s)")

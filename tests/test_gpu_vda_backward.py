@@ -2,10 +2,14 @@
 oracle (oracle.vda_backward, pinned by finite differences of the forward
 oracle in test_vda_backward_oracle.py).
 
-Error measure, per output: max |gpu - oracle| / RMS(oracle), bounded by 2e-2
-for bf16 I/O and 1e-4 for fp32 I/O (fp32 arithmetic inside in both); for the
-bf16 outputs dq, dk, dv the bound applies to the error in excess of each
-element's own bf16 rounding (excess_err), as in the forward parity tests.  Small
+Error measure (tests/measure.py), per output: max |gpu - oracle| / RMS(oracle),
+bounded by 2e-2 for bf16 I/O and 1e-4 for fp32 I/O.  For bf16 I/O the
+token-side products run on bf16 MFMA with fp32 operands split into hi and lo
+bf16 halves and fp32 accumulation; the rest is fp32.  dq, dk and dv are
+gradients, heavy-tailed (max/RMS near 10 at the headline shape), so for those
+bf16 outputs the bar may apply to the error beyond each element's own bf16
+rounding, with all three figures logged; dgamma, dbeta and the RMSNorm weight's
+gradient are held to the plain bar.  Small
 shapes are compared element by element for all six outputs; they span
 several 64-row product tiles with ragged tails (N = 70, 130, 100), head_dim
 32/64/128, batch > 1, frames with beta = 0, and context tokens (whose rows
@@ -23,9 +27,10 @@ from oracle.vda_backward import vda_branch_backward
 from video_diffusion_hybrid_vda_amd import synth
 from video_diffusion_hybrid_vda_amd.synth import VdnConfig
 
+from measure import check
+
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def log(msg):
@@ -43,29 +48,6 @@ def vdn():
 
 def np64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
-
-
-def rel_err(got, ref):
-    """max |got - ref| / RMS(ref); where ref is exactly zero (dgamma of a single
-    frame: no previous state in either scan), max |got| itself."""
-    ref = np.asarray(ref, dtype=np.float64)
-    got = np.asarray(got, dtype=np.float64)
-    rms = np.sqrt(np.mean(ref * ref))
-    err = np.max(np.abs(got - ref))
-    return float(err / rms) if rms > 0 else float(err)
-
-
-def excess_err(got, ref, dtype):
-    """Error beyond each element's own bf16 rounding (half an ulp, 2^-9
-    relative) over RMS(ref); plain rel_err for fp32.  Gradients are heavy-
-    tailed (max/RMS near 10 at the headline shape), so the rounding of a
-    bf16 output alone reaches 2% of RMS."""
-    if dtype != "bf16":
-        return rel_err(got, ref)
-    ref = np.asarray(ref, dtype=np.float64)
-    got = np.asarray(got, dtype=np.float64)
-    exc = np.maximum(np.abs(got - ref) - 2.0 ** -9 * np.abs(ref), 0.0)
-    return float(np.max(exc) / np.sqrt(np.mean(ref * ref)))
 
 
 def grad_inputs(cfg, device):
@@ -114,19 +96,14 @@ def test_vda_backward_small(vdn, name, cfg):
     ref = vda_branch_backward(video(inp["q"], cfg), video(inp["k"], cfg), video(inp["v"], cfg),
                               np64(inp["gamma"]), np64(inp["beta"]), np64(inp["rms_w"]), cfg.rms_eps,
                               d_out_heads(d_out, cfg))
-    tol = TOL[cfg.dtype]
-    errs = {}
     for n in ("q", "k", "v"):
-        errs[n] = excess_err(video(got[n], cfg), ref["d" + n], cfg.dtype)
+        check(log, "d" + n, video(got[n], cfg), ref["d" + n], cfg.dtype, stress=True)
         if cfg.context_tokens:
             L = cfg.frames * cfg.tokens_per_frame
             assert torch.count_nonzero(got[n][:, :, L:]).item() == 0, n
-    errs["gamma"] = rel_err(np64(got["gamma"]), ref["dgamma"])
-    errs["beta"] = rel_err(np64(got["beta"]), ref["dbeta"])
-    errs["rms_w"] = rel_err(np64(got["rms_w"]), ref["drms_w"])
-    log("  " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()))
-    for n, e in errs.items():
-        assert e <= tol, (n, e)
+    check(log, "dgamma", np64(got["gamma"]), ref["dgamma"], cfg.dtype)
+    check(log, "dbeta", np64(got["beta"]), ref["dbeta"], cfg.dtype)
+    check(log, "drms_w", np64(got["rms_w"]), ref["drms_w"], cfg.dtype)
     if "beta0" in name:
         assert torch.count_nonzero(got["k"][0, 0, 100:200]).item() == 0
         assert torch.count_nonzero(got["v"][0, 0, 100:200]).item() == 0
@@ -150,15 +127,12 @@ def test_vda_backward_headline_two_heads(vdn):
         ref = vda_branch_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), np64(inp["gamma"][0:1, h:h + 1]),
                                   np64(inp["beta"][0:1, h:h + 1]), np64(inp["rms_w"][h * d:(h + 1) * d]),
                                   cfg.rms_eps, dh[0:1, h:h + 1])
-        plain = {n: rel_err(sl(got[n]), ref["d" + n]) for n in ("q", "k", "v")}
-        errs = {n: excess_err(sl(got[n]), ref["d" + n], "bf16") for n in ("q", "k", "v")}
-        errs["gamma"] = rel_err(np64(got["gamma"][0, h]), ref["dgamma"][0, 0])
-        errs["beta"] = rel_err(np64(got["beta"][0, h]), ref["dbeta"][0, 0])
-        errs["rms_w"] = rel_err(np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"])
-        log(f"  head {h}: " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items())
-            + " (plain " + " ".join(f"d{n} {e:.2e}" for n, e in plain.items()) + f") ({time.time() - t0:.1f}s)")
-        for n, e in errs.items():
-            assert e <= TOL["bf16"], (h, n, e)
+        log(f"  head {h} ({time.time() - t0:.1f}s)")
+        for n in ("q", "k", "v"):
+            check(log, "d" + n, sl(got[n]), ref["d" + n], "bf16", stress=True)
+        check(log, "dgamma", np64(got["gamma"][0, h]), ref["dgamma"][0, 0], "bf16")
+        check(log, "dbeta", np64(got["beta"][0, h]), ref["dbeta"][0, 0], "bf16")
+        check(log, "drms_w", np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"], "bf16")
 
 
 def test_vda_backward_scan_workload_two_heads(vdn):
@@ -176,13 +150,12 @@ def test_vda_backward_scan_workload_two_heads(vdn):
         ref = vda_branch_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), np64(inp["gamma"][0:1, h:h + 1]),
                                   np64(inp["beta"][0:1, h:h + 1]), np64(inp["rms_w"][h * d:(h + 1) * d]),
                                   cfg.rms_eps, dh[0:1, h:h + 1])
-        errs = {n: excess_err(sl(got[n]), ref["d" + n], "bf16") for n in ("q", "k", "v")}
-        errs["gamma"] = rel_err(np64(got["gamma"][0, h]), ref["dgamma"][0, 0])
-        errs["beta"] = rel_err(np64(got["beta"][0, h]), ref["dbeta"][0, 0])
-        errs["rms_w"] = rel_err(np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"])
-        log(f"  head {h}: " + " ".join(f"d{n} {e:.2e}" for n, e in errs.items()))
-        for n, e in errs.items():
-            assert e <= TOL["bf16"], (h, n, e)
+        log(f"  head {h}")
+        for n in ("q", "k", "v"):
+            check(log, "d" + n, sl(got[n]), ref["d" + n], "bf16", stress=True)
+        check(log, "dgamma", np64(got["gamma"][0, h]), ref["dgamma"][0, 0], "bf16")
+        check(log, "dbeta", np64(got["beta"][0, h]), ref["dbeta"][0, 0], "bf16")
+        check(log, "drms_w", np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"], "bf16")
 
 
 def test_vda_backward_repeatable_and_range_checked(vdn):
