@@ -148,6 +148,25 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
                  const float* rms_w, const void* gate_l, void* out,
                  float* states, void* ws, size_t ws_bytes, void* stream);
 
+/* vda_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without the workspace.  Its scratch (the
+ * per-frame statistics, transitions, states and their hi/lo copies, and the
+ * range-check verdict: vdn_workspace_bytes(shape, VDN_OP_VDA_SCAN) bytes when
+ * states is NULL, less when states is given) is a static device array of the
+ * library, 64 MiB (67108864 bytes) per device, held by each device that loads
+ * the library until the process ends.  The call allocates nothing, device or
+ * host.  A shape whose scratch would exceed 64 MiB returns VDN_ERR_WORKSPACE
+ * with nothing enqueued (B1 H8 d64 T42 needs 33 MiB).  Every call on one
+ * device shares that device's scratch: calls that overlap in time on one
+ * device (on different streams or threads) race and give undefined results;
+ * calls on one stream are ordered and safe.  Nothing in the scratch needs to
+ * start at zero: each call writes every scratch byte it reads. */
+int vda_scan_fwd_noalloc(const vdn_shape* shape, const void* q, const void* k,
+                         const void* v, const float* gamma, const float* beta,
+                         const float* rms_w, const void* gate_l, void* out,
+                         float* states, void* stream);
+
 /* Gradient of the linear branch (10100.com article, 方法概述 part 2, the
  * delta rule, and part 3, RMSNorm per direction; the article's staged
  * adaptation trains this branch).  For the ungated output

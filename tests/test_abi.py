@@ -288,3 +288,25 @@ def test_vda_bwd_workspace_holds_the_adjoint_buffers(vdn):
     low = 17 * nf * d * d * 4 + nf * 2 * N * d * 4
     assert low <= n <= low + 32 * 256 + nf * (4 + 2 * d * 4) + 256
     assert n % 256 == 0
+
+
+def test_noalloc_entry_rejects_bad_arguments_before_any_launch(vdn):
+    """vda_scan_fwd_noalloc checks its arguments and its scratch bound on the
+    host: NULL or misaligned pointers, and a shape whose scratch would exceed
+    the library's static 64 MiB (the 102-frame layer's linear branch needs
+    about 1 GB), are rejected without touching a device."""
+    lib = ctypes.CDLL(LIB)
+    lib.vda_scan_fwd_noalloc.argtypes = [ctypes.POINTER(vdn.vdn_shape)] + [ctypes.c_void_p] * 10
+    lib.vda_scan_fwd_noalloc.restype = ctypes.c_int
+    p = ctypes.c_void_p(1 << 20)
+    big = vdn.make_shape(1, 24, 102, 4032, 128, "bf16")
+    assert vdn.vdn_workspace_bytes(big, vdn.VDN_OP_VDA_SCAN) > (64 << 20)
+    rc = lib.vda_scan_fwd_noalloc(ctypes.byref(big), p, p, p, p, p, None, None, p, None, None)
+    assert rc == -4 and "scratch" in vdn.vdn_last_error()
+    small = vdn.make_shape(1, 8, 42, 1560, 64, "bf16")
+    assert vdn.vdn_workspace_bytes(small, vdn.VDN_OP_VDA_SCAN) <= (64 << 20)
+    rc = lib.vda_scan_fwd_noalloc(ctypes.byref(small), None, p, p, p, p, None, None, p, None, None)
+    assert rc == -1
+    rc = lib.vda_scan_fwd_noalloc(ctypes.byref(small), ctypes.c_void_p((1 << 20) + 4), p, p, p, p, None, None,
+                                  p, None, None)
+    assert rc == -1

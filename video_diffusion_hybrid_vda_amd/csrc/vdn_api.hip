@@ -1,6 +1,7 @@
 // C ABI of libvdn.so (declared in include/vdn.h): argument validation,
 // workspace layout and the launch sequence of each entry point.  No device
-// memory is allocated here; every buffer comes from the caller.
+// memory is allocated here; every buffer comes from the caller, except the
+// fixed static scratch array of the allocation-free linear-branch entry point.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -15,6 +16,15 @@
 #include "vdn_internal.h"
 
 using namespace vdn;
+
+// Scratch of vda_scan_fwd_noalloc (the linear branch's per-frame statistics,
+// transitions, states and their hi/lo copies, and the range-check verdict)
+// for callers that cannot allocate.  Each device that loads the library
+// holds its own copy until the process ends.  In host code the name is only
+// a stand-in: the device address comes from hipGetSymbolAddress, once per
+// device with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -323,6 +333,30 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(VDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(char** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VDN_ERR_INVALID_ARG, "device %d is beyond the %d devices the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return VDN_OK;
+}
+
 // Linear branch on already validated arguments.
 int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
             const float* gamma, const float* beta, const float* rms_w, const void* gate,
@@ -560,6 +594,20 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
   return VDN_OK;
 }
 
+// Argument checks shared by the two linear-branch forward entry points.
+int check_vda_args(const char* fn, const vdn_shape* shape, const void* q, const void* k, const void* v,
+                   const float* gamma, const float* beta, const void* gate_l, const void* out,
+                   const float* states, const void* ws) {
+  int rc = check_shape(shape);
+  if (rc != VDN_OK) return rc;
+  if (!q || !k || !v || !gamma || !beta || !out)
+    return fail(VDN_ERR_INVALID_ARG, "%s: q, k, v, gamma, beta and out must be non-NULL", fn);
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(gate_l) ||
+      misaligned(states) || misaligned(ws) || misaligned(gamma) || misaligned(beta))
+    return fail(VDN_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", fn);
+  return VDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -587,13 +635,8 @@ size_t vdn_workspace_bytes(const vdn_shape* shape, int op) {
 int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k, const void* v,
                  const float* gamma, const float* beta, const float* rms_w, const void* gate_l,
                  void* out, float* states, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_shape(shape);
+  int rc = check_vda_args("vda_scan_fwd", shape, q, k, v, gamma, beta, gate_l, out, states, ws);
   if (rc != VDN_OK) return rc;
-  if (!q || !k || !v || !gamma || !beta || !out)
-    return fail(VDN_ERR_INVALID_ARG, "vda_scan_fwd: q, k, v, gamma, beta and out must be non-NULL");
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(gate_l) ||
-      misaligned(states) || misaligned(ws) || misaligned(gamma) || misaligned(beta))
-    return fail(VDN_ERR_INVALID_ARG, "vda_scan_fwd: device pointers must be 16-byte aligned");
   const size_t need = vda_layout(shape, states == nullptr).total;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(VDN_ERR_WORKSPACE, "vda_scan_fwd: workspace of %zu bytes needed, %zu given", need,
@@ -604,6 +647,25 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k, const voi
   const int64_t D = (int64_t)shape->heads * shape->head_dim;
   return run_vda(shape, q, k, v, gamma, beta, rms_w, gate_l, D, out, D, states, (char*)ws,
                  (hipStream_t)stream);
+}
+
+int vda_scan_fwd_noalloc(const vdn_shape* shape, const void* q, const void* k, const void* v,
+                         const float* gamma, const float* beta, const float* rms_w, const void* gate_l,
+                         void* out, float* states, void* stream) {
+  int rc = check_vda_args("vda_scan_fwd_noalloc", shape, q, k, v, gamma, beta, gate_l, out, states, nullptr);
+  if (rc != VDN_OK) return rc;
+  const VdaLayout l = vda_layout(shape, states == nullptr);
+  if (l.total > kScratchBytes)
+    return fail(VDN_ERR_WORKSPACE,
+                "vda_scan_fwd_noalloc: the shape needs %zu bytes of scratch, the static scratch holds %zu "
+                "(call vda_scan_fwd with a workspace)", l.total, kScratchBytes);
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != VDN_OK) return rc;
+  rc = check_params(shape, gamma, beta, ws + l.flag, (hipStream_t)stream);
+  if (rc != VDN_OK) return rc;
+  const int64_t D = (int64_t)shape->heads * shape->head_dim;
+  return run_vda(shape, q, k, v, gamma, beta, rms_w, gate_l, D, out, D, states, ws, (hipStream_t)stream);
 }
 
 int vda_scan_bwd(const vdn_shape* shape, const void* q, const void* k, const void* v,

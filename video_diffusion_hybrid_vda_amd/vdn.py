@@ -82,6 +82,8 @@ def _load():
     lib.vdn_hybrid_attn_fwd.restype = I
     lib.vda_scan_fwd.argtypes = [S] + [P] * 9 + [P, SZ, P]
     lib.vda_scan_fwd.restype = I
+    lib.vda_scan_fwd_noalloc.argtypes = [S] + [P] * 9 + [P]
+    lib.vda_scan_fwd_noalloc.restype = I
     lib.vda_scan_bwd.argtypes = [S] + [P] * 13 + [P, SZ, P]
     lib.vda_scan_bwd.restype = I
     lib.window_anchor_attn_fwd.argtypes = [S] + [P] * 6 + [P, SZ, P]
@@ -110,7 +112,7 @@ _lib = _load()
 EXPORTS = ("vdn_workspace_bytes", "vdn_hybrid_attn_fwd", "vda_scan_fwd", "window_anchor_attn_fwd",
            "vdn_dense_attn_fwd", "vdn_set_param_check", "vdn_last_error", "vdn_version",
            "vdn_timing_start", "vdn_timing_stop", "vdn_mxfp8_quantize", "window_anchor_attn_mxfp8_fwd",
-           "vda_scan_bwd")
+           "vda_scan_bwd", "vda_scan_fwd_noalloc")
 
 
 def _ptr(t):
@@ -181,6 +183,12 @@ def vda_scan_fwd(shape, q, k, v, gamma, beta, rms_w, gate_l, out, states, ws, st
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(rms_w),
         _ptr(gate_l), _ptr(out), _ptr(states), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def vda_scan_fwd_noalloc(shape, q, k, v, gamma, beta, rms_w, gate_l, out, states, stream=None) -> int:
+    return _check(_lib.vda_scan_fwd_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(rms_w),
+        _ptr(gate_l), _ptr(out), _ptr(states), _stream(stream)))
 
 
 def vda_scan_bwd(shape, q, k, v, gamma, beta, rms_w, d_out, dq, dk, dv, dgamma, dbeta, drms_w, ws,
