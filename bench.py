@@ -15,7 +15,10 @@ events recorded in the timed region, per-phase milliseconds, and the fp64 CPU
 oracle timed on a bounded sample of the same workload on this host.
 
 After the forward, the same line carries `vda_backward`: the linear-branch
-gradient (vda_scan_bwd) timed on the same workload, per phase against HBM.
+gradient (vda_scan_bwd) timed on the same workload, per phase against HBM;
+`scan_workload`: the linear branch alone (vda_scan_fwd) on its own workload,
+B1 H8 d64 T42 N1560, with the scan's time per frame step; and `layer_T42`:
+the 42-latent-frame layer (B1 H24 d128 N4032).
 
     python bench.py [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline] [--bwd-steps 3]
 
@@ -93,7 +96,7 @@ def window_traffic(cfg_name, mxfp8=False):
     return WINDOW_MXFP8_TRAFFIC_BYTES if mxfp8 else WINDOW_TRAFFIC_BYTES
 
 
-def phase_rooflines(cfg, phases):
+def phase_rooflines(cfg, phases, gated=True):
     """Achieved rate of each hot-path kernel against its own roofline, from the library's per-phase
     HIP-event times: algorithmic bytes (HBM-bound kernels) or flops (MFMA-bound kernels) per call."""
     B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
@@ -127,8 +130,8 @@ def phase_rooflines(cfg, phases):
     hbm("vda_gram", 2 * tok + 2 * dd4)
     # MXFP8 mode: q and k read (bf16), their codes (1 byte per element) and scales (1 per 32) written
     hbm("mxfp8_quantize", 2 * tok + 2 * (tok // es) * (1 + 1 / 32))
-    # Q, gate and output once; both directions' states once per frame
-    hbm("vda_readout", 3 * tok + 2 * dd4)
+    # Q, gate (when given) and output once; both directions' states once per frame
+    hbm("vda_readout", (3 if gated else 2) * tok + 2 * dd4)
     mfma("gate_gemm", 2.0 * B * L * D * 2 * D)
     mfma("out_gemm", 2.0 * B * L * 2 * D * D)
     t = ms("vda_scan")
@@ -242,61 +245,172 @@ def length_sweep(args):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(cfg, inp):
-    """The fp64 oracle, unmodified, timed on a bounded sample of the workload
-    (one head's full forward+backward scans, a sample of readout tokens,
-    softmax rows of an interior and an anchor frame, gate/projection rows),
-    scaled to the whole layer by exact token and head counts."""
+def blas_threads():
+    """Host threads given to the oracle's BLAS: the CPUs this process may run
+    on, capped by OMP_NUM_THREADS when that is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(n, 1)
+
+
+def cpu_full_runs():
+    """The oracle on the two workloads small enough to run whole: the tiny fp32
+    layer (B1 H1 d32 T10 N16) and the linear branch at the scan workload (B1 H8
+    d64 T42 N1560, both scans and the RMSNorm readout of every token)."""
     import numpy as np
     from oracle import vdn_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()
-                     if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
-    L, D = T * N, cfg.model_dim
-    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    q, k, v = f64(inp["q"][0, 0]), f64(inp["k"][0, 0]), f64(inp["v"][0, 0])
-    gamma, beta = f64(inp["gamma"][0, 0]), f64(inp["beta"][0, 0])
-    w = np.ones(d)
-
+    from video_diffusion_hybrid_vda_amd import synth
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    out = {}
+    cfg = synth.CONFIGS[1]
+    inp = {k: f64(v) for k, v in synth.make_inputs(cfg, device="cpu").items()}
     t0 = time.perf_counter()
-    sf, sb = O.vda_states(k, v, gamma, beta)
-    t_states = time.perf_counter() - t0
-
-    tmid = min(7, T - 1)
-    R = min(256, N)
+    O.hybrid_layer(*(inp[k] for k in ("x", "q", "k", "v", "gamma", "beta", "w_gs", "w_gl", "rms_w", "w_os",
+                                      "w_ol")), eps=cfg.rms_eps)
+    dt = time.perf_counter() - t0
+    out["tiny_layer"] = {"workload": cfg.name, "s": round(dt, 4), "tokens_per_s": round(cfg.seq_len / dt, 1)}
+    cfg = synth.CONFIGS[2]
+    inp = {k: f64(v) for k, v in synth.make_inputs(cfg, device="cpu", with_layer=False).items()}
     t0 = time.perf_counter()
-    O.vda_readout(q[tmid, :R], sf[tmid], sb[tmid], w, cfg.rms_eps)
-    t_readout_tok = (time.perf_counter() - t0) / R
+    O.vda_branch(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], np.ones(cfg.model_dim), cfg.rms_eps)
+    dt = time.perf_counter() - t0
+    out["scan_workload"] = {"workload": cfg.name, "s": round(dt, 3), "tokens_per_s": round(cfg.seq_len / dt, 1)}
+    return out
 
-    allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
-    Rs = min(64, N)
-    t0 = time.perf_counter()
-    O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(tmid * N, tmid * N + Rs))
-    t_win_tok = (time.perf_counter() - t0) / Rs
-    t0 = time.perf_counter()
-    O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(0, Rs))
-    t_anchor_tok = (time.perf_counter() - t0) / Rs
 
-    xr = f64(inp["x"][0, :Rs])
-    wgs, wgl, wos, wol = (f64(inp[n]) for n in ("w_gs", "w_gl", "w_os", "w_ol"))
-    t0 = time.perf_counter()
-    g_s, g_l = O.gates(xr, wgs, wgl)
-    _ = (g_s * xr) @ wos + (g_l * xr) @ wol
-    t_gemm_tok = (time.perf_counter() - t0) / Rs
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle, unmodified, timed on this host with its BLAS thread
+    count set explicitly.  The benchmark's layer is timed on a bounded sample
+    (one head's full forward+backward scans, a sample of readout tokens, softmax
+    rows of an interior and an anchor frame, gate/projection rows) and scaled to
+    the whole layer: the softmax rows of each query frame by that frame's
+    allowed key frames, the rest by exact token and head counts.  The two small
+    workloads are also run whole."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import vdn_oracle as O
+    threads = blas_threads()
+    with threadpool_limits(limits=threads, user_api="blas"):
+        B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+        L = T * N
+        f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+        q, k, v = f64(inp["q"][0, 0]), f64(inp["k"][0, 0]), f64(inp["v"][0, 0])
+        gamma, beta = f64(inp["gamma"][0, 0]), f64(inp["beta"][0, 0])
+        w = np.ones(d)
 
-    n_anchor = (int(cfg.anchor_first) + int(cfg.anchor_last and T > 1)) * N
-    total = B * (H * (t_states + L * t_readout_tok + n_anchor * t_anchor_tok + (L - n_anchor) * t_win_tok)
-                 + L * t_gemm_tok)
+        t0 = time.perf_counter()
+        sf, sb = O.vda_states(k, v, gamma, beta)
+        t_states = time.perf_counter() - t0
+
+        tmid = min(7, T - 1)
+        R = min(256, N)
+        t0 = time.perf_counter()
+        O.vda_readout(q[tmid, :R], sf[tmid], sb[tmid], w, cfg.rms_eps)
+        t_readout_tok = (time.perf_counter() - t0) / R
+
+        allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+        Rs = min(64, N)
+        t0 = time.perf_counter()
+        O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(tmid * N, tmid * N + Rs))
+        t_win_tok = (time.perf_counter() - t0) / Rs
+        t0 = time.perf_counter()
+        O.window_attention(q, k, v, allowed, 1 / np.sqrt(d), np.arange(0, Rs))
+        t_anchor_tok = (time.perf_counter() - t0) / Rs
+
+        xr = f64(inp["x"][0, :Rs])
+        wgs, wgl, wos, wol = (f64(inp[n]) for n in ("w_gs", "w_gl", "w_os", "w_ol"))
+        t0 = time.perf_counter()
+        g_s, g_l = O.gates(xr, wgs, wgl)
+        _ = (g_s * xr) @ wos + (g_l * xr) @ wol
+        t_gemm_tok = (time.perf_counter() - t0) / Rs
+
+        counts = frame_key_counts(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+        anchors = {0} if cfg.anchor_first else set()
+        if cfg.anchor_last:
+            anchors.add(T - 1)
+        per_key_frame = t_win_tok / counts[tmid]
+        t_softmax = sum(N * (t_anchor_tok if t in anchors else per_key_frame * counts[t]) for t in range(T))
+        total = B * (H * (t_states + L * t_readout_tok + t_softmax) + L * t_gemm_tok)
+        full = cpu_full_runs()
     sample = (f"head 0 of {H}: VDA forward+backward scans over all {T} frames; readout of {R} tokens; "
-              f"softmax of {Rs} tokens of frame {tmid} and {Rs} of anchor frame 0; gates and projections "
-              f"of {Rs} tokens; scaled by exact token/head counts to the B{B} H{H} T{T} N{N} layer "
-              f"(extrapolated layer time {total:.0f} s)")
-    return {"value": B * L / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "host": host_info()}
+              f"softmax of {Rs} tokens of frame {tmid} ({counts[tmid]} key frames) and {Rs} of anchor frame 0; "
+              f"gates and projections of {Rs} tokens; scaled to the B{B} H{H} T{T} N{N} layer by exact head and "
+              f"token counts, the softmax of each query frame by its allowed key frames (extrapolated layer "
+              f"time {total:.0f} s)")
+    return {"value": B * L / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": sample, "full_runs": full, "host": host_info()}
+
+
+def time_scan_workload(vdn, torch, steps):
+    """The linear branch alone (vda_scan_fwd: Gram, solve, both scans, RMSNorm
+    readout, no gate) on its own workload, B1 H8 d64 T42 N1560 bf16."""
+    from video_diffusion_hybrid_vda_amd import synth
+    cfg = synth.CONFIGS[2]
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=False)
+    shape = vdn.shape_from_config(cfg)
+    ws = vdn.workspace(shape, vdn.VDN_OP_VDA_SCAN)
+    B, L, D = cfg.batch, cfg.seq_len, cfg.model_dim
+    out = torch.empty(B, L, D, dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        vdn.vda_scan_fwd(shape, inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"], None, None, out, None, ws)
+
+    call()
+    torch.cuda.synchronize()
+    vdn.vdn_timing_start()
+    ms, calls = timed_calls(call, steps, 0)
+    ph = vdn.vdn_timing_stop()
+    tok_bytes = B * L * D * 2
+    # q, k, v read and out written once (bf16); every d x d statistic, transition and state moved once
+    call_bytes = 4 * tok_bytes
+    return {"workload": cfg.name, "entry_point": "vda_scan_fwd (no gate, unit RMSNorm weight)",
+            "value": B * L / (ms * 1e-3), "unit": "tokens/s", "ms_per_call": round(ms, 4),
+            "call_ms_median": round(median(calls), 4), "steps": steps,
+            "token_bytes_gb": round(call_bytes / 1e9, 4),
+            "token_bytes_frac_of_hbm_peak": round(call_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "phases_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ph.items() if v[0] > 0},
+            "kernel_rooflines": phase_rooflines(cfg, ph, gated=False)}
+
+
+def time_layer(vdn, torch, cfg_id, steps):
+    """The whole hybrid layer on another workload (by default the 42-frame layer)."""
+    from video_diffusion_hybrid_vda_amd import synth
+    cfg = synth.CONFIGS[cfg_id]
+    inp = synth.make_inputs(cfg, device="cuda", with_layer=True)
+    shape = vdn.shape_from_config(cfg)
+    ws = vdn.workspace(shape, vdn.VDN_OP_HYBRID)
+    B, L, D = cfg.batch, cfg.seq_len, cfg.model_dim
+    out = torch.empty(B, L, D, dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        vdn.vdn_hybrid_attn_fwd(shape, inp["x"], inp["q"], inp["k"], inp["v"], inp["gamma"], inp["beta"],
+                                inp["w_gs"], inp["w_gl"], inp["rms_w"], inp["w_os"], inp["w_ol"], out, ws)
+
+    call()
+    torch.cuda.synchronize()
+    vdn.vdn_timing_start()
+    ms, calls = timed_calls(call, steps, 0)
+    ph = vdn.vdn_timing_stop()
+    flops, pairs = window_flops(cfg)
+    n, tot = ph["window_attn"]
+    wms = tot / max(n, 1)
+    ach = flops / (wms * 1e-3) / 1e12
+    return {"workload": cfg.name, "value": B * L / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": round(ms, 3),
+            "call_ms_median": round(median(calls), 3), "call_ms_min": round(min(calls), 3), "steps": steps,
+            "softmax_density": round(pairs / float(L) ** 2, 5),
+            "roofline": {"bound": "mfma", "kernel": "window_attn", "achieved": round(ach, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(wms, 3)},
+            "phases_ms": {k: round(v[1] / max(v[0], 1), 3) for k, v in ph.items() if v[0] > 0},
+            "kernel_rooflines": phase_rooflines(cfg, ph)}
+
+
+# kernels of the gradient's token-side phases at head_dim 128, bf16 I/O
+BWD_KERNELS = {"bwd_u_gemm": "bgemm_mfma_resident_kernel", "bwd_rms": "rms_bwd_kernel",
+               "bwd_dq_gemm": "bgemm_mfma_resident_kernel", "bwd_ds_gemm": "bgemm_mfma_kernel",
+               "bwd_kv_gemm": "bgemm_mfma_resident_kernel"}
 
 
 def time_backward(cfg, inp, vdn, torch, steps):
@@ -346,7 +460,8 @@ def time_backward(cfg, inp, vdn, torch, steps):
                     "RMSNorm weight (vda_scan_bwd; forward quantities recomputed inside)",
             "value": B * L / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": steps,
             "call_ms_median": round(median(calls), 3), "phases_ms": ph_ms,
-            "roofline": dict(kern[dom], kernel=dom + " (bgemm_mfma)", peak=PEAK_HBM_GBS, unit="GB/s",
+            "roofline": dict(kern[dom], kernel=dom + " (" + BWD_KERNELS.get(dom, "?") + ")", peak=PEAK_HBM_GBS,
+                             unit="GB/s",
                              achieved=kern[dom]["achieved_GBps"], traffic=None),
             "kernel_rooflines": kern}
 
@@ -369,6 +484,11 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=3,
                     help="after the forward measurement, also time this many calls of the linear-branch "
                          "gradient (vda_scan_bwd) on the same workload (0: skip)")
+    ap.add_argument("--scan-steps", type=int, default=20,
+                    help="also time this many calls of vda_scan_fwd on the scan workload B1 H8 d64 T42 N1560 "
+                         "(0: skip)")
+    ap.add_argument("--t42-steps", type=int, default=5,
+                    help="also time this many calls of the 42-frame layer B1 H24 d128 T42 N4032 (0: skip)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device-to-device copy of this many MiB "
                          "(a known-traffic kernel for scaling HBM counters)")
@@ -439,7 +559,7 @@ def main():
     if not args.softmax_mxfp8 and args.mxfp8_steps > 0:
         # the same layer with MXFP8 softmax-branch scores, timed after the bf16 region
         shape8 = vdn.shape_from_config(cfg, softmax_mxfp8=True)
-        del ws
+        ws = None
         ws8 = vdn.workspace(shape8, vdn.VDN_OP_HYBRID)
         layer(shape8, ws8)
         torch.cuda.synchronize()
@@ -458,6 +578,11 @@ def main():
     backward = None
     if args.bwd_steps > 0:
         backward = time_backward(cfg, inp, vdn, torch, args.bwd_steps)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
+    inp = ws = out = None      # free the benchmark layer's buffers before the other workloads
+    torch.cuda.empty_cache()
+    scan = time_scan_workload(vdn, torch, args.scan_steps) if args.scan_steps > 0 else None
+    layer42 = time_layer(vdn, torch, 3, args.t42_steps) if args.t42_steps > 0 and args.config != 3 else None
 
     result = {
         "metric": METRIC,
@@ -490,8 +615,12 @@ def main():
         result["mxfp8_softmax"] = mxfp8
     if backward is not None:
         result["vda_backward"] = backward
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    if scan is not None:
+        result["scan_workload"] = scan
+    if layer42 is not None:
+        result["layer_T42"] = layer42
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
