@@ -44,14 +44,87 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per launch of the window/anchor softmax kernel on the 102-frame layer, from two
-# rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy calibration
-# (profiles/window_attn_T102_counters.md).  Valid only for the kernel sources they were
-# taken on: reported as null once those sources change.
-WINDOW_TRAFFIC_BYTES = 257156886872
-WINDOW_MXFP8_TRAFFIC_BYTES = 184544936788   # the MXFP8-score kernel, same passes
-WINDOW_TRAFFIC_SOURCES = ("csrc/window_attn.hip", "csrc/vdn_internal.h", "csrc/vdn_common.h")
-WINDOW_TRAFFIC_SHA = "5df1ca28a90a17d6"
+# HBM bytes each phase moves per call (FETCH_SIZE + WRITE_SIZE of its kernels, FETCH_SIZE scaled by a plain
+# 1 GiB copy measured in the same process), by workload, from the rocprofv3 counter passes summarised in
+# profiles/*_counters.md.  A figure is reported only while the sources of the phase's kernels hash to the
+# version the counters were taken on; after any change to them it is reported as null.
+COUNTER_TRAFFIC = {
+    "hybrid layer B1 H24 d128 T102 N4032": {
+        "gate_gemm": 27819837275,
+        "window_attn": 275487287181,
+        "anchor_merge": 2035524193,
+        "vda_gram": 5374847660,
+        "vda_solve": 321179729,
+        "vda_scan": 1272357501,
+        "vda_readout": 7904839452,
+        "out_gemm": 25918900467
+    },
+    "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
+        "window_attn": 180873085017,
+        "mxfp8_quantize": 7659590516
+    },
+    "hybrid layer B1 H24 d128 T102 N4032 bwd": {
+        "bwd_recompute": 7283761303,
+        "bwd_u_gemm": 15201366372,
+        "bwd_rms": 25270196922,
+        "bwd_dq_gemm": 15200784452,
+        "bwd_ds_gemm": 20564112885,
+        "bwd_scan": 3515977126,
+        "bwd_frame": 5570974220,
+        "bwd_kv_gemm": 16485149904
+    },
+    "VDA scan B1 H8 d64 T42 N1560": {
+        "vda_gram": 145306973,
+        "vda_solve": 11173686,
+        "vda_scan": 58757862,
+        "vda_readout": 222475504
+    },
+    "hybrid layer B1 H24 d128 T42 N4032": {
+        "gate_gemm": 11460269256,
+        "window_attn": 111337037879,
+        "anchor_merge": 1493847400,
+        "vda_gram": 2213161144,
+        "vda_solve": 132434890,
+        "vda_scan": 517340512,
+        "vda_readout": 3254868633,
+        "out_gemm": 10488645703
+    }
+}
+PHASE_SOURCES = {      # phase -> source group of its kernels
+    "gate_gemm": "gemm", "out_gemm": "gemm", "window_attn": "window", "anchor_merge": "window",
+    "vda_gram": "vda", "vda_solve": "vda", "vda_scan": "vda", "vda_readout": "vda", "mxfp8_quantize": "mxfp8",
+    "bwd_recompute": "vda+bwd", "bwd_u_gemm": "bwd", "bwd_rms": "bwd", "bwd_dq_gemm": "bwd", "bwd_ds_gemm": "bwd",
+    "bwd_scan": "bwd", "bwd_frame": "bwd", "bwd_kv_gemm": "bwd",
+}
+SOURCE_GROUPS = {
+    "window": ("window_attn.hip",), "gemm": ("gemm.hip",), "vda": ("vda.hip",), "mxfp8": ("mxfp8.hip",),
+    "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
+}
+SOURCE_SHA = {"window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "4544271a9cf41f32",
+              "mxfp8": "8cdcfa773199d9a4", "bwd": "2489a9c3e0652eee", "vda+bwd": None,
+              "common": "a24de8342071a471"}
+
+
+def _sha(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "video_diffusion_hybrid_vda_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, phase):
+    """Counter-measured HBM bytes per call of `phase` on `workload`, or None if there is no such figure or
+    the phase's kernel sources (or the shared headers) changed since it was taken."""
+    t = COUNTER_TRAFFIC.get(workload, {}).get(phase)
+    grp = PHASE_SOURCES.get(phase)
+    if t is None or grp is None or _sha(("vdn_common.h", "vdn_internal.h")) != SOURCE_SHA["common"]:
+        return None
+    for g in grp.split("+"):
+        if _sha(SOURCE_GROUPS[g]) != SOURCE_SHA[g]:
+            return None
+    return t
 
 
 def frame_key_counts(T, C, W, a0, a1):
@@ -81,24 +154,10 @@ def window_flops(cfg):
     return 4 * cfg.head_dim * cfg.batch * cfg.heads * pairs_per_head, pairs_per_head
 
 
-def window_traffic(cfg_name, mxfp8=False):
-    """Measured HBM bytes per window-kernel launch, or None if the workload or the kernel sources
-    differ from the ones the counters were taken on."""
-    import hashlib
-    if "T102" not in cfg_name:
-        return None
-    h = hashlib.sha256()
-    for f in WINDOW_TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "video_diffusion_hybrid_vda_amd", f), "rb") as fh:
-            h.update(fh.read())
-    if h.hexdigest()[:16] != WINDOW_TRAFFIC_SHA:
-        return None
-    return WINDOW_MXFP8_TRAFFIC_BYTES if mxfp8 else WINDOW_TRAFFIC_BYTES
-
-
-def phase_rooflines(cfg, phases, gated=True):
+def phase_rooflines(cfg, phases, gated=True, mode=""):
     """Achieved rate of each hot-path kernel against its own roofline, from the library's per-phase
-    HIP-event times: algorithmic bytes (HBM-bound kernels) or flops (MFMA-bound kernels) per call."""
+    HIP-event times: algorithmic bytes (HBM-bound kernels) or flops (MFMA-bound kernels) per call, with the
+    bytes the counters measured per call beside them (`traffic`, null when not measured on these sources)."""
     B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
     L, D = T * N, cfg.model_dim
     es = 2 if cfg.dtype == "bf16" else 4
@@ -116,7 +175,8 @@ def phase_rooflines(cfg, phases, gated=True):
         if t:
             gbs = nbytes / (t * 1e-3) / 1e9
             out[name] = {"bound": "hbm", "algorithmic_gb": round(nbytes / 1e9, 3), "ms": round(t, 3),
-                         "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}
+                         "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(cfg.name + mode, name)}
 
     def mfma(name, flops):
         t = ms(name)
@@ -124,7 +184,7 @@ def phase_rooflines(cfg, phases, gated=True):
             tf = flops / (t * 1e-3) / 1e12
             out[name] = {"bound": "mfma", "algorithmic_tflop": round(flops / 1e12, 3), "ms": round(t, 3),
                          "achieved_tflops": round(tf, 1), "peak_tflops": PEAK_BF16_TFLOPS,
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(cfg.name + mode, name)}
 
     # K and V read once; A_t and B_t written (fp32)
     hbm("vda_gram", 2 * tok + 2 * dd4)
@@ -143,11 +203,13 @@ def phase_rooflines(cfg, phases, gated=True):
                            "us_per_step": round(t * 1e3 / T, 2),
                            "algorithmic_gb": round(scan_bytes / 1e9, 3),
                            "achieved_gbs": round(scan_bytes / (t * 1e-3) / 1e9, 1),
-                           "frac_of_hbm_peak": round(scan_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                           "frac_of_hbm_peak": round(scan_bytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "traffic": measured_traffic(cfg.name + mode, "vda_scan")}
     t = ms("vda_solve")
     if t:
         out["vda_solve"] = {"bound": "latency", "ms": round(t, 3), "systems": frames,
-                            "us_per_system_per_cu": round(t * 1e3 * 256 / frames, 2)}
+                            "us_per_system_per_cu": round(t * 1e3 * 256 / frames, 2),
+                            "traffic": measured_traffic(cfg.name + mode, "vda_solve")}
     return out
 
 
@@ -402,7 +464,8 @@ def time_layer(vdn, torch, cfg_id, steps):
             "softmax_density": round(pairs / float(L) ** 2, 5),
             "roofline": {"bound": "mfma", "kernel": "window_attn", "achieved": round(ach, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                         "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(wms, 3)},
+                         "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(wms, 3),
+                         "traffic": measured_traffic(cfg.name, "window_attn")},
             "phases_ms": {k: round(v[1] / max(v[0], 1), 3) for k, v in ph.items() if v[0] > 0},
             "kernel_rooflines": phase_rooflines(cfg, ph)}
 
@@ -453,7 +516,8 @@ def time_backward(cfg, inp, vdn, torch, steps):
         if k in ph_ms:
             gbs = b / (ph_ms[k] * 1e-3) / 1e9
             kern[k] = {"bound": "hbm", "achieved_GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                       "algorithmic_GB": round(b / 1e9, 3), "avg_ms": ph_ms[k]}
+                       "algorithmic_GB": round(b / 1e9, 3), "avg_ms": ph_ms[k],
+                       "traffic": measured_traffic(cfg.name + " bwd", k)}
     dom = max(nbytes, key=lambda k: ph_ms.get(k, 0.0))
     del ws
     return {"mode": "gradient of the ungated linear-branch output w.r.t. q, k, v, gamma, beta and the "
@@ -462,7 +526,7 @@ def time_backward(cfg, inp, vdn, torch, steps):
             "call_ms_median": round(median(calls), 3), "phases_ms": ph_ms,
             "roofline": dict(kern[dom], kernel=dom + " (" + BWD_KERNELS.get(dom, "?") + ")", peak=PEAK_HBM_GBS,
                              unit="GB/s",
-                             achieved=kern[dom]["achieved_GBps"], traffic=None),
+                             achieved=kern[dom]["achieved_GBps"]),
             "kernel_rooflines": kern}
 
 
@@ -553,7 +617,7 @@ def main():
                 "peak": round(mx_peak, 1), "unit": "TFLOP/s", "frac": round(a / mx_peak, 4),
                 "peak_note": "q.k half at the 5.0 PFLOP/s fp8 peak, P V half at the 2.5 PFLOP/s bf16 peak",
                 "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(ms, 3),
-                "traffic": window_traffic(cfg.name, mxfp8=True)}
+                "traffic": measured_traffic(cfg.name + " mxfp8", "window_attn")}
 
     mxfp8 = None
     if not args.softmax_mxfp8 and args.mxfp8_steps > 0:
@@ -572,7 +636,7 @@ def main():
                  "value": B * L / (ms8 * 1e-3), "unit": "tokens/s", "ms_per_step": ms8,
                  "steps": args.mxfp8_steps, "call_ms_median": round(median(call8), 3),
                  "roofline": mx_roofline(ph8_ms["window_attn"]), "phases_ms": ph8_ms,
-                 "kernel_rooflines": phase_rooflines(cfg, ph8)}
+                 "kernel_rooflines": phase_rooflines(cfg, ph8, mode=" mxfp8")}
         del ws8
 
     backward = None
@@ -605,7 +669,7 @@ def main():
                     {"bound": "mfma", "kernel": "window_attn", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "algorithmic_tflop_per_launch": round(flops / 1e12, 3), "avg_ms": round(attn_avg_ms, 3),
-                     "traffic": window_traffic(cfg.name)},
+                     "traffic": measured_traffic(cfg.name, "window_attn")},
         "kernel_rooflines": phase_rooflines(cfg, phases),
         "call_ms_median": round(median(call_ms), 3),
         "call_ms_min": round(min(call_ms), 3),
