@@ -53,6 +53,9 @@ hipError_t launch_frame_bwd(const float* states, const float* bm, const float* g
 // cdb[f][0] = dA + dA^T; dbeta[f] = <dA, kk> + <cdb[f][1], vk>
 hipError_t launch_sym_dbeta(int d, const float* dA, const float* kk, const float* vk, float* cdb,
                             float* dbeta, int64_t nf, hipStream_t st);
+// bf16 tokens, head_dim 128: dK = beta (K cdb[f][0] + V cdb[f][1]), dV = beta K cdb[f][1]^T per frame
+hipError_t launch_kv_grad(const void* k, const void* v, const float* cdb, const float* beta, void* dk, void* dv,
+                          int64_t nf, int T, int N, int Lt, hipStream_t st);
 hipError_t launch_dw_reduce(const float* part, float* drms_w, int B, int H, int T, int d,
                             hipStream_t st);
 

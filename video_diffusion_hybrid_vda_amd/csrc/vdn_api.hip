@@ -522,6 +522,8 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   if (rc != VDN_OK) return rc;
 
   rc = step(kPhBwdKv, "vda_bwd dk/dv launch", [&] {
+    // bf16 at head_dim 128: both in one pass over K and V
+    if (dt == VDN_BF16 && d == 128) return launch_kv_grad(k, v, cdb, beta, dk, dv, nf, T, N, Lt, st);
     // dK = beta (K (dA + dA^T) + V dB)  (K = 2d over [K | V] and [dA + dA^T ; dB])
     BGemm m;
     m.a0 = k; m.a1 = v; m.b0 = cdb; m.b1 = cdb + dd; m.c = dk;
