@@ -93,7 +93,7 @@ COUNTER_TRAFFIC = {
 PHASE_SOURCES = {      # phase -> source group of its kernels
     "gate_gemm": "gemm", "out_gemm": "gemm", "window_attn": "window", "anchor_merge": "window",
     "vda_gram": "vda", "vda_solve": "vda", "vda_scan": "vda", "vda_readout": "vda", "mxfp8_quantize": "mxfp8",
-    "bwd_recompute": "vda+bwd", "bwd_u_gemm": "bwd", "bwd_rms": "bwd", "bwd_dq_gemm": "bwd", "bwd_ds_gemm": "bwd",
+    "bwd_recompute": "vda+bwd", "bwd_token": "bwd",
     "bwd_scan": "bwd", "bwd_frame": "bwd", "bwd_kv_gemm": "bwd",
 }
 SOURCE_GROUPS = {
@@ -471,9 +471,7 @@ def time_layer(vdn, torch, cfg_id, steps):
 
 
 # kernels of the gradient's token-side phases at head_dim 128, bf16 I/O
-BWD_KERNELS = {"bwd_u_gemm": "bgemm_mfma_resident_kernel", "bwd_rms": "rms_bwd_kernel",
-               "bwd_dq_gemm": "bgemm_mfma_resident_kernel", "bwd_ds_gemm": "bgemm_mfma_kernel",
-               "bwd_kv_gemm": "bgemm_mfma_resident_kernel"}
+BWD_KERNELS = {"bwd_token": "tok_grad_bf16_d128_kernel", "bwd_kv_gemm": "kv_grad_bf16_d128_kernel"}
 
 
 def time_backward(cfg, inp, vdn, torch, steps):
@@ -504,11 +502,8 @@ def time_backward(cfg, inp, vdn, torch, steps):
     ph = vdn.vdn_timing_stop()
     ph_ms = {k: round(v[1] / max(v[0], 1), 3) for k, v in ph.items() if v[0] > 0}
     tok = B * H * L * d          # elements of one [B, H, L, d] token tensor
-    nbytes = {                   # algorithmic HBM bytes per call of each phase (bf16 tokens, fp32 u / du)
-        "bwd_u_gemm": tok * 2 + 2 * tok * 4,                 # read q, write u of both directions
-        "bwd_rms": 2 * tok * 4 * 2 + tok * 2,                # read u, write du (both directions), read d_out
-        "bwd_dq_gemm": 2 * tok * 4 + tok * 2,                # read du, write dq
-        "bwd_ds_gemm": 2 * tok * 4 + tok * 2,                # read du and q
+    nbytes = {                   # algorithmic HBM bytes per call of each token-side phase (bf16 tokens)
+        "bwd_token": 3 * tok * 2,                            # read q and d_out, write dq
         "bwd_kv_gemm": 4 * tok * 2,                          # read k, v; write dk, dv
     }
     kern = {}

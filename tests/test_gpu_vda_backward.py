@@ -81,6 +81,7 @@ CASES = [
     ("T4_N100_d128_f32_beta0", VdnConfig(1, 1, 128, 4, 100, dtype="f32", beta_lo=0.0, seed=84)),
     ("T1_N9_d64_f32", VdnConfig(1, 1, 64, 1, 9, dtype="f32", seed=85)),
     ("H2_T6_N20_d32_ctx9_bf16", VdnConfig(1, 2, 32, 6, 20, dtype="bf16", context_tokens=9, seed=86)),
+    ("B2H2_T7_N300_d128_ctx5_bf16", VdnConfig(2, 2, 128, 7, 300, dtype="bf16", context_tokens=5, seed=88)),
 ]
 
 
@@ -158,12 +159,13 @@ def test_vda_backward_scan_workload_two_heads(vdn):
         check(log, "drms_w", np64(got["rms_w"][h * d:(h + 1) * d]), ref["drms_w"], "bf16")
 
 
-def test_vda_backward_repeatable_and_range_checked(vdn):
+@pytest.mark.parametrize("d", [64, 128])
+def test_vda_backward_repeatable_and_range_checked(vdn, d):
     """Two calls on one workspace give bit-identical gradients (no atomics:
     every reduction has a fixed order); with the opt-in range check on,
     beta < 0 or gamma > 1 is rejected with VDN_ERR_PARAM_RANGE (-6) and the
     outputs are left untouched, and valid parameters pass unchanged."""
-    cfg = VdnConfig(1, 2, 64, 6, 50, dtype="bf16", seed=87)
+    cfg = VdnConfig(1, 2, d, 6, 50, dtype="bf16", seed=87)
     inp, d_out = grad_inputs(cfg, "cuda")
     shape = vdn.shape_from_config(cfg)
     ws = vdn.workspace(shape, vdn.VDN_OP_VDA_BWD)

@@ -56,6 +56,11 @@ hipError_t launch_sym_dbeta(int d, const float* dA, const float* kk, const float
 // bf16 tokens, head_dim 128: dK = beta (K cdb[f][0] + V cdb[f][1]), dV = beta K cdb[f][1]^T per frame
 hipError_t launch_kv_grad(const void* k, const void* v, const float* cdb, const float* beta, void* dk, void* dv,
                           int64_t nf, int T, int N, int Lt, hipStream_t st);
+// bf16 tokens, head_dim 128: the readout adjoint of both directions (u, du, RMSNorm weight partials
+// dwp [nf][2][d]), dq (via the fp32 partial dqp [nf][N][d]) and dS into dsg [nf][2][d][d]
+hipError_t launch_tok_grad(const void* q, const void* d_out, int64_t ldo, const float* states, const float* rms_w,
+                           float* dqp, void* dq, float* dsg, float* dwp, int64_t nf, int H, int T, int N, int Lt,
+                           float eps, hipStream_t st);
 hipError_t launch_dw_reduce(const float* part, float* drms_w, int B, int H, int T, int d,
                             hipStream_t st);
 

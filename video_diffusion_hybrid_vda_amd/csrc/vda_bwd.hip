@@ -757,6 +757,298 @@ __global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// tok_grad_bf16_d128<SECOND>: the token side of the readout adjoint, one scan
+// direction of one frame per workgroup (bf16 tokens, head_dim 128):
+//   u = S q,  rho = sqrt(mean u^2 + eps),  r = u / rho,  g = w do,
+//   du = (g - r mean(g r)) / rho,  dq += S^T du,
+//   dS = sum over the frame's tokens of du q^T,  dw = sum of r do.
+// Nothing token-sized but q, do and dq leaves the chip: u and du stay in
+// registers.  The first direction writes its share of dq in fp32 (to the
+// workspace); the second adds its own and writes dq in bf16.
+// S sits in LDS as bf16 hi + lo (64 KB, rows of 256 bytes, chunk c of row r at
+// c ^ (((r & 7) << 1) | ((r >> 3) & 1))).  Each wave takes a 32-token tile and
+// computes u^T = S q^T on v_mfma_f32_32x32x16_bf16 (S rows as A, q rows from
+// HBM as B), so a lane holds 64 of its token's 128 u values and its partner
+// lane (lane ^ 32) the other 64: the RMSNorm sums take one cross-lane add.
+// In that layout du is exactly the B operand of dq^T = S^T du^T when S^T comes
+// from transposed LDS reads (ds_read_b64_tr_b16 hands lane half h the rows
+// 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3 of one column, which are the du
+// values the lane holds for k-step s).  du is split into bf16 hi + lo for the
+// products.  For dS the four waves stage their tiles' du (hi, lo) and q rows in
+// LDS (24 KB each); after a barrier wave w accumulates rows 32 w .. 32 w + 31
+// of dS over all four tiles, both operands as transposed reads (tokens as k).
+namespace tkg {
+constexpr int D = 128, ROWB = 256, MATB = D * ROWB, TILEB = 32 * ROWB;
+constexpr int STG = 2 * MATB, STGW = 3 * TILEB;   // staging: per wave du hi, du lo, q (32 rows each)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+}
+
+template <bool SECOND>
+__global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ d_out, int64_t ldo, const float* __restrict__ states,
+    const float* __restrict__ rms_w, float* __restrict__ dqp, bf16* __restrict__ dq, float* __restrict__ dsg,
+    float* __restrict__ dwp, int dir, int64_t nf, int H, int T, int N, int Lt, float eps) {
+  using namespace tkg;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STG + 4 * STGW];   // 160 KB
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int64_t f = blockIdx.x;
+  const int64_t bh = f / T;
+  const int t = (int)(f % T);
+  const int64_t b = bh / H;
+  const int hh = (int)(bh % H);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
+
+  // S -> hi / lo bf16
+  const float* S = states + ((int64_t)dir * nf + f) * D * D;
+  for (int u = tid; u < D * (D / 8); u += 256) {
+    const int r = u / 16, c = u % 16;
+    const float* src = S + r * D + c * 8;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b4 = *reinterpret_cast<const float4*>(src + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w};
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (bf16)x[e];
+      lo[e] = (bf16)(x[e] - (float)hi[e]);
+    }
+    const int off = r * ROWB + swz(r, c) * 16;
+    *reinterpret_cast<bf16x8*>(lds + off) = hi;
+    *reinterpret_cast<bf16x8*>(lds + MATB + off) = lo;
+  }
+
+  auto tr = [&](int off) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + off)); };
+  auto rd = [&](int off) { return *reinterpret_cast<const bf16x8*>(lds + off); };
+  auto cat = [](i16x4 a, i16x4 c) { return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7)); };
+  // plain row reads (row 32 blk + l32, chunk 2 s + h): the swizzle depends on the row mod 16,
+  // so the block moves the address by a constant
+  int aoff[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) aoff[s] = l32 * ROWB + swz(l32, 2 * s + h) * 16;
+  // transposed reads of a row-major [rows][128] matrix: column block cb, rows rA and rA + 8 of
+  // each 16-row step (the step moves the address by a constant)
+  const int rA = 4 * (g >> 1) + (j16 >> 2);
+  int troff[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int dcol = cb * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+    const int cch = dcol >> 3, off = (dcol & 7) * 2;
+    troff[cb][0] = rA * ROWB + swz(rA, cch) * 16 + off;
+    troff[cb][1] = (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
+  }
+
+  const bf16* qf = q + (bh * Lt + (int64_t)t * N) * D;
+  const bf16* dof = d_out + (b * Lt + (int64_t)t * N) * ldo + (int64_t)hh * D;
+  const float* wf = rms_w ? rms_w + (int64_t)hh * D : nullptr;
+  float* dqpf = dqp + f * (int64_t)N * D;
+  bf16* dqf = dq + (bh * Lt + (int64_t)t * N) * D;
+  const int ntile = (N + 31) / 32, nround = (ntile + 3) / 4;
+
+  float dw[4][16];       // sum over this lane's tokens of r do, C layout
+  f32x16 dsa[4];         // dS rows 32 wave + .., column block jt
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dsa[i] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dw[i][r] = 0.f;
+  }
+  __syncthreads();
+
+  for (int round = 0; round < nround; ++round) {
+    const int tile = round * 4 + wave;
+    unsigned char* sdh = lds + STG + wave * STGW;   // du hi rows of this wave's tile
+    unsigned char* sdl = sdh + TILEB;                // du lo rows
+    unsigned char* sq = sdl + TILEB;                 // q rows
+    if (tile < ntile) {
+      const int n = 32 * tile + l32;
+      const bool valid = n < N;
+      const int nn = valid ? n : N - 1;
+      // q: B operand of u^T = S q^T (k = dims 16 s + 8 h .. + 7), also staged for dS
+      bf16x8 qb[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        qb[s] = *reinterpret_cast<const bf16x8*>(qf + (int64_t)nn * D + 16 * s + 8 * h);
+        *reinterpret_cast<bf16x8*>(sq + l32 * ROWB + swz(l32, 2 * s + h) * 16) = qb[s];
+      }
+      // do at the lane's dims 32 dt + 8 q4 + 4 h + 0..3
+      bf16x4 dob[4][4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          dob[dt][q4] = *reinterpret_cast<const bf16x4*>(dof + (int64_t)nn * ldo + 32 * dt + 8 * q4 + 4 * h);
+      // u^T
+      f32x16 ua[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ua[dt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          asm volatile("" ::: "memory");
+          const int ao = aoff[s] + dt * 32 * ROWB;
+          ua[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(ao), qb[s], ua[dt], 0, 0, 0);
+          ua[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(MATB + ao), qb[s], ua[dt], 0, 0, 0);
+        }
+      // RMSNorm adjoint; ua[dt][r] = u(dim 32 dt + 8 (r / 4) + 4 h + r % 4)
+      float ss = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss += ua[dt][r] * ua[dt][r];
+      ss += __shfl_xor(ss, 32, kWave);
+      const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
+      float gw[4][16];
+      float gr = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 wv = wf ? *reinterpret_cast<const float4*>(wf + 32 * dt + 8 * q4 + 4 * h)
+                               : make_float4(1.f, 1.f, 1.f, 1.f);
+          const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dv = (float)dob[dt][q4][e];
+            gw[dt][4 * q4 + e] = w4[e] * dv;
+            gr += gw[dt][4 * q4 + e] * ua[dt][4 * q4 + e];
+            dw[dt][4 * q4 + e] += valid ? ua[dt][4 * q4 + e] * inv * dv : 0.f;
+          }
+        }
+      gr += __shfl_xor(gr, 32, kWave);
+      const float mg = gr * inv * (1.f / D);   // mean(g r)
+      const float vm = valid ? inv : 0.f;      // tokens past the frame contribute nothing
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ua[dt][r] = (gw[dt][r] - ua[dt][r] * inv * mg) * vm;   // du
+      // du as hi / lo bf16: B operand of dq^T for k-step s (dims 16 s + {4h..4h+3, 8+4h..8+4h+3}),
+      // and staged as rows for dS
+      bf16x8 duh[8], dul[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int dt = s / 2, q0 = 2 * (s % 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = ua[dt][4 * q0 + e];
+          duh[s][e] = (bf16)x;
+          dul[s][e] = (bf16)(x - (float)duh[s][e]);
+        }
+        // logical 16-byte chunks c0, c0 + 1 hold dims 8 c .. 8 c + 7; this lane's four sit at byte 8 h
+        const int c0 = 4 * dt + q0;
+        const int off0 = l32 * ROWB + swz(l32, c0) * 16 + 8 * h, off1 = l32 * ROWB + swz(l32, c0 + 1) * 16 + 8 * h;
+        *reinterpret_cast<bf16x4*>(sdh + off0) = __builtin_shufflevector(duh[s], duh[s], 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(sdh + off1) = __builtin_shufflevector(duh[s], duh[s], 4, 5, 6, 7);
+        *reinterpret_cast<bf16x4*>(sdl + off0) = __builtin_shufflevector(dul[s], dul[s], 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(sdl + off1) = __builtin_shufflevector(dul[s], dul[s], 4, 5, 6, 7);
+      }
+      // dq^T = S^T du^T: A = transposed reads of S (hi, lo), B = du (hi, lo); lo x lo dropped
+      f32x16 qa[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) qa[dt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          asm volatile("" ::: "memory");
+          const int to = s * 16 * ROWB;
+          const bf16x8 ah = cat(tr(troff[dt][0] + to), tr(troff[dt][1] + to));
+          const bf16x8 al = cat(tr(MATB + troff[dt][0] + to), tr(MATB + troff[dt][1] + to));
+          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, duh[s], qa[dt], 0, 0, 0);
+          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, dul[s], qa[dt], 0, 0, 0);
+          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, duh[s], qa[dt], 0, 0, 0);
+        }
+      // qa[dt][r] = dq(dim 32 dt + 8 (r / 4) + 4 h + r % 4) of this direction
+      if (valid) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int j = 32 * dt + 8 * q4 + 4 * h;
+            float4* pp = reinterpret_cast<float4*>(dqpf + (int64_t)n * D + j);
+            if constexpr (SECOND) {
+              const float4 prev = *pp;
+              bf16x4 o;
+              o[0] = (bf16)(prev.x + qa[dt][4 * q4]);
+              o[1] = (bf16)(prev.y + qa[dt][4 * q4 + 1]);
+              o[2] = (bf16)(prev.z + qa[dt][4 * q4 + 2]);
+              o[3] = (bf16)(prev.w + qa[dt][4 * q4 + 3]);
+              *reinterpret_cast<bf16x4*>(dqf + (int64_t)n * D + j) = o;
+            } else {
+              *pp = make_float4(qa[dt][4 * q4], qa[dt][4 * q4 + 1], qa[dt][4 * q4 + 2], qa[dt][4 * q4 + 3]);
+            }
+          }
+      }
+    }
+    __syncthreads();
+    // dS rows 32 wave .. + 31 over the tiles of this round: A = du^T (transposed reads of the
+    // staged du rows, column block = wave), B = q (transposed reads, column block jt)
+    for (int tt = 0; tt < 4; ++tt) {
+      if (round * 4 + tt >= ntile) break;
+      const unsigned char* base = lds + STG + tt * STGW;
+      const int bofs = (int)(base - lds);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int to = bofs + ks * 16 * ROWB;
+        const bf16x8 ah = cat(tr(to + troff[wave & 3][0]), tr(to + troff[wave & 3][1]));
+        const bf16x8 al = cat(tr(to + TILEB + troff[wave & 3][0]), tr(to + TILEB + troff[wave & 3][1]));
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const bf16x8 bq = cat(tr(to + 2 * TILEB + troff[jt][0]), tr(to + 2 * TILEB + troff[jt][1]));
+          dsa[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq, dsa[jt], 0, 0, 0);
+          dsa[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq, dsa[jt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // dS: dsa[jt][r] = dS(row 32 wave + 8 (r / 4) + 4 h + r % 4, column 32 jt + l32)
+  float* ds = dsg + (f * 2 + dir) * D * D;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[(32 * wave + 8 * (r / 4) + 4 * h + r % 4) * D + 32 * jt + l32] = dsa[jt][r];
+  // dw: sum the 32 lanes of each half (they hold the same dims), then the four waves
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = dw[dt][r];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, kWave);
+      dw[dt][r] = x;
+    }
+  float* red = reinterpret_cast<float*>(lds);   // S is no longer read
+  if (l32 == 0) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave * D + 32 * dt + 8 * (r / 4) + 4 * h + r % 4] = dw[dt][r];
+  }
+  __syncthreads();
+  if (tid < D) dwp[(f * 2 + dir) * D + tid] = red[tid] + red[D + tid] + red[2 * D + tid] + red[3 * D + tid];
+}
+
+hipError_t launch_tok_grad(const void* q, const void* d_out, int64_t ldo, const float* states, const float* rms_w,
+                           float* dqp, void* dq, float* dsg, float* dwp, int64_t nf, int H, int T, int N, int Lt,
+                           float eps, hipStream_t st) {
+  if (nf <= 0) return hipSuccess;
+  if (nf > 0x7FFFFFFF) return hipErrorInvalidValue;
+  tok_grad_bf16_d128_kernel<false><<<(unsigned)nf, 256, 0, st>>>(
+      (const bf16*)q, (const bf16*)d_out, ldo, states, rms_w, dqp, (bf16*)dq, dsg, dwp, 0, nf, H, T, N, Lt, eps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tok_grad_bf16_d128_kernel<true><<<(unsigned)nf, 256, 0, st>>>(
+      (const bf16*)q, (const bf16*)d_out, ldo, states, rms_w, dqp, (bf16*)dq, dsg, dwp, 1, nf, H, T, N, Lt, eps);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_grad(const void* k, const void* v, const float* cdb, const float* beta, void* dk, void* dv,
                           int64_t nf, int T, int N, int Lt, hipStream_t st) {
   if (nf <= 0) return hipSuccess;

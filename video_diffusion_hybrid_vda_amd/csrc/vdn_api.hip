@@ -283,7 +283,7 @@ int check_params(const vdn_shape* s, const float* gamma, const float* beta, char
 enum Phase {
   kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhAnchorMerge, kPhGram, kPhSolve, kPhScan,
   kPhReadout, kPhOutGemm, kPhQuantize, kPhBwdRecompute, kPhBwdU, kPhBwdRms, kPhBwdDq, kPhBwdDs,
-  kPhBwdScan, kPhBwdFrame, kPhBwdKv, kPhBwdDw, kNumPhases
+  kPhBwdScan, kPhBwdFrame, kPhBwdKv, kPhBwdDw, kPhBwdToken, kNumPhases
 };
 const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "window_attn",
                                              "anchor_merge",      "vda_gram",  "vda_solve",
@@ -291,7 +291,7 @@ const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "
                                              "mxfp8_quantize", "bwd_recompute", "bwd_u_gemm",
                                              "bwd_rms",        "bwd_dq_gemm", "bwd_ds_gemm",
                                              "bwd_scan",       "bwd_frame",   "bwd_kv_gemm",
-                                             "bwd_dw"};
+                                             "bwd_dw",         "bwd_token"};
 
 struct Timer {
   std::mutex mu;
@@ -449,45 +449,55 @@ int run_vda_bwd(const vdn_shape* s, const void* q, const void* k, const void* v,
   });
   if (rc != VDN_OK) return rc;
 
-  // U[f][dir] = Q_t S_dir,t^T
-  BGemm g;
-  g.a0 = q; g.b0 = states; g.c = u;
-  g.M = N; g.N = d; g.K = d;
-  g.sam = d; g.sak = 1; g.sbk = 1; g.sbn = d; g.ldc = d;
-  g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
-  g.sa[0] = 0; g.sa[1] = Nd; g.sa[2] = Ltd;
-  g.sb[0] = nf * dd; g.sb[1] = dd; g.sb[2] = T * dd;
-  g.sc[0] = Nd; g.sc[1] = 2 * Nd; g.sc[2] = T * 2 * Nd;
-  rc = step(kPhBwdU, "vda_bwd u launch", [&] { return launch_bgemm(dt, 0, 0, g, st, mfma); });
-  if (rc != VDN_OK) return rc;
-  rc = step(kPhBwdRms, "vda_bwd rms launch", [&] {
-    return launch_rms_bwd(dt, d, u, d_out, (int64_t)H * d, rms_w, dwp, nf, H, T, N, Lt, s->rms_eps, st);
-  });
-  if (rc != VDN_OK) return rc;
+  if (dt == VDN_BF16 && d == 128) {
+    // u, du, dq, dS and the RMSNorm-weight partials in one pass per direction; u and du
+    // never leave the chip (the u buffer holds dq's fp32 share of the first direction)
+    rc = step(kPhBwdToken, "vda_bwd token launch", [&] {
+      return launch_tok_grad(q, d_out, (int64_t)H * d, states, rms_w, u, dq, dsg, dwp, nf, H, T, N, Lt,
+                             s->rms_eps, st);
+    });
+    if (rc != VDN_OK) return rc;
+  } else {
+    // U[f][dir] = Q_t S_dir,t^T
+    BGemm g;
+    g.a0 = q; g.b0 = states; g.c = u;
+    g.M = N; g.N = d; g.K = d;
+    g.sam = d; g.sak = 1; g.sbk = 1; g.sbn = d; g.ldc = d;
+    g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
+    g.sa[0] = 0; g.sa[1] = Nd; g.sa[2] = Ltd;
+    g.sb[0] = nf * dd; g.sb[1] = dd; g.sb[2] = T * dd;
+    g.sc[0] = Nd; g.sc[1] = 2 * Nd; g.sc[2] = T * 2 * Nd;
+    rc = step(kPhBwdU, "vda_bwd u launch", [&] { return launch_bgemm(dt, 0, 0, g, st, mfma); });
+    if (rc != VDN_OK) return rc;
+    rc = step(kPhBwdRms, "vda_bwd rms launch", [&] {
+      return launch_rms_bwd(dt, d, u, d_out, (int64_t)H * d, rms_w, dwp, nf, H, T, N, Lt, s->rms_eps, st);
+    });
+    if (rc != VDN_OK) return rc;
 
-  // dq = du_f S_f + du_b S_b (K = 2d over the two directions)
-  g = BGemm();
-  g.a0 = u; g.a1 = u + Nd; g.b0 = states; g.b1 = states + nf * dd; g.c = dq;
-  g.M = N; g.N = d; g.K = 2 * d; g.ks = d;
-  g.sam = d; g.sak = 1; g.sbk = d; g.sbn = 1; g.ldc = d;
-  g.batch = nf; g.n0 = T; g.n1 = 1;
-  g.sa[0] = 2 * Nd; g.sa[2] = T * 2 * Nd;
-  g.sb[0] = dd; g.sb[2] = T * dd;
-  g.sc[0] = Nd; g.sc[2] = Ltd;
-  rc = step(kPhBwdDq, "vda_bwd dq launch", [&] { return launch_bgemm(0, 0, dt, g, st, mfma); });
-  if (rc != VDN_OK) return rc;
+    // dq = du_f S_f + du_b S_b (K = 2d over the two directions)
+    g = BGemm();
+    g.a0 = u; g.a1 = u + Nd; g.b0 = states; g.b1 = states + nf * dd; g.c = dq;
+    g.M = N; g.N = d; g.K = 2 * d; g.ks = d;
+    g.sam = d; g.sak = 1; g.sbk = d; g.sbn = 1; g.ldc = d;
+    g.batch = nf; g.n0 = T; g.n1 = 1;
+    g.sa[0] = 2 * Nd; g.sa[2] = T * 2 * Nd;
+    g.sb[0] = dd; g.sb[2] = T * dd;
+    g.sc[0] = Nd; g.sc[2] = Ltd;
+    rc = step(kPhBwdDq, "vda_bwd dq launch", [&] { return launch_bgemm(0, 0, dt, g, st, mfma); });
+    if (rc != VDN_OK) return rc;
 
-  // dS[f][dir] = du^T Q_t (sum over the frame's tokens)
-  g = BGemm();
-  g.a0 = u; g.b0 = q; g.c = dsg;
-  g.M = d; g.N = d; g.K = N;
-  g.sam = 1; g.sak = d; g.sbk = d; g.sbn = 1; g.ldc = d;
-  g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
-  g.sa[0] = Nd; g.sa[1] = 2 * Nd; g.sa[2] = T * 2 * Nd;
-  g.sb[0] = 0; g.sb[1] = Nd; g.sb[2] = Ltd;
-  g.sc[0] = dd; g.sc[1] = 2 * dd; g.sc[2] = T * 2 * dd;
-  rc = step(kPhBwdDs, "vda_bwd dS launch", [&] { return launch_bgemm(0, dt, 0, g, st, mfma); });
-  if (rc != VDN_OK) return rc;
+    // dS[f][dir] = du^T Q_t (sum over the frame's tokens)
+    g = BGemm();
+    g.a0 = u; g.b0 = q; g.c = dsg;
+    g.M = d; g.N = d; g.K = N;
+    g.sam = 1; g.sak = d; g.sbk = d; g.sbn = 1; g.ldc = d;
+    g.batch = 2 * nf; g.n0 = 2; g.n1 = T;
+    g.sa[0] = Nd; g.sa[1] = 2 * Nd; g.sa[2] = T * 2 * Nd;
+    g.sb[0] = 0; g.sb[1] = Nd; g.sb[2] = Ltd;
+    g.sc[0] = dd; g.sc[1] = 2 * dd; g.sc[2] = T * 2 * dd;
+    rc = step(kPhBwdDs, "vda_bwd dS launch", [&] { return launch_bgemm(0, dt, 0, g, st, mfma); });
+    if (rc != VDN_OK) return rc;
+  }
 
   rc = step(kPhBwdScan, "vda_bwd scan launch", [&] { return launch_scan_bwd(d, am, gamma, dsg, dx, BH, T, st); });
   if (rc != VDN_OK) return rc;
