@@ -196,9 +196,11 @@ def phase_rooflines(cfg, phases, gated=True, mode=""):
     mfma("out_gemm", 2.0 * B * L * 2 * D * D)
     t = ms("vda_scan")
     if t:
-        # per frame-head and direction: M_t and B_t read (fp32), S_t written as fp32 and (bf16 I/O)
-        # as hi/lo bf16 pairs
-        scan_bytes = 2 * frames * (2 * d * d * 4 + d * d * 4 + (2 * d * d * 2 if es == 2 else 0))
+        # per frame-head and direction: M_t and B_t read (fp32); S_t written as hi/lo bf16 pairs
+        # (bf16 I/O) and as fp32 where the readout reads it (fp32 I/O, or head_dim other than 128)
+        keeps_fp32 = not (es == 2 and d == 128)
+        scan_bytes = 2 * frames * (2 * d * d * 4 + (d * d * 4 if keeps_fp32 else 0)
+                                   + (2 * d * d * 2 if es == 2 else 0))
         out["vda_scan"] = {"bound": "latency", "ms": round(t, 3), "frame_steps": T,
                            "us_per_step": round(t * 1e3 / T, 2),
                            "algorithmic_gb": round(scan_bytes / 1e9, 3),

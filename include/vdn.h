@@ -153,7 +153,7 @@ int vda_scan_fwd(const vdn_shape* shape, const void* q, const void* k,
  * the same computation and arguments without the workspace.  Its scratch (the
  * per-frame statistics, transitions, states and their hi/lo copies, and the
  * range-check verdict: vdn_workspace_bytes(shape, VDN_OP_VDA_SCAN) bytes when
- * states is NULL, less when states is given) is a static device array of the
+ * states is NULL, no more when states is given) is a static device array of the
  * library, 64 MiB (67108864 bytes) per device, held by each device that loads
  * the library until the process ends.  The call allocates nothing, device or
  * host.  A shape whose scratch would exceed 64 MiB returns VDN_ERR_WORKSPACE

@@ -417,19 +417,26 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
 // ---------------------------------------------------------------------------
 // scan, head_dim 128, on fp32 MFMA.  One workgroup of four waves per 32 state
 // rows of one (batch, head, direction); wave w produces columns 32w .. 32w+31
-// of those rows with 64 v_mfma_f32_32x32x2_f32 per frame.  The contraction
-// index is permuted so that every operand is a contiguous run: at product s
-// lane half h supplies k = 64h + s, so the A operand is row r0 + l%32 of
-// X = gamma S + B, columns 64h .. 64h+63 (S from LDS, B_t from HBM), and the
-// B operand is row 32w + l%32 of M_t^T, the same columns.  B_{t+1} and
-// M_{t+1}^T are loaded while frame t is multiplied.  The eight workgroups of
-// one (batch, head) share an XCD, so each M_t comes from HBM once per
-// direction.
+// of those rows with 64 v_mfma_f32_32x32x2_f32 per frame: S_t = X_t M_t with
+// X_t = gamma_t S_{t-1} + B_t held in LDS.  The contraction index runs through
+// the products in the order k = 8i + 4h + c (i the product group, h the lane
+// half, c the component), so the A operand is one 16-byte LDS read per group
+// and the B operand (row 32w + l%32 of M_t^T) comes from 16-byte loads in
+// which the two lane halves read adjacent bytes of each row.  After the
+// products the workgroup puts S_t in LDS (double-buffered against X_t) and
+// every thread takes four 16-byte chunks of it: it stores S_t (fp32 and/or
+// the hi/lo bf16 pair) with whole-row coalesced stores and overwrites each
+// chunk with X_{t+1} = gamma_{t+1} S_t + B_{t+1}.  M_{t+1}^T is loaded one
+// frame ahead, B two frames ahead, each B element once per workgroup.  The
+// eight workgroups of one (batch, head) share an XCD, so each M_t comes from
+// HBM once per direction.  kStates / kSplit: S_t is written to `states` (fp32)
+// / to `split` (hi/lo bf16).
 namespace sc {
 constexpr int D = 128, R = 32, LD = D + 4;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 }  // namespace sc
 
+template <bool kStates, bool kSplit>
 __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restrict__ Mt,
                                                             const float* __restrict__ Bm,
                                                             const float* __restrict__ gamma,
@@ -437,71 +444,102 @@ __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restr
                                                             bf16* __restrict__ split, int T,
                                                             int64_t bhtdd, int total) {
   using namespace sc;
-  __shared__ __attribute__((aligned(16))) float Ss[R * LD];   // S_{t-1}, rows r0 .. r0+31
+  __shared__ __attribute__((aligned(16))) float P[2][R * LD];   // X_t and S_t, rows r0 .. r0+31
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l32 = lane % 32, h = lane / 32;
   const int lid = xcd_remap(blockIdx.x, total);
   const int dir = lid & 1, rb = (lid >> 1) & 3;
   const int64_t bh = lid >> 3;
   const int r0 = rb * R, n0 = wave * 32;
-  for (int i = tid; i < R * LD; i += 256) Ss[i] = 0.f;
+  // the thread's chunks: rows crow + 8j (j = 0..3), columns ccol .. ccol+3
+  const int crow = tid / 32, ccol = 4 * (tid % 32);
 
-  auto frame = [&](int step) { return dir ? T - 1 - step : step; };
-  auto load = [&](float4 (&b)[16], float4 (&m)[16], int t) {
-    const int64_t fi = bh * T + t;
-    const float4* bp = reinterpret_cast<const float4*>(Bm + fi * D * D + (int64_t)(r0 + l32) * D + 64 * h);
-    const float4* mp = reinterpret_cast<const float4*>(Mt + fi * D * D + (int64_t)(n0 + l32) * D + 64 * h);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      b[i] = bp[i];
-      m[i] = mp[i];
-    }
+  // frame index of scan step `step`, clamped to the last step (loads past the
+  // end re-read the last frame and are not used)
+  auto fidx = [&](int step) -> int64_t {
+    const int c = step < T ? step : T - 1;
+    return bh * T + (dir ? T - 1 - c : c);
   };
-  float4 bx[16], mx[16];
-  load(bx, mx, frame(0));
-  __syncthreads();
+  auto load_m = [&](float4 (&m)[16], int step) {
+    const float* mp = Mt + fidx(step) * D * D + (int64_t)(n0 + l32) * D + 4 * h;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m[i] = *reinterpret_cast<const float4*>(mp + 8 * i);
+  };
+  auto load_b = [&](float4 (&b)[4], int step) {
+    const float* bp = Bm + fidx(step) * D * D + (int64_t)(r0 + crow) * D + ccol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(bp + 8 * j * D);
+  };
 
-  for (int step = 0; step < T; ++step) {
-    const int t = frame(step);
-    const int64_t fi = bh * T + t;
-    const float g = gamma[fi];
-    float4 bn[16], mn[16];
-    load(bn, mn, frame(step + 1 < T ? step + 1 : step));
-    __builtin_amdgcn_sched_barrier(0);   // the next frame's loads go out before this frame's products
-    const float* srow = Ss + l32 * LD + 64 * h;
+  // one frame step: mc = M_s^T, mn <- M_{s+1}^T, bl <- B_{s+2}, be = B_{s+1};
+  // X_s in X, S_s and then X_{s+1} go to Y
+  auto step = [&](int s, float4 (&mc)[16], float4 (&mn)[16], float4 (&bl)[4], const float4 (&be)[4],
+                  const float* X, float* Y) {
+    const int64_t fi = fidx(s);
+    const float gn = gamma[fidx(s + 1)];
+    load_m(mn, s + 1);
+    load_b(bl, s + 2);
+    __builtin_amdgcn_sched_barrier(0);   // the next frames' loads go out before this frame's products
+    const float* xrow = X + l32 * LD + 4 * h;
+    float4 xv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xv[i] = *reinterpret_cast<const float4*>(xrow + 8 * i);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 sv = *reinterpret_cast<const float4*>(srow + 4 * i);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.x + bx[i].x, mx[i].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.y + bx[i].y, mx[i].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.z + bx[i].z, mx[i].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g * sv.w + bx[i].w, mx[i].w, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].x, mc[i].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].y, mc[i].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].z, mc[i].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].w, mc[i].w, acc, 0, 0, 0);
     }
-    __syncthreads();   // every wave has read S_{t-1}
-    // acc[r] = S_t[r0 + 8 (r/4) + 4h + r%4][n0 + l32]
-    float* sdst = states + dir * bhtdd + fi * D * D + (int64_t)r0 * D + n0 + l32;
-    bf16* hdst = split ? split + (dir * bhtdd + fi * D * D) * 2 + (int64_t)r0 * D + n0 + l32 : nullptr;
+    // acc[r] = S_s[r0 + 8 (r/4) + 4h + r%4][n0 + l32]
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r / 4) + 4 * h + r % 4;
-      Ss[row * LD + n0 + l32] = acc[r];
-      sdst[row * D] = acc[r];
-      if (hdst) {
-        const bf16 hi = (bf16)acc[r];
-        hdst[row * D] = hi;
-        hdst[row * D + D * D] = (bf16)(acc[r] - (float)hi);
+    for (int r = 0; r < 16; ++r) Y[(8 * (r / 4) + 4 * h + r % 4) * LD + n0 + l32] = acc[r];
+    __syncthreads();   // S_s complete in Y
+    const int64_t off = fi * D * D + (int64_t)(r0 + crow) * D + ccol;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float* yp = Y + (crow + 8 * j) * LD + ccol;
+      const float4 sv = *reinterpret_cast<const float4*>(yp);
+      if constexpr (kStates) *reinterpret_cast<float4*>(states + dir * bhtdd + off + 8 * j * D) = sv;
+      if constexpr (kSplit) {
+        bf16x4 hi, lo;
+        hi[0] = (bf16)sv.x; hi[1] = (bf16)sv.y; hi[2] = (bf16)sv.z; hi[3] = (bf16)sv.w;
+        lo[0] = (bf16)(sv.x - (float)hi[0]);
+        lo[1] = (bf16)(sv.y - (float)hi[1]);
+        lo[2] = (bf16)(sv.z - (float)hi[2]);
+        lo[3] = (bf16)(sv.w - (float)hi[3]);
+        bf16* sp = split + dir * bhtdd * 2 + fi * D * D * 2 + (int64_t)(r0 + crow + 8 * j) * D + ccol;
+        *reinterpret_cast<bf16x4*>(sp) = hi;
+        *reinterpret_cast<bf16x4*>(sp + D * D) = lo;
       }
+      // (after the last frame this X is formed from clamped loads and never read)
+      float4 xn;
+      xn.x = gn * sv.x + be[j].x;
+      xn.y = gn * sv.y + be[j].y;
+      xn.z = gn * sv.z + be[j].z;
+      xn.w = gn * sv.w + be[j].w;
+      *reinterpret_cast<float4*>(yp) = xn;
     }
-    __syncthreads();   // S_t visible
+    __syncthreads();   // X_{s+1} complete in Y
+  };
+
+  float4 m0[16], m1[16], b0[4], b1[4];
+  load_m(m0, 0);
+  load_b(b0, 0);
+  load_b(b1, 1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      bx[i] = bn[i];
-      mx[i] = mn[i];
-    }
+  for (int j = 0; j < 4; ++j)   // X_0 = B_0 (S_{-1} = 0)
+    *reinterpret_cast<float4*>(&P[0][(crow + 8 * j) * LD + ccol]) = b0[j];
+  __syncthreads();
+  int s = 0;
+  for (; s + 1 < T; s += 2) {
+    step(s, m0, m1, b0, b1, P[0], P[1]);
+    step(s + 1, m1, m0, b1, b0, P[1], P[0]);
   }
+  if (s < T) step(s, m0, m1, b0, b1, P[0], P[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -889,7 +927,14 @@ hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float*
   const int64_t bhtdd = (int64_t)BH * T * d * d;
   if (d == 128) {
     const int total = BH * 8;   // 4 row blocks x 2 directions per (batch, head)
-    vda_scan_d128_kernel<<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
+    if (states && split)
+      vda_scan_d128_kernel<true, true><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
+    else if (states)
+      vda_scan_d128_kernel<true, false><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
+    else if (split)
+      vda_scan_d128_kernel<false, true><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
+    else
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   dim3 grid(d / kScanRows, BH, 2);

@@ -146,7 +146,13 @@ AttnParams make_attn_params(const vdn_shape* s) {
 struct VdaLayout {
   size_t am, bc, states, split, flag, total;
 };
+// The fp32 states are read back only by the fp32 readout and by a caller that
+// asks for them: in bf16 I/O the readout takes the hi/lo pairs, and with
+// head_dim 128 the scan then writes no fp32 copy at all.
+bool scan_keeps_fp32_states(const vdn_shape* s) { return !(s->dtype == VDN_BF16 && s->head_dim == 128); }
+
 VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
+  need_states = need_states && scan_keeps_fp32_states(s);
   const size_t dd = (size_t)s->head_dim * s->head_dim;
   const size_t frames = (size_t)s->batch * s->heads * s->frames;
   VdaLayout l;
@@ -364,7 +370,7 @@ int run_vda(const vdn_shape* s, const void* q, const void* k, const void* v,
   const VdaLayout l = vda_layout(s, states == nullptr);
   float* am = (float*)(ws + l.am);
   float* bc = (float*)(ws + l.bc);
-  float* st_buf = states ? states : (float*)(ws + l.states);
+  float* st_buf = states ? states : scan_keeps_fp32_states(s) ? (float*)(ws + l.states) : nullptr;
   __bf16* split = s->dtype == VDN_BF16 ? (__bf16*)(ws + l.split) : nullptr;
   const int d = s->head_dim;
   const int nframes = s->batch * s->heads * s->frames;
