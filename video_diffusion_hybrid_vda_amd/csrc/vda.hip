@@ -687,41 +687,36 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 
 // ---------------------------------------------------------------------------
 // readout, bf16 and head_dim 128 (the workload shapes).  One workgroup of four
-// waves per (frame, head) walks all N tokens of the frame.  Both directions'
-// S_hi and S_lo are copied into LDS once by the direct-to-LDS DMA (4 x 32 KB;
-// the 16-byte chunk c of row i at c ^ (i & 15), so that the sixteen rows a
-// 16-lane group reads cover all banks).  Each wave then takes 64-token blocks
-// (block = wave + 4k) and computes U^T = S Q^T on 32x32x16 MFMA: the state
-// fragments are the A operand (one LDS read serves both 32-token tiles), the
-// Q fragments come straight from HBM as the B operand.  The loads of the
-// block's gate and of the next block's Q are issued before the block's 256
-// products, so their latency hides behind the matrix work; the accumulators
-// live in the accumulator registers.  A lane holds 64 of the 128 outputs of
-// one token, its partner lane i ^ 32 the other 64: the RMSNorm needs one
-// cross-lane swap, and one swap per four outputs gives each lane eight
-// consecutive dimensions for 16-byte gate loads and output stores.
+// waves per (frame, head), two workgroups per CU.  Wave w owns the output
+// dimensions 32w .. 32w+31: it keeps rows 32w .. 32w+31 of both directions'
+// S_hi and S_lo in registers as the A operand of 32x32x16 MFMAs, and walks the
+// frame in 32-token tiles computing U^T = S Q^T, 32 products per tile.  The
+// workgroup stages each tile's Q once in LDS (coalesced 16-byte loads one tile
+// ahead; chunk c of token row r at c ^ (r & 15), so the fragment reads of a
+// 16-lane group cover all banks).  RMSNorm needs each token's sum of squares
+// over all 128 dimensions: each wave leaves its 32-dimension partial sums in
+// LDS, and after the tile's one barrier every wave adds the four.  A lane then
+// forms (u_f rn_f + u_b rn_b) w g for 16 dimensions of one token; one
+// cross-lane swap per four dimensions gives it eight consecutive dimensions
+// for each 16-byte gate load and output store.  With two workgroups per CU one
+// workgroup's products run while the other's vector epilogue does.
 namespace ro {
-constexpr int D = 128, SUB = 64;
-constexpr int MATB = D * D * 2;   // one bf16 d x d matrix, 32 KB
-constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0)
+constexpr int D = 128, TT = 32;        // head_dim, tokens per tile
+constexpr int QROW = D * 2;            // bytes per token row of a staged Q tile
+constexpr int QTILE = TT * QROW;       // 8 KB
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & 15); }
-// products with the accumulator in the accumulator registers; a chain starts from zero
-__device__ __forceinline__ void mma_first(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&a"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mma_acc(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
 }  // namespace ro
 
-__global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
+template <bool kGate>
+__global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ split, const float* __restrict__ rms_w,
     const bf16* __restrict__ gate, int64_t ldg, bf16* __restrict__ out, int64_t ldo, int H, int T_, int N,
     int Lt, float eps, int64_t bhtdd) {
   using namespace ro;
-  __shared__ __attribute__((aligned(1024))) unsigned char Sl[4 * MATB];   // [dir][hi, lo][row][chunk]
-  __shared__ float wl[D];
+  __shared__ __attribute__((aligned(16))) unsigned char QL[2][QTILE];
+  __shared__ __attribute__((aligned(16))) float SSX[2][2][TT][4];   // [buffer][dir][token][wave]
+  __shared__ __attribute__((aligned(16))) float wl[D];
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane % 32, h = lane / 32;
@@ -730,145 +725,150 @@ __global__ __launch_bounds__(256) void vda_readout_bf16_d128_kernel(
   const int64_t bh = fi / T_;
   const int hh = (int)(bh % H);
   const int64_t b = bh / H;
-
-  // states -> LDS: 1 KB block j of a direction (j < 32: S_hi rows 4j..4j+3,
-  // else S_lo) by wave j / 16; lane l fills physical chunk l % 16 of row l / 16
-  {
-    const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)Sl;
-#pragma unroll
-    for (int dir = 0; dir < 2; ++dir) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(split + (dir * bhtdd + fi * D * D) * 2), (short)0, 2 * MATB, 0x00020000);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int blk = wave * 16 + i, part = blk / 32;
-        const int row = (blk % 32) * 4 + lane / 16;
-        const int voff = part * MATB + row * 256 + sw(row, lane % 16) * 16;
-        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
-                     "{m0}"(lds0 + dir * 2 * MATB + blk * 1024)
-                     : "memory");
-      }
-    }
-  }
-  if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
-
-  const int64_t NL = Lt;   // rows per (batch, head) of q and per batch entry of out / gate
+  const int d0 = 32 * wave;
+  const int ntile = (N + TT - 1) / TT;
   const bf16* qfr = q + (bh * Lt + (int64_t)t * N) * D;
-  const int nblk = (N + SUB - 1) / SUB;
-  // Q^T fragments of a block: lane holds q[token 32 tt + l32][16 ks + 8 h .. +7].
-  // Token indices past the frame are clamped to its last token (loads stay
-  // unconditional); those lanes' outputs are never stored.
-  auto load_q = [&](bf16x8 (&dst)[2][8], int blk) {
+  const int64_t row0 = b * (int64_t)Lt + (int64_t)t * N;   // output / gate row of the frame's token 0
+
+  if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
+  // sf[dir][part][ks] = S_part of direction dir, row d0 + l32, columns 16 ks + 8 h .. +7
+  bf16x8 sf[2][2][8];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int n = min(blk * SUB + 32 * tt + l32, N - 1);
+  for (int dir = 0; dir < 2; ++dir)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        dst[tt][ks] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 16 * ks + 8 * h);
+    for (int part = 0; part < 2; ++part) {
+      const bf16* sp = split + (dir * bhtdd + fi * D * D) * 2 + part * D * D + (int64_t)(d0 + l32) * D + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sf[dir][part][ks] = *reinterpret_cast<const bf16x8*>(sp + 16 * ks);
+    }
+
+  // the thread's share of a Q tile: 16-byte chunks tid and tid + 256 (token c / 16,
+  // chunk c % 16); tokens past the frame re-read its last token (never stored)
+  // (the tile's offsets are wave-uniform; only a tile that runs past the frame clamps per lane)
+  const bf16* qthr = qfr + (tid / 16) * D + 8 * (tid % 16);   // chunk j: + 16 j rows
+  auto load_q = [&](bf16x8 (&qv)[2], int tile) {
+    const bf16* tp = qthr + (int64_t)tile * (TT * D);
+    if ((tile + 1) * TT <= N) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) qv[j] = *reinterpret_cast<const bf16x8*>(tp + 16 * j * D);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(tile * TT + tid / 16 + 16 * j, N - 1);
+        qv[j] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 8 * (tid % 16));
+      }
     }
   };
-  bf16x8 qf[2][8];
-  load_q(qf, wave);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
+  auto store_q = [&](const bf16x8 (&qv)[2], int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + 256 * j, r = c / 16;
+      *reinterpret_cast<bf16x8*>(&QL[buf][r * QROW + sw(r, c % 16) * 16]) = qv[j];
+    }
+  };
+  // gate of the lane's token, dimensions d0 + 16 pp + 8 h .. +7
+  const bf16* glane = kGate ? gate + (row0 + l32) * ldg + hh * D + d0 + 8 * h : nullptr;
+  auto load_g = [&](bf16x8 (&gv)[2], int tile) {
+    const bf16* grow = (tile + 1) * TT <= N
+                           ? glane + (int64_t)tile * TT * ldg
+                           : gate + (row0 + min(tile * TT + l32, N - 1)) * ldg + hh * D + d0 + 8 * h;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) gv[pp] = *reinterpret_cast<const bf16x8*>(grow + 16 * pp);
+  };
+  bf16* olane = out + (row0 + l32) * ldo + hh * D + d0 + 8 * h;
 
-  for (int blk = wave; blk < nblk; blk += 4) {
-    bf16x8 qn[2][8];
-    load_q(qn, blk + 4);
-    __builtin_amdgcn_sched_barrier(0);   // the loads above go out before the products
+  // One tile.  qv holds Q of tile + 1 (stored into LDS here, then refilled with
+  // tile + 3); gv holds the gate of this tile (refilled with tile + 2): two
+  // register sets alternate, so every load has two tiles' time to arrive.
+  auto body = [&](int tile, bf16x8 (&qv)[2], bf16x8 (&gv)[2]) {
+    const int buf = tile & 1;
+    // B operand: q[token 32 tile + l32][16 ks + 8 h .. +7]
+    bf16x8 bq[8];
+    const unsigned char* qrow = QL[buf] + l32 * QROW;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = *reinterpret_cast<const bf16x8*>(qrow + sw(l32, 2 * ks + h) * 16);
+    // acc_dir[r] = u_dir[dimension d0 + 8 (r/4) + 4 h + r%4] of token 32 tile + l32
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[0][part][ks], bq[ks], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[1][part][ks], bq[ks], acc1, 0, 0, 0);
+      }
+    // the next tile's Q into the other buffer (its readers have passed the previous barrier)
+    store_q(qv, buf ^ 1);
+    load_q(qv, tile + 3);
 
-    // acc[dir][tt][dt][r] = u_dir(token 32 tt + l32)[32 dt + 8 (r/4) + 4 h + r%4].
-    // 128 steps (dir, dt, ks, part), each one state-fragment read and two
-    // products; fragments are read three steps ahead and the steps are fenced,
-    // so at most four fragments are live.
-    f32x16 acc[2][2][4];
-    auto read_sf = [&](int step) {
-      const int dir = step >> 6, dt = (step >> 4) & 3, ks = (step >> 1) & 7, part = step & 1;
-      const int row = 32 * dt + l32;
-      return *reinterpret_cast<const bf16x8*>(Sl + (2 * dir + part) * MATB + row * 256 + sw(row, 2 * ks + h) * 16);
-    };
-    bf16x8 sfb[4];
+    float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) sfb[i] = read_sf(i);
-    // gate of this block (lane: dims 32 dt + 16 p + 8 h .. +7 of its token), loaded
-    // halfway through the products
-    bf16x8 gv[2][4][2];
+    for (int r = 0; r < 16; ++r) {
+      ss0 += acc0[r] * acc0[r];
+      ss1 += acc1[r] * acc1[r];
+    }
+    const auto x0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss0), __float_as_uint(ss0), false, false);
+    const auto x1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss1), __float_as_uint(ss1), false, false);
+    if (h == 0) {
+      SSX[buf][0][l32][wave] = __uint_as_float(x0[0]) + __uint_as_float(x0[1]);
+      SSX[buf][1][l32][wave] = __uint_as_float(x1[0]) + __uint_as_float(x1[1]);
+    }
+    __syncthreads();   // partial sums and the next Q tile complete
+    const float4 p0 = *reinterpret_cast<const float4*>(&SSX[buf][0][l32][0]);
+    const float4 p1 = *reinterpret_cast<const float4*>(&SSX[buf][1][l32][0]);
+    // hardware reciprocal square root (1 ulp)
+    const float rn0 = __builtin_amdgcn_rsqf(((p0.x + p0.y) + (p0.z + p0.w)) * (1.f / D) + eps);
+    const float rn1 = __builtin_amdgcn_rsqf(((p1.x + p1.y) + (p1.z + p1.w)) * (1.f / D) + eps);
+    const int n = tile * TT + l32;
+    bf16* orow = olane + (int64_t)tile * TT * ldo;
 #pragma unroll
-    for (int step = 0; step < 128; ++step) {
-      if (step == 64 && gate) {
+    for (int pp = 0; pp < 2; ++pp) {
+      // ya: dims d0 + 16pp + 4h + e, yb: dims d0 + 16pp + 8 + 4h + e; after the swap
+      // the lane holds dims d0 + 16pp + 8h + {0..3} in ya and + {4..7} in yb
+      float ya[4], yb[4];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int n = min(blk * SUB + 32 * tt + l32, N - 1);
-          const bf16* grow = gate + (b * NL + (int64_t)t * N + n) * ldg + hh * D + 8 * h;
+      for (int e = 0; e < 4; ++e) {
+        const int da = d0 + 16 * pp + 4 * h + e;
+        ya[e] = (acc0[8 * pp + e] * rn0 + acc1[8 * pp + e] * rn1) * wl[da];
+        yb[e] = (acc0[8 * pp + 4 + e] * rn0 + acc1[8 * pp + 4 + e] * rn1) * wl[da + 8];
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ya[e]), __float_as_uint(yb[e]), false, false);
+        ya[e] = __uint_as_float(x[0]);
+        yb[e] = __uint_as_float(x[1]);
+      }
+      bf16x8 ov;
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) gv[tt][dt][pp] = *reinterpret_cast<const bf16x8*>(grow + 32 * dt + 16 * pp);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (kGate) {
+          ov[e] = (bf16)(ya[e] * (float)gv[pp][e]);   // the only rounding of the output
+          ov[4 + e] = (bf16)(yb[e] * (float)gv[pp][4 + e]);
+        } else {
+          ov[e] = (bf16)ya[e];
+          ov[4 + e] = (bf16)yb[e];
         }
       }
-      if (step + 3 < 128) sfb[(step + 3) & 3] = read_sf(step + 3);
-      const int dir = step >> 6, dt = (step >> 4) & 3, ks = (step >> 1) & 7, part = step & 1;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        if (ks == 0 && part == 0) mma_first(acc[dir][tt][dt], sfb[step & 3], qf[tt][ks]);
-        else mma_acc(acc[dir][tt][dt], sfb[step & 3], qf[tt][ks]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      if (n < N) *reinterpret_cast<bf16x8*>(orow + 16 * pp) = ov;
     }
-    // the products' results are read by vector instructions below
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kGate) load_g(gv, tile + 2);
+  };
 
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int n = blk * SUB + 32 * tt + l32;
-      float rn[2];
-#pragma unroll
-      for (int dir = 0; dir < 2; ++dir) {
-        float ss = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ss += acc[dir][tt][dt][r] * acc[dir][tt][dt][r];
-        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-        ss = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
-        rn[dir] = 1.f / sqrtf(ss / D + eps);
-      }
-      const int64_t orow = b * NL + (int64_t)t * N + n;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          // ya: dims 32dt + 16pp + 4h + e, yb: dims 32dt + 16pp + 8 + 4h + e; after the swap
-          // the lane holds dims 32dt + 16pp + 8h + {0..3} in ya and + {4..7} in yb
-          float ya[4], yb[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int da = 32 * dt + 16 * pp + 4 * h + e;
-            ya[e] = (acc[0][tt][dt][8 * pp + e] * rn[0] + acc[1][tt][dt][8 * pp + e] * rn[1]) * wl[da];
-            yb[e] = (acc[0][tt][dt][8 * pp + 4 + e] * rn[0] + acc[1][tt][dt][8 * pp + 4 + e] * rn[1]) * wl[da + 8];
-            const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ya[e]), __float_as_uint(yb[e]),
-                                                            false, false);
-            ya[e] = __uint_as_float(x[0]);
-            yb[e] = __uint_as_float(x[1]);
-          }
-          bf16x8 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ga = gate ? (float)gv[tt][dt][pp][e] : 1.f;
-            const float gb = gate ? (float)gv[tt][dt][pp][4 + e] : 1.f;
-            ov[e] = (bf16)(ya[e] * ga);        // the only rounding of the output
-            ov[4 + e] = (bf16)(yb[e] * gb);
-          }
-          if (n < N) *reinterpret_cast<bf16x8*>(out + orow * ldo + hh * D + 32 * dt + 16 * pp + 8 * h) = ov;
-        }
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[tt][ks] = qn[tt][ks];
+  bf16x8 q0[2], q1[2];
+  bf16x8 g0[2], g1[2];
+  load_q(q0, 0);
+  store_q(q0, 0);
+  load_q(q0, 1);
+  load_q(q1, 2);
+  if constexpr (kGate) {
+    load_g(g0, 0);
+    load_g(g1, 1);
   }
+  __syncthreads();
+  int tile = 0;
+  for (; tile + 2 <= ntile; tile += 2) {
+    body(tile, q0, g0);
+    body(tile + 1, q1, g1);
+  }
+  if (tile < ntile) body(tile, q0, g0);
 }
 
 // ---------------------------------------------------------------------------
@@ -950,9 +950,13 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
   if (sizeof(T) == 2 && d == 128 && split) {
     const int64_t nb = (int64_t)B * H * T_;
-    if (nb == 0) return hipSuccess;
-    vda_readout_bf16_d128_kernel<<<(unsigned)nb, 256, 0, st>>>((const bf16*)q, split, rms_w, (const bf16*)gate,
-                                                               ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
+    if (nb == 0 || N <= 0) return hipSuccess;
+    if (gate)
+      vda_readout_bf16_d128_kernel<true><<<(unsigned)nb, 256, 0, st>>>(
+          (const bf16*)q, split, rms_w, (const bf16*)gate, ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
+    else
+      vda_readout_bf16_d128_kernel<false><<<(unsigned)nb, 256, 0, st>>>(
+          (const bf16*)q, split, rms_w, nullptr, ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
     return hipGetLastError();
   }
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
