@@ -104,7 +104,11 @@ def vda_branch_backward(q, k, v, gamma, beta, rms_w, eps, d_o):
 
     q, k, v, d_o: [B, H, T, N, d]; gamma, beta: [B, H, T]; rms_w: [H*d].
     Returns a dict with dq, dk, dv ([B, H, T, N, d]), dgamma, dbeta
-    ([B, H, T]) and drms_w ([H*d]).
+    ([B, H, T]) and drms_w ([H*d]), and dbeta_mass ([B, H, T]): the sum of
+    the absolute values of the products that make up dbeta, <|dA|, |K^T K|>
+    + <|dB|, |V^T K|>.  dbeta can cancel far below that mass, and a
+    floating-point evaluation of it carries an error of order unit roundoff
+    times the mass (the standard error bound of an inner product).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -117,6 +121,7 @@ def vda_branch_backward(q, k, v, gamma, beta, rms_w, eps, d_o):
     out = {name: np.zeros(q.shape) for name in ("dq", "dk", "dv")}
     out["dgamma"] = np.zeros((B, H, T))
     out["dbeta"] = np.zeros((B, H, T))
+    out["dbeta_mass"] = np.zeros((B, H, T))
     out["drms_w"] = np.zeros(H * d)
     for b in range(B):
         for h in range(H):
@@ -147,4 +152,6 @@ def vda_branch_backward(q, k, v, gamma, beta, rms_w, eps, d_o):
                 out["dk"][b, h, t] = bt * (kt @ (dA + dA.T)) + bt * (vt @ dB[t])
                 out["dv"][b, h, t] = bt * (kt @ dB[t].T)
                 out["dbeta"][b, h, t] = np.sum(dA * (kt.T @ kt)) + np.sum(dB[t] * (vt.T @ kt))
+                out["dbeta_mass"][b, h, t] = (np.sum(np.abs(dA * (kt.T @ kt)))
+                                              + np.sum(np.abs(dB[t] * (vt.T @ kt))))
     return out

@@ -152,3 +152,17 @@ def test_all_zero_beta_closed_form():
                 want[t] += np.prod(gam[s:t]) * np.sum((w * do[s]) * (q[s] @ btil.T))
     want /= np.sqrt(eps)
     np.testing.assert_allclose(gr["dbeta"][0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_dbeta_term_mass_bounds_dbeta_and_scales_with_the_upstream_gradient():
+    """dbeta_mass is a sum of absolute values of the products whose signed sum
+    is dbeta: it bounds |dbeta| (triangle inequality), is zero when the
+    upstream gradient is zero, and is linear in a positive scaling of it."""
+    x, d_o = _inputs(21)
+    gr = _grads(x, d_o, 1e-6)
+    assert np.all(gr["dbeta_mass"] >= np.abs(gr["dbeta"]) * (1 - 1e-12))
+    assert np.all(gr["dbeta_mass"] > 0)
+    g0 = _grads(x, np.zeros_like(d_o), 1e-6)
+    assert np.all(g0["dbeta_mass"] == 0.0) and np.all(g0["dbeta"] == 0.0)
+    g3 = _grads(x, 3.0 * d_o, 1e-6)
+    np.testing.assert_allclose(g3["dbeta_mass"], 3.0 * gr["dbeta_mass"], rtol=1e-12)
