@@ -197,8 +197,8 @@ def phase_rooflines(cfg, phases, gated=True, mode=""):
     t = ms("vda_scan")
     if t:
         # per frame-head and direction: M_t and B_t read (fp32); S_t written as hi/lo bf16 pairs
-        # (bf16 I/O) and as fp32 where the readout reads it (fp32 I/O, or head_dim other than 128)
-        keeps_fp32 = not (es == 2 and d == 128)
+        # (bf16 I/O) and as fp32 where the readout reads it (fp32 I/O, or head_dim 32)
+        keeps_fp32 = not (es == 2 and d in (64, 128))
         scan_bytes = 2 * frames * (2 * d * d * 4 + (d * d * 4 if keeps_fp32 else 0)
                                    + (2 * d * d * 2 if es == 2 else 0))
         out["vda_scan"] = {"bound": "latency", "ms": round(t, 3), "frame_steps": T,

@@ -354,7 +354,7 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
 // from the solve's M^T).  Writes every S_t in fp32 and, when `split` is
 // non-null, also as an unevaluated bf16 pair hi + lo (hi = bf16(S), lo =
 // bf16(S - hi)) for the bf16 readout, laid out [dir][frame][hi|lo][d][d].
-// This is the path for head_dim 32 and 64; head_dim 128 uses the MFMA kernel
+// This is the path for head_dim 32; head_dim 64 and 128 use the MFMA kernel
 // below.
 template <int D, int R>
 __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__ Mt,
@@ -415,9 +415,10 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// scan, head_dim 128, on fp32 MFMA.  One workgroup of four waves per 32 state
-// rows of one (batch, head, direction); wave w produces columns 32w .. 32w+31
-// of those rows with 64 v_mfma_f32_32x32x2_f32 per frame: S_t = X_t M_t with
+// scan, head_dim D = 64 or 128, on fp32 MFMA.  One workgroup of D / 32 waves
+// per 32 state rows of one (batch, head, direction); wave w produces columns
+// 32w .. 32w+31 of those rows with D / 2 v_mfma_f32_32x32x2_f32 per frame:
+// S_t = X_t M_t with
 // X_t = gamma_t S_{t-1} + B_t held in LDS.  The contraction index runs through
 // the products in the order k = 8i + 4h + c (i the product group, h the lane
 // half, c the component), so the A operand is one 16-byte LDS read per group
@@ -428,31 +429,33 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
 // the hi/lo bf16 pair) with whole-row coalesced stores and overwrites each
 // chunk with X_{t+1} = gamma_{t+1} S_t + B_{t+1}.  M_{t+1}^T is loaded one
 // frame ahead, B two frames ahead, each B element once per workgroup.  The
-// eight workgroups of one (batch, head) share an XCD, so each M_t comes from
-// HBM once per direction.  kStates / kSplit: S_t is written to `states` (fp32)
-// / to `split` (hi/lo bf16).
+// 2 D / 32 workgroups of one (batch, head) share an XCD, so each M_t comes
+// from HBM once per direction.  kStates / kSplit: S_t is written to `states`
+// (fp32) / to `split` (hi/lo bf16).
 namespace sc {
-constexpr int D = 128, R = 32, LD = D + 4;
+constexpr int R = 32;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 }  // namespace sc
 
-template <bool kStates, bool kSplit>
-__global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restrict__ Mt,
+template <int D, bool kStates, bool kSplit>
+__global__ __launch_bounds__(2 * D) void vda_scan_mfma_kernel(const float* __restrict__ Mt,
                                                             const float* __restrict__ Bm,
                                                             const float* __restrict__ gamma,
                                                             float* __restrict__ states,
                                                             bf16* __restrict__ split, int T,
                                                             int64_t bhtdd, int total) {
   using namespace sc;
+  constexpr int LD = D + 4, NRB = D / R, KG = D / 8;   // LDS row stride, row blocks, product groups
   __shared__ __attribute__((aligned(16))) float P[2][R * LD];   // X_t and S_t, rows r0 .. r0+31
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int l32 = lane % 32, h = lane / 32;
   const int lid = xcd_remap(blockIdx.x, total);
-  const int dir = lid & 1, rb = (lid >> 1) & 3;
-  const int64_t bh = lid >> 3;
+  const int dir = lid & 1, rb = (lid >> 1) % NRB;
+  const int64_t bh = lid / (2 * NRB);
   const int r0 = rb * R, n0 = wave * 32;
-  // the thread's chunks: rows crow + 8j (j = 0..3), columns ccol .. ccol+3
-  const int crow = tid / 32, ccol = 4 * (tid % 32);
+  // the thread's chunks (2 D threads, a chunk is 4 floats of a row): rows
+  // crow + 8j (j = 0..3), columns ccol .. ccol+3
+  const int crow = tid / (D / 4), ccol = 4 * (tid % (D / 4));
 
   // frame index of scan step `step`, clamped to the last step (loads past the
   // end re-read the last frame and are not used)
@@ -460,10 +463,10 @@ __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restr
     const int c = step < T ? step : T - 1;
     return bh * T + (dir ? T - 1 - c : c);
   };
-  auto load_m = [&](float4 (&m)[16], int step) {
+  auto load_m = [&](float4 (&m)[KG], int step) {
     const float* mp = Mt + fidx(step) * D * D + (int64_t)(n0 + l32) * D + 4 * h;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m[i] = *reinterpret_cast<const float4*>(mp + 8 * i);
+    for (int i = 0; i < KG; ++i) m[i] = *reinterpret_cast<const float4*>(mp + 8 * i);
   };
   auto load_b = [&](float4 (&b)[4], int step) {
     const float* bp = Bm + fidx(step) * D * D + (int64_t)(r0 + crow) * D + ccol;
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restr
 
   // one frame step: mc = M_s^T, mn <- M_{s+1}^T, bl <- B_{s+2}, be = B_{s+1};
   // X_s in X, S_s and then X_{s+1} go to Y
-  auto step = [&](int s, float4 (&mc)[16], float4 (&mn)[16], float4 (&bl)[4], const float4 (&be)[4],
+  auto step = [&](int s, float4 (&mc)[KG], float4 (&mn)[KG], float4 (&bl)[4], const float4 (&be)[4],
                   const float* X, float* Y) {
     const int64_t fi = fidx(s);
     const float gn = gamma[fidx(s + 1)];
@@ -481,14 +484,14 @@ __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restr
     load_b(bl, s + 2);
     __builtin_amdgcn_sched_barrier(0);   // the next frames' loads go out before this frame's products
     const float* xrow = X + l32 * LD + 4 * h;
-    float4 xv[16];
+    float4 xv[KG];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xv[i] = *reinterpret_cast<const float4*>(xrow + 8 * i);
+    for (int i = 0; i < KG; ++i) xv[i] = *reinterpret_cast<const float4*>(xrow + 8 * i);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < KG; ++i) {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].x, mc[i].x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].y, mc[i].y, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].z, mc[i].z, acc, 0, 0, 0);
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(256) void vda_scan_d128_kernel(const float* __restr
     __syncthreads();   // X_{s+1} complete in Y
   };
 
-  float4 m0[16], m1[16], b0[4], b1[4];
+  float4 m0[KG], m1[KG], b0[4], b1[4];
   load_m(m0, 0);
   load_b(b0, 0);
   load_b(b1, 1);
@@ -925,21 +928,25 @@ hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float*
                            float* states, bf16* split, int BH, int T, hipStream_t st) {
   if (BH == 0) return hipSuccess;
   const int64_t bhtdd = (int64_t)BH * T * d * d;
-  if (d == 128) {
-    const int total = BH * 8;   // 4 row blocks x 2 directions per (batch, head)
-    if (states && split)
-      vda_scan_d128_kernel<true, true><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
-    else if (states)
-      vda_scan_d128_kernel<true, false><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
-    else if (split)
-      vda_scan_d128_kernel<false, true><<<total, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total);
-    else
-      return hipErrorInvalidValue;
+  if (d == 128 || d == 64) {
+    const int total = BH * 2 * (d / 32);   // d / 32 row blocks x 2 directions per (batch, head)
+#define VDN_SCAN(DD, WS, WH) \
+  vda_scan_mfma_kernel<DD, WS, WH><<<total, 2 * DD, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total)
+    if (!states && !split) return hipErrorInvalidValue;
+    if (d == 128) {
+      if (states && split) VDN_SCAN(128, true, true);
+      else if (states) VDN_SCAN(128, true, false);
+      else VDN_SCAN(128, false, true);
+    } else {
+      if (states && split) VDN_SCAN(64, true, true);
+      else if (states) VDN_SCAN(64, true, false);
+      else VDN_SCAN(64, false, true);
+    }
+#undef VDN_SCAN
     return hipGetLastError();
   }
   dim3 grid(d / kScanRows, BH, 2);
-  if (d == 32) vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd);
-  else vda_scan_kernel<64, kScanRows><<<grid, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd);
+  vda_scan_kernel<32, kScanRows><<<grid, 256, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd);
   return hipGetLastError();
 }
 

@@ -148,8 +148,10 @@ struct VdaLayout {
 };
 // The fp32 states are read back only by the fp32 readout and by a caller that
 // asks for them: in bf16 I/O the readout takes the hi/lo pairs, and with
-// head_dim 128 the scan then writes no fp32 copy at all.
-bool scan_keeps_fp32_states(const vdn_shape* s) { return !(s->dtype == VDN_BF16 && s->head_dim == 128); }
+// head_dim 64 or 128 (the MFMA scan) the scan then writes no fp32 copy at all.
+bool scan_keeps_fp32_states(const vdn_shape* s) {
+  return !(s->dtype == VDN_BF16 && (s->head_dim == 128 || s->head_dim == 64));
+}
 
 VdaLayout vda_layout(const vdn_shape* s, bool need_states) {
   need_states = need_states && scan_keeps_fp32_states(s);
