@@ -50,44 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27819837275,
-        "window_attn": 275487287181,
-        "anchor_merge": 2035524193,
-        "vda_gram": 5374847660,
-        "vda_solve": 321179729,
-        "vda_scan": 1272357501,
-        "vda_readout": 7904839452,
-        "out_gemm": 25918900467
+        "gate_gemm": 27820884274,
+        "window_attn": 263735667775,
+        "anchor_merge": 2046579261,
+        "vda_gram": 5374820637,
+        "vda_solve": 321178264,
+        "vda_scan": 946849090,
+        "vda_readout": 7904707979,
+        "out_gemm": 25578294659
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 180873085017,
-        "mxfp8_quantize": 7659590516
+        "window_attn": 182885411278,
+        "mxfp8_quantize": 7659466089
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7283761303,
-        "bwd_u_gemm": 15201366372,
-        "bwd_rms": 25270196922,
-        "bwd_dq_gemm": 15200784452,
-        "bwd_ds_gemm": 20564112885,
-        "bwd_scan": 3515977126,
-        "bwd_frame": 5570974220,
-        "bwd_kv_gemm": 16485149904
+        "bwd_recompute": 7284740121,
+        "bwd_token": 23393128083,
+        "bwd_scan": 3516038432,
+        "bwd_frame": 5570934487,
+        "bwd_kv_gemm": 10440075175
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145306973,
-        "vda_solve": 11173686,
-        "vda_scan": 58757862,
-        "vda_readout": 222475504
+        "vda_gram": 145306925,
+        "vda_solve": 11173684,
+        "vda_scan": 22120561,
+        "vda_readout": 222452921
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11460269256,
-        "window_attn": 111337037879,
-        "anchor_merge": 1493847400,
-        "vda_gram": 2213161144,
-        "vda_solve": 132434890,
-        "vda_scan": 517340512,
-        "vda_readout": 3254868633,
-        "out_gemm": 10488645703
+        "gate_gemm": 11472781785,
+        "window_attn": 112809594025,
+        "anchor_merge": 1483779567,
+        "vda_gram": 2213140688,
+        "vda_solve": 132434738,
+        "vda_scan": 379500243,
+        "vda_readout": 3255810043,
+        "out_gemm": 10569544381
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -100,9 +97,11 @@ SOURCE_GROUPS = {
     "window": ("window_attn.hip",), "gemm": ("gemm.hip",), "vda": ("vda.hip",), "mxfp8": ("mxfp8.hip",),
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
-SOURCE_SHA = {"window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "4544271a9cf41f32",
-              "mxfp8": "8cdcfa773199d9a4", "bwd": "2489a9c3e0652eee", "vda+bwd": None,
-              "common": "a24de8342071a471"}
+SOURCE_SHA = {
+    "window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "9a332cafc88dc0f3",
+    "mxfp8": "8cdcfa773199d9a4", "bwd": "486b4152ce7b0b68", "vda+bwd": "1ece9f5dc2b9cb72",
+    "common": "a24de8342071a471"
+}
 
 
 def _sha(files):
