@@ -117,6 +117,9 @@ def measured_traffic(workload, phase):
     """Counter-measured HBM bytes per call of `phase` on `workload`, or None if there is no such figure or
     the phase's kernel sources (or the shared headers) changed since it was taken."""
     t = COUNTER_TRAFFIC.get(workload, {}).get(phase)
+    if t is None and workload.endswith(" mxfp8"):
+        # MXFP8 mode changes only the softmax branch's kernels; the others run as in bf16 mode
+        t = COUNTER_TRAFFIC.get(workload[:-len(" mxfp8")], {}).get(phase)
     grp = PHASE_SOURCES.get(phase)
     if t is None or grp is None or _sha(("vdn_common.h", "vdn_internal.h")) != SOURCE_SHA["common"]:
         return None
