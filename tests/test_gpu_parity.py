@@ -145,6 +145,12 @@ VDA = [
     ("H3_T9_N40_d64_bf16", VdnConfig(1, 3, 64, 9, 40, dtype="bf16", seed=43)),
     ("T5_N1000_d128_bf16", VdnConfig(1, 1, 128, 5, 1000, dtype="bf16", seed=44)),
     ("T6_N2_d128_f32_rankdef", VdnConfig(1, 1, 128, 6, 2, dtype="f32", beta_lo=0.0, seed=45)),
+    # bf16 readout edges: one token per frame, exactly one 32-token tile, an even
+    # frame count (the scan's two-frame loop without a remainder), head_dim 64 in
+    # fp32 (MFMA scan with the fp32 states)
+    ("T2_N1_d128_bf16", VdnConfig(1, 1, 128, 2, 1, dtype="bf16", seed=46)),
+    ("H2_T4_N32_d128_bf16", VdnConfig(1, 2, 128, 4, 32, dtype="bf16", seed=47)),
+    ("B2_T8_N45_d64_f32", VdnConfig(2, 1, 64, 8, 45, dtype="f32", seed=48)),
 ]
 
 

@@ -292,16 +292,25 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
 // ---------------------------------------------------------------------------
 // solve: one workgroup of 2d threads per (frame, head).  M_t = (I + A_t)^-1 by
 // Gauss-Jordan elimination of the augmented [I + A_t | I]: thread c keeps
-// column c in registers; at step k the pivot row and the pivot column go
-// through LDS (double-buffered, one barrier per step) and every column is
-// updated with a rank-1 step.  I + A_t is symmetric positive definite (beta
-// >= 0, eigenvalues >= 1), for which elimination without pivoting is stable.
+// column c in registers and every column is updated with a rank-1 step per
+// pivot.  I + A_t is symmetric positive definite (beta >= 0, eigenvalues
+// >= 1), for which elimination without pivoting is stable, and that symmetry
+// also delivers the pivot column from the pivot row: after k steps the
+// not yet eliminated block of the left half is a Schur complement of I + A_t,
+// itself symmetric, so column k holds row k's left-half entries in rows >= k;
+// and in rows i < k it holds minus row k's right-half entry i (the upper
+// part of the left half is (I+A)_{<k,<k}^-1 (I+A)_{<k,k}, the lower part of the
+// right half -(I+A)_{k,<k} (I+A)_{<k,<k}^-1, transposes of each other).  So every
+// thread writes only its own pivot-row entry to LDS (right half negated), at
+// the rotated position (c - k) mod 2d, and slots 0 .. d-1 of that buffer are
+// the pivot column in the rotated row order each thread keeps (one barrier
+// per step, double-buffered).  Columns of the left half that were already
+// eliminated are never read again and are not stored.
 // AM holds A_t on entry and M_t^T on exit (row j = column j of M_t, so the
 // scan reads contiguous runs of a column).
 template <int D>
 __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM) {
-  __shared__ __attribute__((aligned(16))) float colb[2][D];
-  __shared__ float rowb[2][2 * D];
+  __shared__ __attribute__((aligned(16))) float rowb[2][2 * D];
   const int64_t f = blockIdx.x;
   float* am = AM + f * D * D;
   const int c = threadIdx.x;
@@ -316,19 +325,15 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
   // (all register indices stay compile-time constants): the update writes
   // row i+1 into slot i and the normalised pivot row goes to slot D-1.  After
   // D steps every row is back in its place.
+  const float sgn = c < D ? 1.f : -1.f;
   for (int k = 0; k < D; ++k) {
     const int buf = k & 1;
-    rowb[buf][c] = a[0];
-    if (c == k) {
-#pragma unroll
-      for (int i = 0; i < D; i += 4)
-        *reinterpret_cast<float4*>(&colb[buf][i]) = make_float4(a[i], a[i + 1], a[i + 2], a[i + 3]);
-    }
+    rowb[buf][(c - k) & (2 * D - 1)] = sgn * a[0];
     __syncthreads();
-    const float x = rowb[buf][c] / rowb[buf][k];
+    const float x = a[0] / rowb[buf][0];
 #pragma unroll
     for (int i = 0; i < D; i += 4) {
-      const float4 cv = *reinterpret_cast<const float4*>(&colb[buf][i]);
+      const float4 cv = *reinterpret_cast<const float4*>(&rowb[buf][i]);
       if (i > 0) a[i - 1] = a[i] - cv.x * x;
       a[i] = a[i + 1] - cv.y * x;
       a[i + 1] = a[i + 2] - cv.z * x;
