@@ -483,7 +483,7 @@ def time_backward(cfg, inp, vdn, torch, steps):
     <d_out, ungated linear-branch output> with respect to q, k, v, gamma, beta and
     the RMSNorm weight, d_out seeded N(0, 1) in bf16.  Each token-side phase is
     reported against HBM with its algorithmic bytes (every tensor it must read or
-    write once); the dominant phase (dK and dV) is the roofline entry."""
+    write once); the longer of the two is the roofline entry."""
     B, H, d, T, N = cfg.batch, cfg.heads, cfg.head_dim, cfg.frames, cfg.tokens_per_frame
     L, D = cfg.seq_len, cfg.model_dim
     shape = vdn.shape_from_config(cfg)

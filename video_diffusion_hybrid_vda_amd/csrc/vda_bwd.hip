@@ -903,6 +903,7 @@ __global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
         for (int r = 0; r < 16; ++r) ss += ua[dt][r] * ua[dt][r];
       ss += __shfl_xor(ss, 32, kWave);
       const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
+      const float vm = valid ? inv : 0.f;      // tokens past the frame contribute nothing
       float gw[4][16];
       float gr = 0.f;
 #pragma unroll
@@ -915,18 +916,21 @@ __global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float dv = (float)dob[dt][q4][e];
+            const float u = ua[dt][4 * q4 + e];
             gw[dt][4 * q4 + e] = w4[e] * dv;
-            gr += gw[dt][4 * q4 + e] * ua[dt][4 * q4 + e];
-            dw[dt][4 * q4 + e] += valid ? ua[dt][4 * q4 + e] * inv * dv : 0.f;
+            gr += gw[dt][4 * q4 + e] * u;
+            const float rr = u * vm;                // r = u / rho (zero past the frame)
+            ua[dt][4 * q4 + e] = rr;
+            dw[dt][4 * q4 + e] += rr * dv;
           }
         }
       gr += __shfl_xor(gr, 32, kWave);
-      const float mg = gr * inv * (1.f / D);   // mean(g r)
-      const float vm = valid ? inv : 0.f;      // tokens past the frame contribute nothing
+      const float c = gr * inv * inv * (1.f / D);   // mean(g r) / rho
+      // du = (g - r mean(g r)) / rho
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ua[dt][r] = (gw[dt][r] - ua[dt][r] * inv * mg) * vm;   // du
+        for (int r = 0; r < 16; ++r) ua[dt][r] = gw[dt][r] * vm - ua[dt][r] * c;
       // du as hi / lo bf16: B operand of dq^T for k-step s (dims 16 s + {4h..4h+3, 8+4h..8+4h+3}),
       // and staged as rows for dS
       bf16x8 duh[8], dul[8];
