@@ -70,23 +70,39 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int n0 = 0; n0 < N; n0 += NC) {
-    __syncthreads();
-    for (int c = tid; c < NC * CPR; c += 256) {
-      const int row = c % NC, cc = c / NC;
-      Chunk16 kk = zero_chunk(), vv = zero_chunk();
-      if (n0 + row < N) {
-        kk = *reinterpret_cast<const Chunk16*>(kf + (int64_t)(n0 + row) * D + cc * EPC);
-        vv = *reinterpret_cast<const Chunk16*>(vf + (int64_t)(n0 + row) * D + cc * EPC);
-      }
-      const T* ke = reinterpret_cast<const T*>(&kk);
-      const T* ve = reinterpret_cast<const T*>(&vv);
+  // the thread's 16-byte chunks of a stage (chunk c = tid + 256 i: token row c % NC,
+  // column chunk c / NC); the next stage's are loaded while this stage is multiplied
+  constexpr int CH = (NC * CPR + 255) / 256;
+  Chunk16 kk[CH], vv[CH];
+  auto load_stage = [&](int n0) {
 #pragma unroll
-      for (int x = 0; x < EPC; ++x) {
-        Sm[(cc * EPC + x) * LDT + row] = ke[x];
-        Sm[D * LDT + (cc * EPC + x) * LDT + row] = ve[x];
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i, row = c % NC, cc = c / NC;
+      kk[i] = vv[i] = zero_chunk();
+      if (c < NC * CPR && n0 + row < N) {
+        kk[i] = *reinterpret_cast<const Chunk16*>(kf + (int64_t)(n0 + row) * D + cc * EPC);
+        vv[i] = *reinterpret_cast<const Chunk16*>(vf + (int64_t)(n0 + row) * D + cc * EPC);
       }
     }
+  };
+  load_stage(0);
+
+  for (int n0 = 0; n0 < N; n0 += NC) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + 256 * i, row = c % NC, cc = c / NC;
+      if (c < NC * CPR) {
+        const T* ke = reinterpret_cast<const T*>(&kk[i]);
+        const T* ve = reinterpret_cast<const T*>(&vv[i]);
+#pragma unroll
+        for (int x = 0; x < EPC; ++x) {
+          Sm[(cc * EPC + x) * LDT + row] = ke[x];
+          Sm[D * LDT + (cc * EPC + x) * LDT + row] = ve[x];
+        }
+      }
+    }
+    if (n0 + NC < N) load_stage(n0 + NC);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < NC / KS; ++ks)
