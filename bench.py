@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27820884274,
-        "window_attn": 263735667775,
-        "anchor_merge": 2046579261,
-        "vda_gram": 5374820637,
-        "vda_solve": 321178264,
-        "vda_scan": 946849090,
-        "vda_readout": 7904707979,
-        "out_gemm": 25578294659
+        "gate_gemm": 27823611549,
+        "window_attn": 269500874443,
+        "anchor_merge": 2050280677,
+        "vda_gram": 5374808793,
+        "vda_solve": 321173113,
+        "vda_scan": 946882892,
+        "vda_readout": 7904830852,
+        "out_gemm": 27145143155
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 182885411278,
-        "mxfp8_quantize": 7659466089
+        "window_attn": 179862447065,
+        "mxfp8_quantize": 7659473829
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284740121,
-        "bwd_token": 23393128083,
-        "bwd_scan": 3516038432,
-        "bwd_frame": 5570934487,
-        "bwd_kv_gemm": 10440075175
+        "bwd_recompute": 7284701570,
+        "bwd_token": 23428387304,
+        "bwd_scan": 3516308452,
+        "bwd_frame": 5573391906,
+        "bwd_kv_gemm": 10441042788
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145306925,
-        "vda_solve": 11173684,
-        "vda_scan": 22120561,
-        "vda_readout": 222452921
+        "vda_gram": 145322204,
+        "vda_solve": 11161393,
+        "vda_scan": 22120554,
+        "vda_readout": 222449628
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11472781785,
-        "window_attn": 112809594025,
-        "anchor_merge": 1483779567,
-        "vda_gram": 2213140688,
-        "vda_solve": 132434738,
-        "vda_scan": 379500243,
-        "vda_readout": 3255810043,
-        "out_gemm": 10569544381
+        "gate_gemm": 11460696813,
+        "window_attn": 114409186268,
+        "anchor_merge": 1488954485,
+        "vda_gram": 2213139704,
+        "vda_solve": 132414091,
+        "vda_scan": 379786677,
+        "vda_readout": 3255784982,
+        "out_gemm": 11103694864
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,8 +98,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "9a332cafc88dc0f3",
-    "mxfp8": "8cdcfa773199d9a4", "bwd": "486b4152ce7b0b68", "vda+bwd": "1ece9f5dc2b9cb72",
+    "window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "3cae34d1e0bee408",
+    "mxfp8": "8cdcfa773199d9a4", "bwd": "867876673bea4dcc", "vda+bwd": "fb3e1a5c8343ec87",
     "common": "a24de8342071a471"
 }
 
