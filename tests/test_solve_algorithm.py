@@ -48,5 +48,5 @@ def test_rank_deficient_and_zero_write_strength():
     np.testing.assert_allclose(solve_like_kernel(np.zeros((d, d)), np.float64), np.eye(d), atol=0)
     v = np.arange(1, d + 1, dtype=np.float64)[:, None] / d
     a = v @ v.T
-    ref = np.eye(d) - a / (1.0 + float(v.T @ v))            # Sherman-Morrison
+    ref = np.eye(d) - a / (1.0 + float((v.T @ v)[0, 0]))    # Sherman-Morrison
     np.testing.assert_allclose(solve_like_kernel(a, np.float64), ref, rtol=0, atol=1e-14)
