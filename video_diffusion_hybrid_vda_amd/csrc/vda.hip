@@ -710,66 +710,78 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// readout, bf16 and head_dim 128 (the workload shapes).  One workgroup of four
-// waves per (frame, head), two workgroups per CU.  Wave w owns the output
-// dimensions 32w .. 32w+31: it keeps rows 32w .. 32w+31 of both directions'
-// S_hi and S_lo in registers as the A operand of 32x32x16 MFMAs, and walks the
-// frame in 32-token tiles computing U^T = S Q^T, 32 products per tile.  The
-// workgroup stages each tile's Q once in LDS (coalesced 16-byte loads one tile
-// ahead; chunk c of token row r at c ^ (r & 15), so the fragment reads of a
-// 16-lane group cover all banks).  RMSNorm needs each token's sum of squares
-// over all 128 dimensions: each wave leaves its 32-dimension partial sums in
-// LDS, and after the tile's one barrier every wave adds the four.  A lane then
-// forms (u_f rn_f + u_b rn_b) w g for 16 dimensions of one token; one
-// cross-lane swap per four dimensions gives it eight consecutive dimensions
-// for each 16-byte gate load and output store.  With two workgroups per CU one
-// workgroup's products run while the other's vector epilogue does.
+// readout, bf16 and head_dim D = 64 or 128 (the workload shapes).  One
+// workgroup of D/32 waves per (frame, head) or per share of a frame's tokens,
+// two workgroups per CU at D = 128.  Wave w owns the output dimensions
+// 32w .. 32w+31: it keeps rows 32w .. 32w+31 of both directions' S_hi and S_lo
+// in registers as the A operand of 32x32x16 MFMAs, and walks its tokens in
+// 32-token tiles computing U^T = S Q^T, D/4 products per tile.  The workgroup
+// stages each tile's Q once in LDS (coalesced 16-byte loads two tiles ahead;
+// chunk c of token row r at c ^ (r mod the row's chunk count), so the
+// fragment reads of a 16-lane group spread over the banks).  RMSNorm needs
+// each token's sum of squares over all D dimensions: each wave leaves its
+// 32-dimension partial sums in LDS, and after the tile's one barrier every
+// wave adds the D/32 partials.  A lane then forms (u_f rn_f + u_b rn_b) w g
+// for 16 dimensions of one token; one cross-lane swap per four dimensions
+// gives it eight consecutive dimensions for each 16-byte gate load and output
+// store.  With two workgroups per CU one workgroup's products run while the
+// other's vector epilogue does.  nsplit > 1 gives each frame that many
+// workgroups over consecutive runs of its tiles (each loads the frame's
+// states), for shapes with too few frames to fill the chip.
 namespace ro {
-constexpr int D = 128, TT = 32;        // head_dim, tokens per tile
-constexpr int QROW = D * 2;            // bytes per token row of a staged Q tile
-constexpr int QTILE = TT * QROW;       // 8 KB
+constexpr int TT = 32;                 // tokens per tile
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & 15); }
+template <int D>
+__device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & (D / 8 - 1)); }
 }  // namespace ro
 
-template <bool kGate>
-__global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
+template <int D, bool kGate>
+__global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ split, const float* __restrict__ rms_w,
     const bf16* __restrict__ gate, int64_t ldg, bf16* __restrict__ out, int64_t ldo, int H, int T_, int N,
-    int Lt, float eps, int64_t bhtdd) {
+    int Lt, float eps, int64_t bhtdd, int nsplit) {
   using namespace ro;
+  constexpr int NW = D / 32, NT = 2 * D;   // waves, threads
+  constexpr int CPR = D / 8;               // 16-byte chunks per token row
+  constexpr int KS = D / 16;               // 16-deep product steps
+  constexpr int QROW = D * 2;              // bytes per token row of a staged Q tile
+  constexpr int QTILE = TT * QROW;
   __shared__ __attribute__((aligned(16))) unsigned char QL[2][QTILE];
-  __shared__ __attribute__((aligned(16))) float SSX[2][2][TT][4];   // [buffer][dir][token][wave]
+  __shared__ __attribute__((aligned(16))) float SSX[2][2][TT][NW];   // [buffer][dir][token][wave]
   __shared__ __attribute__((aligned(16))) float wl[D];
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane % 32, h = lane / 32;
-  const int64_t fi = blockIdx.x;                       // (b*H + hh)*T + t
+  const int64_t fi = blockIdx.x / nsplit;              // (b*H + hh)*T + t
+  const int sp = blockIdx.x % nsplit;
   const int t = (int)(fi % T_);
   const int64_t bh = fi / T_;
   const int hh = (int)(bh % H);
   const int64_t b = bh / H;
   const int d0 = 32 * wave;
-  const int ntile = (N + TT - 1) / TT;
+  const int ftiles = (N + TT - 1) / TT, tps = (ftiles + nsplit - 1) / nsplit;
+  const int tile0 = sp * tps, ntile = min(ftiles, tile0 + tps);   // this workgroup's tiles: tile0 .. ntile-1
+  if (tile0 >= ntile) return;   // the whole workgroup (no barrier reached)
   const bf16* qfr = q + (bh * Lt + (int64_t)t * N) * D;
   const int64_t row0 = b * (int64_t)Lt + (int64_t)t * N;   // output / gate row of the frame's token 0
 
   if (tid < D) wl[tid] = rms_w ? rms_w[hh * D + tid] : 1.f;
   // sf[dir][part][ks] = S_part of direction dir, row d0 + l32, columns 16 ks + 8 h .. +7
-  bf16x8 sf[2][2][8];
+  bf16x8 sf[2][2][KS];
 #pragma unroll
   for (int dir = 0; dir < 2; ++dir)
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
       const bf16* sp = split + (dir * bhtdd + fi * D * D) * 2 + part * D * D + (int64_t)(d0 + l32) * D + 8 * h;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sf[dir][part][ks] = *reinterpret_cast<const bf16x8*>(sp + 16 * ks);
+      for (int ks = 0; ks < KS; ++ks) sf[dir][part][ks] = *reinterpret_cast<const bf16x8*>(sp + 16 * ks);
     }
 
-  // the thread's share of a Q tile: 16-byte chunks tid and tid + 256 (token c / 16,
-  // chunk c % 16); tokens past the frame re-read its last token (never stored)
-  // (the tile's offsets are wave-uniform; only a tile that runs past the frame clamps per lane)
-  const bf16* qthr = qfr + (tid / 16) * D + 8 * (tid % 16);   // chunk j: + 16 j rows
+  // the thread's share of a Q tile: 16-byte chunks tid and tid + NT (token c / CPR,
+  // chunk c % CPR; chunk j is 16 j rows further); tokens past the frame re-read its last
+  // token (never stored).  The tile's offsets are wave-uniform; only a tile that runs past
+  // the frame clamps per lane.
+  const bf16* qthr = qfr + (tid / CPR) * D + 8 * (tid % CPR);
   auto load_q = [&](bf16x8 (&qv)[2], int tile) {
     const bf16* tp = qthr + (int64_t)tile * (TT * D);
     if ((tile + 1) * TT <= N) {
@@ -778,16 +790,16 @@ __global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int n = min(tile * TT + tid / 16 + 16 * j, N - 1);
-        qv[j] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 8 * (tid % 16));
+        const int n = min(tile * TT + tid / CPR + 16 * j, N - 1);
+        qv[j] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 8 * (tid % CPR));
       }
     }
   };
   auto store_q = [&](const bf16x8 (&qv)[2], int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int c = tid + 256 * j, r = c / 16;
-      *reinterpret_cast<bf16x8*>(&QL[buf][r * QROW + sw(r, c % 16) * 16]) = qv[j];
+      const int c = tid + NT * j, r = c / CPR;
+      *reinterpret_cast<bf16x8*>(&QL[buf][r * QROW + sw<D>(r, c % CPR) * 16]) = qv[j];
     }
   };
   // gate of the lane's token, dimensions d0 + 16 pp + 8 h .. +7
@@ -807,16 +819,16 @@ __global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
   auto body = [&](int tile, bf16x8 (&qv)[2], bf16x8 (&gv)[2]) {
     const int buf = tile & 1;
     // B operand: q[token 32 tile + l32][16 ks + 8 h .. +7]
-    bf16x8 bq[8];
+    bf16x8 bq[KS];
     const unsigned char* qrow = QL[buf] + l32 * QROW;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bq[ks] = *reinterpret_cast<const bf16x8*>(qrow + sw(l32, 2 * ks + h) * 16);
+    for (int ks = 0; ks < KS; ++ks) bq[ks] = *reinterpret_cast<const bf16x8*>(qrow + sw<D>(l32, 2 * ks + h) * 16);
     // acc_dir[r] = u_dir[dimension d0 + 8 (r/4) + 4 h + r%4] of token 32 tile + l32
     f32x16 acc0, acc1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int part = 0; part < 2; ++part) {
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[0][part][ks], bq[ks], acc0, 0, 0, 0);
@@ -839,11 +851,21 @@ __global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
       SSX[buf][1][l32][wave] = __uint_as_float(x1[0]) + __uint_as_float(x1[1]);
     }
     __syncthreads();   // partial sums and the next Q tile complete
-    const float4 p0 = *reinterpret_cast<const float4*>(&SSX[buf][0][l32][0]);
-    const float4 p1 = *reinterpret_cast<const float4*>(&SSX[buf][1][l32][0]);
+    float s0, s1;
+    if constexpr (NW == 4) {
+      const float4 p0 = *reinterpret_cast<const float4*>(&SSX[buf][0][l32][0]);
+      const float4 p1 = *reinterpret_cast<const float4*>(&SSX[buf][1][l32][0]);
+      s0 = (p0.x + p0.y) + (p0.z + p0.w);
+      s1 = (p1.x + p1.y) + (p1.z + p1.w);
+    } else {
+      const float2 p0 = *reinterpret_cast<const float2*>(&SSX[buf][0][l32][0]);
+      const float2 p1 = *reinterpret_cast<const float2*>(&SSX[buf][1][l32][0]);
+      s0 = p0.x + p0.y;
+      s1 = p1.x + p1.y;
+    }
     // hardware reciprocal square root (1 ulp)
-    const float rn0 = __builtin_amdgcn_rsqf(((p0.x + p0.y) + (p0.z + p0.w)) * (1.f / D) + eps);
-    const float rn1 = __builtin_amdgcn_rsqf(((p1.x + p1.y) + (p1.z + p1.w)) * (1.f / D) + eps);
+    const float rn0 = __builtin_amdgcn_rsqf(s0 * (1.f / D) + eps);
+    const float rn1 = __builtin_amdgcn_rsqf(s1 * (1.f / D) + eps);
     const int n = tile * TT + l32;
     bf16* orow = olane + (int64_t)tile * TT * ldo;
 #pragma unroll
@@ -878,16 +900,16 @@ __global__ __launch_bounds__(256, 2) void vda_readout_bf16_d128_kernel(
 
   bf16x8 q0[2], q1[2];
   bf16x8 g0[2], g1[2];
-  load_q(q0, 0);
-  store_q(q0, 0);
-  load_q(q0, 1);
-  load_q(q1, 2);
+  load_q(q0, tile0);
+  store_q(q0, tile0 & 1);
+  load_q(q0, tile0 + 1);
+  load_q(q1, tile0 + 2);
   if constexpr (kGate) {
-    load_g(g0, 0);
-    load_g(g1, 1);
+    load_g(g0, tile0);
+    load_g(g1, tile0 + 1);
   }
   __syncthreads();
-  int tile = 0;
+  int tile = tile0;
   for (; tile + 2 <= ntile; tile += 2) {
     body(tile, q0, g0);
     body(tile + 1, q1, g1);
@@ -976,15 +998,27 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
                             const float* rms_w, const void* gate, int64_t ldg, void* out, int64_t ldo,
                             int B, int H, int T_, int N, int Lt, float eps, hipStream_t st) {
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
-  if (sizeof(T) == 2 && d == 128 && split) {
+  if (sizeof(T) == 2 && (d == 128 || d == 64) && split) {
     const int64_t nb = (int64_t)B * H * T_;
     if (nb == 0 || N <= 0) return hipSuccess;
-    if (gate)
-      vda_readout_bf16_d128_kernel<true><<<(unsigned)nb, 256, 0, st>>>(
-          (const bf16*)q, split, rms_w, (const bf16*)gate, ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
-    else
-      vda_readout_bf16_d128_kernel<false><<<(unsigned)nb, 256, 0, st>>>(
-          (const bf16*)q, split, rms_w, nullptr, ldg, (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd);
+    // frames too few to give every workgroup slot one (two per CU at d = 128, about six at
+    // d = 64) get several workgroups each, each with at least 8 tiles
+    const int ftiles = (N + 31) / 32;
+    const int64_t target = d == 128 ? 512 : 1536;
+    int nsplit = 1;
+    while (nsplit < 8 && nb * nsplit < target && ftiles >= 16 * nsplit) nsplit *= 2;
+    const unsigned grid = (unsigned)(nb * nsplit);
+#define VDN_RO(DD, G) \
+  vda_readout_bf16_kernel<DD, G><<<grid, 2 * DD, 0, st>>>((const bf16*)q, split, rms_w, (const bf16*)gate, ldg, \
+                                                          (bf16*)out, ldo, H, T_, N, Lt, eps, bhtdd, nsplit)
+    if (d == 128) {
+      if (gate) VDN_RO(128, true);
+      else VDN_RO(128, false);
+    } else {
+      if (gate) VDN_RO(64, true);
+      else VDN_RO(64, false);
+    }
+#undef VDN_RO
     return hipGetLastError();
   }
   const int tpf = (N + kReadoutBT - 1) / kReadoutBT;
