@@ -1566,47 +1566,70 @@ __global__ __launch_bounds__(256) void window_attn_mxfp8_d128_kernel(AttnParams 
 
 // Combine the key splits of the dense query rows (anchor frames, context
 // tokens): out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, then gate.
-// One thread per (dense row, quarter of d).
+// D / 8 threads per dense row, 8 consecutive dimensions each: every partial-output
+// read is two 16-byte loads and every gate read and output write one 16-byte access
+// (gate and output strides and head offsets are multiples of 8 elements).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  const int nqb = (p.dense_rows + 63) / 64;
+  constexpr int TPR = D / 8, RPB = 256 / TPR;   // threads per row, rows per workgroup
+  const int nqb = (p.dense_rows + RPB - 1) / RPB;
   const int qb = blockIdx.x % nqb;
   const int bh = blockIdx.x / nqb;             // b*H + h
   const int h = bh % p.H, b = bh / p.H;
-  const int n = qb * 64 + threadIdx.x / 4;     // index among the dense rows
+  const int n = qb * RPB + threadIdx.x / TPR;  // index among the dense rows
   if (n >= p.dense_rows) return;
   // the group holding dense row n (groups are stored in row order)
   const int g = (p.nG > 2 && n >= p.grp_part[2]) ? 2 : ((p.nG > 1 && n >= p.grp_part[1]) ? 1 : 0);
   const int qrow = (g == 0 ? p.grp_row0[0] : (g == 1 ? p.grp_row0[1] : p.grp_row0[2])) + n -
                    (g == 0 ? p.grp_part[0] : (g == 1 ? p.grp_part[1] : p.grp_part[2]));
-  const int dq = threadIdx.x % 4;
-  constexpr int DQ = D / 4;
+  const int d0 = (threadIdx.x % TPR) * 8;
   float M = -INFINITY;
   for (int s = 0; s < p.nsplit; ++s)
     M = fmaxf(M, p.part_ml[(((int64_t)bh * p.nsplit + s) * p.dense_rows + n) * 2]);
   float L = 0.f;
-  float acc[DQ];
+  float acc[8];
 #pragma unroll
-  for (int x = 0; x < DQ; ++x) acc[x] = 0.f;
+  for (int x = 0; x < 8; ++x) acc[x] = 0.f;
   for (int s = 0; s < p.nsplit; ++s) {
     const int64_t prow = ((int64_t)bh * p.nsplit + s) * p.dense_rows + n;
     const float wgt = fast_exp2(p.part_ml[prow * 2] - M);
     L += wgt * p.part_ml[prow * 2 + 1];
-#pragma unroll
-    for (int x = 0; x < DQ; ++x) acc[x] += wgt * p.part_o[prow * D + dq * DQ + x];
+    const float4 o0 = *reinterpret_cast<const float4*>(p.part_o + prow * D + d0);
+    const float4 o1 = *reinterpret_cast<const float4*>(p.part_o + prow * D + d0 + 4);
+    acc[0] += wgt * o0.x; acc[1] += wgt * o0.y; acc[2] += wgt * o0.z; acc[3] += wgt * o0.w;
+    acc[4] += wgt * o1.x; acc[5] += wgt * o1.y; acc[6] += wgt * o1.z; acc[7] += wgt * o1.w;
   }
   const float inv = 1.f / L;
   const int64_t orow = (int64_t)b * p.Lt + qrow;
   const T* gate = (const T*)p.gate;
   T* out = (T*)p.out;
+  float val[8];
 #pragma unroll
-  for (int x = 0; x < DQ; ++x) {
-    const int dd = dq * DQ + x;
-    float val = acc[x] * inv;
-    if (gate) val *= to_f32(gate[orow * p.ldg + h * D + dd]);
-    out[orow * p.ldo + h * D + dd] = from_f32<T>(val);
+  for (int x = 0; x < 8; ++x) val[x] = acc[x] * inv;
+  if (gate) {
+    const T* gp = gate + orow * p.ldg + h * D + d0;
+    if constexpr (sizeof(T) == 2) {
+      const Chunk16 gv = *reinterpret_cast<const Chunk16*>(gp);
+      const T* ge = reinterpret_cast<const T*>(&gv);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) val[x] *= to_f32(ge[x]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) val[x] *= to_f32(gp[x]);
+    }
   }
-  if (p.lse && dq == 0) p.lse[(int64_t)bh * p.Lt + qrow] = (M + log2f(L)) * kLn2;
+  T* op = out + orow * p.ldo + h * D + d0;
+  if constexpr (sizeof(T) == 2) {
+    Chunk16 ov;
+    T* oe = reinterpret_cast<T*>(&ov);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) oe[x] = from_f32<T>(val[x]);
+    *reinterpret_cast<Chunk16*>(op) = ov;
+  } else {
+#pragma unroll
+    for (int x = 0; x < 8; x += 4) *reinterpret_cast<float4*>(op + x) = make_float4(val[x], val[x + 1], val[x + 2], val[x + 3]);
+  }
+  if (p.lse && d0 == 0) p.lse[(int64_t)bh * p.Lt + qrow] = (M + log2f(L)) * kLn2;
 }
 
 template <typename T, int D>
@@ -1623,7 +1646,8 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
 template <typename T, int D>
 static hipError_t launch_merge_t(const AttnParams& p, hipStream_t st) {
   if (p.nsplit > 1 && p.nG > 0) {
-    const int blocks = p.B * p.H * ((p.dense_rows + 63) / 64);
+    constexpr int RPB = 256 / (D / 8);   // dense rows per workgroup
+    const int blocks = p.B * p.H * ((p.dense_rows + RPB - 1) / RPB);
     attn_merge_kernel<T, D><<<blocks, 256, 0, st>>>(p);
   }
   return hipGetLastError();
