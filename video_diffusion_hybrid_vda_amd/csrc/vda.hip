@@ -721,18 +721,26 @@ __global__ __launch_bounds__(256) void vda_readout_kernel(
 // fragment reads of a 16-lane group spread over the banks).  RMSNorm needs
 // each token's sum of squares over all D dimensions: each wave leaves its
 // 32-dimension partial sums in LDS, and after the tile's one barrier every
-// wave adds the D/32 partials.  A lane then forms (u_f rn_f + u_b rn_b) w g
-// for 16 dimensions of one token; one cross-lane swap per four dimensions
-// gives it eight consecutive dimensions for each 16-byte gate load and output
-// store.  With two workgroups per CU one workgroup's products run while the
+// wave adds the D/32 partials.  A lane then forms u_f rn_f + u_b rn_b for 16
+// dimensions of one token (one cross-lane swap per four dimensions makes them
+// two runs of eight) and stages them in LDS; two tiles later, after the
+// barriers in between, the workgroup scales them by w and the gate and
+// writes whole 2D-byte rows of the head's slice, so each gate load and
+// output store instruction covers four full rows instead of 32 bytes of 32
+// rows.  With two workgroups per CU one workgroup's products run while the
 // other's vector epilogue does.  nsplit > 1 gives each frame that many
 // workgroups over consecutive runs of its tiles (each loads the frame's
 // states), for shapes with too few frames to fill the chip.
 namespace ro {
 constexpr int TT = 32;                 // tokens per tile
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ int sw(int row, int ch) { return ch ^ (row & (D / 8 - 1)); }
+// 16-byte slot s of row r of a staged output tile: the 16 rows written by one
+// half-wave (same slot) and the 2 rows x 8 chunks read by 16 lanes spread over
+// all 64 banks
+__device__ __forceinline__ int ysw(int r, int s) { return s ^ (r & 15); }
 }  // namespace ro
 
 template <int D, bool kGate>
@@ -746,7 +754,10 @@ __global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
   constexpr int KS = D / 16;               // 16-deep product steps
   constexpr int QROW = D * 2;              // bytes per token row of a staged Q tile
   constexpr int QTILE = TT * QROW;
+  constexpr int YS = D / 4;                // 16-byte slots per row of a staged output tile (fp32)
+  constexpr int NBLK = D / 64;             // 8-chunk blocks per output row
   __shared__ __attribute__((aligned(16))) unsigned char QL[2][QTILE];
+  __shared__ __attribute__((aligned(16))) float4 YL[2][TT * YS];
   __shared__ __attribute__((aligned(16))) float SSX[2][2][TT][NW];   // [buffer][dir][token][wave]
   __shared__ __attribute__((aligned(16))) float wl[D];
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -777,23 +788,22 @@ __global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
       for (int ks = 0; ks < KS; ++ks) sf[dir][part][ks] = *reinterpret_cast<const bf16x8*>(sp + 16 * ks);
     }
 
+  // Global traffic goes through buffer descriptors that start at a tile's first row
+  // and end at the frame's last: rows past the frame read as zero and their stores
+  // are dropped, and every lane offset is a fixed 32-bit value (the host keeps a
+  // frame's rows below 2^31 bytes).
+  auto rows_rsrc = [&](const bf16* frame, int64_t ld, int tile) {
+    const int rows = max(N - tile * TT, 0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(frame + (int64_t)tile * TT * ld), (short)0,
+                                             (int)(rows * ld * 2), 0x00020000);
+  };
   // the thread's share of a Q tile: 16-byte chunks tid and tid + NT (token c / CPR,
-  // chunk c % CPR; chunk j is 16 j rows further); tokens past the frame re-read its last
-  // token (never stored).  The tile's offsets are wave-uniform; only a tile that runs past
-  // the frame clamps per lane.
-  const bf16* qthr = qfr + (tid / CPR) * D + 8 * (tid % CPR);
+  // chunk c % CPR), i.e. bytes 16 tid and 16 tid + 32 D of the tile
   auto load_q = [&](bf16x8 (&qv)[2], int tile) {
-    const bf16* tp = qthr + (int64_t)tile * (TT * D);
-    if ((tile + 1) * TT <= N) {
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qfr, D, tile);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) qv[j] = *reinterpret_cast<const bf16x8*>(tp + 16 * j * D);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = min(tile * TT + tid / CPR + 16 * j, N - 1);
-        qv[j] = *reinterpret_cast<const bf16x8*>(qfr + (int64_t)n * D + 8 * (tid % CPR));
-      }
-    }
+    for (int j = 0; j < 2; ++j)
+      qv[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * tid + 32 * D * j, 0, 0));
   };
   auto store_q = [&](const bf16x8 (&qv)[2], int buf) {
 #pragma unroll
@@ -802,22 +812,61 @@ __global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
       *reinterpret_cast<bf16x8*>(&QL[buf][r * QROW + sw<D>(r, c % CPR) * 16]) = qv[j];
     }
   };
-  // gate of the lane's token, dimensions d0 + 16 pp + 8 h .. +7
-  const bf16* glane = kGate ? gate + (row0 + l32) * ldg + hh * D + d0 + 8 * h : nullptr;
+  // Output emission, coalesced: a tile's normalised values go to LDS (fp32, YL) and
+  // after the next barrier every thread scales two 16-byte chunks of whole token
+  // rows by the RMSNorm weight and the gate and writes them, 16 lanes covering two rows x 8 chunks, with the gate chunk at the same
+  // place loaded the same way.  Chunk j of thread t: row crow(t, j), columns
+  // 8 ccol(t, j) .. +7 of the head's slice.
+  // (the chunk coordinates are recomputed from an opaque copy of tid at each use,
+  // so that the compiler does not keep them, and the weights they index, in
+  // registers across the tile loop)
+  auto opaque_tid = [&]() { int v = tid; asm volatile("" : "+v"(v)); return v; };
+  auto crow = [&](int t, int j) { const int idx = t + NT * j; return 2 * (idx / (16 * NBLK)) + (idx / 8) % 2; };
+  auto ccol = [&](int t, int j) { const int idx = t + NT * j; return 8 * ((idx / 16) % NBLK) + idx % 8; };
+  const bf16* gfr = kGate ? gate + row0 * ldg + hh * D : nullptr;
+  bf16* ofr = out + row0 * ldo + hh * D;
   auto load_g = [&](bf16x8 (&gv)[2], int tile) {
-    const bf16* grow = (tile + 1) * TT <= N
-                           ? glane + (int64_t)tile * TT * ldg
-                           : gate + (row0 + min(tile * TT + l32, N - 1)) * ldg + hh * D + d0 + 8 * h;
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(gfr, ldg, tile);
+    const int t = opaque_tid();
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) gv[pp] = *reinterpret_cast<const bf16x8*>(grow + 16 * pp);
+    for (int j = 0; j < 2; ++j) {
+      const int off = 2 * (crow(t, j) * (int)ldg + 8 * ccol(t, j));   // a tile spans 32 rows
+      gv[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+    }
   };
-  bf16* olane = out + (row0 + l32) * ldo + hh * D + d0 + 8 * h;
+  // write tile's staged values (gated, rounded once) to its output rows
+  auto emit = [&](int tile, const bf16x8 (&gv)[2]) {
+    const float4* yt = YL[tile & 1];
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc(ofr, ldo, tile);
+    const int t = opaque_tid();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = crow(t, j), c = ccol(t, j);
+      const float4 lo = yt[r * YS + ysw(r, 2 * c)];
+      const float4 hi = yt[r * YS + ysw(r, 2 * c + 1)];
+      const float4 wlo = *reinterpret_cast<const float4*>(&wl[8 * c]);
+      const float4 whi = *reinterpret_cast<const float4*>(&wl[8 * c + 4]);
+      const float y[8] = {lo.x * wlo.x, lo.y * wlo.y, lo.z * wlo.z, lo.w * wlo.w,
+                          hi.x * whi.x, hi.y * whi.y, hi.z * whi.z, hi.w * whi.w};
+      bf16x8 ov;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kGate) ov[e] = (bf16)(y[e] * (float)gv[j][e]);   // the only rounding of the output
+        else ov[e] = (bf16)y[e];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro, 2 * (r * (int)ldo + 8 * c), 0, 0);
+    }
+  };
 
   // One tile.  qv holds Q of tile + 1 (stored into LDS here, then refilled with
-  // tile + 3); gv holds the gate of this tile (refilled with tile + 2): two
-  // register sets alternate, so every load has two tiles' time to arrive.
-  auto body = [&](int tile, bf16x8 (&qv)[2], bf16x8 (&gv)[2]) {
+  // tile + 3); gv holds the gate of tile - 2, whose staged values (complete since
+  // the previous barrier, overwritten only after this tile's) are emitted first,
+  // then the gate of this tile: two register sets alternate, so every load has
+  // two tiles' time to arrive.
+  auto body = [&](int tile, bf16x8 (&qv)[2], bf16x8 (&gv)[2], auto EMIT) {
     const int buf = tile & 1;
+    if constexpr (decltype(EMIT)::value) emit(tile - 2, gv);
+    if constexpr (kGate) load_g(gv, tile);
     // B operand: q[token 32 tile + l32][16 ks + 8 h .. +7]
     bf16x8 bq[KS];
     const unsigned char* qrow = QL[buf] + l32 * QROW;
@@ -866,36 +915,25 @@ __global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
     // hardware reciprocal square root (1 ulp)
     const float rn0 = __builtin_amdgcn_rsqf(s0 * (1.f / D) + eps);
     const float rn1 = __builtin_amdgcn_rsqf(s1 * (1.f / D) + eps);
-    const int n = tile * TT + l32;
-    bf16* orow = olane + (int64_t)tile * TT * ldo;
+    float4* yw = YL[buf] + l32 * YS;
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       // ya: dims d0 + 16pp + 4h + e, yb: dims d0 + 16pp + 8 + 4h + e; after the swap
-      // the lane holds dims d0 + 16pp + 8h + {0..3} in ya and + {4..7} in yb
+      // the lane holds dims d0 + 16pp + 8h + {0..3} in ya and + {4..7} in yb, i.e.
+      // chunk 4 wave + 2 pp + h of its token's row
       float ya[4], yb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int da = d0 + 16 * pp + 4 * h + e;
-        ya[e] = (acc0[8 * pp + e] * rn0 + acc1[8 * pp + e] * rn1) * wl[da];
-        yb[e] = (acc0[8 * pp + 4 + e] * rn0 + acc1[8 * pp + 4 + e] * rn1) * wl[da + 8];
+        ya[e] = acc0[8 * pp + e] * rn0 + acc1[8 * pp + e] * rn1;
+        yb[e] = acc0[8 * pp + 4 + e] * rn0 + acc1[8 * pp + 4 + e] * rn1;
         const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ya[e]), __float_as_uint(yb[e]), false, false);
         ya[e] = __uint_as_float(x[0]);
         yb[e] = __uint_as_float(x[1]);
       }
-      bf16x8 ov;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (kGate) {
-          ov[e] = (bf16)(ya[e] * (float)gv[pp][e]);   // the only rounding of the output
-          ov[4 + e] = (bf16)(yb[e] * (float)gv[pp][4 + e]);
-        } else {
-          ov[e] = (bf16)ya[e];
-          ov[4 + e] = (bf16)yb[e];
-        }
-      }
-      if (n < N) *reinterpret_cast<bf16x8*>(orow + 16 * pp) = ov;
+      const int c = 4 * wave + 2 * pp + h;
+      yw[ysw(l32, 2 * c)] = make_float4(ya[0], ya[1], ya[2], ya[3]);
+      yw[ysw(l32, 2 * c + 1)] = make_float4(yb[0], yb[1], yb[2], yb[3]);
     }
-    if constexpr (kGate) load_g(gv, tile + 2);
   };
 
   bf16x8 q0[2], q1[2];
@@ -904,17 +942,29 @@ __global__ __launch_bounds__(2 * D, 2) void vda_readout_bf16_kernel(
   store_q(q0, tile0 & 1);
   load_q(q0, tile0 + 1);
   load_q(q1, tile0 + 2);
-  if constexpr (kGate) {
-    load_g(g0, tile0);
-    load_g(g1, tile0 + 1);
-  }
   __syncthreads();
-  int tile = tile0;
+  // tile t uses the register sets of parity t - tile0 (q0, g0 even)
+  body(tile0, q0, g0, std::false_type{});
+  if (tile0 + 1 < ntile) body(tile0 + 1, q1, g1, std::false_type{});
+  int tile = tile0 + 2;
   for (; tile + 2 <= ntile; tile += 2) {
-    body(tile, q0, g0);
-    body(tile + 1, q1, g1);
+    body(tile, q0, g0, std::true_type{});
+    body(tile + 1, q1, g1, std::true_type{});
   }
-  if (tile < ntile) body(tile, q0, g0);
+  if (tile < ntile) body(tile, q0, g0, std::true_type{});
+  __syncthreads();   // the last tile's staged values complete
+  // the last two tiles (gates in the sets of their parity)
+  if (ntile - tile0 >= 2) {
+    if ((ntile - tile0) & 1) {
+      emit(ntile - 2, g1);
+      emit(ntile - 1, g0);
+    } else {
+      emit(ntile - 2, g0);
+      emit(ntile - 1, g1);
+    }
+  } else {
+    emit(ntile - 1, g0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -998,7 +1048,9 @@ static hipError_t readout_t(int d, const void* q, const float* states, const bf1
                             const float* rms_w, const void* gate, int64_t ldg, void* out, int64_t ldo,
                             int B, int H, int T_, int N, int Lt, float eps, hipStream_t st) {
   const int64_t bhtdd = (int64_t)B * H * T_ * d * d;
-  if (sizeof(T) == 2 && (d == 128 || d == 64) && split) {
+  // the register-resident kernel addresses a frame's rows of q, gate and out with 32-bit offsets
+  const int64_t frame_bytes = (int64_t)N * std::max<int64_t>(std::max<int64_t>(ldo, gate ? ldg : 0), d) * 2;
+  if (sizeof(T) == 2 && (d == 128 || d == 64) && split && frame_bytes < (int64_t(1) << 31)) {
     const int64_t nb = (int64_t)B * H * T_;
     if (nb == 0 || N <= 0) return hipSuccess;
     // frames too few to give every workgroup slot one (two per CU at d = 128, about six at
