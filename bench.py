@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27823611549,
-        "window_attn": 269500874443,
-        "anchor_merge": 2050280677,
-        "vda_gram": 5374808793,
-        "vda_solve": 321173113,
-        "vda_scan": 946882892,
-        "vda_readout": 7904830852,
-        "out_gemm": 27145143155
+        "gate_gemm": 27823952246,
+        "window_attn": 261595938937,
+        "anchor_merge": 710104268,
+        "vda_gram": 5374819433,
+        "vda_solve": 321169810,
+        "vda_scan": 946869676,
+        "vda_readout": 7901687201,
+        "out_gemm": 26626039414
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 179862447065,
-        "mxfp8_quantize": 7659473829
+        "window_attn": 179171192265,
+        "mxfp8_quantize": 7659477812
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284701570,
-        "bwd_token": 23428387304,
-        "bwd_scan": 3516308452,
-        "bwd_frame": 5573391906,
-        "bwd_kv_gemm": 10441042788
+        "bwd_recompute": 7284795930,
+        "bwd_token": 23428324174,
+        "bwd_scan": 3515788411,
+        "bwd_frame": 5570180910,
+        "bwd_kv_gemm": 10441681190
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145322204,
-        "vda_solve": 11161393,
-        "vda_scan": 22120554,
-        "vda_readout": 222449628
+        "vda_gram": 145315084,
+        "vda_solve": 11161395,
+        "vda_scan": 22113390,
+        "vda_readout": 186671776
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11460696813,
-        "window_attn": 114409186268,
-        "anchor_merge": 1488954485,
-        "vda_gram": 2213139704,
-        "vda_solve": 132414091,
-        "vda_scan": 379786677,
-        "vda_readout": 3255784982,
-        "out_gemm": 11103694864
+        "gate_gemm": 11461615451,
+        "window_attn": 113432377166,
+        "anchor_merge": 401531478,
+        "vda_gram": 2213158880,
+        "vda_solve": 132419363,
+        "vda_scan": 379724432,
+        "vda_readout": 3253827891,
+        "out_gemm": 10526502064
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,8 +98,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "31de2d51e6f308eb", "gemm": "7422a6247fbbc44f", "vda": "3cae34d1e0bee408",
-    "mxfp8": "8cdcfa773199d9a4", "bwd": "867876673bea4dcc", "vda+bwd": "fb3e1a5c8343ec87",
+    "window": "5d640cb7bc3d22c2", "gemm": "7422a6247fbbc44f", "vda": "757b4ab0db00276f",
+    "mxfp8": "8cdcfa773199d9a4", "bwd": "867876673bea4dcc", "vda+bwd": "0aa9e191e0bc6c51",
     "common": "a24de8342071a471"
 }
 
