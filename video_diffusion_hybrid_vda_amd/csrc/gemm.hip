@@ -441,27 +441,32 @@ __global__ __launch_bounds__(512) void gemm_bf16_nt_k64_kernel(const bf16* __res
 }
 
 // bf16, K a multiple of 128: the layer's two projections.  256x256 output
-// tile, four waves (one per SIMD) of 128x128, v_mfma_f32_32x32x16_bf16 with
-// 256 accumulator registers per wave.  K advances in 64-wide slabs through a
-// two-stage LDS ring filled by the direct-to-LDS DMA.  As in the softmax
-// kernel, a slab is a fixed list of 64 slots, one product each, every
-// instruction its own asm statement so that the order holds: the 8 fragment
-// reads of K step ks+1 go out in every other slot of step ks (each product
-// waits, with an explicit lgkmcnt, for exactly the reads it needs), and the
-// slab after next's 16 DMA loads go out one per slot of the last step.  The
-// barrier that retires a slab sits before its last step: that step's
-// fragments are already in registers, so its products run while the next
-// slab's first fragments are read and the slab after it streams into the
-// freed stage.  The kernel is persistent (one workgroup per compute unit):
-// the slab stream runs on from one output tile into the next, so a tile's
-// epilogue overlaps the next tile's first loads instead of a fresh
-// workgroup's start-up.
+// tile, four waves (one per SIMD) of 128x128, v_mfma_f32_16x16x32_bf16: the
+// wave's block is 8 x 8 products of 16 x 16 (256 accumulator registers).  K
+// advances in 64-wide slabs through a two-stage LDS ring filled by the
+// direct-to-LDS DMA; a slab is two 32-deep steps.  As in the softmax kernel, a
+// step is a fixed list of 64 slots, one product each, every instruction its
+// own asm statement so that the order holds: the 16 fragment reads of the next
+// step go out one every fourth slot (each product waits, with an explicit
+// lgkmcnt, for exactly the reads it needs), and the slab after next's 16 DMA
+// loads go out every fourth slot of the step after the barrier.  The barrier
+// that retires a slab sits between its two steps: the second step's fragments
+// were read during the first (in its first 16 slots), so its products run
+// while the next slab's first fragments are read and the slab after it streams
+// into the freed stage.  The kernel is persistent (one workgroup per compute
+// unit): the slab stream runs on from one output tile into the next, so a
+// tile's epilogue overlaps the next tile's first loads instead of a fresh
+// workgroup's start-up.  A fragment (16 rows x 32 k) is one 16-byte read per
+// lane: row l % 16 of the tile, logical chunk 4 ks + l / 16 of the slab row;
+// the swizzle's row term, (row >> 1) & 7, is the same for every 16-row tile of
+// a lane, so tile t's address is the lane's base plus the constant 2048 t.
+// (The same kernel on 32x32x16 products, 16 per 16-deep step, ran 12% slower.)
 namespace gemm_s {
 constexpr int BM = 256, BN = 256, BK = 64, ROWB = BK * 2;   // 128-byte slab rows
 constexpr int TILEB = BM * ROWB;                              // 32 KB per operand and stage
 constexpr int BBASE = 2 * TILEB;                              // A slabs of both stages, then Bt slabs
 constexpr int GROUP_M = 8;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 // chunk c of row r at c ^ ((r >> 1) & 7): the sixteen rows of a 16-lane
 // fragment read cover all 64 banks
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -475,29 +480,33 @@ template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (E > B) static_for_impl<B>(f, std::make_integer_sequence<int, E - B>{});
 }
-// Fragment reads of a step, in issue order: Bt tile 0, A tiles 0-3, Bt tiles
-// 1-3; read r goes out in slot 2 r of the step before, or in slot r when
-// that step is the one before a barrier (early), so that its reads are in
-// when the barrier's lgkmcnt(0) comes.  Product (jn, im) is slot 4 jn + im.
-// The first product that uses read r waits until at most (7 - r) reads of
-// its own step plus the next step's reads issued before slot s are
-// outstanding.
-constexpr bool first_use(int s) { return s <= 4 || s == 8 || s == 12; }
-constexpr int first_use_read(int s) { return s == 0 ? 1 : s <= 4 ? s + 1 : s == 8 ? 6 : 7; }
-constexpr int reads_before(int s, bool early) { return early ? (s < 8 ? s : 8) : (s + 1) / 2; }
-constexpr int first_use_wait(int s, bool early) { return 7 - first_use_read(s) + reads_before(s, early); }
-static_assert(first_use_wait(0, false) == 6 && first_use_wait(2, false) == 5 && first_use_wait(12, false) == 6 &&
-              first_use_wait(8, true) == 9 && first_use_wait(12, true) == 8, "lgkmcnt table");
-__device__ __forceinline__ void mma(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+// Fragment reads of a step, in issue order: Bt tile 0, A tiles 0-7, Bt tiles
+// 1-7; read r goes out in slot 4 r of the step before, or in slot r when that
+// step is the one before a barrier (early), so that its reads are in when the
+// barrier's lgkmcnt(0) comes.  Product (jn, im) is slot 8 jn + im.  The first
+// product that uses read r waits until at most (15 - r) reads of its own step
+// plus the next step's reads issued before slot s are outstanding, capped at
+// 15: a wave has at most 15 LDS operations outstanding, so a larger count is
+// only met once the read is in.
+constexpr bool first_use(int s) { return s <= 8 || s % 8 == 0; }
+constexpr int first_use_read(int s) { return s == 0 ? 1 : s <= 7 ? s + 1 : 8 + s / 8; }
+constexpr int reads_before(int s, bool early) { return early ? (s < 16 ? s : 16) : (s + 3) / 4; }
+constexpr int first_use_wait(int s, bool early) {
+  return 15 - first_use_read(s) + reads_before(s, early) < 15 ? 15 - first_use_read(s) + reads_before(s, early) : 15;
+}
+static_assert(first_use_wait(0, false) == 14 && first_use_wait(1, false) == 14 && first_use_wait(7, false) == 9 &&
+              first_use_wait(8, false) == 8 && first_use_wait(56, false) == 14 && first_use_wait(8, true) == 14 &&
+              first_use_wait(56, true) == 15, "lgkmcnt table");
+__device__ __forceinline__ void mma(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// the first product of a tile: C operand zero, so no accumulator is cleared
+__device__ __forceinline__ void mma_zero(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
 }
 template <int OFF>
 __device__ __forceinline__ void ds_frag(bf16x8& d, int addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
-}
-// the first product of a tile: C operand zero, so no accumulator is cleared
-__device__ __forceinline__ void mma_zero(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
 }
 template <int N>
 __device__ __forceinline__ void wait_lgkm() {
@@ -521,12 +530,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
   __shared__ __attribute__((aligned(1024))) unsigned char ring[4 * TILEB];
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int l32 = lane % 32, h = lane / 32;
+  const int l16 = lane % 16, g = lane / 16;
   const int wm = wave >> 1, wn = wave & 1;   // 128-row block of A, 128-row block of Bt
 
-  // Persistent: workgroup b takes logical tiles r G + xcd_remap(b, G), r = 0, 1, ...,
-  // so that in every round the workgroups of one XCD hold consecutive tiles
-  // of the grouped order below and share their A and Bt slabs in that L2.
   const int total = tiles_m * tiles_n, G = gridDim.x;
   auto coords = [&](int l, int& tm, int& tn) {
     const int group = l / (GROUP_M * tiles_n);
@@ -536,7 +542,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
     tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsize);
     tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
   };
-  // Rows past M (N) read as zero through the descriptors' ranges.
   auto rsrc_a = [&](int tm) {
     const int64_t m0 = (int64_t)tm * BM;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * lda), (short)0,
@@ -548,9 +553,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
                                              (int)(min((int64_t)BN, N - n0) * ldb * 2), 0x00020000);
   };
 
-  // DMA: wave w fills rows 64 w .. 64 w + 63 of each operand's slab, eight
-  // 8-row blocks; lane l of block i loads row 64 w + 8 i + l/8, the global
-  // chunk that lands at physical chunk l % 8.
   const int lds0 = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)ring;
   int offa[8], offb[8];
 #pragma unroll
@@ -560,8 +562,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
     offa[i] = (int)(row * lda * 2) + 16 * c;
     offb[i] = (int)(row * ldb * 2) + 16 * c;
   }
-  // load i (0..15) of the slab at byte column kb into stage st: i < 8 A
-  // block i, else Bt block i - 8
   auto issue_one = [&](__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int kb, int st, int i) {
     if (i < 8)
       asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(offa[i]), "s"(ra), "s"(kb),
@@ -572,16 +572,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
                    "{m0}"(lds0 + BBASE + st * TILEB + (8 * wave + i - 8) * 1024)
                    : "memory");
   };
-  // fragment addresses (stage 0) of A tile im and Bt tile jn at step ks
-  int adA[4][4], adB[4][4];
+  // fragment base addresses (stage 0, tile 0) of step ks: row 128 w + l16, chunk 4 ks + g
+  int adA[2], adB[2];
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int rA = 128 * wm + 32 * t4 + l32, rB = 128 * wn + 32 * t4 + l32;
-      adA[t4][ks] = lds0 + rA * ROWB + 16 * swz(rA, 2 * ks + h);
-      adB[t4][ks] = lds0 + BBASE + rB * ROWB + 16 * swz(rB, 2 * ks + h);
-    }
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rA = 128 * wm + l16, rB = 128 * wn + l16;
+    adA[ks] = lds0 + rA * ROWB + 16 * swz(rA, 4 * ks + g);
+    adB[ks] = lds0 + BBASE + rB * ROWB + 16 * swz(rB, 4 * ks + g);
+  }
 
   int li = xcd_remap(blockIdx.x, G);
   int tm, tn;
@@ -595,21 +593,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
   __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): slab 0 landed
   asm volatile("s_barrier" ::: "memory");
 
-  f32x16 acc[4][4];            // [Bt tile jn][A tile im]: C^T tile
-  bf16x8 fa[2][4], fb[2][4];   // fragments of two steps: [step parity][tile]
-  // read r of step (stage ST, ks KS) into fragment set P
+  f32x4 acc[8][8];              // [Bt tile jn][A tile im]: C^T tile
+  bf16x8 fa[2][8], fb[2][8];    // fragments of two steps: [step parity][tile]
   auto read = [&](auto ST, auto KS, auto P, auto R) {
     constexpr int st = decltype(ST)::value, ks = decltype(KS)::value, p = decltype(P)::value;
     constexpr int r = decltype(R)::value;
-    if constexpr (r == 0) ds_frag<st * TILEB>(fb[p][0], adB[0][ks]);
-    else if constexpr (r <= 4) ds_frag<st * TILEB>(fa[p][r - 1], adA[r - 1][ks]);
-    else ds_frag<st * TILEB>(fb[p][r - 4], adB[r - 4][ks]);
+    if constexpr (r == 0) ds_frag<st * TILEB>(fb[p][0], adB[ks]);
+    else if constexpr (r <= 8) ds_frag<st * TILEB + (r - 1) * 2048>(fa[p][r - 1], adA[ks]);
+    else ds_frag<st * TILEB + (r - 8) * 2048>(fb[p][r - 8], adB[ks]);
   };
-  static_for<0, 8>([&](auto R) { read(IC<0>{}, IC<0>{}, IC<0>{}, R); });
+  static_for<0, 16>([&](auto R) { read(IC<0>{}, IC<0>{}, IC<0>{}, R); });
 
-  // The slab stream runs on across tiles: the last two slabs of a tile load
-  // the next tile's first two, and the last step of a tile reads the next
-  // tile's first fragments, so only the epilogue separates two tiles.
   for (;;) {
     const int lnext = li + G;
     const bool has_next = lnext < total;
@@ -617,34 +611,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
     if (has_next) coords(lnext, ntm, ntn);
     const __amdgpu_buffer_rsrc_t nra = rsrc_a(ntm), nrb = rsrc_b(ntn);
 
-    // One step: 16 products on fragment set P (the first step of a tile
-    // starts them from zero), the next step's reads (stage NST, step NKS)
-    // into set P ^ 1, and on the last step of a slab the DMA of the slab two
-    // ahead into stage DST.
+    // one 32-deep step: 64 products on fragment set P, the next step's reads (stage NST,
+    // step NKS) into set P ^ 1, and after a barrier the DMA of the slab two ahead
     auto step = [&](auto P, auto NST, auto NKS, auto ZERO, auto DMA, auto EARLY, __amdgpu_buffer_rsrc_t da,
                     __amdgpu_buffer_rsrc_t db, int dkb, int dst) __attribute__((always_inline)) {
       constexpr int p = decltype(P)::value;
-      static_for<0, 16>([&](auto S) {
-        constexpr int sl = decltype(S)::value, jn = sl / 4, im = sl % 4;
-        if constexpr (first_use(sl)) wait_lgkm<first_use_wait(sl, decltype(EARLY)::value)>();
+      static_for<0, 64>([&](auto S) {
+        constexpr int sl = decltype(S)::value, jn = sl / 8, im = sl % 8;
+        constexpr bool early = decltype(EARLY)::value;
+        if constexpr (first_use(sl)) wait_lgkm<first_use_wait(sl, early)>();
         if constexpr (decltype(ZERO)::value) mma_zero(acc[jn][im], fb[p][jn], fa[p][im]);
         else mma(acc[jn][im], fb[p][jn], fa[p][im]);
-        if constexpr (decltype(EARLY)::value) {
-          if constexpr (sl < 8) read(NST, NKS, IC<1 - p>{}, IC<sl>{});
-        } else if constexpr (sl % 2 == 0) {
-          read(NST, NKS, IC<1 - p>{}, IC<sl / 2>{});
+        if constexpr (early) {
+          if constexpr (sl < 16) read(NST, NKS, IC<1 - p>{}, IC<sl>{});
+        } else if constexpr (sl % 4 == 0) {
+          read(NST, NKS, IC<1 - p>{}, IC<sl / 4>{});
         }
-        if constexpr (decltype(DMA)::value) issue_one(da, db, dkb, dst, sl);
+        if constexpr (decltype(DMA)::value && sl % 4 == 2) issue_one(da, db, dkb, dst, sl / 4);
       });
     };
-    // Slab kt in stage ST: steps 0-2, then the barrier that publishes the
-    // next slab and frees stage ST, then step 3 (its fragments are in
-    // registers) with the DMA of the slab two ahead into stage ST.
+    // slab kt in stage ST: step 0 (reading step 1's fragments early), the barrier that
+    // publishes the next slab and frees stage ST, then step 1 with the next slab's
+    // first reads and the DMA of the slab two ahead into stage ST
     auto slab = [&](int kt, auto ST, auto FIRST) __attribute__((always_inline)) {
       constexpr int st = decltype(ST)::value;
-      step(IC<0>{}, ST, IC<1>{}, FIRST, IC<0>{}, IC<0>{}, ra, rb, 0, 0);
-      step(IC<1>{}, ST, IC<2>{}, IC<0>{}, IC<0>{}, IC<0>{}, ra, rb, 0, 0);
-      step(IC<0>{}, ST, IC<3>{}, IC<0>{}, IC<0>{}, IC<1>{}, ra, rb, 0, 0);
+      step(IC<0>{}, ST, IC<1>{}, FIRST, IC<0>{}, IC<1>{}, ra, rb, 0, 0);
       const bool wrap = kt + 2 >= nk;
       const int dkb = (wrap ? kt + 2 - nk : kt + 2) * ROWB;
       wait_lgkm<0>();
@@ -661,46 +652,42 @@ __global__ __launch_bounds__(256) void gemm_bf16_nt_slot_kernel(const bf16* __re
     // the last products' results are read by vector instructions below
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
-    // Epilogue: acc[jn][im][4 r4 + e] = C[m0 + 128 wm + 32 im + l32][n0 + 128 wn + 32 jn + 8 r4 + 4 h + e].
-    // Swapping the upper half-wave of the r4 = 2 q pair with the lower half
-    // of r4 = 2 q + 1 gives every lane eight consecutive columns,
-    // 32 jn + 16 q + 8 h + (0..7): one 16-byte store.  Rows past M fall
-    // outside the descriptor's range and columns past N get an offset past
-    // it, so the hardware drops both.
+    // Epilogue: acc[jn][im][e] = C[m0 + 128 wm + 16 im + l16][n0 + 128 wn + 16 jn + 4 g + e].
+    // v_permlane16_swap between the packed values of tiles 2 p and 2 p + 1 leaves
+    // the lanes of even g with eight consecutive columns of tile 2 p and those of
+    // odd g with eight of tile 2 p + 1: one 16-byte store each.
     {
       const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
       const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(C + m0 * ldc), (short)0, (int)(min((int64_t)BM, M - m0) * ldc * 2), 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 128 * wm + 32 * i + l32;
+      for (int i = 0; i < 8; ++i) {
+        const int row = 128 * wm + 16 * i + l16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // one accumulator block at a time: reading them all first would
-          // push the loop's address registers to scratch
-          asm volatile("" : "+a"(acc[j][i]));
-          unsigned pk[4][2];
+        for (int pj = 0; pj < 4; ++pj) {
+          asm volatile("" : "+a"(acc[2 * pj][i]), "+a"(acc[2 * pj + 1][i]));
+          unsigned px[2], py[2];
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              float x0 = acc[j][i][4 * r4 + 2 * e2], x1 = acc[j][i][4 * r4 + 2 * e2 + 1];
-              if (EPI == kEpiSigmoid) { x0 = sigmoidf(x0); x1 = sigmoidf(x1); }
-              pk[r4][e2] = pack_bf16x2(x0, x1);
+          for (int e2 = 0; e2 < 2; ++e2) {
+            float x0 = acc[2 * pj][i][2 * e2], x1 = acc[2 * pj][i][2 * e2 + 1];
+            float y0 = acc[2 * pj + 1][i][2 * e2], y1 = acc[2 * pj + 1][i][2 * e2 + 1];
+            if (EPI == kEpiSigmoid) {
+              x0 = sigmoidf(x0); x1 = sigmoidf(x1);
+              y0 = sigmoidf(y0); y1 = sigmoidf(y1);
             }
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-#pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * q][e2], pk[2 * q + 1][e2], false, false);
-              pk[2 * q][e2] = sw[0];
-              pk[2 * q + 1][e2] = sw[1];
-            }
-            const int64_t col = n0 + 128 * wn + 32 * j + 16 * q + 8 * h;
-            const int off = col < N ? (int)((row * ldc + col) * 2) : int(0x80000000u);
-            const u32x4 v = {pk[2 * q][0], pk[2 * q][1], pk[2 * q + 1][0], pk[2 * q + 1][1]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+            px[e2] = pack_bf16x2(x0, x1);
+            py[e2] = pack_bf16x2(y0, y1);
           }
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(px[e2], py[e2], false, false);
+            px[e2] = sw[0];
+            py[e2] = sw[1];
+          }
+          const int64_t col = n0 + 128 * wn + 16 * (2 * pj + (g & 1)) + 4 * (g & 2);
+          const int off = col < N ? (int)((row * ldc + col) * 2) : int(0x80000000u);
+          const u32x4 v = {px[0], px[1], py[0], py[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
         }
       }
     }
