@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27823952246,
-        "window_attn": 261595938937,
-        "anchor_merge": 710104268,
-        "vda_gram": 5374819433,
-        "vda_solve": 321169810,
-        "vda_scan": 946869676,
-        "vda_readout": 7901687201,
-        "out_gemm": 26626039414
+        "gate_gemm": 27864640021,
+        "window_attn": 269046832111,
+        "anchor_merge": 710113907,
+        "vda_gram": 5374825698,
+        "vda_solve": 321172280,
+        "vda_scan": 947027249,
+        "vda_readout": 7901736740,
+        "out_gemm": 30813469654
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 179171192265,
-        "mxfp8_quantize": 7659477812
+        "window_attn": 179770395958,
+        "mxfp8_quantize": 7659487789
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284795930,
-        "bwd_token": 23428324174,
-        "bwd_scan": 3515788411,
-        "bwd_frame": 5570180910,
-        "bwd_kv_gemm": 10441681190
+        "bwd_recompute": 7284709011,
+        "bwd_token": 23428478711,
+        "bwd_scan": 3515100530,
+        "bwd_frame": 5562754643,
+        "bwd_kv_gemm": 10440336875
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145315084,
-        "vda_solve": 11161395,
-        "vda_scan": 22113390,
-        "vda_readout": 186671776
+        "vda_gram": 145315196,
+        "vda_solve": 11161400,
+        "vda_scan": 22113400,
+        "vda_readout": 186671620
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11461615451,
-        "window_attn": 113432377166,
-        "anchor_merge": 401531478,
-        "vda_gram": 2213158880,
-        "vda_solve": 132419363,
-        "vda_scan": 379724432,
-        "vda_readout": 3253827891,
-        "out_gemm": 10526502064
+        "gate_gemm": 11459538319,
+        "window_attn": 111047536287,
+        "anchor_merge": 401542395,
+        "vda_gram": 2213160360,
+        "vda_solve": 132464090,
+        "vda_scan": 379817307,
+        "vda_readout": 3253791852,
+        "out_gemm": 10431389079
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,7 +98,7 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "5d640cb7bc3d22c2", "gemm": "7422a6247fbbc44f", "vda": "757b4ab0db00276f",
+    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "757b4ab0db00276f",
     "mxfp8": "8cdcfa773199d9a4", "bwd": "867876673bea4dcc", "vda+bwd": "0aa9e191e0bc6c51",
     "common": "a24de8342071a471"
 }
