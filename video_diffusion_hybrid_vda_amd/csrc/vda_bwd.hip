@@ -1274,6 +1274,117 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// scan_bwd on fp32 MFMA for head_dim 64 and 128: the same row-parallel scheme
+// as the forward scan (one workgroup of D/32 waves per 32 state rows of one
+// (batch, head, direction); G_t in LDS; wave w forms the 32 x 32 block of
+// columns 32w.. of dX_t = G_t M_t^T with v_mfma_f32_32x32x2f32; M_t rows, the
+// next frames' dS two frames ahead and the next M one frame ahead are loaded
+// while a frame's products run).  M_t is the inverse of the symmetric matrix
+// I + A_t, so M_t^T = M_t: the B operand is read from the stored M_t^T in the
+// forward scan's row order (16-byte loads) rather than down its columns.  The
+// epilogue writes dX_t and G_next = dS_next + gamma_t dX_t (over dS_next, which
+// the later stages read as G).
+namespace sb {
+constexpr int R = 32;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+}  // namespace sb
+
+template <int D>
+__global__ __launch_bounds__(2 * D) void scan_bwd_mfma_kernel(const float* __restrict__ Mt,
+                                                             const float* __restrict__ gamma,
+                                                             float* __restrict__ dsg, float* __restrict__ dx,
+                                                             int T, int total) {
+  using namespace sb;
+  constexpr int LD = D + 4, NRB = D / R, KG = D / 8;
+  __shared__ __attribute__((aligned(16))) float P[2][R * LD];   // G_t and dX_t, rows r0 .. r0+31
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int l32 = lane % 32, h = lane / 32;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int dir = lid & 1, rb = (lid >> 1) % NRB;
+  const int64_t bh = lid / (2 * NRB);
+  const int r0 = rb * R, n0 = wave * 32;
+  const int crow = tid / (D / 4), ccol = 4 * (tid % (D / 4));
+
+  // frame of adjoint step `step` (the forward direction runs backwards in time and
+  // vice versa), clamped to the last step (loads past the end are not used)
+  auto fidx = [&](int step) -> int64_t {
+    const int c = step < T ? step : T - 1;
+    return bh * T + (dir ? c : T - 1 - c);
+  };
+  // element (r0 + row, col) of frame f's matrix of this direction in dsg / dx
+  auto eoff = [&](int64_t f, int row, int col) { return ((f * 2 + dir) * D + r0 + row) * (int64_t)D + col; };
+  auto load_m = [&](float4 (&m)[KG], int step) {
+    const float* mp = Mt + fidx(step) * D * D + (int64_t)(n0 + l32) * D + 4 * h;
+#pragma unroll
+    for (int i = 0; i < KG; ++i) m[i] = *reinterpret_cast<const float4*>(mp + 8 * i);
+  };
+  auto load_g = [&](float4 (&b)[4], int step) {
+    const float* bp = dsg + eoff(fidx(step), crow, ccol);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4*>(bp + 8 * j * D);
+  };
+
+  // one adjoint step: mc = M_s, mn <- M_{s+1}, bl <- dS_{s+2}, be = dS_{s+1};
+  // G_s in X, dX_s and then G_{s+1} go to Y
+  auto step = [&](int s, float4 (&mc)[KG], float4 (&mn)[KG], float4 (&bl)[4], const float4 (&be)[4],
+                  const float* X, float* Y) {
+    const int64_t fi = fidx(s), fn = fidx(s + 1);
+    const float gc = gamma[fi];
+    load_m(mn, s + 1);
+    load_g(bl, s + 2);
+    __builtin_amdgcn_sched_barrier(0);   // the next frames' loads go out before this frame's products
+    const float* xrow = X + l32 * LD + 4 * h;
+    float4 xv[KG];
+#pragma unroll
+    for (int i = 0; i < KG; ++i) xv[i] = *reinterpret_cast<const float4*>(xrow + 8 * i);
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].x, mc[i].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].y, mc[i].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].z, mc[i].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[i].w, mc[i].w, acc, 0, 0, 0);
+    }
+    // acc[r] = dX_s[r0 + 8 (r/4) + 4h + r%4][n0 + l32]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Y[(8 * (r / 4) + 4 * h + r % 4) * LD + n0 + l32] = acc[r];
+    __syncthreads();   // dX_s complete in Y
+    const bool more = s + 1 < T;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float* yp = Y + (crow + 8 * j) * LD + ccol;
+      const float4 sv = *reinterpret_cast<const float4*>(yp);
+      *reinterpret_cast<float4*>(dx + eoff(fi, crow + 8 * j, ccol)) = sv;
+      float4 gn;
+      gn.x = gc * sv.x + be[j].x;
+      gn.y = gc * sv.y + be[j].y;
+      gn.z = gc * sv.z + be[j].z;
+      gn.w = gc * sv.w + be[j].w;
+      if (more) *reinterpret_cast<float4*>(dsg + eoff(fn, crow + 8 * j, ccol)) = gn;
+      *reinterpret_cast<float4*>(yp) = gn;
+    }
+    __syncthreads();   // G_{s+1} complete in Y
+  };
+
+  float4 m0[KG], m1[KG], b0[4], b1[4];
+  load_m(m0, 0);
+  load_g(b0, 0);
+  load_g(b1, 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)   // G of the first adjoint step is its dS (nothing follows it)
+    *reinterpret_cast<float4*>(&P[0][(crow + 8 * j) * LD + ccol]) = b0[j];
+  __syncthreads();
+  int s = 0;
+  for (; s + 1 < T; s += 2) {
+    step(s, m0, m1, b0, b1, P[0], P[1]);
+    step(s + 1, m1, m0, b1, b0, P[1], P[0]);
+  }
+  if (s < T) step(s, m0, m1, b0, b1, P[0], P[1]);
+}
+
+// ---------------------------------------------------------------------------
 // frame_bwd: per frame f, X_t = gamma_t S_prev + B_t for both directions
 // (S_prev = S_{t-1} forward, S_{t+1} backward, zero past the ends), into
 // xs[f][dir]; dB_t = dX_f + dX_b into cdb[f][1]; dgamma_t.
@@ -1376,11 +1487,15 @@ hipError_t launch_rms_bwd(int dtype, int d, float* U, const void* d_out, int64_t
 hipError_t launch_scan_bwd(int d, const float* Mt, const float* gamma, float* dsg, float* dx, int BH,
                            int T, hipStream_t st) {
   if (BH <= 0) return hipSuccess;
+  if (d == 64 || d == 128) {
+    const int total = BH * 2 * (d / sb::R);   // d / 32 row blocks x 2 directions per (batch, head)
+    if (d == 128) scan_bwd_mfma_kernel<128><<<total, 256, 0, st>>>(Mt, gamma, dsg, dx, T, total);
+    else scan_bwd_mfma_kernel<64><<<total, 128, 0, st>>>(Mt, gamma, dsg, dx, T, total);
+    return hipGetLastError();
+  }
   constexpr int R = 16;
   dim3 grid(d / R, BH, 2);
-  if (d == 32) scan_bwd_kernel<32, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
-  else if (d == 64) scan_bwd_kernel<64, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
-  else scan_bwd_kernel<128, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
+  scan_bwd_kernel<32, R><<<grid, 256, 0, st>>>(Mt, gamma, dsg, dx, T);
   return hipGetLastError();
 }
 
