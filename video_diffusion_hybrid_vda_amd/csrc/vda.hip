@@ -436,7 +436,8 @@ __global__ __launch_bounds__(256) void vda_scan_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// scan, head_dim D = 64 or 128, on fp32 MFMA.  One workgroup of D / 32 waves
+// scan on fp32 MFMA (instantiated for head_dim 128; head_dim 64 takes the
+// 16-row kernel below).  One workgroup of D / 32 waves
 // per 32 state rows of one (batch, head, direction); wave w produces columns
 // 32w .. 32w+31 of those rows with D / 2 v_mfma_f32_32x32x2_f32 per frame:
 // S_t = X_t M_t with
@@ -557,6 +558,115 @@ __global__ __launch_bounds__(2 * D) void vda_scan_mfma_kernel(const float* __res
 #pragma unroll
   for (int j = 0; j < 4; ++j)   // X_0 = B_0 (S_{-1} = 0)
     *reinterpret_cast<float4*>(&P[0][(crow + 8 * j) * LD + ccol]) = b0[j];
+  __syncthreads();
+  int s = 0;
+  for (; s + 1 < T; s += 2) {
+    step(s, m0, m1, b0, b1, P[0], P[1]);
+    step(s + 1, m1, m0, b1, b0, P[1], P[0]);
+  }
+  if (s < T) step(s, m0, m1, b0, b1, P[0], P[1]);
+}
+
+// The same scan with 16 state rows per workgroup on v_mfma_f32_16x16x4f32 (the
+// head_dim 64 path): D/16 waves, wave w forming the 16 x 16 block of columns
+// 16w.. of S_s = X_s M_s (D/4 products of 32 cycles instead of D/2 of 64), so a
+// frame step's products are a quarter of the 32-row kernel's per wave, and twice
+// as many workgroups share the chip.  Lane group g = l / 16 takes
+// k = 16 g .. 16 g + 15 over the D/4 products: its X row and M_s^T row
+// fragments are four 16-byte reads each.  The epilogue gives every thread one
+// 16-byte chunk of the 16 rows.
+namespace sc16 {
+constexpr int R = 16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+}  // namespace sc16
+
+template <int D, bool kStates, bool kSplit>
+__global__ __launch_bounds__(4 * D) void vda_scan_mfma16_kernel(const float* __restrict__ Mt,
+                                                              const float* __restrict__ Bm,
+                                                              const float* __restrict__ gamma,
+                                                              float* __restrict__ states,
+                                                              bf16* __restrict__ split, int T,
+                                                              int64_t bhtdd, int total) {
+  using namespace sc16;
+  constexpr int LD = D + 4, NRB = D / R, KQ = D / 16;   // LDS row stride, row blocks, 4-k groups per lane
+  __shared__ __attribute__((aligned(16))) float P[2][R * LD];   // X_t and S_t, rows r0 .. r0+15
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int l16 = lane % 16, g = lane / 16;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int dir = lid & 1, rb = (lid >> 1) % NRB;
+  const int64_t bh = lid / (2 * NRB);
+  const int r0 = rb * R, n0 = wave * 16;
+  const int crow = tid / (D / 4), ccol = 4 * (tid % (D / 4));   // the thread's chunk
+
+  auto fidx = [&](int step) -> int64_t {
+    const int c = step < T ? step : T - 1;
+    return bh * T + (dir ? T - 1 - c : c);
+  };
+  // M_s^T row n0 + l16, columns 16 g .. 16 g + 15 (k of this lane group)
+  auto load_m = [&](float4 (&m)[KQ], int step) {
+    const float* mp = Mt + fidx(step) * D * D + (int64_t)(n0 + l16) * D + (D / 4) * g;
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) m[i] = *reinterpret_cast<const float4*>(mp + 4 * i);
+  };
+  auto load_b = [&](float4& b, int step) {
+    b = *reinterpret_cast<const float4*>(Bm + fidx(step) * D * D + (int64_t)(r0 + crow) * D + ccol);
+  };
+
+  // one frame step: mc = M_s^T, mn <- M_{s+1}^T, bl <- B_{s+2}, be = B_{s+1};
+  // X_s in X, S_s and then X_{s+1} go to Y
+  auto step = [&](int s, float4 (&mc)[KQ], float4 (&mn)[KQ], float4& bl, const float4& be, const float* X,
+                  float* Y) {
+    const int64_t fi = fidx(s);
+    const float gn = gamma[fidx(s + 1)];
+    load_m(mn, s + 1);
+    load_b(bl, s + 2);
+    __builtin_amdgcn_sched_barrier(0);   // the next frames' loads go out before this frame's products
+    const float* xrow = X + l16 * LD + (D / 4) * g;
+    float4 xv[KQ];
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) xv[i] = *reinterpret_cast<const float4*>(xrow + 4 * i);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i].x, mc[i].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i].y, mc[i].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i].z, mc[i].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i].w, mc[i].w, acc, 0, 0, 0);
+    }
+    // acc[e] = S_s[r0 + 4 g + e][n0 + l16]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Y[(4 * g + e) * LD + n0 + l16] = acc[e];
+    __syncthreads();   // S_s complete in Y
+    float* yp = Y + crow * LD + ccol;
+    const float4 sv = *reinterpret_cast<const float4*>(yp);
+    const int64_t off = fi * D * D + (int64_t)(r0 + crow) * D + ccol;
+    if constexpr (kStates) *reinterpret_cast<float4*>(states + dir * bhtdd + off) = sv;
+    if constexpr (kSplit) {
+      bf16x4 hi, lo;
+      hi[0] = (bf16)sv.x; hi[1] = (bf16)sv.y; hi[2] = (bf16)sv.z; hi[3] = (bf16)sv.w;
+      lo[0] = (bf16)(sv.x - (float)hi[0]);
+      lo[1] = (bf16)(sv.y - (float)hi[1]);
+      lo[2] = (bf16)(sv.z - (float)hi[2]);
+      lo[3] = (bf16)(sv.w - (float)hi[3]);
+      bf16* sp = split + dir * bhtdd * 2 + fi * D * D * 2 + (int64_t)(r0 + crow) * D + ccol;
+      *reinterpret_cast<bf16x4*>(sp) = hi;
+      *reinterpret_cast<bf16x4*>(sp + D * D) = lo;
+    }
+    // (after the last frame this X is formed from clamped loads and never read)
+    float4 xn;
+    xn.x = gn * sv.x + be.x;
+    xn.y = gn * sv.y + be.y;
+    xn.z = gn * sv.z + be.z;
+    xn.w = gn * sv.w + be.w;
+    *reinterpret_cast<float4*>(yp) = xn;
+    __syncthreads();   // X_{s+1} complete in Y
+  };
+
+  float4 m0[KQ], m1[KQ], b0, b1;
+  load_m(m0, 0);
+  load_b(b0, 0);
+  load_b(b1, 1);
+  *reinterpret_cast<float4*>(&P[0][crow * LD + ccol]) = b0;   // X_0 = B_0 (S_{-1} = 0)
   __syncthreads();
   int s = 0;
   for (; s + 1 < T; s += 2) {
@@ -1025,17 +1135,21 @@ hipError_t launch_vda_scan(int d, const float* Mt, const float* Bm, const float*
     const int total = BH * 2 * (d / 32);   // d / 32 row blocks x 2 directions per (batch, head)
 #define VDN_SCAN(DD, WS, WH) \
   vda_scan_mfma_kernel<DD, WS, WH><<<total, 2 * DD, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total)
+#define VDN_SCAN16(DD, WS, WH) \
+  vda_scan_mfma16_kernel<DD, WS, WH><<<total16, 4 * DD, 0, st>>>(Mt, Bm, gamma, states, split, T, bhtdd, total16)
+    const int total16 = BH * 2 * (d / sc16::R);
     if (!states && !split) return hipErrorInvalidValue;
     if (d == 128) {
       if (states && split) VDN_SCAN(128, true, true);
       else if (states) VDN_SCAN(128, true, false);
       else VDN_SCAN(128, false, true);
-    } else {
-      if (states && split) VDN_SCAN(64, true, true);
-      else if (states) VDN_SCAN(64, true, false);
-      else VDN_SCAN(64, false, true);
+    } else {   // 16 rows per workgroup (at d = 128 the 32-row kernel measured faster)
+      if (states && split) VDN_SCAN16(64, true, true);
+      else if (states) VDN_SCAN16(64, true, false);
+      else VDN_SCAN16(64, false, true);
     }
 #undef VDN_SCAN
+#undef VDN_SCAN16
     return hipGetLastError();
   }
   dim3 grid(d / kScanRows, BH, 2);
