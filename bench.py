@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27864640021,
-        "window_attn": 269046832111,
-        "anchor_merge": 710113907,
-        "vda_gram": 5374825698,
-        "vda_solve": 321172280,
-        "vda_scan": 947027249,
-        "vda_readout": 7901736740,
-        "out_gemm": 30813469654
+        "gate_gemm": 27820371541,
+        "window_attn": 262359585305,
+        "anchor_merge": 710161561,
+        "vda_gram": 5374824899,
+        "vda_solve": 321165413,
+        "vda_scan": 946797561,
+        "vda_readout": 7901709728,
+        "out_gemm": 27472642719
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 179770395958,
-        "mxfp8_quantize": 7659487789
+        "window_attn": 181636485900,
+        "mxfp8_quantize": 7659465870
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284709011,
-        "bwd_token": 23428478711,
-        "bwd_scan": 3515100530,
-        "bwd_frame": 5562754643,
-        "bwd_kv_gemm": 10440336875
+        "bwd_recompute": 7284918932,
+        "bwd_token": 23428765156,
+        "bwd_scan": 1274377110,
+        "bwd_frame": 5567839284,
+        "bwd_kv_gemm": 10439794695
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145315196,
-        "vda_solve": 11161400,
-        "vda_scan": 22113400,
-        "vda_readout": 186671620
+        "vda_gram": 145315100,
+        "vda_solve": 11161396,
+        "vda_scan": 22065265,
+        "vda_readout": 186662959
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11459538319,
-        "window_attn": 111047536287,
-        "anchor_merge": 401542395,
-        "vda_gram": 2213160360,
-        "vda_solve": 132464090,
-        "vda_scan": 379817307,
-        "vda_readout": 3253791852,
-        "out_gemm": 10431389079
+        "gate_gemm": 11460102660,
+        "window_attn": 111951492055,
+        "anchor_merge": 401570430,
+        "vda_gram": 2213157976,
+        "vda_solve": 132420394,
+        "vda_scan": 379731629,
+        "vda_readout": 3253810620,
+        "out_gemm": 10435141587
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,8 +98,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "757b4ab0db00276f",
-    "mxfp8": "8cdcfa773199d9a4", "bwd": "867876673bea4dcc", "vda+bwd": "0aa9e191e0bc6c51",
+    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "3f50dbab563a4fc3",
+    "mxfp8": "8cdcfa773199d9a4", "bwd": "aea2c9438de5f29c", "vda+bwd": "e4b87bc7d409a6ff",
     "common": "a24de8342071a471"
 }
 
