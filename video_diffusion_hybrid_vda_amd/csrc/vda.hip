@@ -14,6 +14,8 @@
 //   readout : u = S_t q both directions, RMSNorm, sum, gate     (MFMA, HBM-bound)
 #include <math.h>
 
+#include <utility>
+
 #include "vdn_common.h"
 #include "vdn_internal.h"
 
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
-// gram, bf16 / head_dim 128 (the workload shape).  One workgroup of four waves
-// per (frame, head); K_t and V_t stream through a four-stage LDS ring of
+// gram, bf16, head_dim 64 and 128 (described at 128).  One workgroup of four
+// waves per (frame, head); K_t and V_t stream through a four-stage LDS ring of
 // 64-token tiles by the direct-to-LDS DMA path (a buffer load with the lds
 // modifier), row-major with XOR-swizzled 16-byte chunks; token rows past N
 // read as zero.  Wave w consumes token rows 16w .. 16w+15 of every tile.  A
@@ -146,30 +148,70 @@ __global__ __launch_bounds__(256) void vda_gram_kernel(const T* __restrict__ k,
 // data movement.  Each wave accumulates the 10 upper 32x32 tiles of K^T K and
 // the 16 tiles of V^T K over its quarter of the tokens (416 fp32 per lane);
 // the four partial sums are added through LDS at the end, scaled by beta_t,
-// and A's off-diagonal tiles are mirrored.
+// and A's off-diagonal tiles are mirrored.  At head_dim 64 the same holds
+// with 3 + 4 tiles and 128-byte rows.
 namespace gr {
-constexpr int D = 128, BN = 64, ROWB = D * 2, TILEB = BN * ROWB, STAGEB = 2 * TILEB, STAGES = 4;
-constexpr int NA = 10, NTILE = NA + 16;      // output tiles: upper A tiles, then B tiles
-constexpr int TB = 7;                        // tiles per reduction batch (4 x 7 x 16 x 65 floats fit the ring)
+constexpr int BN = 64, STAGES = 4;
 constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0)
-constexpr int kWaitVm8 = 0x0F78;             // vmcnt(8): one tile's loads may be outstanding
-constexpr int kWaitVm16 = 0x4F70;            // vmcnt(16): two tiles' loads may be outstanding
+template <int D>
+struct Geo {
+  static constexpr int ROWB = D * 2, TILEB = BN * ROWB, STAGEB = 2 * TILEB;
+  static constexpr int NT = D / 32;                       // 32-wide blocks per dimension
+  static constexpr int NA = NT * (NT + 1) / 2, NTILE = NA + NT * NT;   // upper A tiles, then B tiles
+  static constexpr int BPW = TILEB / 1024 / 4;            // 1 KB DMA blocks per wave and tensor
+  static constexpr int RPB = 1024 / ROWB;                 // token rows per DMA block
+  static constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
+  // tiles per reduction batch: 4 waves x TB tiles x 16 x 65 floats fit the ring
+  static constexpr int TB = STAGES * STAGEB / (4 * 16 * 65 * 4);
+  // s_waitcnt vmcnt(n) with n = one or two tiles' loads outstanding
+  static constexpr int kWaitOne = 0x0F70 | (2 * BPW);
+  static constexpr int kWaitTwo = 0x0F70 | ((4 * BPW) & 15) | (((4 * BPW) >> 4) << 14);
+};
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-// Physical chunk of logical 16-byte chunk c of row r: 8 rows x 4 chunks of a
-// transpose read touch every bank exactly twice.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
-// (tile row block, tile column block) of output tile u
+// Physical chunk of logical 16-byte chunk c of row r.  256-byte rows: 8 rows x
+// 4 chunks of a transpose read touch every bank exactly twice.  128-byte rows:
+// the 4 rows x 4 chunks of each half-wave cover the 64 banks once (rows r and
+// r + 2 share banks, so bit 1 of the row flips the chunk's upper half).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+  else return c ^ (((r >> 1) & 1) << 2);
+}
+// (tile row block, tile column block) of output tile u: the upper tiles of
+// A row by row, then the tiles of B row by row
+// (branch-free: row r of the upper tiles starts at tile r NT - r (r - 1) / 2)
+__device__ __forceinline__ constexpr int upper_start(int nt, int r) { return r * nt - r * (r - 1) / 2; }
+template <int D>
 __device__ __forceinline__ constexpr int tile_i(int u) {
-  return u < 4 ? 0 : u < 7 ? 1 : u < 9 ? 2 : u < 10 ? 3 : (u - NA) / 4;
+  constexpr int NT = Geo<D>::NT, NA = Geo<D>::NA;
+  int i = 0;
+  for (int r = 1; r < NT; ++r) i += u >= upper_start(NT, r) ? 1 : 0;
+  return u >= NA ? (u - NA) / NT : i;
 }
+template <int D>
 __device__ __forceinline__ constexpr int tile_j(int u) {
-  return u < 4 ? u : u < 7 ? u - 3 : u < 9 ? u - 5 : u < 10 ? 3 : (u - NA) % 4;
+  constexpr int NT = Geo<D>::NT, NA = Geo<D>::NA;
+  const int i = tile_i<D>(u);
+  return u >= NA ? (u - NA) % NT : i + u - upper_start(NT, i);
 }
-// Accumulating products with the accumulator's register file fixed: the 10
-// K^T K tiles in vector registers, the 16 V^T K tiles in accumulator
-// registers (416 fp32 per lane do not fit one file; left to itself the
+static_assert(tile_i<128>(9) == 3 && tile_j<128>(9) == 3 && tile_i<128>(5) == 1 && tile_j<128>(5) == 2 &&
+                  tile_i<128>(25) == 3 && tile_j<128>(25) == 3 && tile_i<64>(1) == 0 && tile_j<64>(1) == 1 &&
+                  tile_i<64>(2) == 1 && tile_j<64>(2) == 1 && tile_i<64>(5) == 1 && tile_j<64>(5) == 0,
+              "tile enumeration");
+static_assert(Geo<128>::TB == 7 && Geo<64>::TB == 3, "reduction batches fit the ring");
+static_assert(Geo<128>::kWaitOne == 0x0F78 && Geo<128>::kWaitTwo == 0x4F70 && Geo<64>::kWaitOne == 0x0F74 &&
+                  Geo<64>::kWaitTwo == 0x0F78,
+              "vmcnt encodings");
+// f(integral_constant<int, U>) for U = 0 .. sizeof...(U) - 1, each a compile-time constant
+template <typename F, int... U>
+__device__ __forceinline__ void for_each_tile(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+// Accumulating products with the accumulator's register file fixed: the
+// K^T K tiles in vector registers, the V^T K tiles in accumulator registers
+// (416 fp32 per lane at head_dim 128 do not fit one file; left to itself the
 // compiler shuttles tiles between the files around every product).
 // The first product of a tile starts from zero, so the accumulators need no
 // initialisation (and no vector-write -> matrix-read wait states).
@@ -183,13 +225,16 @@ __device__ __forceinline__ void mma_a(f32x16& d, bf16x8 a, bf16x8 b, bool first)
 }
 }  // namespace gr
 
-__global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __restrict__ k,
-                                                                 const bf16* __restrict__ v,
-                                                                 const float* __restrict__ beta,
-                                                                 float* __restrict__ A,
-                                                                 float* __restrict__ Bm, int T_, int N,
-                                                                 int Lt) {
+template <int D>
+__global__ __launch_bounds__(256) void vda_gram_bf16_kernel(const bf16* __restrict__ k,
+                                                            const bf16* __restrict__ v,
+                                                            const float* __restrict__ beta,
+                                                            float* __restrict__ A,
+                                                            float* __restrict__ Bm, int T_, int N, int Lt) {
   using namespace gr;
+  using G = Geo<D>;
+  constexpr int ROWB = G::ROWB, TILEB = G::TILEB, STAGEB = G::STAGEB, NT = G::NT, NA = G::NA,
+                NTILE = G::NTILE, BPW = G::BPW, TB = G::TB;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGEB];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int g = lane / 16, j16 = lane % 16;
@@ -200,20 +245,20 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc((void*)(v + row0 * D), (short)0, N * ROWB, 0x00020000);
 
-  // DMA: lane l of block b fills physical chunk l%16 of tile row 4b + l/16
-  int lane_off[4];
+  // DMA: lane l of block b fills physical chunk l % CPR of tile row RPB b + l / CPR
+  int lane_off[BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 4 + lane / 16;
-    lane_off[i] = row * ROWB + swz(row, lane % 16) * 16;
+  for (int i = 0; i < BPW; ++i) {
+    const int row = (wave * BPW + i) * G::RPB + lane / G::CPR;
+    lane_off[i] = row * ROWB + swz<D>(row, lane % G::CPR) * 16;
   }
   const int ntiles = (N + BN - 1) / BN;
   auto issue = [&](int t) {
     const int lds = (int)(size_t)(__attribute__((address_space(3))) unsigned char*)(ring + (t & 3) * STAGEB);
     const int base = t * BN * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wave * 4 + i;
+    for (int i = 0; i < BPW; ++i) {
+      const int blk = wave * BPW + i;
       const int voff = base + lane_off[i];
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rk), "{m0}"(lds + blk * 1024)
                    : "memory");
@@ -224,14 +269,14 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
   };
   // transpose-read offsets inside a tile: tokens 16 wave + 4 (g/2) + {0..3} and
   // {8..11}, dimension 32 dt + 16 (g%2) + j16
-  int offA[4], offB[4];
+  int offA[NT], offB[NT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < NT; ++dt) {
     const int rowA = 16 * wave + 4 * (g >> 1) + (j16 >> 2), rowB = rowA + 8;
     const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
     const int cch = dcol >> 3, off = (dcol & 7) * 2;
-    offA[dt] = rowA * ROWB + swz(rowA, cch) * 16 + off;
-    offB[dt] = rowB * ROWB + swz(rowB, cch) * 16 + off;
+    offA[dt] = rowA * ROWB + swz<D>(rowA, cch) * 16 + off;
+    offB[dt] = rowB * ROWB + swz<D>(rowB, cch) * 16 + off;
   }
   auto frag = [&](const unsigned char* base, int dt) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + offA[dt]));
@@ -245,23 +290,26 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm16);
-    else if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    if (t + 2 < ntiles) __builtin_amdgcn_s_waitcnt(G::kWaitTwo);
+    else if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(G::kWaitOne);
     else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();                       // tile t visible; tile t-1's stage free
     if (t + 3 < ntiles) issue(t + 3);
     const unsigned char* sb = ring + (t & 3) * STAGEB;
-    bf16x8 kf[4], vf[4];
+    bf16x8 kf[NT], vf[NT];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < NT; ++dt) {
       kf[dt] = frag(sb, dt);
       vf[dt] = frag(sb + TILEB, dt);
     }
     const bool first = t == 0;
-#pragma unroll
-    for (int u = 0; u < NA; ++u) mma_v(accA[u], kf[tile_i(u)], kf[tile_j(u)], first);
-#pragma unroll
-    for (int u = NA; u < NTILE; ++u) mma_a(accB[u - NA], vf[tile_i(u)], kf[tile_j(u)], first);
+    for_each_tile(
+        [&](auto U) {
+          constexpr int u = decltype(U)::value, ti = tile_i<D>(u), tj = tile_j<D>(u);
+          if constexpr (u < NA) mma_v(accA[u], kf[ti], kf[tj], first);
+          else mma_a(accB[u - NA], vf[ti], kf[tj], first);
+        },
+        std::make_integer_sequence<int, NTILE>{});
   }
   // the last products' results are read by vector instructions below: wait
   // out the matrix pipeline (fenced so that no read is scheduled above it)
@@ -287,7 +335,7 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_d128_kernel(const bf16* __r
     __syncthreads();
     for (int e = tid; e < nb * 1024; e += 256) {
       const int uu = e >> 10, u = b0 + uu, w = e & 1023, row = w >> 5, col = w & 31;
-      const int ti = tile_i(u), tj = tile_j(u);
+      const int ti = tile_i<D>(u), tj = tile_j<D>(u);
       auto sum4 = [&](int rr, int cc) {
         const int r = (rr >> 3) * 4 + (rr & 3), ln = cc + 32 * ((rr >> 2) & 1);
         float s = 0.f;
@@ -331,10 +379,16 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
   float* am = AM + f * D * D;
   const int c = threadIdx.x;
 
+  // Every thread loads column c mod D and the right half multiplies it by 0,
+  // so the D loads carry no branch and are all in flight before the first
+  // wait.  Column c of [I + A | I] is keep * A[:, c mod D] + e_(c mod D).
   float a[D];
+  const int cl = c & (D - 1);
+  const float keep = c < D ? 1.f : 0.f;
 #pragma unroll
-  for (int i = 0; i < D; ++i)
-    a[i] = c < D ? am[i * D + c] + (i == c ? 1.f : 0.f) : (i == c - D ? 1.f : 0.f);
+  for (int i = 0; i < D; ++i) a[i] = am[i * D + cl];
+#pragma unroll
+  for (int i = 0; i < D; ++i) a[i] = fmaf(a[i], keep, i == cl ? 1.f : 0.f);
   __syncthreads();   // every column is read before any thread overwrites AM below
 
   // The rows rotate by one per step, so that the pivot row is always a[0]
@@ -346,14 +400,38 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
     const int buf = k & 1;
     rowb[buf][(c - k) & (2 * D - 1)] = sgn * a[0];
     __syncthreads();
-    const float x = a[0] / rowb[buf][0];
+    const float4* rb = reinterpret_cast<const float4*>(rowb[buf]);
+    float x;
+    if constexpr (D <= 64) {
+      // all D/4 reads of the pivot column issued before the products use them
+      // (one frame-head system per workgroup is latency-bound at this size)
+      float4 cv[D / 4];
 #pragma unroll
-    for (int i = 0; i < D; i += 4) {
-      const float4 cv = *reinterpret_cast<const float4*>(&rowb[buf][i]);
-      if (i > 0) a[i - 1] = a[i] - cv.x * x;
-      a[i] = a[i + 1] - cv.y * x;
-      a[i + 1] = a[i + 2] - cv.z * x;
-      a[i + 2] = a[i + 3] - cv.w * x;
+      for (int j = 0; j < D / 4; ++j) cv[j] = rb[j];
+      x = a[0] / cv[0].x;
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) {
+        const int i = 4 * j;
+        if (i > 0) a[i - 1] = a[i] - cv[j].x * x;
+        a[i] = a[i + 1] - cv[j].y * x;
+        a[i + 1] = a[i + 2] - cv[j].z * x;
+        a[i + 2] = a[i + 3] - cv[j].w * x;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 4, 0);   // the reads first
+      __builtin_amdgcn_sched_group_barrier(0x2, D + 16, 0);    // then the vector work
+    } else {
+      // at head_dim 128 the compiler's own interleave keeps 3 workgroups per
+      // CU (more reads in flight cost occupancy and measured slower)
+      x = a[0] / rowb[buf][0];
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) {
+        const int i = 4 * j;
+        const float4 cv = rb[j];
+        if (i > 0) a[i - 1] = a[i] - cv.x * x;
+        a[i] = a[i + 1] - cv.y * x;
+        a[i + 1] = a[i + 2] - cv.z * x;
+        a[i + 2] = a[i + 3] - cv.w * x;
+      }
     }
     a[D - 1] = x;
   }
@@ -1082,7 +1160,9 @@ template <typename T>
 static hipError_t gram_t(int d, const void* k, const void* v, const float* beta, float* A,
                          float* Bm, int nframes, int T_, int N, int Lt, hipStream_t st) {
   if (sizeof(T) == 2 && d == 128)
-    vda_gram_bf16_d128_kernel<<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, T_, N, Lt);
+    vda_gram_bf16_kernel<128><<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, T_, N, Lt);
+  else if (sizeof(T) == 2 && d == 64)
+    vda_gram_bf16_kernel<64><<<nframes, 256, 0, st>>>((const bf16*)k, (const bf16*)v, beta, A, Bm, T_, N, Lt);
   else if (d == 32)
     vda_gram_kernel<T, 32><<<nframes, 256, 0, st>>>((const T*)k, (const T*)v, beta, A, Bm, T_, N, Lt);
   else if (d == 64)
