@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27820371541,
-        "window_attn": 262359585305,
-        "anchor_merge": 710161561,
-        "vda_gram": 5374824899,
-        "vda_solve": 321165413,
-        "vda_scan": 946797561,
-        "vda_readout": 7901709728,
-        "out_gemm": 27472642719
+        "gate_gemm": 27821503700,
+        "window_attn": 259769343354,
+        "anchor_merge": 710108757,
+        "vda_gram": 5374835628,
+        "vda_solve": 320992440,
+        "vda_scan": 946921503,
+        "vda_readout": 7901698724,
+        "out_gemm": 25342881761
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 181636485900,
-        "mxfp8_quantize": 7659465870
+        "window_attn": 179930237813,
+        "mxfp8_quantize": 7659436024
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284918932,
-        "bwd_token": 23428765156,
-        "bwd_scan": 1274377110,
-        "bwd_frame": 5567839284,
-        "bwd_kv_gemm": 10439794695
+        "bwd_recompute": 7284416417,
+        "bwd_token": 23428471651,
+        "bwd_scan": 1274577214,
+        "bwd_frame": 5568489957,
+        "bwd_kv_gemm": 10440061993
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145315100,
-        "vda_solve": 11161396,
-        "vda_scan": 22065265,
-        "vda_readout": 186662959
+        "vda_gram": 145294685,
+        "vda_solve": 11072314,
+        "vda_scan": 22079606,
+        "vda_readout": 186661352
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11460102660,
-        "window_attn": 111951492055,
-        "anchor_merge": 401570430,
-        "vda_gram": 2213157976,
-        "vda_solve": 132420394,
-        "vda_scan": 379731629,
-        "vda_readout": 3253810620,
-        "out_gemm": 10435141587
+        "gate_gemm": 11459584144,
+        "window_attn": 109221438125,
+        "anchor_merge": 401554599,
+        "vda_gram": 2213162424,
+        "vda_solve": 132255280,
+        "vda_scan": 379596456,
+        "vda_readout": 3253926871,
+        "out_gemm": 10436137520
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,9 +98,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "3f50dbab563a4fc3",
-    "mxfp8": "8cdcfa773199d9a4", "bwd": "aea2c9438de5f29c", "vda+bwd": "e4b87bc7d409a6ff",
-    "common": "a24de8342071a471"
+    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "35070dfbe11f61a9", "mxfp8": "8cdcfa773199d9a4",
+    "bwd": "aea2c9438de5f29c", "vda+bwd": "9b854d6b9a57dbe8", "common": "a24de8342071a471"
 }
 
 
