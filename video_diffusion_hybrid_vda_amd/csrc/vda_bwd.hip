@@ -766,33 +766,42 @@ __global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __re
 // Nothing token-sized but q, do and dq leaves the chip: u and du stay in
 // registers.  The first direction writes its share of dq in fp32 (to the
 // workspace); the second adds its own and writes dq in bf16.
-// S sits in LDS as bf16 hi + lo (64 KB, rows of 256 bytes, chunk c of row r at
-// c ^ (((r & 7) << 1) | ((r >> 3) & 1))).  Each wave takes a 32-token tile and
-// computes u^T = S q^T on v_mfma_f32_32x32x16_bf16 (S rows as A, q rows from
-// HBM as B), so a lane holds 64 of its token's 128 u values and its partner
-// lane (lane ^ 32) the other 64: the RMSNorm sums take one cross-lane add.
-// In that layout du is exactly the B operand of dq^T = S^T du^T when S^T comes
-// from transposed LDS reads (ds_read_b64_tr_b16 hands lane half h the rows
-// 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3 of one column, which are the du
-// values the lane holds for k-step s).  du is split into bf16 hi + lo for the
-// products.  For dS the four waves stage their tiles' du (hi, lo) and q rows in
-// LDS (24 KB each); after a barrier wave w accumulates rows 32 w .. 32 w + 31
-// of dS over all four tiles, both operands as transposed reads (tokens as k).
+// Eight waves (two per SIMD, so that one wave's vector and LDS work runs
+// beside the other's matrix products) each take a 16-token tile per round:
+//   u^T = S q^T      v_mfma_f32_16x16x32_bf16, A = rows of S (hi, lo) from LDS,
+//                    B = q straight from HBM (lane: token l%16, dims 8(l/16)..+7
+//                    of each 32-dim step); the result holds, per lane, token
+//                    l%16 at dims 16 ib + 4(l/16) + 0..3, so a token's 128 values
+//                    sit in four lanes and the RMSNorm sums take two cross-lane
+//                    adds;
+//   dq^T = S^T du^T  same product shape; du is already the B operand if the
+//                    32-dim step's k order is taken as dims 4(l/16) + 0..3 then
+//                    16 + 4(l/16) + 0..3, and A (columns of S) comes from two
+//                    ds_read_b64_tr_b16 reads of four rows each in that order;
+//   dS = du^T q      after the round's barrier, wave w forms dS rows
+//                    16 w .. 16 w + 15 over the round's tiles on
+//                    v_mfma_f32_16x16x16_bf16 (one tile = one 16-token step),
+//                    both operands transposed reads of the staged rows.
+// LDS: S as bf16 hi + lo (64 KB, rows of 256 bytes, chunk c of row r at
+// c ^ (((r & 7) << 1) | ((r >> 3) & 1))) and, per wave, the tile's du hi, du lo
+// and q rows (12 KB): 160 KB, one workgroup per CU.  (With 32-token tiles on
+// 32x32x16 products, which read S half as often, one wave per SIMD needs all
+// 512 registers and runs the phases one after another: 8.6 against 7.5 ms.)
 namespace tkg {
-constexpr int D = 128, ROWB = 256, MATB = D * ROWB, TILEB = 32 * ROWB;
-constexpr int STG = 2 * MATB, STGW = 3 * TILEB;   // staging: per wave du hi, du lo, q (32 rows each)
+constexpr int D = 128, ROWB = 256, MATB = D * ROWB, TT = 16, TILEB = TT * ROWB;
+constexpr int NW = 8, STG = 2 * MATB, STGW = 3 * TILEB;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+static_assert(STG + NW * STGW == 160 * 1024, "LDS budget");
 }
 
 template <bool SECOND>
-__global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
+__global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ d_out, int64_t ldo, const float* __restrict__ states,
     const float* __restrict__ rms_w, float* __restrict__ dqp, bf16* __restrict__ dq, float* __restrict__ dsg,
     float* __restrict__ dwp, int dir, int64_t nf, int H, int T, int N, int Lt, float eps) {
   using namespace tkg;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[STG + 4 * STGW];   // 160 KB
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STG + NW * STGW];   // 160 KB
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const int64_t f = blockIdx.x;
@@ -801,11 +810,11 @@ __global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
   const int64_t b = bh / H;
   const int hh = (int)(bh % H);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
+  const int g = lane / 16, j16 = lane % 16;
 
-  // S -> hi / lo bf16
+  // S -> hi / lo bf16, rows of 256 bytes with swizzled 16-byte chunks
   const float* S = states + ((int64_t)dir * nf + f) * D * D;
-  for (int u = tid; u < D * (D / 8); u += 256) {
+  for (int u = tid; u < D * (D / 8); u += 512) {
     const int r = u / 16, c = u % 16;
     const float* src = S + r * D + c * 8;
     const float4 a = *reinterpret_cast<const float4*>(src);
@@ -825,21 +834,19 @@ __global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
   auto tr = [&](int off) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_u8*)lds + off)); };
   auto rd = [&](int off) { return *reinterpret_cast<const bf16x8*>(lds + off); };
   auto cat = [](i16x4 a, i16x4 c) { return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7)); };
-  // plain row reads (row 32 blk + l32, chunk 2 s + h): the swizzle depends on the row mod 16,
-  // so the block moves the address by a constant
-  int aoff[8];
+  // row reads of S for the u product: row 16 ib + j16, chunk 4 ks + g (the
+  // swizzle depends on the row mod 16, so ib moves the address by a constant)
+  int aoff[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) aoff[s] = l32 * ROWB + swz(l32, 2 * s + h) * 16;
-  // transposed reads of a row-major [rows][128] matrix: column block cb, rows rA and rA + 8 of
-  // each 16-row step (the step moves the address by a constant)
-  const int rA = 4 * (g >> 1) + (j16 >> 2);
-  int troff[4][2];
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = j16 * ROWB + swz(j16, 4 * ks + g) * 16;
+  // transposed reads of a row-major [rows][128] matrix, four rows from row r0:
+  // lane j16 of group g reads row r0 + 4 g + j16 / 4, columns 16 cb + 4 (j16 % 4)
+  // .. + 3, and receives column 16 cb + j16 of rows r0 + 4 g .. + 3
+  int toff[8];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int dcol = cb * 32 + 16 * (g & 1) + 4 * (j16 & 3);
-    const int cch = dcol >> 3, off = (dcol & 7) * 2;
-    troff[cb][0] = rA * ROWB + swz(rA, cch) * 16 + off;
-    troff[cb][1] = (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
+  for (int cb = 0; cb < 8; ++cb) {
+    const int r = 4 * g + j16 / 4;
+    toff[cb] = r * ROWB + swz(r, 2 * cb + (j16 % 4) / 2) * 16 + 8 * (j16 % 2);
   }
 
   const bf16* qf = q + (bh * Lt + (int64_t)t * N) * D;
@@ -847,196 +854,192 @@ __global__ __launch_bounds__(256) void tok_grad_bf16_d128_kernel(
   const float* wf = rms_w ? rms_w + (int64_t)hh * D : nullptr;
   float* dqpf = dqp + f * (int64_t)N * D;
   bf16* dqf = dq + (bh * Lt + (int64_t)t * N) * D;
-  const int ntile = (N + 31) / 32, nround = (ntile + 3) / 4;
+  const int ntile = (N + TT - 1) / TT, nround = (ntile + NW - 1) / NW;
 
-  float dw[4][16];       // sum over this lane's tokens of r do, C layout
-  f32x16 dsa[4];         // dS rows 32 wave + .., column block jt
+  float dw[8][4];        // sum over this lane's tokens of r do at dims 16 ib + 4 g + e
+  f32x4 dsa[8];          // dS rows 16 wave + 4 g + e, column 16 cb + j16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dsa[i] = f32x16{};
+  for (int i = 0; i < 8; ++i) {
+    dsa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dw[i][r] = 0.f;
+    for (int e = 0; e < 4; ++e) dw[i][e] = 0.f;
   }
   __syncthreads();
 
   for (int round = 0; round < nround; ++round) {
-    const int tile = round * 4 + wave;
+    const int tile = round * NW + wave;
     unsigned char* sdh = lds + STG + wave * STGW;   // du hi rows of this wave's tile
     unsigned char* sdl = sdh + TILEB;                // du lo rows
     unsigned char* sq = sdl + TILEB;                 // q rows
     if (tile < ntile) {
-      const int n = 32 * tile + l32;
+      const int n = TT * tile + j16;
       const bool valid = n < N;
       const int nn = valid ? n : N - 1;
-      // q: B operand of u^T = S q^T (k = dims 16 s + 8 h .. + 7), also staged for dS
-      bf16x8 qb[8];
+      // q: B operand of u^T = S q^T, also staged as rows for dS
+      bf16x8 qb[4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        qb[s] = *reinterpret_cast<const bf16x8*>(qf + (int64_t)nn * D + 16 * s + 8 * h);
-        *reinterpret_cast<bf16x8*>(sq + l32 * ROWB + swz(l32, 2 * s + h) * 16) = qb[s];
+      for (int ks = 0; ks < 4; ++ks) {
+        qb[ks] = *reinterpret_cast<const bf16x8*>(qf + (int64_t)nn * D + 32 * ks + 8 * g);
+        *reinterpret_cast<bf16x8*>(sq + j16 * ROWB + swz(j16, 4 * ks + g) * 16) = qb[ks];
       }
-      // do at the lane's dims 32 dt + 8 q4 + 4 h + 0..3
-      bf16x4 dob[4][4];
+      bf16x4 dob[8];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int ib = 0; ib < 8; ++ib)
+        dob[ib] = *reinterpret_cast<const bf16x4*>(dof + (int64_t)nn * ldo + 16 * ib + 4 * g);
+      // u^T; ua[ib][e] = u(token j16, dim 16 ib + 4 g + e)
+      f32x4 ua[8];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          dob[dt][q4] = *reinterpret_cast<const bf16x4*>(dof + (int64_t)nn * ldo + 32 * dt + 8 * q4 + 4 * h);
-      // u^T
-      f32x16 ua[4];
+      for (int ib = 0; ib < 8; ++ib) ua[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) ua[dt] = f32x16{};
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          asm volatile("" ::: "memory");
-          const int ao = aoff[s] + dt * 32 * ROWB;
-          ua[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(ao), qb[s], ua[dt], 0, 0, 0);
-          ua[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(MATB + ao), qb[s], ua[dt], 0, 0, 0);
+        for (int ib = 0; ib < 8; ++ib) {
+          asm volatile("" ::: "memory");   // keeps each step's LDS reads next to its products
+          const int ao = aoff[ks] + ib * 16 * ROWB;
+          ua[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd(ao), qb[ks], ua[ib], 0, 0, 0);
+          ua[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rd(MATB + ao), qb[ks], ua[ib], 0, 0, 0);
         }
-      // RMSNorm adjoint; ua[dt][r] = u(dim 32 dt + 8 (r / 4) + 4 h + r % 4)
+      // RMSNorm adjoint (the four lanes j16 + 16 g' hold the token's 128 values)
       float ss = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ss += ua[dt][r] * ua[dt][r];
+        for (int e = 0; e < 4; ++e) ss += ua[ib][e] * ua[ib][e];
+      ss += __shfl_xor(ss, 16, kWave);
       ss += __shfl_xor(ss, 32, kWave);
       const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
       const float vm = valid ? inv : 0.f;      // tokens past the frame contribute nothing
-      float gw[4][16];
+      float gw[8][4];
       float gr = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int ib = 0; ib < 8; ++ib) {
+        const float4 wv = wf ? *reinterpret_cast<const float4*>(wf + 16 * ib + 4 * g) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 wv = wf ? *reinterpret_cast<const float4*>(wf + 32 * dt + 8 * q4 + 4 * h)
-                               : make_float4(1.f, 1.f, 1.f, 1.f);
-          const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float dv = (float)dob[dt][q4][e];
-            const float u = ua[dt][4 * q4 + e];
-            gw[dt][4 * q4 + e] = w4[e] * dv;
-            gr += gw[dt][4 * q4 + e] * u;
-            const float rr = u * vm;                // r = u / rho (zero past the frame)
-            ua[dt][4 * q4 + e] = rr;
-            dw[dt][4 * q4 + e] += rr * dv;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float dv = (float)dob[ib][e];
+          const float u = ua[ib][e];
+          gw[ib][e] = w4[e] * dv;
+          gr += gw[ib][e] * u;
+          const float rr = u * vm;                // r = u / rho (zero past the frame)
+          ua[ib][e] = rr;
+          dw[ib][e] += rr * dv;
         }
+      }
+      gr += __shfl_xor(gr, 16, kWave);
       gr += __shfl_xor(gr, 32, kWave);
       const float c = gr * inv * inv * (1.f / D);   // mean(g r) / rho
-      // du = (g - r mean(g r)) / rho
+      // du = (g - r mean(g r)) / rho as hi / lo bf16: B operand of dq^T for the
+      // 32-dim step ks in the k order (dims 32 ks + 4 g + 0..3, 32 ks + 16 + 4 g + 0..3),
+      // and staged as rows for dS (8-byte pieces at dims 16 ib + 4 g)
+      bf16x8 duh[4], dul[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int ib = 0; ib < 8; ++ib) {
+        bf16x4 hv, lv;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ua[dt][r] = gw[dt][r] * vm - ua[dt][r] * c;
-      // du as hi / lo bf16: B operand of dq^T for k-step s (dims 16 s + {4h..4h+3, 8+4h..8+4h+3}),
-      // and staged as rows for dS
-      bf16x8 duh[8], dul[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int dt = s / 2, q0 = 2 * (s % 2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = ua[dt][4 * q0 + e];
-          duh[s][e] = (bf16)x;
-          dul[s][e] = (bf16)(x - (float)duh[s][e]);
+        for (int e = 0; e < 4; ++e) {
+          const float x = gw[ib][e] * vm - ua[ib][e] * c;
+          hv[e] = (bf16)x;
+          lv[e] = (bf16)(x - (float)hv[e]);
+          duh[ib / 2][4 * (ib % 2) + e] = hv[e];
+          dul[ib / 2][4 * (ib % 2) + e] = lv[e];
         }
-        // logical 16-byte chunks c0, c0 + 1 hold dims 8 c .. 8 c + 7; this lane's four sit at byte 8 h
-        const int c0 = 4 * dt + q0;
-        const int off0 = l32 * ROWB + swz(l32, c0) * 16 + 8 * h, off1 = l32 * ROWB + swz(l32, c0 + 1) * 16 + 8 * h;
-        *reinterpret_cast<bf16x4*>(sdh + off0) = __builtin_shufflevector(duh[s], duh[s], 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4*>(sdh + off1) = __builtin_shufflevector(duh[s], duh[s], 4, 5, 6, 7);
-        *reinterpret_cast<bf16x4*>(sdl + off0) = __builtin_shufflevector(dul[s], dul[s], 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4*>(sdl + off1) = __builtin_shufflevector(dul[s], dul[s], 4, 5, 6, 7);
+        const int off = j16 * ROWB + swz(j16, 2 * ib + g / 2) * 16 + 8 * (g % 2);
+        *reinterpret_cast<bf16x4*>(sdh + off) = hv;
+        *reinterpret_cast<bf16x4*>(sdl + off) = lv;
+      }
+      // the first direction's dq share, loaded before the products so that they
+      // cover its latency (rows past the frame read the last row and are not stored)
+      float4 prev[8];
+      if constexpr (SECOND) {
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+          prev[ib] = *reinterpret_cast<const float4*>(dqpf + (int64_t)nn * D + 16 * ib + 4 * g);
       }
       // dq^T = S^T du^T: A = transposed reads of S (hi, lo), B = du (hi, lo); lo x lo dropped
-      f32x16 qa[4];
+      f32x4 qa[8];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) qa[dt] = f32x16{};
+      for (int ib = 0; ib < 8; ++ib) qa[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int ib = 0; ib < 8; ++ib) {
           asm volatile("" ::: "memory");
-          const int to = s * 16 * ROWB;
-          const bf16x8 ah = cat(tr(troff[dt][0] + to), tr(troff[dt][1] + to));
-          const bf16x8 al = cat(tr(MATB + troff[dt][0] + to), tr(MATB + troff[dt][1] + to));
-          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, duh[s], qa[dt], 0, 0, 0);
-          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, dul[s], qa[dt], 0, 0, 0);
-          qa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, duh[s], qa[dt], 0, 0, 0);
+          const int to = ks * 32 * ROWB + toff[ib];
+          const bf16x8 ah = cat(tr(to), tr(to + 16 * ROWB));
+          const bf16x8 al = cat(tr(MATB + to), tr(MATB + to + 16 * ROWB));
+          qa[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, duh[ks], qa[ib], 0, 0, 0);
+          qa[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, dul[ks], qa[ib], 0, 0, 0);
+          qa[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, duh[ks], qa[ib], 0, 0, 0);
         }
-      // qa[dt][r] = dq(dim 32 dt + 8 (r / 4) + 4 h + r % 4) of this direction
+      // qa[ib][e] = dq(token j16, dim 16 ib + 4 g + e) of this direction
       if (valid) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int j = 32 * dt + 8 * q4 + 4 * h;
-            float4* pp = reinterpret_cast<float4*>(dqpf + (int64_t)n * D + j);
-            if constexpr (SECOND) {
-              const float4 prev = *pp;
-              bf16x4 o;
-              o[0] = (bf16)(prev.x + qa[dt][4 * q4]);
-              o[1] = (bf16)(prev.y + qa[dt][4 * q4 + 1]);
-              o[2] = (bf16)(prev.z + qa[dt][4 * q4 + 2]);
-              o[3] = (bf16)(prev.w + qa[dt][4 * q4 + 3]);
-              *reinterpret_cast<bf16x4*>(dqf + (int64_t)n * D + j) = o;
-            } else {
-              *pp = make_float4(qa[dt][4 * q4], qa[dt][4 * q4 + 1], qa[dt][4 * q4 + 2], qa[dt][4 * q4 + 3]);
-            }
+        for (int ib = 0; ib < 8; ++ib) {
+          const int j = 16 * ib + 4 * g;
+          if constexpr (SECOND) {
+            bf16x4 o;
+            o[0] = (bf16)(prev[ib].x + qa[ib][0]);
+            o[1] = (bf16)(prev[ib].y + qa[ib][1]);
+            o[2] = (bf16)(prev[ib].z + qa[ib][2]);
+            o[3] = (bf16)(prev[ib].w + qa[ib][3]);
+            *reinterpret_cast<bf16x4*>(dqf + (int64_t)n * D + j) = o;
+          } else {
+            *reinterpret_cast<float4*>(dqpf + (int64_t)n * D + j) = make_float4(qa[ib][0], qa[ib][1], qa[ib][2], qa[ib][3]);
           }
+        }
       }
     }
     __syncthreads();
-    // dS rows 32 wave .. + 31 over the tiles of this round: A = du^T (transposed reads of the
-    // staged du rows, column block = wave), B = q (transposed reads, column block jt)
-    for (int tt = 0; tt < 4; ++tt) {
-      if (round * 4 + tt >= ntile) break;
-      const unsigned char* base = lds + STG + tt * STGW;
-      const int bofs = (int)(base - lds);
+    // dS rows 16 wave .. + 15 over the tiles of this round (one 16-token step
+    // each): A = du^T (transposed reads of the staged du rows, column block =
+    // wave), B = q (transposed reads, column block cb)
+    for (int tt = 0; tt < NW; ++tt) {
+      if (round * NW + tt >= ntile) break;
+      const int base = STG + tt * STGW;
+      const i16x4 ah = tr(base + toff[wave]);
+      const i16x4 al = tr(base + TILEB + toff[wave]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int to = bofs + ks * 16 * ROWB;
-        const bf16x8 ah = cat(tr(to + troff[wave & 3][0]), tr(to + troff[wave & 3][1]));
-        const bf16x8 al = cat(tr(to + TILEB + troff[wave & 3][0]), tr(to + TILEB + troff[wave & 3][1]));
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const bf16x8 bq = cat(tr(to + 2 * TILEB + troff[jt][0]), tr(to + 2 * TILEB + troff[jt][1]));
-          dsa[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq, dsa[jt], 0, 0, 0);
-          dsa[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq, dsa[jt], 0, 0, 0);
-        }
+      for (int cb = 0; cb < 8; ++cb) {
+        asm volatile("" ::: "memory");
+        const i16x4 bq = tr(base + 2 * TILEB + toff[cb]);
+        dsa[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bq, dsa[cb], 0, 0, 0);
+        dsa[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bq, dsa[cb], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
-  // dS: dsa[jt][r] = dS(row 32 wave + 8 (r / 4) + 4 h + r % 4, column 32 jt + l32)
+  // dS: dsa[cb][e] = dS(row 16 wave + 4 g + e, column 16 cb + j16)
   float* ds = dsg + (f * 2 + dir) * D * D;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds[(32 * wave + 8 * (r / 4) + 4 * h + r % 4) * D + 32 * jt + l32] = dsa[jt][r];
-  // dw: sum the 32 lanes of each half (they hold the same dims), then the four waves
+    for (int e = 0; e < 4; ++e) ds[(16 * wave + 4 * g + e) * D + 16 * cb + j16] = dsa[cb][e];
+  // dw: sum the 16 lanes of each group (they hold the same dims), then the eight waves
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = dw[dt][r];
+    for (int e = 0; e < 4; ++e) {
+      float x = dw[ib][e];
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o, kWave);
-      dw[dt][r] = x;
+      for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, kWave);
+      dw[ib][e] = x;
     }
   float* red = reinterpret_cast<float*>(lds);   // S is no longer read
-  if (l32 == 0) {
+  if (j16 == 0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave * D + 32 * dt + 8 * (r / 4) + 4 * h + r % 4] = dw[dt][r];
+      for (int e = 0; e < 4; ++e) red[wave * D + 16 * ib + 4 * g + e] = dw[ib][e];
   }
   __syncthreads();
-  if (tid < D) dwp[(f * 2 + dir) * D + tid] = red[tid] + red[D + tid] + red[2 * D + tid] + red[3 * D + tid];
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[w * D + tid];
+    dwp[(f * 2 + dir) * D + tid] = s;
+  }
 }
 
 hipError_t launch_tok_grad(const void* q, const void* d_out, int64_t ldo, const float* states, const float* rms_w,
@@ -1044,11 +1047,11 @@ hipError_t launch_tok_grad(const void* q, const void* d_out, int64_t ldo, const 
                            float eps, hipStream_t st) {
   if (nf <= 0) return hipSuccess;
   if (nf > 0x7FFFFFFF) return hipErrorInvalidValue;
-  tok_grad_bf16_d128_kernel<false><<<(unsigned)nf, 256, 0, st>>>(
+  tok_grad_bf16_d128_kernel<false><<<(unsigned)nf, 512, 0, st>>>(
       (const bf16*)q, (const bf16*)d_out, ldo, states, rms_w, dqp, (bf16*)dq, dsg, dwp, 0, nf, H, T, N, Lt, eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  tok_grad_bf16_d128_kernel<true><<<(unsigned)nf, 256, 0, st>>>(
+  tok_grad_bf16_d128_kernel<true><<<(unsigned)nf, 512, 0, st>>>(
       (const bf16*)q, (const bf16*)d_out, ldo, states, rms_w, dqp, (bf16*)dq, dsg, dwp, 1, nf, H, T, N, Lt, eps);
   return hipGetLastError();
 }
