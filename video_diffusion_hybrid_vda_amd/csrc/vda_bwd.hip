@@ -787,6 +787,16 @@ __global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __re
 // and q rows (12 KB): 160 KB, one workgroup per CU.  (With 32-token tiles on
 // 32x32x16 products, which read S half as often, one wave per SIMD needs all
 // 512 registers and runs the phases one after another: 8.6 against 7.5 ms.)
+// RMSNorm weight of ones, for callers that pass none
+__device__ float kUnitWeight[128] = {   // global (not constant) memory: loads stay global, not flat
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 namespace tkg {
 constexpr int D = 128, ROWB = 256, MATB = D * ROWB, TT = 16, TILEB = TT * ROWB;
 constexpr int NW = 8, STG = 2 * MATB, STGW = 3 * TILEB;
@@ -851,7 +861,7 @@ __global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
 
   const bf16* qf = q + (bh * Lt + (int64_t)t * N) * D;
   const bf16* dof = d_out + (b * Lt + (int64_t)t * N) * ldo + (int64_t)hh * D;
-  const float* wf = rms_w ? rms_w + (int64_t)hh * D : nullptr;
+  const float* wf = rms_w ? rms_w + (int64_t)hh * D : kUnitWeight;
   float* dqpf = dqp + f * (int64_t)N * D;
   bf16* dqf = dq + (bh * Lt + (int64_t)t * N) * D;
   const int ntile = (N + TT - 1) / TT, nround = (ntile + NW - 1) / NW;
@@ -883,9 +893,12 @@ __global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
         *reinterpret_cast<bf16x8*>(sq + j16 * ROWB + swz(j16, 4 * ks + g) * 16) = qb[ks];
       }
       bf16x4 dob[8];
+      float4 wv[8];   // the RMSNorm weight at the same dims, loaded here so that the u products cover it
 #pragma unroll
-      for (int ib = 0; ib < 8; ++ib)
+      for (int ib = 0; ib < 8; ++ib) {
         dob[ib] = *reinterpret_cast<const bf16x4*>(dof + (int64_t)nn * ldo + 16 * ib + 4 * g);
+        wv[ib] = *reinterpret_cast<const float4*>(wf + 16 * ib + 4 * g);
+      }
       // u^T; ua[ib][e] = u(token j16, dim 16 ib + 4 g + e)
       f32x4 ua[8];
 #pragma unroll
@@ -913,8 +926,7 @@ __global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
       float gr = 0.f;
 #pragma unroll
       for (int ib = 0; ib < 8; ++ib) {
-        const float4 wv = wf ? *reinterpret_cast<const float4*>(wf + 16 * ib + 4 * g) : make_float4(1.f, 1.f, 1.f, 1.f);
-        const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
+        const float w4[4] = {wv[ib].x, wv[ib].y, wv[ib].z, wv[ib].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float dv = (float)dob[ib][e];
