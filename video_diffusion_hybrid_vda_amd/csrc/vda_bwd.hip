@@ -16,7 +16,8 @@
 // Kernels:
 //   bgemm        batched fp32-accumulate product with strided, two-segment
 //                operands: every contraction above (token-side products and the
-//                per-frame d x d products); fp32 FMA
+//                per-frame d x d products); fp32 FMA, or fp32 MFMA when both
+//                operands and the result are fp32
 //   bgemm_mfma   the same on bf16 MFMA with fp32 operands split into hi + lo
 //                bf16: the token-side products of bf16 I/O
 //   rms_bwd      per token and direction: du from u (in place) and partial dw
@@ -42,6 +43,7 @@ namespace vdn {
 // Operand elements are fetched along the operand's unit-stride axis.
 namespace bg {
 constexpr int BM = 64, BN = 64, BK = 16, LDT = 64 + 4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 }
 
 __device__ __forceinline__ void batch_index(const BGemm& p, int64_t z, int64_t& z0, int64_t& z1,
@@ -51,11 +53,14 @@ __device__ __forceinline__ void batch_index(const BGemm& p, int64_t z, int64_t& 
   z2 = z / ((int64_t)p.n0 * p.n1);
 }
 
-template <typename TA, typename TB, typename TC>
+template <typename TA, typename TB, typename TC, bool MF>
 __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
   using namespace bg;
-  __shared__ float As[BK][LDT];
-  __shared__ float Bs[BK][LDT];
+  static_assert(!MF || (std::is_same<TA, float>::value && std::is_same<TB, float>::value), "fp32 MFMA takes fp32");
+  // fp32 MFMA reads k and k + 1 of one column in the two lane halves: rows 32 banks apart
+  constexpr int LD = MF ? 64 + 32 : LDT;
+  __shared__ float As[BK][LD];
+  __shared__ float Bs[BK][LD];
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
   const int64_t z = blockIdx.x / tiles;
@@ -106,7 +111,13 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
     }
   };
 
+  // FMA path: 4 x 4 outputs per thread.  MFMA path: wave w forms the 32 x 32
+  // block (32 (w / 2), 32 (w % 2)) with v_mfma_f32_32x32x2_f32 (lane l: row or
+  // column l % 32, k = l / 32 of each pair)
   float acc[4][4];
+  f32x16 accm = {};
+  const int wave = tid / kWave, lane = tid % kWave, l32 = lane % 32, h = lane / 32;
+  const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -126,35 +137,44 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
     }
     __syncthreads();
     if (k0 + BK < p.K) load(k0 + BK);
+    if constexpr (MF) {
 #pragma unroll
-    for (int kk = 0; kk < BK; ++kk) {
-      float av[4], bv[4];
+      for (int s2 = 0; s2 < BK / 2; ++s2)
+        accm = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * s2 + h][wm + l32], Bs[2 * s2 + h][wn + l32], accm, 0, 0, 0);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
+      for (int kk = 0; kk < BK; ++kk) {
+        float av[4], bv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx + 16 * j];
+        for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx + 16 * j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      }
     }
   }
 
   const float alpha = p.alpha * (p.alpha_z ? p.alpha_z[z] : 1.f);
   TC* c = (TC*)p.c + oc;
+  auto put = [&](int m, int n, float v) {
+    if (m >= p.M || n >= p.N) return;
+    const int64_t idx = m * p.ldc + n;
+    float val = alpha * v;
+    if (p.accumulate) val += to_f32(c[idx]);
+    c[idx] = from_f32<TC>(val);
+  };
+  if constexpr (MF) {
+    // accm[r] = block element (row 8 (r / 4) + 4 h + r % 4, column l32)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty + 16 * i;
-    if (m >= p.M) continue;
+    for (int r = 0; r < 16; ++r) put(m0 + wm + 8 * (r / 4) + 4 * h + r % 4, n0 + wn + l32, accm[r]);
+  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx + 16 * j;
-      if (n >= p.N) continue;
-      const int64_t idx = m * p.ldc + n;
-      float val = alpha * acc[i][j];
-      if (p.accumulate) val += to_f32(c[idx]);
-      c[idx] = from_f32<TC>(val);
-    }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put(m0 + ty + 16 * i, n0 + tx + 16 * j, acc[i][j]);
   }
 }
 
@@ -1128,13 +1148,14 @@ hipError_t launch_bgemm(int ta, int tb, int tc, BGemm p, hipStream_t st, bool mf
 #undef VDN_BM
     return hipGetLastError();
   }
-#define VDN_BG(A, B, C) bgemm_kernel<A, B, C><<<(unsigned)blocks, 256, 0, st>>>(p)
+#define VDN_BG(A, B, C) bgemm_kernel<A, B, C, false><<<(unsigned)blocks, 256, 0, st>>>(p)
   // the combinations the gradient uses: bf16 or fp32 tokens against fp32 matrices
   if (ta == 1 && tb == 0 && tc == 0) VDN_BG(bf16, float, float);
   else if (ta == 0 && tb == 1 && tc == 0) VDN_BG(float, bf16, float);
   else if (ta == 0 && tb == 0 && tc == 1) VDN_BG(float, float, bf16);
   else if (ta == 1 && tb == 0 && tc == 1) VDN_BG(bf16, float, bf16);
-  else if (ta == 0 && tb == 0 && tc == 0) VDN_BG(float, float, float);
+  // fp32 operands and result: fp32 MFMA
+  else if (ta == 0 && tb == 0 && tc == 0) bgemm_kernel<float, float, float, true><<<(unsigned)blocks, 256, 0, st>>>(p);
   else return hipErrorInvalidValue;
 #undef VDN_BG
   return hipGetLastError();
