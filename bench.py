@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27821503700,
-        "window_attn": 259769343354,
-        "anchor_merge": 710108757,
-        "vda_gram": 5374835628,
-        "vda_solve": 320992440,
-        "vda_scan": 946921503,
-        "vda_readout": 7901698724,
-        "out_gemm": 25342881761
+        "gate_gemm": 27819645708,
+        "window_attn": 275370810276,
+        "anchor_merge": 710164081,
+        "vda_gram": 5374831713,
+        "vda_solve": 321038878,
+        "vda_scan": 946987442,
+        "vda_readout": 7901758371,
+        "out_gemm": 25298151435
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 179930237813,
-        "mxfp8_quantize": 7659436024
+        "window_attn": 181743735168,
+        "mxfp8_quantize": 7659463917
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284416417,
-        "bwd_token": 23428471651,
-        "bwd_scan": 1274577214,
-        "bwd_frame": 5568489957,
-        "bwd_kv_gemm": 10440061993
+        "bwd_recompute": 7284761330,
+        "bwd_token": 23390862362,
+        "bwd_scan": 1274318175,
+        "bwd_frame": 5572815120,
+        "bwd_kv_gemm": 10439832235
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145294685,
-        "vda_solve": 11072314,
-        "vda_scan": 22079606,
-        "vda_readout": 186661352
+        "vda_gram": 145294717,
+        "vda_solve": 11072315,
+        "vda_scan": 22079609,
+        "vda_readout": 186668292
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11459584144,
-        "window_attn": 109221438125,
-        "anchor_merge": 401554599,
-        "vda_gram": 2213162424,
-        "vda_solve": 132255280,
-        "vda_scan": 379596456,
-        "vda_readout": 3253926871,
-        "out_gemm": 10436137520
+        "gate_gemm": 11459926782,
+        "window_attn": 112662225728,
+        "anchor_merge": 401553147,
+        "vda_gram": 2213163048,
+        "vda_solve": 132254496,
+        "vda_scan": 379685728,
+        "vda_readout": 3253839466,
+        "out_gemm": 10435461128
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -99,7 +99,7 @@ SOURCE_GROUPS = {
 }
 SOURCE_SHA = {
     "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "35070dfbe11f61a9", "mxfp8": "8cdcfa773199d9a4",
-    "bwd": "aea2c9438de5f29c", "vda+bwd": "9b854d6b9a57dbe8", "common": "a24de8342071a471"
+    "bwd": "dca958de74f15000", "vda+bwd": "5f6db7dd157c4bc6", "common": "a24de8342071a471"
 }
 
 
