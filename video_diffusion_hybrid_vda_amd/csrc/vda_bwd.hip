@@ -622,25 +622,26 @@ __global__ __launch_bounds__(256) void bgemm_mfma_resident_kernel(BGemm p, int t
 // C1 = dA_t + dA_t^T (symmetric) and C2 = dB_t from cdb[frame][0 / 1] (fp32).
 // One workgroup per frame reads K_t and V_t once and writes dK_t and dV_t once.
 // C1 and C2 sit in LDS as bf16 hi + lo pairs (four 32 KB matrices, 16-byte
-// chunk c of row r at c ^ (((r & 7) << 1) | ((r >> 3) & 1))); each wave takes
-// 32-token tiles and computes the transposed outputs dK^T, dV^T (rows = output
-// dimension, columns = tokens) on v_mfma_f32_32x32x16_bf16, the token rows of
-// K and V being the B operand straight from HBM (the next tile's rows are
-// loaded while the current one is multiplied).  The A operand is a 16-byte
-// row read of C1 or C2 (C1 = C1^T) for the K terms and, for V C2, a
-// transposed read of C2 (ds_read_b64_tr_b16: lane half h gets rows
-// 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3 of one column), so V is loaded
+// chunk c of row r at c ^ (((r & 7) << 1) | ((r >> 3) & 1))).  Eight waves (two
+// per SIMD) take 16-token tiles and compute the transposed outputs dK^T, dV^T
+// (rows = output dimension, columns = tokens) on v_mfma_f32_16x16x32_bf16,
+// the token rows of K and V being the B operand straight from HBM (the next
+// tile's rows are loaded while the current one is multiplied).  The A operand
+// is a 16-byte row read of C1 or C2 (C1 = C1^T) for the K terms and, for
+// V C2, two transposed reads of C2 (ds_read_b64_tr_b16: lane group g gets rows
+// 32 ks + 4 g + 0..3 and 32 ks + 16 + 4 g + 0..3 of one column), so V is loaded
 // in that dimension order.  Every fp32 operand gives two products (hi, lo);
-// K and V are exact in bf16.
+// K and V are exact in bf16.  (Four waves of 32-token tiles on 32x32x16
+// products read C1 and C2 half as often per token, but need 482 registers,
+// one wave per SIMD.)
 namespace kvg {
-constexpr int D = 128, ROWB = D * 2, MATB = D * ROWB;
+constexpr int D = 128, ROWB = D * 2, MATB = D * ROWB, TT = 16, NW = 8;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 }
 
-__global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __restrict__ k,
+__global__ __launch_bounds__(512) void kv_grad_bf16_d128_kernel(const bf16* __restrict__ k,
                                                                 const bf16* __restrict__ v,
                                                                 const float* __restrict__ cdb,
                                                                 const float* __restrict__ beta,
@@ -650,11 +651,11 @@ __global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __re
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * MATB];   // C1 hi, C1 lo, C2 hi, C2 lo
   const int f = blockIdx.x;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
+  const int g = lane / 16, j16 = lane % 16;
 
   // C1, C2 -> hi / lo bf16 in LDS, 8 elements (one 16-byte chunk) per step
   const float* c1 = cdb + (int64_t)f * 2 * D * D;
-  for (int u = tid; u < 2 * D * (D / 8); u += 256) {
+  for (int u = tid; u < 2 * D * (D / 8); u += 512) {
     const int m = u / (D * D / 8), rem = u % (D * D / 8), r = rem / 16, c = rem % 16;
     const float* src = c1 + m * D * D + r * D + c * 8;
     const float4 a = *reinterpret_cast<const float4*>(src);
@@ -676,104 +677,98 @@ __global__ __launch_bounds__(256) void kv_grad_bf16_d128_kernel(const bf16* __re
   const int64_t row0 = (int64_t)(f / T) * Lt + (int64_t)(f % T) * N;   // first token row of the frame
   const bf16* kf = k + row0 * D;
   const bf16* vf = v + row0 * D;
-  const int ntile = (N + 31) / 32;
+  const int ntile = (N + TT - 1) / TT;
 
-  // A-operand addresses (bytes into lds): plain reads of row n = 32 dt + l32,
-  // chunk 2 s + h (the swizzle depends on n % 16 only, so dt moves the address
-  // by the constant 32 dt rows); transposed reads of C2, rows rA / rA + 8 of
-  // each 16-row step (s moves them by the constant 16 s rows)
-  int aoff[8];
+  // A-operand addresses (bytes into lds): row reads of row 16 nb + j16, chunk
+  // 4 ks + g (the swizzle depends on the row mod 16, so nb moves the address by
+  // a constant); transposed reads: lane j16 of group g reads row 4 g + j16 / 4
+  // of a 16-row step, columns 16 nb + 4 (j16 % 4) .. + 3, and receives column
+  // 16 nb + j16 of rows 4 g .. 4 g + 3
+  int aoff[4];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) aoff[s] = l32 * ROWB + swz(l32, 2 * s + h) * 16;
-  int troff[4][2];
-  {
-    const int rA = 4 * (g >> 1) + (j16 >> 2);
+  for (int ks = 0; ks < 4; ++ks) aoff[ks] = j16 * ROWB + swz(j16, 4 * ks + g) * 16;
+  int toff[8];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int dcol = dt * 32 + 16 * (g & 1) + 4 * (j16 & 3);
-      const int cch = dcol >> 3, off = (dcol & 7) * 2;
-      troff[dt][0] = 2 * MATB + rA * ROWB + swz(rA, cch) * 16 + off;
-      troff[dt][1] = 2 * MATB + (rA + 8) * ROWB + swz(rA + 8, cch) * 16 + off;
-    }
+  for (int nb = 0; nb < 8; ++nb) {
+    const int r = 4 * g + j16 / 4;
+    toff[nb] = 2 * MATB + r * ROWB + swz(r, 2 * nb + (j16 % 4) / 2) * 16 + 8 * (j16 % 2);
   }
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   auto tr = [&](int off) { return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)lds + off)); };
   auto rd = [&](int off) { return *reinterpret_cast<const bf16x8*>(lds + off); };
 
-  // token operands of one tile: K row chunk (16 s + 8 h .. + 7) and V in the transposed read's order
-  bf16x8 kb[2][8];
-  u32x2 va[2][8], vb[2][8];
+  // token operands of one tile: K dims 32 ks + 8 g .. + 7, V dims 32 ks + 4 g .. + 3
+  // and 32 ks + 16 + 4 g .. + 3 (the transposed reads' order)
+  bf16x8 kb[2][4];
+  u32x2 va[2][4], vb[2][4];
   auto load = [&](int buf, int tile) {
-    const int t = min(32 * tile + l32, N - 1);   // rows past the frame repeat its last row (not stored)
+    const int t = min(TT * tile + j16, N - 1);   // rows past the frame repeat its last row (not stored)
     const bf16* kr = kf + (int64_t)t * D;
     const bf16* vr = vf + (int64_t)t * D;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kb[buf][s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s + 8 * h);
-      va[buf][s] = *reinterpret_cast<const u32x2*>(vr + 16 * s + 4 * h);
-      vb[buf][s] = *reinterpret_cast<const u32x2*>(vr + 16 * s + 8 + 4 * h);
+    for (int ks = 0; ks < 4; ++ks) {
+      kb[buf][ks] = *reinterpret_cast<const bf16x8*>(kr + 32 * ks + 8 * g);
+      va[buf][ks] = *reinterpret_cast<const u32x2*>(vr + 32 * ks + 4 * g);
+      vb[buf][ks] = *reinterpret_cast<const u32x2*>(vr + 32 * ks + 16 + 4 * g);
     }
   };
   auto compute = [&](int buf, int tile) {
-    f32x16 ak[4], av[4];
+    f32x4 ak[8], av[8];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      ak[dt] = f32x16{};
-      av[dt] = f32x16{};
+    for (int nb = 0; nb < 8; ++nb) {
+      ak[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      av[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 kk = kb[buf][s];
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[buf][s], vb[buf][s], 0, 1, 2, 3));
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kk = kb[buf][ks];
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va[buf][ks], vb[buf][ks], 0, 1, 2, 3));
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        // keep each step's LDS reads next to its products (hoisting them all
-        // would need several hundred registers)
+      for (int nb = 0; nb < 8; ++nb) {
+        // keep each step's LDS reads next to its products
         asm volatile("" ::: "memory");
-        const int ao = aoff[s] + dt * 32 * ROWB;
+        const int ao = aoff[ks] + nb * 16 * ROWB;
         const bf16x8 c1h = rd(ao), c1l = rd(MATB + ao), c2h = rd(2 * MATB + ao), c2l = rd(3 * MATB + ao);
-        const int to = s * 16 * ROWB;
-        const i16x4 th0 = tr(troff[dt][0] + to), th1 = tr(troff[dt][1] + to);
-        const i16x4 tl0 = tr(troff[dt][0] + MATB + to), tl1 = tr(troff[dt][1] + MATB + to);
+        const int to = toff[nb] + ks * 32 * ROWB;
+        const i16x4 th0 = tr(to), th1 = tr(to + 16 * ROWB);
+        const i16x4 tl0 = tr(to + MATB), tl1 = tr(to + MATB + 16 * ROWB);
         const bf16x8 c2th = __builtin_bit_cast(bf16x8, __builtin_shufflevector(th0, th1, 0, 1, 2, 3, 4, 5, 6, 7));
         const bf16x8 c2tl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tl0, tl1, 0, 1, 2, 3, 4, 5, 6, 7));
-        ak[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1h, kk, ak[dt], 0, 0, 0);
-        av[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c2h, kk, av[dt], 0, 0, 0);
-        ak[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c2th, vv, ak[dt], 0, 0, 0);
-        av[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c2l, kk, av[dt], 0, 0, 0);
-        ak[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1l, kk, ak[dt], 0, 0, 0);
-        ak[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c2tl, vv, ak[dt], 0, 0, 0);
+        ak[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1h, kk, ak[nb], 0, 0, 0);
+        av[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c2h, kk, av[nb], 0, 0, 0);
+        ak[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c2th, vv, ak[nb], 0, 0, 0);
+        av[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c2l, kk, av[nb], 0, 0, 0);
+        ak[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1l, kk, ak[nb], 0, 0, 0);
+        ak[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c2tl, vv, ak[nb], 0, 0, 0);
       }
     }
-    // ak[dt][r] = dK^T(n = 32 dt + 8 (r / 4) + 4 h + r % 4, token 32 tile + l32)
-    const int t = 32 * tile + l32;
+    // ak[nb][e] = dK^T(n = 16 nb + 4 g + e, token 16 tile + j16)
+    const int t = TT * tile + j16;
     if (t < N) {
       bf16* dkr = dk + (row0 + t) * D;
       bf16* dvr = dv + (row0 + t) * D;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int nb = 0; nb < 8; ++nb) {
+        const int n = 16 * nb + 4 * g;
+        bf16x4 ok, ov;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = 32 * dt + 8 * q + 4 * h;
-          bf16x4 ok, ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ok[e] = (bf16)(bt * ak[dt][4 * q + e]);
-            ov[e] = (bf16)(bt * av[dt][4 * q + e]);
-          }
-          *reinterpret_cast<bf16x4*>(dkr + n) = ok;
-          *reinterpret_cast<bf16x4*>(dvr + n) = ov;
+        for (int e = 0; e < 4; ++e) {
+          ok[e] = (bf16)(bt * ak[nb][e]);
+          ov[e] = (bf16)(bt * av[nb][e]);
         }
+        *reinterpret_cast<bf16x4*>(dkr + n) = ok;
+        *reinterpret_cast<bf16x4*>(dvr + n) = ov;
+      }
     }
   };
   int tile = wave;
   if (tile < ntile) load(0, tile);
-  for (; tile < ntile; tile += 8) {
-    if (tile + 4 < ntile) load(1, tile + 4);
+  for (; tile < ntile; tile += 2 * NW) {
+    if (tile + NW < ntile) load(1, tile + NW);
     compute(0, tile);
-    if (tile + 4 >= ntile) break;
-    if (tile + 8 < ntile) load(0, tile + 8);
-    compute(1, tile + 4);
+    if (tile + NW >= ntile) break;
+    if (tile + 2 * NW < ntile) load(0, tile + 2 * NW);
+    compute(1, tile + NW);
   }
 }
 
@@ -1093,7 +1088,7 @@ hipError_t launch_kv_grad(const void* k, const void* v, const float* cdb, const 
                           int64_t nf, int T, int N, int Lt, hipStream_t st) {
   if (nf <= 0) return hipSuccess;
   if (nf > 0x7FFFFFFF) return hipErrorInvalidValue;
-  kv_grad_bf16_d128_kernel<<<(unsigned)nf, 256, 0, st>>>((const bf16*)k, (const bf16*)v, cdb, beta, (bf16*)dk,
+  kv_grad_bf16_d128_kernel<<<(unsigned)nf, 512, 0, st>>>((const bf16*)k, (const bf16*)v, cdb, beta, (bf16*)dk,
                                                          (bf16*)dv, T, N, Lt);
   return hipGetLastError();
 }
