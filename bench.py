@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27819645708,
-        "window_attn": 275370810276,
-        "anchor_merge": 710164081,
-        "vda_gram": 5374831713,
-        "vda_solve": 321038878,
-        "vda_scan": 946987442,
-        "vda_readout": 7901758371,
-        "out_gemm": 25298151435
+        "gate_gemm": 27821937937,
+        "window_attn": 251342840093,
+        "anchor_merge": 710121911,
+        "vda_gram": 5374826232,
+        "vda_solve": 321037809,
+        "vda_scan": 947041286,
+        "vda_readout": 7901742881,
+        "out_gemm": 25347882158
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 181743735168,
-        "mxfp8_quantize": 7659463917
+        "window_attn": 184573674345,
+        "mxfp8_quantize": 7659452035
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284761330,
-        "bwd_token": 23390862362,
-        "bwd_scan": 1274318175,
-        "bwd_frame": 5572815120,
-        "bwd_kv_gemm": 10439832235
+        "bwd_recompute": 7284715161,
+        "bwd_token": 23391546169,
+        "bwd_scan": 1274515369,
+        "bwd_frame": 5574373998,
+        "bwd_kv_gemm": 10452168055
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145294717,
-        "vda_solve": 11072315,
-        "vda_scan": 22079609,
-        "vda_readout": 186668292
+        "vda_gram": 145294653,
+        "vda_solve": 11072312,
+        "vda_scan": 22079604,
+        "vda_readout": 186677323
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11459926782,
-        "window_attn": 112662225728,
-        "anchor_merge": 401553147,
-        "vda_gram": 2213163048,
-        "vda_solve": 132254496,
-        "vda_scan": 379685728,
-        "vda_readout": 3253839466,
-        "out_gemm": 10435461128
+        "gate_gemm": 11459795532,
+        "window_attn": 110081560678,
+        "anchor_merge": 401552979,
+        "vda_gram": 2213162312,
+        "vda_solve": 132271552,
+        "vda_scan": 379797606,
+        "vda_readout": 3253838539,
+        "out_gemm": 10435156627
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -99,7 +99,7 @@ SOURCE_GROUPS = {
 }
 SOURCE_SHA = {
     "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "35070dfbe11f61a9", "mxfp8": "8cdcfa773199d9a4",
-    "bwd": "dca958de74f15000", "vda+bwd": "5f6db7dd157c4bc6", "common": "a24de8342071a471"
+    "bwd": "f6e01e04dfa367f0", "vda+bwd": "92c7fbae5d0a0a3f", "common": "a24de8342071a471"
 }
 
 
