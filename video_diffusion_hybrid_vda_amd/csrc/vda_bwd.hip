@@ -59,8 +59,10 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
   static_assert(!MF || (std::is_same<TA, float>::value && std::is_same<TB, float>::value), "fp32 MFMA takes fp32");
   // fp32 MFMA reads k and k + 1 of one column in the two lane halves: rows 32 banks apart
   constexpr int LD = MF ? 64 + 32 : LDT;
-  __shared__ float As[BK][LD];
-  __shared__ float Bs[BK][LD];
+  constexpr int KB = BK;                         // k slab (32 deep measured slower on the matrix unit)
+  constexpr int PER = BM * KB / 256;             // slab elements per thread and operand
+  __shared__ float As[KB][LD];
+  __shared__ float Bs[KB][LD];
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles = ((p.M + BM - 1) / BM) * tiles_n;
   const int64_t z = blockIdx.x / tiles;
@@ -80,16 +82,16 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
   // element r of this thread's share of a slab: (row of the tile, k in the slab)
   auto a_pos = [&](int r, int& mm, int& kk) {
     const int e = tid + 256 * r;
-    if (p.a_kfast) { kk = e % BK; mm = e / BK; } else { mm = e % BM; kk = e / BM; }
+    if (p.a_kfast) { kk = e % KB; mm = e / KB; } else { mm = e % BM; kk = e / BM; }
   };
   auto b_pos = [&](int r, int& nn, int& kk) {
     const int e = tid + 256 * r;
-    if (p.b_nfast) { nn = e % BN; kk = e / BN; } else { kk = e % BK; nn = e / BK; }
+    if (p.b_nfast) { nn = e % BN; kk = e / BN; } else { kk = e % KB; nn = e / KB; }
   };
-  float ra[4], rb[4];
+  float ra[PER], rb[PER];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < PER; ++r) {
       int mm, kk;
       a_pos(r, mm, kk);
       const int m = m0 + mm, k = k0 + kk;
@@ -124,10 +126,10 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 
   load(0);
-  for (int k0 = 0; k0 < p.K; k0 += BK) {
+  for (int k0 = 0; k0 < p.K; k0 += KB) {
     __syncthreads();   // the previous slab has been read
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < PER; ++r) {
       int mm, kk;
       a_pos(r, mm, kk);
       As[kk][mm] = ra[r];
@@ -136,14 +138,14 @@ __global__ __launch_bounds__(256) void bgemm_kernel(BGemm p) {
       Bs[kk][nn] = rb[r];
     }
     __syncthreads();
-    if (k0 + BK < p.K) load(k0 + BK);
+    if (k0 + KB < p.K) load(k0 + KB);
     if constexpr (MF) {
 #pragma unroll
-      for (int s2 = 0; s2 < BK / 2; ++s2)
+      for (int s2 = 0; s2 < KB / 2; ++s2)
         accm = __builtin_amdgcn_mfma_f32_32x32x2f32(As[2 * s2 + h][wm + l32], Bs[2 * s2 + h][wn + l32], accm, 0, 0, 0);
     } else {
 #pragma unroll
-      for (int kk = 0; kk < BK; ++kk) {
+      for (int kk = 0; kk < KB; ++kk) {
         float av[4], bv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = As[kk][ty + 16 * i];
@@ -813,6 +815,15 @@ __device__ float kUnitWeight[128] = {   // global (not constant) memory: loads s
 // and q rows (12 KB): 160 KB, one workgroup per CU.  (With 32-token tiles on
 // 32x32x16 products, which read S half as often, one wave per SIMD needs all
 // 512 registers and runs the phases one after another: 8.6 against 7.5 ms.)
+// x summed over lanes l, l ^ 16, l ^ 32 and l ^ 48 with two lane swaps (each
+// returns the pair {own, partner} in some order, so their sum is exact and
+// the same in every lane of the group)
+__device__ __forceinline__ float sum_lanes_16_32(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 namespace tkg {
 constexpr int D = 128, ROWB = 256, MATB = D * ROWB, TT = 16, TILEB = TT * ROWB;
 constexpr int NW = 8, STG = 2 * MATB, STGW = 3 * TILEB;
@@ -934,8 +945,7 @@ __global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
       for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
         for (int e = 0; e < 4; ++e) ss += ua[ib][e] * ua[ib][e];
-      ss += __shfl_xor(ss, 16, kWave);
-      ss += __shfl_xor(ss, 32, kWave);
+      ss = sum_lanes_16_32(ss);
       const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
       const float vm = valid ? inv : 0.f;      // tokens past the frame contribute nothing
       float gw[8][4];
@@ -954,8 +964,7 @@ __global__ __launch_bounds__(512) void tok_grad_bf16_d128_kernel(
           dw[ib][e] += rr * dv;
         }
       }
-      gr += __shfl_xor(gr, 16, kWave);
-      gr += __shfl_xor(gr, 32, kWave);
+      gr = sum_lanes_16_32(gr);
       const float c = gr * inv * inv * (1.f / D);   // mean(g r) / rho
       // du = (g - r mean(g r)) / rho as hi / lo bf16: B operand of dq^T for the
       // 32-dim step ks in the k order (dims 32 ks + 4 g + 0..3, 32 ks + 16 + 4 g + 0..3),
