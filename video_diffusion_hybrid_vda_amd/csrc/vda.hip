@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void vda_gram_bf16_kernel(const bf16* __restri
 // AM holds A_t on entry and M_t^T on exit (row j = column j of M_t, so the
 // scan reads contiguous runs of a column).
 template <int D>
-__global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM) {
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(3))) void vda_solve_kernel(float* __restrict__ AM) {
   __shared__ __attribute__((aligned(16))) float rowb[2][2 * D];
   const int64_t f = blockIdx.x;
   float* am = AM + f * D * D;
@@ -395,12 +395,18 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
   // (all register indices stay compile-time constants): the update writes
   // row i+1 into slot i and the normalised pivot row goes to slot D-1.  After
   // D steps every row is back in its place.
+  // Each thread publishes its next pivot-row entry as soon as it is formed
+  // (the first update of the step), so that the LDS write's latency runs
+  // beside the rest of the step's products; the other buffer was last read
+  // before this step's barrier.
   const float sgn = c < D ? 1.f : -1.f;
+  rowb[0][c] = sgn * a[0];
   for (int k = 0; k < D; ++k) {
     const int buf = k & 1;
-    rowb[buf][(c - k) & (2 * D - 1)] = sgn * a[0];
     __syncthreads();
     const float4* rb = reinterpret_cast<const float4*>(rowb[buf]);
+    float* next = rowb[buf ^ 1];
+    const int nslot = (c - k - 1) & (2 * D - 1);
     float x;
     if constexpr (D <= 64) {
       // all D/4 reads of the pivot column issued before the products use them
@@ -409,25 +415,38 @@ __global__ __launch_bounds__(2 * D) void vda_solve_kernel(float* __restrict__ AM
 #pragma unroll
       for (int j = 0; j < D / 4; ++j) cv[j] = rb[j];
       x = a[0] / cv[0].x;
+      a[0] = a[1] - cv[0].y * x;
+      if (k + 1 < D) next[nslot] = sgn * a[0];
+      a[1] = a[2] - cv[0].z * x;
+      a[2] = a[3] - cv[0].w * x;
 #pragma unroll
-      for (int j = 0; j < D / 4; ++j) {
+      for (int j = 1; j < D / 4; ++j) {
         const int i = 4 * j;
-        if (i > 0) a[i - 1] = a[i] - cv[j].x * x;
+        a[i - 1] = a[i] - cv[j].x * x;
         a[i] = a[i + 1] - cv[j].y * x;
         a[i + 1] = a[i + 2] - cv[j].z * x;
         a[i + 2] = a[i + 3] - cv[j].w * x;
       }
       __builtin_amdgcn_sched_group_barrier(0x100, D / 4, 0);   // the reads first
-      __builtin_amdgcn_sched_group_barrier(0x2, D + 16, 0);    // then the vector work
+      __builtin_amdgcn_sched_group_barrier(0x2, 12, 0);        // the division and the first update
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // its publication
+      __builtin_amdgcn_sched_group_barrier(0x2, D + 16, 0);    // then the rest of the vector work
     } else {
       // at head_dim 128 the compiler's own interleave keeps 3 workgroups per
       // CU (more reads in flight cost occupancy and measured slower)
       x = a[0] / rowb[buf][0];
+      {
+        const float4 cv = rb[0];
+        a[0] = a[1] - cv.y * x;
+        if (k + 1 < D) next[nslot] = sgn * a[0];
+        a[1] = a[2] - cv.z * x;
+        a[2] = a[3] - cv.w * x;
+      }
 #pragma unroll
-      for (int j = 0; j < D / 4; ++j) {
+      for (int j = 1; j < D / 4; ++j) {
         const int i = 4 * j;
         const float4 cv = rb[j];
-        if (i > 0) a[i - 1] = a[i] - cv.x * x;
+        a[i - 1] = a[i] - cv.x * x;
         a[i] = a[i + 1] - cv.y * x;
         a[i + 1] = a[i + 2] - cv.z * x;
         a[i + 2] = a[i + 3] - cv.w * x;
