@@ -84,6 +84,9 @@ CASES = [
     ("T1_N9_d64_f32", VdnConfig(1, 1, 64, 1, 9, dtype="f32", seed=85)),
     ("H2_T6_N20_d32_ctx9_bf16", VdnConfig(1, 2, 32, 6, 20, dtype="bf16", context_tokens=9, seed=86)),
     ("B2H2_T7_N300_d128_ctx5_bf16", VdnConfig(2, 2, 128, 7, 300, dtype="bf16", context_tokens=5, seed=88)),
+    # one partial 16-token tile per frame: seven of the eight waves of the
+    # bf16 token-side and dK/dV kernels have no tile
+    ("T3_N5_d128_bf16", VdnConfig(1, 1, 128, 3, 5, dtype="bf16", seed=89)),
 ]
 
 
