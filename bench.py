@@ -50,41 +50,41 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27821937937,
-        "window_attn": 251342840093,
-        "anchor_merge": 710121911,
-        "vda_gram": 5374826232,
-        "vda_solve": 321037809,
-        "vda_scan": 947041286,
-        "vda_readout": 7901742881,
-        "out_gemm": 25347882158
+        "gate_gemm": 27820728087,
+        "window_attn": 263537916889,
+        "anchor_merge": 710211715,
+        "vda_gram": 5374836818,
+        "vda_solve": 321028643,
+        "vda_scan": 946765658,
+        "vda_readout": 7901747105,
+        "out_gemm": 25293562783
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 184573674345,
-        "mxfp8_quantize": 7659452035
+        "window_attn": 178920871176,
+        "mxfp8_quantize": 7659488670
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284715161,
-        "bwd_token": 23391546169,
-        "bwd_scan": 1274515369,
-        "bwd_frame": 5574373998,
-        "bwd_kv_gemm": 10452168055
+        "bwd_recompute": 7284559293,
+        "bwd_token": 23391076980,
+        "bwd_scan": 1274393977,
+        "bwd_frame": 5571987766,
+        "bwd_kv_gemm": 10454345912
     },
     "VDA scan B1 H8 d64 T42 N1560": {
-        "vda_gram": 145294653,
-        "vda_solve": 11072312,
-        "vda_scan": 22079604,
-        "vda_readout": 186677323
+        "vda_gram": 145294669,
+        "vda_solve": 11091768,
+        "vda_scan": 22079605,
+        "vda_readout": 186671193
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11459795532,
-        "window_attn": 110081560678,
-        "anchor_merge": 401552979,
-        "vda_gram": 2213162312,
-        "vda_solve": 132271552,
-        "vda_scan": 379797606,
-        "vda_readout": 3253838539,
-        "out_gemm": 10435156627
+        "gate_gemm": 11459483253,
+        "window_attn": 111576329763,
+        "anchor_merge": 401566332,
+        "vda_gram": 2213161536,
+        "vda_solve": 132286919,
+        "vda_scan": 379572363,
+        "vda_readout": 3253903568,
+        "out_gemm": 10430359006
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,8 +98,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "35070dfbe11f61a9", "mxfp8": "8cdcfa773199d9a4",
-    "bwd": "f6e01e04dfa367f0", "vda+bwd": "92c7fbae5d0a0a3f", "common": "a24de8342071a471"
+    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "71ddd2f45e486dc2", "mxfp8": "8cdcfa773199d9a4",
+    "bwd": "cdf096da5a826c0d", "vda+bwd": "633b208094b4abf4", "common": "a24de8342071a471"
 }
 
 
