@@ -88,7 +88,7 @@ COUNTER_TRAFFIC = {
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
-    "gate_gemm": "gemm", "out_gemm": "gemm", "window_attn": "window", "anchor_merge": "window",
+    "gate_gemm": "gemm", "out_gemm": "gemm", "window_attn": "window", "anchor_merge": "window", "key_norms": "window",
     "vda_gram": "vda", "vda_solve": "vda", "vda_scan": "vda", "vda_readout": "vda", "mxfp8_quantize": "mxfp8",
     "bwd_recompute": "vda+bwd", "bwd_token": "bwd",
     "bwd_scan": "bwd", "bwd_frame": "bwd", "bwd_kv_gemm": "bwd",
@@ -189,6 +189,8 @@ def phase_rooflines(cfg, phases, gated=True, mode=""):
 
     # K and V read once; A_t and B_t written (fp32)
     hbm("vda_gram", 2 * tok + 2 * dd4)
+    # the softmax kernel's fixed-maximum bound: K read once
+    hbm("key_norms", tok)
     # MXFP8 mode: q and k read (bf16), their codes (1 byte per element) and scales (1 per 32) written
     hbm("mxfp8_quantize", 2 * tok + 2 * (tok // es) * (1 + 1 / 32))
     # Q, gate (when given) and output once; both directions' states once per frame

@@ -124,8 +124,9 @@ typedef struct vdn_shape {
 
 /* Bytes of device workspace `op` needs for `shape` (0 on an invalid shape,
  * with vdn_last_error() set).  The workspace holds per-frame statistics,
- * transitions and states of the linear branch, anchor-row partial results of
- * the softmax branch, transposed weights, gates and branch outputs. */
+ * transitions and states of the linear branch, anchor-row partial results,
+ * per-head key-norm maxima and per-work-item flags of the softmax branch,
+ * transposed weights, gates and branch outputs. */
 size_t vdn_workspace_bytes(const vdn_shape* shape, int op); /* >= 256 when valid */
 
 /* Full hybrid attention forward (10100.com article, 方法概述 parts 1-3):

@@ -203,7 +203,7 @@ VdaBwdLayout vda_bwd_layout(const vdn_shape* s) {
 }
 
 struct AttnLayout {
-  size_t part_o, part_ml, qc, qs, kc, ks, total;
+  size_t part_o, part_ml, qc, qs, kc, ks, kmax, fallback, total;
 };
 // with softmax_mxfp8, q and k quantised to MXFP8 (codes [B, H, Lt, d], scales [B, H, Lt, d / 32])
 AttnLayout attn_layout(const vdn_shape* s, const AttnParams& p) {
@@ -217,6 +217,11 @@ AttnLayout attn_layout(const vdn_shape* s, const AttnParams& p) {
   l.qs = off; off = align_up(off + elems / 32);
   l.kc = off; off = align_up(off + elems);
   l.ks = off; off = align_up(off + elems / 32);
+  // the bf16 head_dim-128 softmax kernel's fixed maximum: key-norm maxima and
+  // the per-work-item fallback marks
+  const bool fx = s->dtype == VDN_BF16 && s->head_dim == 128;
+  l.kmax = off; off = align_up(off + (fx ? (size_t)p.B * p.H * kKeyNormParts * 4 : 0));
+  l.fallback = off; off = align_up(off + (fx ? (size_t)p.total : 0));
   l.total = off;
   return l;
 }
@@ -291,7 +296,7 @@ int check_params(const vdn_shape* s, const float* gamma, const float* beta, char
 enum Phase {
   kPhTranspose, kPhGateGemm, kPhWindowAttn, kPhAnchorMerge, kPhGram, kPhSolve, kPhScan,
   kPhReadout, kPhOutGemm, kPhQuantize, kPhBwdRecompute, kPhBwdU, kPhBwdRms, kPhBwdDq, kPhBwdDs,
-  kPhBwdScan, kPhBwdFrame, kPhBwdKv, kPhBwdDw, kPhBwdToken, kNumPhases
+  kPhBwdScan, kPhBwdFrame, kPhBwdKv, kPhBwdDw, kPhBwdToken, kPhKeyNorms, kNumPhases
 };
 const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "window_attn",
                                              "anchor_merge",      "vda_gram",  "vda_solve",
@@ -299,7 +304,7 @@ const char* const kPhaseNames[kNumPhases] = {"transpose_weights", "gate_gemm", "
                                              "mxfp8_quantize", "bwd_recompute", "bwd_u_gemm",
                                              "bwd_rms",        "bwd_dq_gemm", "bwd_ds_gemm",
                                              "bwd_scan",       "bwd_frame",   "bwd_kv_gemm",
-                                             "bwd_dw",         "bwd_token"};
+                                             "bwd_dw",         "bwd_token",   "key_norms"};
 
 struct Timer {
   std::mutex mu;
@@ -602,6 +607,15 @@ int run_attn(const vdn_shape* s, const void* q, const void* k, const void* v, co
   } else if (mx) {
     p.qs = qs;
     p.ks = ks;
+  }
+  if (!mx && s->dtype == VDN_BF16 && s->head_dim == 128 && p.total > 0) {
+    p.kmax = (float*)(ws + l.kmax);
+    p.kmax_parts = kKeyNormParts;
+    p.fallback = (unsigned char*)(ws + l.fallback);
+    ph = phase_begin(kPhKeyNorms, st);
+    e = launch_key_norm_max(k, (float*)(ws + l.kmax), (int64_t)p.B * p.H, p.Lt, kKeyNormParts, st);
+    phase_end(ph, st);
+    if (e != hipSuccess) return hip_fail(e, "key norm launch");
   }
   ph = phase_begin(kPhWindowAttn, st);
   e = mx ? launch_window_attn_mxfp8(p, st) : launch_window_attn(s->dtype, s->head_dim, p, st);

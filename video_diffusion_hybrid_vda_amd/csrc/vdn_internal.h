@@ -59,6 +59,9 @@ struct AttnParams {
   float scale_log2;
   const void* qs;     // MXFP8 kernel: E8M0 scales of q and k [B, H, Lt, 4] (q, k hold E4M3 codes)
   const void* ks;
+  const float* kmax;  // nullable: max squared key norm of each (batch, head) in kmax_parts parts
+  int kmax_parts;
+  unsigned char* fallback;   // with kmax: per work item, 1 = needs the running-maximum kernel
 };
 
 enum GemmEpilogue { kEpiStore = 0, kEpiSigmoid = 1 };
@@ -70,6 +73,10 @@ hipError_t launch_gemm_nt(int dtype, int epi, const void* A, const void* Bt, voi
                           int N, int K, int64_t lda, int64_t ldb, int64_t ldc, hipStream_t st);
 hipError_t launch_window_attn(int dtype, int d, const AttnParams& p, hipStream_t st);
 hipError_t launch_attn_merge(int dtype, int d, const AttnParams& p, hipStream_t st);
+// per (batch, head) and part of its Lt rows: the largest squared L2 norm of a
+// key row (bf16, head_dim 128), out [B*H, parts]
+hipError_t launch_key_norm_max(const void* k, float* out, int64_t bh, int Lt, int parts, hipStream_t st);
+constexpr int kKeyNormParts = 64;
 // head_dim 128, bf16 v / gate / out; p.q, p.k E4M3 codes with scales p.qs, p.ks
 hipError_t launch_window_attn_mxfp8(const AttnParams& p, hipStream_t st);
 // MXFP8 (E4M3 codes, one E8M0 scale per 32 consecutive elements) of n_elems bf16 values

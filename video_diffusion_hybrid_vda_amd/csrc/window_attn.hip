@@ -376,6 +376,11 @@ constexpr int ROWB = D * 2;          // bytes per K/V row
 constexpr int TILEB = BN * ROWB;     // 16 KB
 constexpr int VBASE = STAGES * TILEB;   // V tiles follow the four K tiles
 constexpr float kRescaleSlack = 1.f;
+// log2 units: the largest bound the fixed maximum takes.  A row's scores then
+// lie within +-4 of 0, so no key outweighs another by more than 2^8 and no row
+// is peaked; peaked rows, whose error rests on the dominant probability being
+// exactly 1, keep the running maximum.
+constexpr float kFixedMaxCap = 4.f;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -564,6 +569,9 @@ __device__ __forceinline__ float halves_max(float x) {
 }
 }  // namespace v3
 
+// FIXED: the workgroups whose bound allows it run with a fixed maximum and
+// mark the others in p.fallback; !FIXED with p.fallback set runs only those.
+template <bool FIXED>
 __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p) {
   using namespace v3;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * 2 * TILEB];
@@ -572,6 +580,7 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int l32 = lane % 32, h = lane / 32, g = lane / 16, j16 = lane % 16;
 
+  if (!FIXED && p.fallback && !p.fallback[blockIdx.x]) return;   // done by the fixed-maximum launch
   const WorkItem wi = decode_work(p, BM);
   const int NL = p.Lt;   // rows per (batch, head)
   const bf16* Qb = (const bf16*)p.q + (int64_t)wi.bh * NL * D;
@@ -652,6 +661,46 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       qf[qt][ks] = ok ? *reinterpret_cast<const bf16x8*>(Qb + (int64_t)qrow * D + ks * 16 + h * 8)
                       : bf16x8{};
   }
+  // Fixed softmax maximum.  With the largest key norm of this (batch, head)
+  // (p.kmax), every score of query q satisfies c2 |q.k| <= c2 |q| max|k| = bnd,
+  // so p = 2^(c2 s - bnd) <= 1 without a running maximum, and since the row's
+  // largest score is >= -bnd its largest p is >= 2^(-2 bnd).  When bnd <=
+  // kFixedMaxCap for every query of the workgroup, it takes that path;
+  // otherwise it marks itself for the running-maximum launch.
+  const float c2 = p.scale_log2;
+  float bnd[QT] = {};
+  if constexpr (FIXED) {
+    float k2 = 0.f;
+    for (int i = 0; i < p.kmax_parts; ++i) k2 = fmaxf(k2, p.kmax[(int64_t)wi.bh * p.kmax_parts + i]);
+    const float kn = sqrtf(k2);
+    float worst = 0.f;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float s2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s2 += (float)qf[qt][ks][e] * (float)qf[qt][ks][e];
+      // lanes l and l ^ 32 hold the two halves of the query's dims
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s2), __float_as_uint(s2), false, false);
+      s2 = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      bnd[qt] = c2 * sqrtf(s2) * kn;
+      worst = fmaxf(worst, bnd[qt]);
+    }
+    // dense items (anchor-frame and context queries over every key) keep the
+    // running maximum: their rows are long, and their outputs are merged
+    // over key splits
+    const int lid = xcd_remap(blockIdx.x, p.total);
+    const bool dense = lid - (lid / p.tiles_per_bh) * p.tiles_per_bh >= p.n_window_tiles;
+    const bool unsafe = dense || __syncthreads_or(worst > kFixedMaxCap);
+    if (tid == 0) p.fallback[blockIdx.x] = unsafe ? 1 : 0;
+    if (unsafe) {
+      // this workgroup's tiles go to the running-maximum launch; no load may
+      // still write its LDS when it exits
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      return;
+    }
+  }
   // Q lives in the accumulator file (the score products read it from there)
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
@@ -665,8 +714,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   float mrun[QT], negm[QT], mtile[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = -INFINITY;
-    negm[qt] = INFINITY;
+    mrun[qt] = FIXED ? bnd[qt] : -INFINITY;
+    negm[qt] = FIXED ? -bnd[qt] : INFINITY;
     lsum[qt] = f32x4{};
     asm volatile("" : "+a"(lsum[qt]));
 #pragma unroll
@@ -683,7 +732,6 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
 #pragma unroll
     for (int e = 0; e < 8; ++e) sel[e] = one;
   }
-  const float c2 = p.scale_log2;
   // compute cursor: first key and interval end of the tile whose scores are
   // the most recent ones
   int civ = 0, ck0 = kb_of(0), cke = ke_of(0);
@@ -801,7 +849,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // after that, whose K fragments 0-2 this one reads; DST >= 0: issue the
   // loads of a tile into that stage.
   auto half_step = [&](const f32x16 (&cur)[QT], f32x16 (&nxt)[QT], auto SST, auto SKT, auto PST, auto PKT,
-                       auto NST, auto NKT, int dst) __attribute__((always_inline)) {
+                       auto NST, auto NKT, int dst, auto FX) __attribute__((always_inline)) {
+    constexpr bool kFixed = decltype(FX)::value;
     constexpr int ks_off = koffc(decltype(SST)::value, decltype(SKT)::value);
     constexpr int kn_off = koffc(decltype(NST)::value, decltype(NKT)::value);
     constexpr int v0_off = voffc(decltype(PST)::value, decltype(PKT)::value, 0);
@@ -883,11 +932,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       // ---- vector work
       if constexpr (m <= 20) static_for<units_before(m), units_before(m + 1)>(unit);
       // max of the next scores: the score chains end in slots 14 / 15
-      if constexpr (m == 21) {
+      if constexpr (kFixed) {
+      } else if constexpr (m == 21) {
         max3(mx[0], nxt[0][0], nxt[0][1], nxt[0][2]);
         max3(mx[1], nxt[1][0], nxt[1][1], nxt[1][2]);
       }
-      if constexpr (m >= 22 && m <= 28) {
+      if constexpr (!kFixed && m >= 22 && m <= 28) {
         constexpr int r = 3 + 2 * (m - 22);   // 3, 5, .., 15
         if constexpr (r < 15) {
           max3_acc(mx[0], nxt[0][r], nxt[0][r + 1]);
@@ -897,14 +947,21 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
           max_acc(mx[1], nxt[1][15]);
         }
       }
-      if constexpr (m == 29) halves_max_scaled(mx[0], c2);
-      if constexpr (m == 30) halves_max_scaled(mx[1], c2);
-      if constexpr (m == 32) grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
+      if constexpr (!kFixed && m == 29) halves_max_scaled(mx[0], c2);
+      if constexpr (!kFixed && m == 30) halves_max_scaled(mx[1], c2);
+      if constexpr (!kFixed && m == 32) grow = grow_mask(mx[0], mrun[0], mx[1], mrun[1]);
     };
     static_for<0, 36>(slot);
-    mtile[0] = mx[0];
-    mtile[1] = mx[1];
+    if constexpr (!kFixed) {
+      mtile[0] = mx[0];
+      mtile[1] = mx[1];
+    }
     return grow;
+  };
+  // between half steps on the fixed-maximum path: only a partial half tile's
+  // masking (keys >= lim)
+  auto boundary_fixed = [&](f32x16 (&sc)[QT], int lim) {
+    if (lim < 32) mask(sc, lim);
   };
 
   // Q and the first three tiles resident
@@ -927,8 +984,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   });
   // the vector unit reads the scores next: wait for the last products
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  half_max(sa);
-  boundary(sa, kn, outran() ? 1ull : 0ull);
+  if constexpr (FIXED) {
+    boundary_fixed(sa, kn);
+  } else {
+    half_max(sa);
+    boundary(sa, kn, outran() ? 1ull : 0ull);
+  }
   ds_k<koffc(0, 1)>(kf[0], koff[0]);
   ds_k<koffc(0, 1)>(kf[1], koff[1]);
   ds_k<koffc(0, 1)>(kf[2], koff[2]);
@@ -937,10 +998,11 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   // half of tile t+1 (for the last tile they come from a stale stage and are
   // never used).  Tile t sits in ring stage t % 4; the loop is unrolled over
   // the four stages so that every stage offset is a constant.
-  auto tile = [&](int t, auto S0, auto S1, int s3) __attribute__((always_inline)) {
-    const unsigned long long g1 = half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3);
-    boundary(sb, kn - 32, g1);
-    const unsigned long long g2 = half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1);
+  auto tile = [&](int t, auto S0, auto S1, int s3, auto FX) __attribute__((always_inline)) {
+    const unsigned long long g1 = half_step(sa, sb, S0, IC<1>{}, S0, IC<0>{}, S1, IC<0>{}, s3, FX);
+    if constexpr (decltype(FX)::value) boundary_fixed(sb, kn - 32);
+    else boundary(sb, kn - 32, g1);
+    const unsigned long long g2 = half_step(sb, sa, S1, IC<0>{}, S0, IC<1>{}, S1, IC<1>{}, -1, FX);
     advance();
     kn = min(BN, cke - ck0);
     // tile t+2's loads (issued one tile ago) are complete once at most the 8
@@ -948,17 +1010,23 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     // the stage of tile t for the next tile's loads
     __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
     __builtin_amdgcn_s_barrier();
-    if (t + 1 < ntiles) boundary(sa, kn, g2);
+    if (t + 1 < ntiles) {
+      if constexpr (decltype(FX)::value) boundary_fixed(sa, kn);
+      else boundary(sa, kn, g2);
+    }
   };
-  for (int t = 0; t < ntiles; t += 4) {
-    tile(t, IC<0>{}, IC<1>{}, 3);
-    if (t + 1 >= ntiles) break;
-    tile(t + 1, IC<1>{}, IC<2>{}, 0);
-    if (t + 2 >= ntiles) break;
-    tile(t + 2, IC<2>{}, IC<3>{}, 1);
-    if (t + 3 >= ntiles) break;
-    tile(t + 3, IC<3>{}, IC<0>{}, 2);
-  }
+  auto run = [&](auto FX) __attribute__((always_inline)) {
+    for (int t = 0; t < ntiles; t += 4) {
+      tile(t, IC<0>{}, IC<1>{}, 3, FX);
+      if (t + 1 >= ntiles) break;
+      tile(t + 1, IC<1>{}, IC<2>{}, 0, FX);
+      if (t + 2 >= ntiles) break;
+      tile(t + 2, IC<2>{}, IC<3>{}, 1, FX);
+      if (t + 3 >= ntiles) break;
+      tile(t + 3, IC<3>{}, IC<0>{}, 2, FX);
+    }
+  };
+  run(IC<FIXED>{});
   // no load may still write this workgroup's LDS when it exits; the last
   // products' results are read next
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
@@ -1635,9 +1703,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 template <typename T, int D>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t st) {
   if (p.total > 0) {
-    if (attn_uses_v2(sizeof(T) == 2 ? 1 : 0, D))
-      window_attn_bf16_d128_kernel<<<p.total, 256, 0, st>>>(p);
-    else
+    if (attn_uses_v2(sizeof(T) == 2 ? 1 : 0, D)) {
+      if (p.kmax && p.fallback) {
+        // fixed maximum where the key-norm bound allows it, then the running
+        // maximum for the workgroups it marked (the others return at once)
+        window_attn_bf16_d128_kernel<true><<<p.total, 256, 0, st>>>(p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        window_attn_bf16_d128_kernel<false><<<p.total, 256, 0, st>>>(p);
+      } else {
+        AttnParams q = p;
+        q.fallback = nullptr;
+        window_attn_bf16_d128_kernel<false><<<p.total, 256, 0, st>>>(q);
+      }
+    } else
       window_attn_kernel<T, D><<<p.total, 256, 0, st>>>(p);
   }
   return hipGetLastError();
@@ -1650,6 +1729,48 @@ static hipError_t launch_merge_t(const AttnParams& p, hipStream_t st) {
     const int blocks = p.B * p.H * ((p.dense_rows + RPB - 1) / RPB);
     attn_merge_kernel<T, D><<<blocks, 256, 0, st>>>(p);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// key_norm_max: the largest squared L2 norm of the key rows (bf16, head_dim
+// 128) of one part of one (batch, head), the bound behind the softmax
+// kernel's fixed maximum.  Four threads per 256-byte row, each summing four
+// 16-byte chunks (one 64-byte line), 64 rows per pass of the workgroup.
+__global__ __launch_bounds__(256) void key_norm_max_kernel(const bf16* __restrict__ k, float* __restrict__ out,
+                                                           int Lt, int parts) {
+  const int64_t bh = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
+  const int rpp = (Lt + parts - 1) / parts;
+  const int r0 = part * rpp, r1 = min(Lt, r0 + rpp);
+  const int tid = threadIdx.x, quarter = tid % 4;
+  const bf16* kb = k + bh * (int64_t)Lt * 128 + 32 * quarter;
+  float best = 0.f;
+  for (int r = r0 + tid / 4; r < r1; r += 64) {
+    const bf16* row = kb + (int64_t)r * 128;
+    float sq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(row + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += (float)x[e] * (float)x[e];
+    }
+    sq += __shfl_xor(sq, 1, kWave);
+    sq += __shfl_xor(sq, 2, kWave);
+    best = fmaxf(best, sq);
+  }
+#pragma unroll
+  for (int o = 4; o < kWave; o <<= 1) best = fmaxf(best, __shfl_xor(best, o, kWave));
+  __shared__ float red[4];
+  if (tid % kWave == 0) red[tid / kWave] = best;
+  __syncthreads();
+  if (tid == 0) out[bh * parts + part] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+hipError_t launch_key_norm_max(const void* k, float* out, int64_t bh, int Lt, int parts, hipStream_t st) {
+  if (bh <= 0 || Lt <= 0) return hipSuccess;
+  if (bh * parts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  key_norm_max_kernel<<<(unsigned)(bh * parts), 256, 0, st>>>((const bf16*)k, out, Lt, parts);
   return hipGetLastError();
 }
 
