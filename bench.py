@@ -50,41 +50,43 @@ PEAK_HBM_GBS = 8000.0
 # version the counters were taken on; after any change to them it is reported as null.
 COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
-        "gate_gemm": 27820728087,
-        "window_attn": 263537916889,
-        "anchor_merge": 710211715,
-        "vda_gram": 5374836818,
-        "vda_solve": 321028643,
-        "vda_scan": 946765658,
-        "vda_readout": 7901747105,
-        "out_gemm": 25293562783
+        "gate_gemm": 27818898264,
+        "key_norms": 2528918822,
+        "window_attn": 203484454385,
+        "anchor_merge": 710121606,
+        "vda_gram": 5374755541,
+        "vda_solve": 321107363,
+        "vda_scan": 947370309,
+        "vda_readout": 7901734562,
+        "out_gemm": 26780832459
     },
     "hybrid layer B1 H24 d128 T102 N4032 mxfp8": {
-        "window_attn": 178920871176,
-        "mxfp8_quantize": 7659488670
+        "window_attn": 183153494679,
+        "mxfp8_quantize": 7659447006
     },
     "hybrid layer B1 H24 d128 T102 N4032 bwd": {
-        "bwd_recompute": 7284559293,
-        "bwd_token": 23391076980,
-        "bwd_scan": 1274393977,
-        "bwd_frame": 5571987766,
-        "bwd_kv_gemm": 10454345912
+        "bwd_recompute": 7284527134,
+        "bwd_token": 23391046577,
+        "bwd_scan": 1274386041,
+        "bwd_frame": 5567570132,
+        "bwd_kv_gemm": 10453076697
     },
     "VDA scan B1 H8 d64 T42 N1560": {
         "vda_gram": 145294669,
         "vda_solve": 11091768,
         "vda_scan": 22079605,
-        "vda_readout": 186671193
+        "vda_readout": 186676697
     },
     "hybrid layer B1 H24 d128 T42 N4032": {
-        "gate_gemm": 11459483253,
-        "window_attn": 111576329763,
-        "anchor_merge": 401566332,
-        "vda_gram": 2213161536,
-        "vda_solve": 132286919,
-        "vda_scan": 379572363,
-        "vda_readout": 3253903568,
-        "out_gemm": 10430359006
+        "gate_gemm": 11459876583,
+        "key_norms": 1041320133,
+        "window_attn": 97153009489,
+        "anchor_merge": 401536381,
+        "vda_gram": 2213162048,
+        "vda_solve": 132282439,
+        "vda_scan": 379714950,
+        "vda_readout": 3253857106,
+        "out_gemm": 10500861517
     }
 }
 PHASE_SOURCES = {      # phase -> source group of its kernels
@@ -98,8 +100,8 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "5d640cb7bc3d22c2", "gemm": "ca60a1396242bbce", "vda": "71ddd2f45e486dc2", "mxfp8": "8cdcfa773199d9a4",
-    "bwd": "cdf096da5a826c0d", "vda+bwd": "633b208094b4abf4", "common": "a24de8342071a471"
+    "window": "b65573aca4b7cc64", "gemm": "ca60a1396242bbce", "vda": "71ddd2f45e486dc2", "mxfp8": "8cdcfa773199d9a4",
+    "bwd": "cdf096da5a826c0d", "vda+bwd": "633b208094b4abf4", "common": "9c829e344fbc21af"
 }
 
 
