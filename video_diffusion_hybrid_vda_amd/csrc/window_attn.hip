@@ -522,6 +522,10 @@ __device__ __forceinline__ void wait_lgkm() {
 __device__ __forceinline__ void fma_exp(float& t, float s, float c2, float negm) {
   asm volatile("v_fma_f32 %0, %1, %2, %3\n\tv_exp_f32 %0, %0" : "=&v"(t) : "v"(s), "s"(c2), "v"(negm));
 }
+// t = 2^s (fixed-maximum path: s is already the scaled score)
+__device__ __forceinline__ void exp_only(float& t, float s) {
+  asm volatile("v_exp_f32 %0, %1" : "=v"(t) : "v"(s));
+}
 __device__ __forceinline__ void cvt_pk(unsigned& w, float a, float b) {
   asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(a), "v"(b));
 }
@@ -700,6 +704,19 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
       return;
     }
+    // Every scaled score now lies in [-bnd, bnd] with bnd <= kFixedMaxCap, so
+    // 2^(c2 s) itself stays within [2^-4, 2^4]: no maximum needs subtracting
+    // (softmax is shift-invariant), and with q stored as bf16(c2 q) the score
+    // products deliver c2 s directly and p is one v_exp_f32 per score.  The
+    // extra rounding of c2 q moves a score by at most 2^-8 bnd <= 2^-6 (log2
+    // units), i.e. p by under 1.1% relative in the worst case of aligned
+    // signs; sharp rows, where that would count, never get here.
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qt][ks][e] = (bf16)((float)qf[qt][ks][e] * c2);
   }
   // Q lives in the accumulator file (the score products read it from there)
 #pragma unroll
@@ -714,8 +731,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
   float mrun[QT], negm[QT], mtile[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    mrun[qt] = FIXED ? bnd[qt] : -INFINITY;
-    negm[qt] = FIXED ? -bnd[qt] : INFINITY;
+    mrun[qt] = FIXED ? 0.f : -INFINITY;
+    negm[qt] = FIXED ? 0.f : INFINITY;
     lsum[qt] = f32x4{};
     asm volatile("" : "+a"(lsum[qt]));
 #pragma unroll
@@ -857,7 +874,8 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
     constexpr int v1_off = voffc(decltype(PST)::value, decltype(PKT)::value, 1);
     auto val = [&](auto J, int e) {
       constexpr int j = decltype(J)::value, s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
-      fma_exp(tt[(2 * j + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
+      if constexpr (kFixed) exp_only(tt[(2 * j + e) % 4], cur[qt][8 * s4 + 2 * w + e]);
+      else fma_exp(tt[(2 * j + e) % 4], cur[qt][8 * s4 + 2 * w + e], c2, negm[qt]);
     };
     auto cvt = [&](auto J) {
       constexpr int j = decltype(J)::value, s4 = j / 8, w = (j % 8) / 2, qt = j % 2;
