@@ -52,7 +52,7 @@ COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T102 N4032": {
         "gate_gemm": 27818898264,
         "key_norms": 2528918822,
-        "window_attn": 203484454385,
+        "window_attn": 202261787002,
         "anchor_merge": 710121606,
         "vda_gram": 5374755541,
         "vda_solve": 321107363,
@@ -80,7 +80,7 @@ COUNTER_TRAFFIC = {
     "hybrid layer B1 H24 d128 T42 N4032": {
         "gate_gemm": 11459876583,
         "key_norms": 1041320133,
-        "window_attn": 97153009489,
+        "window_attn": 97548988098,
         "anchor_merge": 401536381,
         "vda_gram": 2213162048,
         "vda_solve": 132282439,
@@ -100,7 +100,7 @@ SOURCE_GROUPS = {
     "bwd": ("vda_bwd.hip", "vda_bwd.h"), "vda+bwd": ("vda.hip", "vda_bwd.hip", "vda_bwd.h"),
 }
 SOURCE_SHA = {
-    "window": "b65573aca4b7cc64", "gemm": "ca60a1396242bbce", "vda": "71ddd2f45e486dc2", "mxfp8": "8cdcfa773199d9a4",
+    "window": "387d4af33907e61b", "gemm": "ca60a1396242bbce", "vda": "71ddd2f45e486dc2", "mxfp8": "8cdcfa773199d9a4",
     "bwd": "cdf096da5a826c0d", "vda+bwd": "633b208094b4abf4", "common": "9c829e344fbc21af"
 }
 

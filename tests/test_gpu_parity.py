@@ -139,6 +139,56 @@ def test_window_attn(vdn, name, cfg, sharp):
     assert e3 <= (1e-4 if cfg.dtype == "f32" else 1e-2)
 
 
+def test_window_attn_fixed_max_near_cap(vdn):
+    """bf16 head_dim 128 softmax branch with every query's score bound just
+    under the fixed-maximum cap (4 in log2 units), on clustered directions:
+    queries and keys lie near one of 8 shared unit directions, so each row
+    gives about an eighth of its keys a scaled score near +3.5 and the rest
+    near 0.  Every window work item then takes the fixed-maximum path (no
+    running maximum, q stored as bf16(c q)) on rows that are as uneven as
+    that path admits; the anchor and context items take the running one."""
+    cfg = VdnConfig(1, 2, 128, 17, 40, dtype="bf16", seed=91)
+    log("[window] fixed maximum near its cap")
+    B, H, T, N, d = cfg.batch, cfg.heads, cfg.frames, cfg.tokens_per_frame, cfg.head_dim
+    L = T * N
+    c2 = float(np.float32(np.log2(np.e) / np.sqrt(d)))
+    g = torch.Generator().manual_seed(cfg.seed)
+    dirs = torch.linalg.qr(torch.randn(d, 8, generator=g, dtype=torch.float64))[0].T   # 8 orthonormal rows
+
+    def clustered(scale):
+        pick = torch.randint(0, 8, (B, H, L), generator=g)
+        x = dirs[pick] + 0.25 * torch.randn(B, H, L, d, generator=g, dtype=torch.float64) / np.sqrt(d)
+        return (x / x.norm(dim=-1, keepdim=True) * scale).to(torch.bfloat16).view(B, H, T, N, d)
+
+    q = clustered(3.9 / c2)
+    k = clustered(1.0)
+    v = torch.randn(B, H, T, N, d, generator=g).to(torch.bfloat16)
+    # the kernel's bound, formed as it forms it (fp32, from the bf16 values)
+    qn = q.float().pow(2).sum(-1).sqrt()
+    kn = k.float().pow(2).sum(-1).flatten(2).max(dim=-1).values.sqrt()
+    bound = c2 * qn * kn[..., None, None]
+    assert float(bound.max()) < 4.0, float(bound.max())
+    inp = synth.make_inputs(cfg, device="cpu", with_layer=False)
+    inp.update(q=q, k=k, v=v)
+    inp = {kk: vv.cuda() for kk, vv in inp.items()}
+    out, lse = vdn.window_attn(vdn.shape_from_config(cfg), inp, with_lse=True)
+    torch.cuda.synchronize()
+    allowed = O.allowed_frames(T, cfg.chunk_frames, cfg.window_chunks, cfg.anchor_first, cfg.anchor_last)
+    qh, kh, vh = (np32(t).astype(np.float64) for t in (q, k, v))
+    ref = np.zeros((B, H, L, d))
+    ref_lse = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            ref[b, h], ref_lse[b, h] = O.window_attention(qh[b, h], kh[b, h], vh[b, h], allowed, 1 / np.sqrt(d))
+    ref_tok = np.transpose(ref, (0, 2, 1, 3)).reshape(B, L, H * d)
+    # a named stress input (its output peaks at about 5.4 x RMS); an fp64
+    # emulation of the path's roundings puts its plain error near 1.6e-2
+    check(log, "ungated", np32(out), ref_tok, cfg.dtype, stress=True)
+    e3 = float(np.max(np.abs(np32(lse) - ref_lse)))
+    log(f"  lse abs {e3:.3e}")
+    assert e3 <= 1e-2
+
+
 VDA = [
     ("B2H2_T17_N6_d32_f32", VdnConfig(2, 2, 32, 17, 6, dtype="f32", seed=41)),
     ("T13_N300_d128_f32", VdnConfig(1, 1, 128, 13, 300, dtype="f32", seed=42)),
