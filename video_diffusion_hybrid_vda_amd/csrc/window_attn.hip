@@ -381,8 +381,6 @@ constexpr float kRescaleSlack = 1.f;
 // is peaked; peaked rows, whose error rests on the dominant probability being
 // exactly 1, keep the running maximum.
 constexpr float kFixedMaxCap = 4.f;
-// fewest keys per (batch, head) for which dense items take the fixed maximum
-constexpr int kFixedDenseMinKeys = 1 << 16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -693,16 +691,12 @@ __global__ __launch_bounds__(256) void window_attn_bf16_d128_kernel(AttnParams p
       bnd[qt] = c2 * sqrtf(s2) * kn;
       worst = fmaxf(worst, bnd[qt]);
     }
-    // Dense items (anchor-frame and context queries over every key) take it
-    // only when their rows hold at least kFixedDenseMinKeys keys: with every
-    // score within +-bnd no key then carries more than 2^(2 bnd) / 2^16 <=
-    // 1/256 of the row's weight, so the rounding of single p values averages
-    // out as in the window rows.  Short dense rows, where one key can
-    // dominate without a p of exactly 1, keep the running maximum.  (Split
-    // partials need no common maximum: every split of a row uses 0.)
+    // dense items (anchor-frame and context queries over every key) keep the
+    // running maximum: their rows are long, and their outputs are merged
+    // over key splits
     const int lid = xcd_remap(blockIdx.x, p.total);
     const bool dense = lid - (lid / p.tiles_per_bh) * p.tiles_per_bh >= p.n_window_tiles;
-    const bool unsafe = (dense && p.Lt < kFixedDenseMinKeys) || __syncthreads_or(worst > kFixedMaxCap);
+    const bool unsafe = dense || __syncthreads_or(worst > kFixedMaxCap);
     if (tid == 0) p.fallback[blockIdx.x] = unsafe ? 1 : 0;
     if (unsafe) {
       // this workgroup's tiles go to the running-maximum launch; no load may
